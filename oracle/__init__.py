@@ -1,0 +1,9 @@
+"""Plain CPU oracle of the AdaLN DiT block (test infrastructure only).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s cpu_baseline
+leg may import this package.  The product library never does.
+"""
+from .dit_oracle import (  # noqa: F401
+    LN_EPS, MOD_CHUNKS, adaln_modulation, attention, block_forward, dequantize_int8,
+    gelu_tanh, layer_norm, linear, modulate, quantize_int8, softmax_rows, stack_forward,
+)
