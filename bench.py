@@ -1,0 +1,237 @@
+#!/usr/bin/env python3
+"""Throughput of one denoising step of the DiT: 50 stacked AdaLN DiT blocks at
+the 864x480x56-frame latent shape (N = 14x54x30 = 22680 tokens, D = 5120,
+40 heads x 128, MLP 13824, bf16), on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--layers L] [--no-cpu-baseline]
+
+Prints ONE JSON line on stdout.  `value` is the whole step's algorithmic
+TFLOP/s (attention 4 N^2 D, projections 2 N D (3D + D + 2F), AdaLN 12 D C per
+block), with weights and activations resident in HBM before timing starts.
+The timed region is bracketed by torch.cuda.synchronize(); every kernel
+launch is also bracketed by hipEvents recorded by the library itself on the
+launch stream (h3k_profiler), which gives the per-kernel durations used for
+the roofline of the dominant kernel.  The CPU baseline times the plain numpy
+oracle on the host cores on a bounded sample (see `cpu_baseline.sample`).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "DiT step ms + TFLOP/s (MFMA util %) at 22.7k latent tokens, bf16, 1 GPU"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def block_flops(N, D, F, C):
+    return {
+        "adaln": 2.0 * 6 * D * C,
+        "qkv": 2.0 * N * D * 3 * D,
+        "attention": 4.0 * N * N * D,
+        "out_proj": 2.0 * N * D * D,
+        "mlp_up": 2.0 * N * D * F,
+        "mlp_down": 2.0 * N * D * F,
+    }
+
+
+def ln_bytes(N, D, eb=2):
+    # read x row, write h row, read shift and scale (fp32)
+    return 2.0 * N * D * eb + 2.0 * D * 4
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--layers", type=int, default=50)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-layers45", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the DiT step runs on a single MI355X here "
+              "(multi-GPU sequence parallelism is a design note, not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import seeded_inputs as si
+    from video_diffusion_transformer_adaln_amd import binding as B
+    from video_diffusion_transformer_adaln_amd import runtime as R
+
+    B.lib()
+    shape = si.C3
+    N, D, F, C, H, d = shape.n_tokens, shape.hidden, shape.mlp_hidden, shape.cond_dim, shape.n_heads, shape.head_dim
+    L = args.layers
+    cfg = B.make_config(N, D, H, d, F, C, B.H3K_BF16, B.H3K_BF16, True)
+
+    # ---- inputs, resident in HBM (drawn on the device with torch's seeded generator)
+    t0 = time.time()
+    blocks = []
+    for l in range(L):
+        t = {}
+        for i, (name, shp) in enumerate(shape.weight_shapes().items()):
+            if name.startswith("b_"):
+                t[name] = torch.zeros(shp, dtype=torch.bfloat16, device="cuda")
+            else:
+                t[name] = si.torch_device_normal(shp, si.WEIGHT_STD, si.BASE_SEED, 1000 * l + i, "cuda",
+                                                 torch.bfloat16)
+        blocks.append(t)
+    x = si.torch_device_normal((N, D), 1.0, si.BASE_SEED, 999_000, "cuda", torch.bfloat16)
+    c = si.torch_device_normal((C,), 1.0, si.BASE_SEED, 999_001, "cuda", torch.bfloat16)
+    stack = R.DitStack(cfg, blocks)
+    out = torch.empty_like(x)
+    torch.cuda.synchronize()
+    log(f"inputs ready in {time.time() - t0:.1f} s; workspace {stack.workspace.numel() / 2**30:.2f} GiB")
+
+    # ---- warmup
+    for i in range(args.warmup):
+        stack.forward(x, c, out)
+        torch.cuda.synchronize()
+        log(f"warmup step {i + 1}/{args.warmup} done")
+
+    # ---- timed steps, with per-kernel events recorded by the library
+    prof = B.Profiler(capacity=8 * L * args.steps + 64)
+    stats = prof.stats()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record()
+    for i in range(args.steps):
+        stack.forward(x, c, out, stats=stats)
+    ev1.record()
+    torch.cuda.synchronize()
+    total_ms = ev0.elapsed_time(ev1)
+    ms_step = total_ms / args.steps
+    log(f"timed {args.steps} steps: {ms_step:.2f} ms/step")
+    kern = prof.summary()
+    prof.close()
+    if not torch.isfinite(out.float()).all():
+        log("non-finite output")
+        sys.exit(3)
+
+    ms45 = None
+    if not args.no_layers45 and L >= 45:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(args.steps):
+            stack.forward(x, c, out, n_layers=45)
+        e1.record()
+        torch.cuda.synchronize()
+        ms45 = e0.elapsed_time(e1) / args.steps
+        log(f"45-layer step: {ms45:.2f} ms")
+
+    fl = block_flops(N, D, F, C)
+    step_flops = L * sum(fl.values())
+    tflops = step_flops / (ms_step * 1e-3) / 1e12
+
+    per_kernel = {}
+    for name, v in kern.items():
+        if v["launches"] == 0:
+            continue
+        avg_ms = v["total_ms"] / v["launches"]
+        e = {"avg_ms": round(avg_ms, 4), "launches": v["launches"], "share": round(v["total_ms"] / total_ms, 4)}
+        if name in fl:
+            e["tflops"] = round(fl[name] / (avg_ms * 1e-3) / 1e12, 1)
+            e["mfma_frac"] = round(e["tflops"] / PEAK_BF16_TFLOPS, 4) if name != "adaln" else None
+        if name == "ln_mod":
+            e["gbs"] = round(ln_bytes(N, D) / (avg_ms * 1e-3) / 1e9, 1)
+        if name == "adaln":
+            e["gbs"] = round((6 * D * C * 2 + C * 2 + 6 * D * 4) / (avg_ms * 1e-3) / 1e9, 1)
+        per_kernel[name] = e
+    dom = max((k for k in per_kernel if k in fl and k != "adaln"), key=lambda k: kern[k]["total_ms"])
+    dom_avg = per_kernel[dom]["avg_ms"]
+    achieved = fl[dom] / (dom_avg * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "algorithmic_per_launch": f"{fl[dom] / 1e12:.3f} TFLOP"}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(step_flops, L)
+
+    result = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02^2) weights, zero biases; random init)",
+        "config": {"workload": f"denoising step: {L} stacked AdaLN DiT blocks, N=22680 tokens "
+                               "(14x54x30 latent of 864x480x56 frames), D=5120, 40x128 heads, F=13824, "
+                               "GELU-tanh, bf16, activation aliasing on",
+                   "layers": L, "tokens": N, "hidden": D, "heads": H, "head_dim": d, "mlp": F},
+        "mfma_util": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "ms_per_step_layers45": round(ms45, 2) if ms45 is not None else None,
+        "tflop_per_step": round(step_flops / 1e12, 2),
+        "kernels": per_kernel,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(step_flops, L):
+    """Time the numpy oracle on the host for one full-shape block.
+
+    The oracle's block cost is affine in the number of query rows it
+    computes (k and v for all tokens once, then per-row attention and MLP),
+    so it is timed for two row samples and extrapolated to all 22680 rows;
+    the step time is L times that block time."""
+    import oracle  # test infrastructure: CPU baseline only
+    import seeded_inputs as si
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([p.get("num_threads", 0) for p in threadpool_info()] + [1])
+    except Exception:
+        blas_threads = len(os.sched_getaffinity(0))
+    shape = si.C2
+    log("cpu baseline: generating one full-shape block on the host")
+    hx, hc = si.gen_activation(shape)
+    hw = si.gen_block_weights(shape, 0)
+    w = {k: v.values for k, v in hw.items()}
+    n = shape.n_tokens
+    samples = (256, 1024)
+    times = []
+    for r in samples:
+        rows = np.linspace(0, n - 1, r).astype(np.int64)
+        t0 = time.perf_counter()
+        oracle.block_forward(hx.values, hc.values, w, shape.n_heads, rows=rows)
+        times.append(time.perf_counter() - t0)
+        log(f"cpu baseline: {r} rows in {times[-1]:.2f} s")
+    slope = (times[1] - times[0]) / (samples[1] - samples[0])
+    t_block = times[0] + slope * (n - samples[0])
+    t_step = L * t_block
+    return {
+        "value": round(step_flops / t_step / 1e12, 4),
+        "unit": "TFLOP/s",
+        "ms_per_step": round(t_step * 1e3, 1),
+        "cores": int(blas_threads),
+        "kind": "oracle",
+        "sample": (f"one 864x480x56-frame block (the step's unit) timed for {samples[0]} and {samples[1]} "
+                   f"query rows (k, v for all {n} tokens), extrapolated affinely to {n} rows and times {L} "
+                   f"blocks; measured {times[0]:.2f} s and {times[1]:.2f} s; numpy fp32, BLAS threads = "
+                   f"{blas_threads}"),
+    }
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,87 @@
+"""Helpers for GPU tests: upload seeded inputs, run the library, sample rows.
+
+Inputs come from ``seeded_inputs`` on the host, so the oracle and the GPU see
+the same values; nothing here computes any part of the block.
+"""
+import sys
+
+import numpy as np
+
+import seeded_inputs as si
+
+ROWS_PER_SAMPLE = 48
+
+
+def flush(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def torch_mod():
+    import torch
+    return torch
+
+
+def has_gpu():
+    try:
+        import torch
+        return torch.cuda.device_count() > 0
+    except Exception:
+        return False
+
+
+def dev(ht):
+    from video_diffusion_transformer_adaln_amd import runtime as R
+    return R.upload(ht.storage, ht.dtype)
+
+
+def act_code(shape):
+    from video_diffusion_transformer_adaln_amd import binding as B
+    return B.H3K_F32 if shape.dtype == "f32" else B.H3K_BF16
+
+
+def config_for(shape, alias=True):
+    from video_diffusion_transformer_adaln_amd import binding as B
+    act = act_code(shape)
+    return B.make_config(shape.n_tokens, shape.hidden, shape.n_heads, shape.head_dim, shape.mlp_hidden,
+                         shape.cond_dim, act, B.H3K_INT8 if shape.int8_weights else act, alias)
+
+
+def sample_rows(n, count=ROWS_PER_SAMPLE, seed=5):
+    """Deterministic rows: the first few, the ragged tail and a random middle."""
+    rng = np.random.default_rng(seed)
+    head = list(range(min(n, 8)))
+    tail = list(range(max(0, n - 8), n))
+    mid = rng.choice(n, size=min(n, max(0, count - 16)), replace=False).tolist() if n > 16 else []
+    return np.array(sorted(set(head + tail + mid)), dtype=np.int64)
+
+
+def to_np(t):
+    torch = torch_mod()
+    if t.dtype == torch.bfloat16:
+        return t.float().cpu().numpy()
+    return t.cpu().numpy()
+
+
+def upload_block(shape, hw):
+    """Device tensors of one block; int8 matrices are quantised on the GPU.
+
+    Returns (device dict, oracle weight dict).  For int8 the oracle gets its
+    own quantisation of the same fp32 matrices; tests assert bit-equality of
+    the two quantisations separately."""
+    import oracle
+    from video_diffusion_transformer_adaln_amd import runtime as R
+    d = {}
+    ow = {}
+    for name, ht in hw.items():
+        if shape.int8_weights and name in si.MATRIX_NAMES:
+            w32 = R.upload(ht.storage, "f32")
+            q, s = R.quantize_int8(w32)
+            del w32
+            d[name] = q
+            d["s_" + name[2:]] = s
+            ow[name] = oracle.quantize_int8(ht.values)
+        else:
+            d[name] = dev(ht)
+            ow[name] = ht.values
+    return d, ow

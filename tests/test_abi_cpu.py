@@ -1,0 +1,198 @@
+"""CPU-side checks of the C ABI: the library loads, exports exactly what the
+header declares, plans its workspace correctly, and rejects every bad
+argument before touching the GPU.  No kernel is launched here: every call
+either fails validation or (valid arguments, no device) reports ERR_HIP,
+and the latter only runs on a machine without a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import video_diffusion_transformer_adaln_amd as h3k
+from video_diffusion_transformer_adaln_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "h3k.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(h3k_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = h3k.lib()
+    declared = _declared()
+    assert declared, "no declarations parsed"
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert sorted(B.EXPORTED) == declared
+
+
+def test_struct_sizes_match_header_layout():
+    assert ctypes.sizeof(B.DitConfig) == 40
+    assert ctypes.sizeof(B.DitBlockWeights) == 14 * 8
+    assert ctypes.sizeof(B.DitStats) == 40
+    assert ctypes.sizeof(B.DitPlanInfo) == 7 * 8 * 2 + 7 * 4 * 2 + 8 * 5 + 8
+
+
+def cfg_c2(**kw):
+    base = dict(n_tokens=22680, hidden=5120, n_heads=40, head_dim=128, mlp_hidden=13824, cond_dim=5120,
+                act_dtype=B.H3K_BF16)
+    base.update(kw)
+    return B.make_config(**base)
+
+
+def _live(info, t, s):
+    return info.first_step[t] <= s <= info.last_step[t]
+
+
+@pytest.mark.parametrize("alias", [True, False])
+@pytest.mark.parametrize("shape", [
+    dict(n_tokens=22680, hidden=5120, n_heads=40, head_dim=128, mlp_hidden=13824, cond_dim=5120, act_dtype=1),
+    dict(n_tokens=6144, hidden=3072, n_heads=24, head_dim=128, mlp_hidden=12288, cond_dim=3072, act_dtype=1),
+    dict(n_tokens=512, hidden=256, n_heads=4, head_dim=64, mlp_hidden=1024, cond_dim=256, act_dtype=0),
+    dict(n_tokens=1, hidden=128, n_heads=2, head_dim=64, mlp_hidden=64, cond_dim=8, act_dtype=1),
+    dict(n_tokens=333, hidden=320, n_heads=5, head_dim=64, mlp_hidden=2048, cond_dim=64, act_dtype=1),
+])
+def test_plan_no_live_overlap(shape, alias):
+    cfg = B.make_config(alias=alias, **shape)
+    info = h3k.h3k_dit_plan(cfg)
+    n = len(B.TENSOR_NAMES)
+    for t in range(n):
+        assert info.offset[t] % 256 == 0
+        assert info.offset[t] + info.bytes[t] <= info.workspace_bytes
+    for s in range(8):
+        live = [t for t in range(n) if _live(info, t, s)]
+        for i in live:
+            for j in live:
+                if i < j:
+                    a0, a1 = info.offset[i], info.offset[i] + info.bytes[i]
+                    b0, b1 = info.offset[j], info.offset[j] + info.bytes[j]
+                    assert a1 <= b0 or b1 <= a0, (B.TENSOR_NAMES[i], B.TENSOR_NAMES[j], s)
+    if alias:
+        assert info.workspace_bytes < info.unaliased_bytes
+        assert info.workspace_bytes >= info.peak_live_bytes
+    else:
+        assert info.workspace_bytes == info.unaliased_bytes
+    assert h3k.h3k_dit_workspace_size(cfg, 3) == info.workspace_bytes
+
+
+def test_plan_c2_sizes_and_layout():
+    """The 864x480x56-frame block: tensor sizes and the aliasing it yields."""
+    N, D, F = 22680, 5120, 13824
+    on = h3k.h3k_dit_plan(cfg_c2(alias=True))
+    off = h3k.h3k_dit_plan(cfg_c2(alias=False))
+    act = N * D * 2
+    assert on.bytes[1] == act and on.bytes[3] == act and on.bytes[4] == act and on.bytes[5] == act
+    assert on.bytes[6] == N * F * 2
+    assert on.bytes[2] == N * 2 * D * 2 + D * N * 2          # [Q | K] + V^T (22680 is a multiple of 8)
+    assert on.vt_pitch == N
+    # first fit: o and h2 reuse h's region; x1 sits at the start of the dead qkv; u follows x1
+    assert on.offset[3] == on.offset[1] and on.offset[5] == on.offset[1]
+    assert on.offset[4] == on.offset[2]
+    assert on.offset[6] == on.offset[4] + act
+    assert on.workspace_bytes == on.offset[6] + N * F * 2
+    assert off.workspace_bytes - on.workspace_bytes > 1_000_000_000      # > 1 GB saved
+    assert on.peak_live_bytes == on.workspace_bytes
+
+
+def test_env_switch_disables_aliasing(monkeypatch):
+    monkeypatch.setenv("H3K_DISABLE_ACTIVATION_ALIAS", "1")
+    info = h3k.h3k_dit_plan(cfg_c2(alias=True))
+    assert info.alias_activations == 0
+    assert info.workspace_bytes == info.unaliased_bytes
+    monkeypatch.delenv("H3K_DISABLE_ACTIVATION_ALIAS")
+    assert h3k.h3k_dit_plan(cfg_c2(alias=True)).alias_activations == 1
+
+
+# ---------------------------------------------------------------- validation
+FAKE = 0x7f0000000000          # never dereferenced: every call below fails before a launch
+
+
+def _weights(**over):
+    base = {f: FAKE + (i + 1) * (1 << 32) for i, f in enumerate(B.WEIGHT_FIELDS) if not f.startswith("s_")}
+    base.update(over)
+    return B.DitBlockWeights(*[base.get(f) for f in B.WEIGHT_FIELDS])
+
+
+def _block(cfg, weights=None, x=FAKE + (100 << 32), c=FAKE + (101 << 32), out=FAKE + (102 << 32),
+           ws=FAKE + (110 << 32), ws_bytes=None):
+    lib = h3k.lib()
+    if ws_bytes is None:
+        ws_bytes = h3k.h3k_dit_workspace_size(cfg) if lib.h3k_dit_workspace_size(
+            ctypes.byref(cfg), 1, ctypes.byref(ctypes.c_uint64())) == 0 else 1 << 40
+    w = weights if weights is not None else _weights()
+    return lib.h3k_dit_block_forward(ctypes.byref(cfg), ctypes.byref(w), x, c, out, ws, ws_bytes, None, None)
+
+
+def test_reject_null_config_and_pointers():
+    lib = h3k.lib()
+    assert lib.h3k_dit_block_forward(None, None, 0, 0, 0, 0, 0, None, None) == B.H3K_ERR_NULL
+    assert _block(cfg_c2(), x=None) == B.H3K_ERR_NULL
+    assert _block(cfg_c2(), weights=_weights(w_qkv=None)) == B.H3K_ERR_NULL
+    assert "w_qkv" in h3k.last_error()
+
+
+def test_reject_bad_shapes_and_dtypes():
+    assert _block(cfg_c2(hidden=5000)) == B.H3K_ERR_SHAPE                        # D != H*d
+    assert _block(cfg_c2(n_tokens=0)) == B.H3K_ERR_SHAPE
+    assert _block(cfg_c2(head_dim=96, n_heads=40, hidden=3840)) == B.H3K_ERR_UNSUPPORTED
+    assert _block(cfg_c2(mlp_hidden=13800)) == B.H3K_ERR_UNSUPPORTED
+    assert _block(cfg_c2(act_dtype=B.H3K_INT8)) == B.H3K_ERR_UNSUPPORTED
+    assert _block(cfg_c2(act_dtype=7)) == B.H3K_ERR_DTYPE
+    assert _block(cfg_c2(act_dtype=B.H3K_F32, weight_dtype=B.H3K_INT8)) == B.H3K_ERR_UNSUPPORTED
+    assert _block(cfg_c2(ln_eps=0.0)) == B.H3K_ERR_SHAPE
+
+
+def test_reject_int8_without_scales():
+    cfg = cfg_c2(weight_dtype=B.H3K_INT8)
+    assert _block(cfg) == B.H3K_ERR_NULL
+    assert "scale" in h3k.last_error()
+
+
+def test_reject_misalignment_workspace_overlap():
+    cfg = cfg_c2()
+    assert _block(cfg, x=FAKE + (100 << 32) + 4) == B.H3K_ERR_ALIGN
+    assert _block(cfg, ws=FAKE + (110 << 32) + 64) == B.H3K_ERR_ALIGN
+    need = h3k.h3k_dit_workspace_size(cfg)
+    assert _block(cfg, ws_bytes=need - 1) == B.H3K_ERR_WORKSPACE
+    assert _block(cfg, out=FAKE + (100 << 32) + 4096) == B.H3K_ERR_OVERLAP          # out inside x
+    assert _block(cfg, out=FAKE + (110 << 32) + 1024) == B.H3K_ERR_OVERLAP          # out inside workspace
+    w = _weights(w_up=FAKE + (110 << 32) + 4096)                                    # weight inside workspace
+    assert _block(cfg, weights=w) == B.H3K_ERR_OVERLAP
+
+
+def test_reject_bad_kernel_level_arguments():
+    lib = h3k.lib()
+    # linear: k not a multiple of 64 for bf16
+    assert lib.h3k_linear(1, 1, 10, 64, 100, FAKE, 100, FAKE + (1 << 32), 100, None, None, 0, None, 0, None,
+                          FAKE + (2 << 32), 64, None, 0, 64, None) == B.H3K_ERR_SHAPE
+    # gated residual without gate
+    assert lib.h3k_linear(1, 1, 10, 64, 64, FAKE, 64, FAKE + (1 << 32), 64, None, None, 2, FAKE + (3 << 32), 64,
+                          None, FAKE + (2 << 32), 64, None, 0, 64, None) == B.H3K_ERR_NULL
+    # transposed part with GELU is not supported
+    assert lib.h3k_linear(1, 1, 10, 64, 64, FAKE, 64, FAKE + (1 << 32), 64, None, None, 1, None, 0, None,
+                          FAKE + (2 << 32), 64, FAKE + (4 << 32), 16, 32, None) == B.H3K_ERR_UNSUPPORTED
+    # attention: head_dim 32, pitch too small
+    assert lib.h3k_attention(1, 100, 2, 32, FAKE, 64, FAKE, 64, FAKE, 104, FAKE, 64, None) == B.H3K_ERR_UNSUPPORTED
+    assert lib.h3k_attention(1, 100, 2, 64, FAKE, 128, FAKE + (1 << 32), 128, FAKE + (2 << 32), 96,
+                             FAKE + (3 << 32), 128, None) == B.H3K_ERR_SHAPE
+    # quantiser: int8 source, overlapping q / w
+    assert lib.h3k_quantize_weights_int8(FAKE, 2, 4, 64, FAKE + (1 << 32), FAKE + (2 << 32), None) == B.H3K_ERR_UNSUPPORTED
+    assert lib.h3k_quantize_weights_int8(FAKE, 0, 4, 64, FAKE + 64, FAKE + (2 << 32), None) == B.H3K_ERR_OVERLAP
+    assert lib.h3k_ln_modulate(1, 4, 100, 1e-6, FAKE, 100, FAKE, FAKE, FAKE + (1 << 32), 100, None) == B.H3K_ERR_SHAPE
+    assert lib.h3k_adaln_modulation(1, 10, 12, FAKE, None, FAKE, FAKE + (1 << 32), None) == B.H3K_ERR_SHAPE
+
+
+def _no_gpu():
+    import torch
+    return torch.cuda.device_count() == 0
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="only meaningful (and only safe) without a GPU")
+def test_valid_arguments_without_device_report_hip_error():
+    assert _block(cfg_c2()) == B.H3K_ERR_HIP
+    assert "device" in h3k.last_error()

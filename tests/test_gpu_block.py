@@ -1,0 +1,211 @@
+"""Block- and stack-level parity of the HIP path against the CPU oracle.
+
+  * the small fp32 block, every element (fp32 vs fp32: 1e-4);
+  * the 512x512x22-frame block (N=6144, D=3072), every element;
+  * the 864x480x56-frame block (N=22680, D=5120) and its int8-weight
+    variant, on sampled token rows (the oracle computes k and v for all
+    tokens, the rest for those rows);
+  * aliasing on vs off: byte-identical outputs, with the workspace filled
+    with 0xFF (bf16/fp32 NaN) before each run so that a read of an unwritten
+    or stale aliased byte would show;
+  * the layer stack: a 50-block bf16 stack at reduced width against the
+    oracle, and at full width the layer-prefix property (the state after 45
+    blocks is the output of the 45-block stack) and call-to-call determinism.
+Tolerance for bf16 paths: relative L2 <= 2e-2 per output tensor.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import seeded_inputs as si
+from gpu_util import config_for, dev, flush, has_gpu, sample_rows, to_np, upload_block
+from helpers import rel_l2
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not has_gpu(), reason="needs a GPU")]
+
+TOL = 2e-2
+
+
+@pytest.fixture(scope="module")
+def R():
+    from video_diffusion_transformer_adaln_amd import binding, runtime
+    binding.lib()
+    return runtime
+
+
+def _run_block(R, shape, dw, xd, cd, alias=True, poison=True, stats=None):
+    import torch
+    from video_diffusion_transformer_adaln_amd import binding as B
+    cfg = config_for(shape, alias)
+    ws = R.alloc_workspace(cfg)
+    if poison:
+        ws.fill_(0xFF)
+    out = torch.empty_like(xd)
+    B.h3k_dit_block_forward(cfg, B.make_weights(dw), xd, cd, out, ws, stats=stats)
+    torch.cuda.synchronize()
+    return out
+
+
+def _block_case(shape, bias_std=0.0):
+    hx, hc = si.gen_activation(shape)
+    hw = si.gen_block_weights(shape, 0, bias_std=bias_std)
+    return hx, hc, hw
+
+
+def test_block_c0_fp32_full(R):
+    shape = si.C0
+    flush(f"block {shape.name}")
+    hx, hc, hw = _block_case(shape, bias_std=0.05)
+    dw, ow = upload_block(shape, hw)
+    from video_diffusion_transformer_adaln_amd import binding as B
+    st = B.DitStats()
+    out = _run_block(R, shape, dw, dev(hx), dev(hc), stats=st)
+    ref = oracle.block_forward(hx.values, hc.values, ow, shape.n_heads)
+    got = to_np(out)
+    assert st.dispatches == 8
+    assert rel_l2(got, ref) < 1e-4
+
+
+@pytest.mark.parametrize("n", [1, 37, 300])
+def test_block_ragged_bf16_full(R, n):
+    shape = si.custom_shape(f"ragged{n}", 950 + n, n, 4, 128, 1024, "bf16")
+    flush(f"block {shape.name}")
+    hx, hc, hw = _block_case(shape, bias_std=0.05)
+    dw, ow = upload_block(shape, hw)
+    got = to_np(_run_block(R, shape, dw, dev(hx), dev(hc)))
+    ref = oracle.block_forward(hx.values, hc.values, ow, shape.n_heads)
+    assert np.isfinite(got).all()
+    assert rel_l2(got, ref) < TOL
+
+
+def test_block_c1_full(R):
+    shape = si.C1
+    flush(f"block {shape.name}")
+    hx, hc, hw = _block_case(shape)
+    dw, ow = upload_block(shape, hw)
+    got = to_np(_run_block(R, shape, dw, dev(hx), dev(hc)))
+    ref = oracle.block_forward(hx.values, hc.values, ow, shape.n_heads)
+    err = rel_l2(got, ref)
+    flush(f"  rel_l2 = {err:.3e}")
+    assert err < TOL
+
+
+@pytest.fixture(scope="module")
+def c2_case():
+    flush("generating the 864x480x56-frame block inputs")
+    return _block_case(si.C2)
+
+
+def test_block_c2_sampled_rows(R, c2_case):
+    shape = si.C2
+    flush(f"block {shape.name}")
+    hx, hc, hw = c2_case
+    dw, ow = upload_block(shape, hw)
+    got = to_np(_run_block(R, shape, dw, dev(hx), dev(hc)))
+    rows = sample_rows(shape.n_tokens)
+    ref = oracle.block_forward(hx.values, hc.values, ow, shape.n_heads, rows=rows)
+    assert np.isfinite(got).all()
+    err = rel_l2(got[rows], ref)
+    flush(f"  rel_l2 = {err:.3e}")
+    assert err < TOL
+
+
+def test_alias_on_off_byte_identical_c2(R, c2_case):
+    import torch
+    shape = si.C2
+    flush("alias on/off")
+    hx, hc, hw = c2_case
+    dw, _ = upload_block(shape, hw)
+    xd, cd = dev(hx), dev(hc)
+    on = _run_block(R, shape, dw, xd, cd, alias=True)
+    off = _run_block(R, shape, dw, xd, cd, alias=False)
+    again = _run_block(R, shape, dw, xd, cd, alias=True)
+    assert torch.equal(on.view(torch.int16), off.view(torch.int16))
+    assert torch.equal(on.view(torch.int16), again.view(torch.int16))
+
+
+def test_block_c4_int8_sampled_rows(R):
+    shape = si.C4
+    flush(f"block {shape.name}")
+    hx, hc, hw = _block_case(shape)
+    dw, ow = upload_block(shape, hw)
+    # the GPU quantiser and the oracle's agree bit for bit
+    for name in si.MATRIX_NAMES:
+        q, s = ow[name]
+        assert np.array_equal(dw[name].cpu().numpy(), q)
+        assert np.array_equal(dw["s_" + name[2:]].cpu().numpy(), s)
+    got = to_np(_run_block(R, shape, dw, dev(hx), dev(hc)))
+    rows = sample_rows(shape.n_tokens)
+    ref = oracle.block_forward(hx.values, hc.values, ow, shape.n_heads, rows=rows)
+    err = rel_l2(got[rows], ref)
+    flush(f"  rel_l2 = {err:.3e}")
+    assert err < TOL
+
+
+def test_stack50_reduced_width_vs_oracle(R):
+    """50 blocks (bf16 residual stream between blocks) at N=512, D=512."""
+    import torch
+    from video_diffusion_transformer_adaln_amd import binding as B
+    shape = si.custom_shape("stack50", 960, 512, 4, 128, 2048, "bf16", n_blocks=50)
+    flush("stack of 50 reduced-width blocks")
+    hx, hc = si.gen_activation(shape)
+    blocks_h = [si.gen_block_weights(shape, l) for l in range(50)]
+    up = [upload_block(shape, hw) for hw in blocks_h]
+    stack = R.DitStack(config_for(shape), [u[0] for u in up])
+    stack.workspace.fill_(0xFF)
+    xd, cd = dev(hx), dev(hc)
+    out = torch.empty_like(xd)
+    st = B.DitStats()
+    stack.forward(xd, cd, out, stats=st)
+    torch.cuda.synchronize()
+    assert st.dispatches == 8 * 50
+    ref = oracle.stack_forward(hx.values, hc.values, [u[1] for u in up], shape.n_heads)
+    err = rel_l2(to_np(out), ref)
+    flush(f"  rel_l2 after 50 blocks = {err:.3e}")
+    assert err < TOL
+    # L = 1 is the block call
+    one = torch.empty_like(xd)
+    stack.forward(xd, cd, one, n_layers=1)
+    single = _run_block(R, shape, up[0][0], xd, cd)
+    assert torch.equal(one.view(torch.int16), single.view(torch.int16))
+
+
+@pytest.fixture(scope="module")
+def c3_stack(R):
+    """50 blocks at the full 864x480x56-frame shape, weights drawn on the device
+    (same recipe, no oracle comparison)."""
+    import torch
+    shape = si.C3
+    flush("drawing 50 full-size blocks on the device")
+    D, F, C = shape.hidden, shape.mlp_hidden, shape.cond_dim
+    blocks = []
+    for l in range(50):
+        t = {}
+        for i, (name, shp) in enumerate(shape.weight_shapes().items()):
+            if name.startswith("b_"):
+                continue
+            t[name] = si.torch_device_normal(shp, si.WEIGHT_STD, 42, 1000 * l + i, "cuda", torch.bfloat16)
+        blocks.append(t)
+    x = si.torch_device_normal((shape.n_tokens, D), 1.0, 42, 999_000, "cuda", torch.bfloat16)
+    c = si.torch_device_normal((C,), 1.0, 42, 999_001, "cuda", torch.bfloat16)
+    stack = R.DitStack(config_for(shape), blocks)
+    return stack, x, c
+
+
+def test_c3_layer_prefix_and_determinism(R, c3_stack):
+    import torch
+    from video_diffusion_transformer_adaln_amd import binding as B
+    stack, x, c = c3_stack
+    flush("c3: 45-block prefix, then blocks 45..49")
+    y45 = torch.empty_like(x)
+    stack.forward(x, c, y45, n_layers=45)
+    y50 = torch.empty_like(x)
+    stack.forward(x, c, y50)
+    tail = torch.empty_like(x)
+    B.h3k_dit_stack_forward(stack.cfg, stack.structs[45:], y45, c, tail, stack.workspace)
+    again = torch.empty_like(x)
+    stack.forward(x, c, again)
+    torch.cuda.synchronize()
+    assert torch.isfinite(y50.float()).all()
+    assert torch.equal(tail.view(torch.int16), y50.view(torch.int16))
+    assert torch.equal(again.view(torch.int16), y50.view(torch.int16))

@@ -1,0 +1,230 @@
+"""Kernel-level parity of the HIP path against the CPU oracle's stages.
+
+Each kernel is called through the C ABI on seeded inputs and compared with
+the oracle function of the same stage: element-wise at small, ragged sizes
+(several tiles plus a tail), and on sampled rows at the full 864x480x56-frame
+shapes in the launch configuration the block uses.
+
+Tolerances (relative L2 per output tensor): the bf16 kernels read
+bf16-exact inputs, accumulate in fp32 and round once at the store, which
+alone gives an rms relative error of about 2^-9/sqrt(3) ~ 1.1e-3; attention
+adds one bf16 rounding of the probabilities.  The bound used is 1e-2 (the
+block-level bound is 2e-2).  fp32 kernels differ from the oracle only in
+summation order: 1e-5.  The int8 quantiser must be bit-exact.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import seeded_inputs as si
+from gpu_util import dev, flush, has_gpu, sample_rows, to_np
+from helpers import rel_l2
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not has_gpu(), reason="needs a GPU")]
+
+BF16_TOL = 1e-2
+F32_TOL = 1e-5
+
+
+@pytest.fixture(scope="module")
+def B():
+    from video_diffusion_transformer_adaln_amd import binding
+    binding.lib()
+    return binding
+
+
+def _f32(shape, std, cid, tensor="x", block=0):
+    return si.normal_f32(shape, std, 42, cid, block, tensor)
+
+
+def _ht(a, dtype):
+    return si._finish(np.ascontiguousarray(a, dtype=np.float32), dtype)
+
+
+# ------------------------------------------------------------------ AdaLN GEMV
+
+@pytest.mark.parametrize("rows,cols,dtype", [(6 * 5120, 5120, "bf16"), (6 * 256, 256, "f32"), (72, 24, "bf16"),
+                                             (6 * 3072, 3072, "bf16")])
+def test_adaln_gemv(B, rows, cols, dtype):
+    import torch
+    flush(f"adaln gemv rows={rows} cols={cols} {dtype}")
+    w = _ht(_f32((rows, cols), 0.02, 800, "w_ada"), dtype)
+    b = _ht(_f32((rows,), 0.1, 800, "b_ada"), dtype)
+    c = _ht(_f32((cols,), 1.0, 800, "c"), dtype)
+    mod = torch.empty(rows, dtype=torch.float32, device="cuda")
+    code = B.H3K_F32 if dtype == "f32" else B.H3K_BF16
+    B.h3k_adaln_modulation(code, rows, cols, dev(w), dev(b), dev(c), mod)
+    torch.cuda.synchronize()
+    ref = np.concatenate(list(oracle.adaln_modulation(w.values, b.values, c.values).values()))
+    assert rel_l2(to_np(mod), ref) < 1e-5
+
+
+# ------------------------------------------------------------------ LayerNorm + modulation
+
+@pytest.mark.parametrize("n,D,dtype,full", [(22680, 5120, "bf16", False), (512, 256, "f32", True),
+                                             (37, 320, "bf16", True), (1, 64, "bf16", True),
+                                             (6144, 3072, "bf16", False), (100, 8192, "bf16", True),
+                                             (3, 8192, "f32", True)])
+def test_ln_modulate(B, n, D, dtype, full):
+    import torch
+    flush(f"ln_modulate n={n} D={D} {dtype}")
+    x = _ht(_f32((n, D), 1.0, 801) * 3 + 0.5, dtype)
+    shift = _f32((D,), 0.5, 801, "b_ada")
+    scale = _f32((D,), 0.5, 801, "b_qkv")
+    xd = dev(x)
+    out = torch.empty_like(xd)
+    code = B.H3K_F32 if dtype == "f32" else B.H3K_BF16
+    B.h3k_ln_modulate(code, n, D, 1e-6, xd, D, torch.from_numpy(shift).cuda(), torch.from_numpy(scale).cuda(),
+                      out, D)
+    torch.cuda.synchronize()
+    rows = np.arange(n) if full else sample_rows(n)
+    ref = oracle.modulate(oracle.layer_norm(x.values[rows]), shift, scale)
+    got = to_np(out)[rows]
+    assert rel_l2(got, ref) < (F32_TOL if dtype == "f32" else BF16_TOL / 2)
+
+
+# ------------------------------------------------------------------ GEMMs
+
+def _linear_ref(x, w, b, epi, residual=None, gate=None):
+    z = oracle.linear(x, w, b)
+    if epi == 1:
+        return oracle.gelu_tanh(z)
+    if epi == 2:
+        return residual + gate * z
+    return z
+
+
+GEMM_CASES = [
+    # m, n, k, epilogue, dtype, int8, split, full
+    (300, 320, 128, 0, "bf16", False, None, True),
+    (300, 320, 128, 1, "bf16", False, None, True),
+    (300, 320, 128, 2, "bf16", False, None, True),
+    (1, 64, 64, 0, "bf16", False, None, True),
+    (513, 768, 256, 0, "bf16", False, 512, True),     # Q|K row-major, V transposed (straddling tile)
+    (300, 1536, 256, 0, "bf16", False, 1024, True),   # split on a tile boundary
+    (300, 320, 128, 0, "bf16", True, None, True),
+    (300, 576, 192, 2, "bf16", True, None, True),
+    (97, 1024, 256, 0, "bf16", True, 512, True),
+    (512, 768, 256, 0, "f32", False, 512, True),
+    (512, 1024, 256, 1, "f32", False, None, True),
+    (512, 256, 1024, 2, "f32", False, None, True),
+    (22680, 15360, 5120, 0, "bf16", False, 10240, False),   # QKV projection
+    (22680, 5120, 5120, 2, "bf16", False, None, False),     # out projection
+    (22680, 13824, 5120, 1, "bf16", False, None, False),    # MLP up
+    (22680, 5120, 13824, 2, "bf16", False, None, False),    # MLP down
+    (22680, 13824, 5120, 1, "bf16", True, None, False),     # MLP up, int8 weights
+    (22680, 15360, 5120, 0, "bf16", True, 10240, False),    # QKV, int8 weights
+]
+
+
+@pytest.mark.parametrize("m,n,k,epi,dtype,int8,split,full", GEMM_CASES)
+def test_linear(B, m, n, k, epi, dtype, int8, split, full):
+    import torch
+    flush(f"linear m={m} n={n} k={k} epi={epi} {dtype} int8={int8} split={split}")
+    cid = 810 + epi
+    x = _ht(_f32((m, k), 1.0, cid), dtype)
+    w32 = _f32((n, k), 0.02, cid, "w_up")
+    bias = _ht(_f32((n,), 0.05, cid, "b_up"), dtype)
+    split = n if split is None else split
+    code = B.H3K_F32 if dtype == "f32" else B.H3K_BF16
+    if int8:
+        q_ref, s_ref = oracle.quantize_int8(w32)
+        from video_diffusion_transformer_adaln_amd import runtime as R
+        q, s = R.quantize_int8(torch.from_numpy(w32).cuda())
+        torch.cuda.synchronize()
+        assert np.array_equal(q.cpu().numpy(), q_ref) and np.array_equal(s.cpu().numpy(), s_ref)
+        wd, wcode, w_ref = q, B.H3K_INT8, oracle.dequantize_int8(q_ref, s_ref)
+        sd = s
+    else:
+        wt = _ht(w32, dtype)
+        wd, wcode, w_ref, sd = dev(wt), code, wt.values, None
+    res = gate = None
+    resd = gated = None
+    if epi == 2:
+        res = _ht(_f32((m, split), 1.0, cid, "x", 1), dtype)
+        gate = _f32((split,), 0.5, cid, "b_down")
+        resd, gated = dev(res), torch.from_numpy(gate).cuda()
+    xd = dev(x)
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    y = torch.full((m, split), float("nan"), dtype=tdt, device="cuda")
+    ldyt = ((m + 7) // 8) * 8
+    yt = torch.full((n - split, ldyt), float("nan"), dtype=tdt, device="cuda") if split < n else None
+    B.h3k_linear(code, wcode, m, n, k, xd, k, wd, k, sd, dev(bias), epi, resd, split, gated, y, split,
+                 yt, ldyt if yt is not None else 0, split)
+    torch.cuda.synchronize()
+    rows = np.arange(m) if full else sample_rows(m)
+    if epi == 2:
+        ref = _linear_ref(x.values[rows], w_ref, bias.values, 2, res.values[rows], gate)
+    else:
+        ref = _linear_ref(x.values[rows], w_ref, bias.values, epi)
+    got = to_np(y)[rows]
+    tol = F32_TOL if dtype == "f32" else BF16_TOL / 2
+    assert np.isfinite(got).all()
+    assert rel_l2(got, ref[:, :split] if split < n else ref) < tol
+    if split < n:
+        got_t = to_np(yt)[:, :m].T[rows]
+        assert np.isfinite(got_t).all()
+        assert rel_l2(got_t, ref[:, split:]) < tol
+        assert np.isnan(to_np(yt)[:, m:]).all()                # padding columns untouched
+
+
+# ------------------------------------------------------------------ attention
+
+ATTN_CASES = [
+    # n, heads, head_dim, dtype, full
+    (1, 2, 128, "bf16", True),
+    (37, 2, 128, "bf16", True),
+    (300, 3, 64, "bf16", True),
+    (1000, 2, 128, "bf16", True),
+    (513, 4, 64, "f32", True),
+    (512, 4, 64, "f32", True),
+    (100, 2, 128, "f32", True),
+    (6144, 24, 128, "bf16", False),
+    (22680, 40, 128, "bf16", False),
+    (9000, 40, 64, "bf16", False),
+]
+
+
+@pytest.mark.parametrize("n,heads,hd,dtype,full", ATTN_CASES)
+def test_attention(B, n, heads, hd, dtype, full):
+    import torch
+    flush(f"attention n={n} heads={heads} d={hd} {dtype}")
+    D = heads * hd
+    # q, k scaled so that logits have std ~ 3 (peaked, like the block's)
+    q = _ht(_f32((n, D), 1.0, 820, "x") * 0.6, dtype)
+    k = _ht(_f32((n, D), 1.0, 820, "c") * 0.6, dtype)
+    v = _ht(_f32((n, D), 1.0, 820, "w_qkv"), dtype)
+    ldvt = ((n + 7) // 8) * 8
+    vt = np.zeros((D, ldvt), dtype=np.float32)
+    vt[:, :n] = v.values.T
+    code = B.H3K_F32 if dtype == "f32" else B.H3K_BF16
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    vtd = torch.from_numpy(vt).to(tdt).cuda()
+    if ldvt > n:
+        vtd[:, n:] = float("nan")        # padding must never reach the output
+    o = torch.full((n, D), float("nan"), dtype=tdt, device="cuda")
+    B.h3k_attention(code, n, heads, hd, dev(q), D, dev(k), D, vtd, ldvt, o, D)
+    torch.cuda.synchronize()
+    rows = np.arange(n) if full else sample_rows(n)
+    ref = oracle.attention(q.values[rows], k.values, v.values, heads)
+    got = to_np(o)[rows]
+    assert np.isfinite(got).all()
+    assert rel_l2(got, ref) < (F32_TOL if dtype == "f32" else BF16_TOL)
+
+
+# ------------------------------------------------------------------ int8 quantiser
+
+@pytest.mark.parametrize("rows,cols,dtype", [(15360, 5120, "f32"), (5120, 13824, "f32"), (300, 77, "f32"),
+                                             (257, 1000, "bf16"), (3, 1, "f32")])
+def test_quantize_int8_bit_exact(B, rows, cols, dtype):
+    import torch
+    flush(f"quantize rows={rows} cols={cols} {dtype}")
+    w = _f32((rows, cols), 0.02, 830, "w_up")
+    w[min(1, rows - 1)] = 0.0                      # a zero row
+    ht = _ht(w, dtype)
+    from video_diffusion_transformer_adaln_amd import runtime as R
+    q, s = R.quantize_int8(dev(ht))
+    torch.cuda.synchronize()
+    q_ref, s_ref = oracle.quantize_int8(ht.values)
+    assert np.array_equal(s.cpu().numpy(), s_ref)
+    assert np.array_equal(q.cpu().numpy(), q_ref)

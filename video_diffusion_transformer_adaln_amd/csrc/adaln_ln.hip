@@ -1,0 +1,181 @@
+// AdaLN modulation GEMV and the fused LayerNorm + AdaLN modulation kernel.
+//
+// Both are bound by HBM bandwidth: the GEMV streams the [6D, C] AdaLN matrix
+// once (the modulation precompute of the h3.c memory-techniques page,
+// technique 3), and the LayerNorm reads one activation row and writes one.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace h3k {
+
+// ---------------------------------------------------------------------------
+// mod[row] = sum_k W[row, k] c[k] + b[row].  One wave per output row, 16-byte
+// loads along k; c is staged once per workgroup in LDS as fp32.  The sum
+// order is fixed by (lane, iteration), so results are deterministic.
+template <typename T>
+__global__ __launch_bounds__(256) void adaln_gemv_kernel(const T* __restrict__ w, const T* __restrict__ b,
+                                                         const T* __restrict__ c, float* __restrict__ mod,
+                                                         int rows, int cols) {
+  extern __shared__ float c_lds[];
+  for (int i = threadIdx.x; i < cols; i += blockDim.x) c_lds[i] = to_f32(c[i]);
+  __syncthreads();
+  const int lane = threadIdx.x % kWave;
+  const int row = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  if (row >= rows) return;
+  constexpr int V = 16 / sizeof(T);
+  const T* wr = w + (int64_t)row * cols;
+  float acc = 0.f;
+#pragma unroll 4
+  for (int k0 = lane * V; k0 < cols; k0 += kWave * V) {
+    const u32x4 raw = *reinterpret_cast<const u32x4*>(wr + k0);
+    const T* e = reinterpret_cast<const T*>(&raw);
+#pragma unroll
+    for (int j = 0; j < V; ++j) acc += to_f32(e[j]) * c_lds[k0 + j];
+  }
+  acc = wave_sum(acc);
+  if (lane == 0) mod[row] = acc + (b ? to_f32(b[row]) : 0.f);
+}
+
+hipError_t launch_adaln_gemv(DType dt, int rows, int cols, const void* w, const void* b, const void* c,
+                             float* mod, hipStream_t stream) {
+  const dim3 block(256), grid((rows + 3) / 4);
+  const size_t lds = sizeof(float) * (size_t)cols;
+  if (dt == kBF16)
+    adaln_gemv_kernel<bf16><<<grid, block, lds, stream>>>((const bf16*)w, (const bf16*)b, (const bf16*)c, mod,
+                                                          rows, cols);
+  else
+    adaln_gemv_kernel<float><<<grid, block, lds, stream>>>((const float*)w, (const float*)b, (const float*)c,
+                                                           mod, rows, cols);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// out = LN(x) (1 + scale) + shift.  One wave per row; the row is held in
+// registers (MAXC 16-byte chunks per lane), so mean and the biased variance
+// are two exact passes over registers, each closed by a wave reduction.
+template <typename T, int MAXC>
+__global__ __launch_bounds__(256) void ln_modulate_kernel(const T* __restrict__ x, int64_t ldx,
+                                                          const float* __restrict__ shift,
+                                                          const float* __restrict__ scale, T* __restrict__ out,
+                                                          int64_t ldo, int n, int D, float eps) {
+  constexpr int V = 16 / sizeof(T);
+  const int lane = threadIdx.x % kWave;
+  const int row = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  if (row >= n) return;
+  const int chunks = D / V;
+  const T* xr = x + (int64_t)row * ldx;
+  float v[MAXC][V];
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i) {
+    const int ch = lane + i * kWave;
+    if (ch < chunks) {
+      const u32x4 raw = *reinterpret_cast<const u32x4*>(xr + ch * V);
+      const T* e = reinterpret_cast<const T*>(&raw);
+#pragma unroll
+      for (int j = 0; j < V; ++j) { v[i][j] = to_f32(e[j]); s += v[i][j]; }
+    } else {
+#pragma unroll
+      for (int j = 0; j < V; ++j) v[i][j] = 0.f;
+    }
+  }
+  const float mean = wave_sum(s) / (float)D;
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i) {
+    const int ch = lane + i * kWave;
+    if (ch < chunks) {
+#pragma unroll
+      for (int j = 0; j < V; ++j) { const float dlt = v[i][j] - mean; ss += dlt * dlt; }
+    }
+  }
+  const float var = wave_sum(ss) / (float)D;
+  const float rstd = 1.0f / sqrtf(var + eps);
+  T* orow = out + (int64_t)row * ldo;
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i) {
+    const int ch = lane + i * kWave;
+    if (ch < chunks) {
+      const int c0 = ch * V;
+      u32x4 raw;
+      T* e = reinterpret_cast<T*>(&raw);
+#pragma unroll
+      for (int j = 0; j < V; ++j)
+        e[j] = from_f32<T>((v[i][j] - mean) * rstd * (1.0f + scale[c0 + j]) + shift[c0 + j]);
+      *reinterpret_cast<u32x4*>(orow + c0) = raw;
+    }
+  }
+}
+
+template <typename T, int MAXC>
+static void ln_launch(int n, int D, float eps, const void* x, int64_t ldx, const float* shift,
+                      const float* scale, void* out, int64_t ldo, hipStream_t stream) {
+  ln_modulate_kernel<T, MAXC><<<dim3((n + 3) / 4), dim3(256), 0, stream>>>(
+      (const T*)x, ldx, shift, scale, (T*)out, ldo, n, D, eps);
+}
+
+template <typename T>
+static void ln_dispatch(int n, int D, float eps, const void* x, int64_t ldx, const float* shift,
+                        const float* scale, void* out, int64_t ldo, hipStream_t stream) {
+  constexpr int V = 16 / sizeof(T);
+  const int per_lane = (D / V + kWave - 1) / kWave;
+  if (per_lane <= 2)       ln_launch<T, 2>(n, D, eps, x, ldx, shift, scale, out, ldo, stream);
+  else if (per_lane <= 4)  ln_launch<T, 4>(n, D, eps, x, ldx, shift, scale, out, ldo, stream);
+  else if (per_lane <= 6)  ln_launch<T, 6>(n, D, eps, x, ldx, shift, scale, out, ldo, stream);
+  else if (per_lane <= 8)  ln_launch<T, 8>(n, D, eps, x, ldx, shift, scale, out, ldo, stream);
+  else if (per_lane <= 10) ln_launch<T, 10>(n, D, eps, x, ldx, shift, scale, out, ldo, stream);
+  else if (per_lane <= 12) ln_launch<T, 12>(n, D, eps, x, ldx, shift, scale, out, ldo, stream);
+  else if (per_lane <= 16) ln_launch<T, 16>(n, D, eps, x, ldx, shift, scale, out, ldo, stream);
+  else                     ln_launch<T, 32>(n, D, eps, x, ldx, shift, scale, out, ldo, stream);
+}
+
+hipError_t launch_ln_modulate(DType dt, int n, int D, float eps, const void* x, int64_t ldx,
+                              const float* shift, const float* scale, void* out, int64_t ldo,
+                              hipStream_t stream) {
+  if (dt == kBF16) ln_dispatch<bf16>(n, D, eps, x, ldx, shift, scale, out, ldo, stream);
+  else ln_dispatch<float>(n, D, eps, x, ldx, shift, scale, out, ldo, stream);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Per-row symmetric int8 quantiser: s = max|w| / 127, q = clamp(rint(w/s)).
+// One workgroup per row: absmax over the row (exact, order-independent), then
+// one correctly rounded fp32 division per element and round-half-to-even.
+template <typename T>
+__global__ __launch_bounds__(256) void quantize_int8_kernel(const T* __restrict__ w, int64_t cols,
+                                                            int8_t* __restrict__ q, float* __restrict__ scales) {
+  __shared__ float red[256 / kWave];
+  const int64_t row = blockIdx.x;
+  const T* wr = w + row * cols;
+  float mx = 0.f;
+  for (int64_t k = threadIdx.x; k < cols; k += blockDim.x) mx = fmaxf(mx, fabsf(to_f32(wr[k])));
+  mx = wave_max(mx);
+  if (threadIdx.x % kWave == 0) red[threadIdx.x / kWave] = mx;
+  __syncthreads();
+  mx = red[0];
+#pragma unroll
+  for (int i = 1; i < 256 / kWave; ++i) mx = fmaxf(mx, red[i]);
+  const float s = mx / 127.0f;
+  if (threadIdx.x == 0) scales[row] = s;
+  int8_t* qr = q + row * cols;
+  for (int64_t k = threadIdx.x; k < cols; k += blockDim.x) {
+    int qi = 0;
+    if (s != 0.f) {
+      const float t = rintf(to_f32(wr[k]) / s);
+      qi = (int)fminf(127.f, fmaxf(-127.f, t));
+    }
+    qr[k] = (int8_t)qi;
+  }
+}
+
+hipError_t launch_quantize_int8(DType dt, const void* w, int64_t rows, int64_t cols, int8_t* q, float* scales,
+                                hipStream_t stream) {
+  if (rows == 0) return hipSuccess;
+  if (dt == kBF16)
+    quantize_int8_kernel<bf16><<<dim3((unsigned)rows), dim3(256), 0, stream>>>((const bf16*)w, cols, q, scales);
+  else
+    quantize_int8_kernel<float><<<dim3((unsigned)rows), dim3(256), 0, stream>>>((const float*)w, cols, q, scales);
+  return hipGetLastError();
+}
+
+}  // namespace h3k

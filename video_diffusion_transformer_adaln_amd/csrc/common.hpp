@@ -1,0 +1,71 @@
+// Device-side helpers shared by the gfx950 kernels: vector types, bf16
+// conversion, wave reductions, the LDS chunk swizzle and the XCD-aware
+// workgroup remap.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+namespace h3k {
+
+constexpr int kWave = 64;
+// MI355X (gfx950) has 8 accelerator complex dies; consecutive workgroup ids
+// are dispatched round-robin over them, and each has its own L2.
+constexpr int kXcds = 8;
+
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(bf16 v) { return static_cast<float>(v); }
+
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+// Round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float v) { return static_cast<bf16>(v); }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+  return v;
+}
+
+// Position of 16-byte chunk `c` of LDS row `r` for rows of 8 chunks
+// (128 bytes): XOR with a row hash so that 8 (32-bank view) or 16 (64-bank
+// view) consecutive rows reading the same logical chunk hit distinct banks.
+__device__ __forceinline__ int swz8(int r, int c) { return c ^ ((r ^ (r >> 3)) & 7); }
+// Same for rows of 16 chunks (256 bytes).
+__device__ __forceinline__ int swz16(int r, int c) { return c ^ (r & 15); }
+
+// Remap a linear workgroup id so that each XCD receives one contiguous range
+// of logical tiles (neighbouring tiles then share that XCD's L2).
+__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
+  const int q = nblocks / kXcds, r = nblocks % kXcds;
+  const int xcd = bid % kXcds, local = bid / kXcds;
+  return (xcd < r) ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
+}
+
+// GELU, tanh form.  Uses the identity 0.5 (1 + tanh(y)) = 1 / (1 + exp(-2y)),
+// so gelu(z) = z / (1 + exp(-2y)) with y = sqrt(2/pi) (z + 0.044715 z^3);
+// exp through v_exp_f32 (exp2) and the reciprocal through v_rcp_f32.  For
+// z -> -inf the exponential overflows to +inf and the result is -0.
+__device__ __forceinline__ float gelu_tanh(float z) {
+  const float k0 = 0.7978845608028654f;           // sqrt(2/pi)
+  const float k1 = 0.044715f;
+  const float m2log2e = -2.0f * 1.4426950408889634f;
+  const float y = k0 * (z + k1 * z * z * z);
+  const float e = __builtin_amdgcn_exp2f(m2log2e * y);
+  return z * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+}  // namespace h3k

@@ -1,0 +1,399 @@
+// Projection GEMMs of the DiT block: y = epilogue(x W^T), with x the
+// activations [m, k] and W the weight [n, k] (both k-contiguous).
+//
+//  * bf16 path: 256x256x64 workgroup tile, 4 waves in a 2x2 grid, each wave a
+//    128x128 sub-tile built from v_mfma_f32_32x32x16_bf16 (fp32 accumulate).
+//    Operands are staged through double-buffered, XOR-swizzled LDS
+//    (128 KiB of gfx950's 160 KiB), the next k-tile's global loads are in
+//    flight while the current one is multiplied.
+//  * int8-weight path (W8A16): the weight tile is read as int8 (half the
+//    bytes), widened to bf16 exactly while it is staged into LDS, multiplied
+//    on the bf16 MFMA, and the per-output-channel scale is applied to the
+//    fp32 accumulator in the epilogue (it factors out of the k-sum).
+//  * fp32 path: a plain LDS-tiled SIMT kernel for the small fp32 workload.
+//
+// Epilogues (fused, fp32 math, one rounding at the store): bias; bias + GELU
+// (tanh form); gated residual r + g * z.  Columns at or beyond split_col are
+// written transposed (V^T for the attention kernel).
+//
+// Output layout trick: the MFMA accumulator holds 4 consecutive rows of its
+// A operand per lane, so the operand whose index is contiguous in the output
+// is fed as A: weights for the row-major output (4 consecutive features per
+// lane), activations for the transposed output (4 consecutive tokens).
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace h3k {
+
+struct GemmParams {
+  const bf16* x; int64_t ldx;
+  const void* w; int64_t ldw;
+  const float* w_scale;
+  const bf16* bias;
+  const bf16* residual; int64_t ldr;
+  const float* gate;
+  bf16* y; int64_t ldy;
+  bf16* yt; int64_t ldyt;
+  int64_t split_col;
+  int m, n, k;
+  int tiles_m, tiles_n;
+};
+
+constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int kGroupM = 8;
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// 16 int8 -> 16 bf16, exact (|q| <= 127 fits bf16's 8-bit significand):
+// flip the sign bit to get q + 128 as an unsigned byte, convert that byte to
+// fp32 (v_cvt_f32_ubyte*), subtract 128, round to bf16 (no rounding occurs).
+__device__ __forceinline__ void i8x16_to_bf16(const u32x4& src, u32x4& lo, u32x4& hi) {
+  bf16* l = reinterpret_cast<bf16*>(&lo);
+  bf16* h = reinterpret_cast<bf16*>(&hi);
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const uint32_t u = src[d] ^ 0x80808080u;
+    bf16* dst = d < 2 ? l + 4 * d : h + 4 * (d - 2);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      dst[e] = static_cast<bf16>(static_cast<float>((u >> (8 * e)) & 0xffu) - 128.0f);
+  }
+}
+
+// Raw buffer resource over [base, base + bytes): loads at offsets >= bytes
+// return zero, which masks the ragged edges of the token and feature axes.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+
+// LDS tile of one operand: 4 "planes", one per 16-wide k-step of the 64-wide
+// k-tile; plane = [256 rows][32 bytes] (two 16-byte halves = the two lane
+// halves of a 32x32x16 MFMA fragment).  The halves of a row are swapped when
+// bit 2 xor bit 3 of the row is set, so that 8 (or 16) lanes reading 8 (16)
+// consecutive rows hit distinct banks; as row offsets of a wave's fragments
+// are multiples of 32, each lane's fragment address is one per-lane base plus
+// compile-time offsets.
+constexpr int kPlaneBytes = 256 * 32;
+constexpr int kTileBytes = 4 * kPlaneBytes;   // 32 KiB per operand per buffer
+
+__device__ __forceinline__ int half_swap(int r) { return ((r >> 2) ^ (r >> 3)) & 1; }
+__device__ __forceinline__ int plane_off(int ks, int r, int h) {
+  return ks * kPlaneBytes + r * 32 + ((h ^ half_swap(r)) << 4);
+}
+
+template <int EPI, bool W8>
+__global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmParams p) {
+  __shared__ __attribute__((aligned(16))) char lds[4 * kTileBytes];   // X0 W0 X1 W1
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // ---- tile order: XCD-contiguous ranges, then groups of kGroupM m-tiles
+  const int nblk = p.tiles_m * p.tiles_n;
+  const int lin = xcd_remap(blockIdx.x, nblk);
+  const int per_group = kGroupM * p.tiles_n;
+  const int group = lin / per_group;
+  const int first_m = group * kGroupM;
+  const int gm = min(p.tiles_m - first_m, kGroupM);
+  const int in_group = lin - group * per_group;
+  const int tile_m = first_m + in_group % gm;
+  const int tile_n = in_group / gm;
+  const int tok0 = tile_m * BM, feat0 = tile_n * BN;
+  const bool trans = (int64_t)feat0 >= p.split_col;
+  const int KT = p.k / BK;
+
+  // ---- global -> register staging.  bf16 tiles: per instruction a wave
+  // covers 8 full 128-byte rows; lane -> plane l/16, row (l%16)/2, half l%2.
+  // int8 weight tile: a wave covers 16 rows of 64 bytes; lane -> plane l/16,
+  // row l%16.
+  u32x4 rx[8];
+  u32x4 rw[W8 ? 4 : 8];
+  const int ld_ks = lane >> 4;
+  const int ld_rsub = (lane & 15) >> 1, ld_h = lane & 1;
+  const __amdgpu_buffer_rsrc_t rsx = make_rsrc(p.x, (uint32_t)((uint64_t)p.m * p.ldx * 2));
+  const __amdgpu_buffer_rsrc_t rsw = make_rsrc(p.w, (uint32_t)((uint64_t)p.n * p.ldw * (W8 ? 1 : 2)));
+  // byte offset of this thread's first row at k = 0; rows step by 32 (bf16)
+  // or 64 (int8) per staging instruction
+  const uint32_t x_off0 = (uint32_t)((tok0 + wave * 8 + ld_rsub) * (uint32_t)p.ldx * 2u + (ld_ks * 16 + ld_h * 8) * 2);
+  const uint32_t x_step = 32u * (uint32_t)p.ldx * 2u;
+  const uint32_t w_off0 = W8 ? (uint32_t)((feat0 + wave * 16 + (lane & 15)) * (uint32_t)p.ldw + ld_ks * 16)
+                             : (uint32_t)((feat0 + wave * 8 + ld_rsub) * (uint32_t)p.ldw * 2u + (ld_ks * 16 + ld_h * 8) * 2);
+  const uint32_t w_step = W8 ? 64u * (uint32_t)p.ldw : 32u * (uint32_t)p.ldw * 2u;
+
+  auto gload = [&](int kt) {
+    const uint32_t kx = (uint32_t)kt * BK * 2u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) rx[i] = buf_load16(rsx, x_off0 + i * x_step + kx);
+    const uint32_t kw = (uint32_t)kt * BK * (W8 ? 1u : 2u);
+#pragma unroll
+    for (int i = 0; i < (W8 ? 4 : 8); ++i) rw[i] = buf_load16(rsw, w_off0 + i * w_step + kw);
+  };
+
+  auto lstore = [&](char* sx, char* sw) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = i * 32 + wave * 8 + ld_rsub;
+      *reinterpret_cast<u32x4*>(sx + plane_off(ld_ks, r, ld_h)) = rx[i];
+    }
+    if constexpr (W8) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = i * 64 + wave * 16 + (lane & 15);
+        u32x4 lo, hi;
+        i8x16_to_bf16(rw[i], lo, hi);
+        *reinterpret_cast<u32x4*>(sw + plane_off(ld_ks, r, 0)) = lo;
+        *reinterpret_cast<u32x4*>(sw + plane_off(ld_ks, r, 1)) = hi;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int r = i * 32 + wave * 8 + ld_rsub;
+        *reinterpret_cast<u32x4*>(sw + plane_off(ld_ks, r, ld_h)) = rw[i];
+      }
+    }
+  };
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+
+  // MFMA A operand: weights (row-major output) or activations (transposed).
+  const int a_row0 = trans ? wm * 128 : wn * 128;
+  const int b_row0 = trans ? wn * 128 : wm * 128;
+  const int frag = (lane & 31) * 32 + (((lane >> 5) ^ half_swap(lane & 31)) << 4);
+  const int a_off = (trans ? 0 : kTileBytes) + a_row0 * 32 + frag;
+  const int b_off = (trans ? kTileBytes : 0) + b_row0 * 32 + frag;
+
+  auto compute = [&](const char* base) {
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      bf16x8 a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        a[i] = *reinterpret_cast<const bf16x8*>(base + a_off + ks * kPlaneBytes + i * 1024);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        b[j] = *reinterpret_cast<const bf16x8*>(base + b_off + ks * kPlaneBytes + j * 1024);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
+    }
+  };
+
+  gload(0);
+  lstore(lds, lds + kTileBytes);
+  __syncthreads();
+  for (int kt = 0; kt < KT; ++kt) {
+    char* cur = lds + (kt & 1) * (2 * kTileBytes);
+    char* nxt = lds + ((kt + 1) & 1) * (2 * kTileBytes);
+    if (kt + 1 < KT) gload(kt + 1);
+    compute(cur);
+    if (kt + 1 < KT) lstore(nxt, nxt + kTileBytes);
+    __syncthreads();
+  }
+
+  // ---- epilogue.  Accumulator register r of lane l in tile (i, j):
+  //      A-row = i*32 + 8*(r/4) + 4*(l/32) + r%4, B-row = j*32 + l%32.
+  const float* wsc = p.w_scale;
+  if (!trans) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int f = feat0 + wn * 128 + i * 32 + 8 * g + 4 * (lane >> 5);
+          const int t = tok0 + wm * 128 + j * 32 + (lane & 31);
+          if (t >= p.m || f >= p.n) continue;
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            v[e] = acc[i][j][4 * g + e];
+            if constexpr (W8) v[e] *= wsc[f + e];
+            if (p.bias) v[e] += static_cast<float>(p.bias[f + e]);
+          }
+          if ((int64_t)f >= p.split_col) {   // straddling tile: transposed part, bias only
+#pragma unroll
+            for (int e = 0; e < 4; ++e) p.yt[(int64_t)(f + e - p.split_col) * p.ldyt + t] = static_cast<bf16>(v[e]);
+            continue;
+          }
+          if constexpr (EPI == kEpiGelu) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = gelu_tanh(v[e]);
+          }
+          if constexpr (EPI == kEpiGatedResidual) {
+            const u32x2 rr = *reinterpret_cast<const u32x2*>(p.residual + (int64_t)t * p.ldr + f);
+            const bf16* re = reinterpret_cast<const bf16*>(&rr);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = static_cast<float>(re[e]) + p.gate[f + e] * v[e];
+          }
+          u32x2 out;
+          bf16* oe = reinterpret_cast<bf16*>(&out);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) oe[e] = static_cast<bf16>(v[e]);
+          *reinterpret_cast<u32x2*>(p.y + (int64_t)t * p.ldy + f) = out;
+        }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int t0 = tok0 + wm * 128 + i * 32 + 8 * g + 4 * (lane >> 5);
+          const int f = feat0 + wn * 128 + j * 32 + (lane & 31);
+          if (f >= p.n || t0 >= p.m) continue;
+          const float sc = W8 ? wsc[f] : 1.0f;
+          const float bb = p.bias ? static_cast<float>(p.bias[f]) : 0.0f;
+          u32x2 out;
+          bf16* oe = reinterpret_cast<bf16*>(&out);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float v = acc[i][j][4 * g + e];
+            if constexpr (W8) v *= sc;
+            oe[e] = static_cast<bf16>(v + bb);
+          }
+          bf16* dst = p.yt + (int64_t)(f - p.split_col) * p.ldyt + t0;
+          if (t0 + 3 < p.m) {
+            *reinterpret_cast<u32x2*>(dst) = out;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (t0 + e < p.m) dst[e] = oe[e];
+          }
+        }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 SIMT GEMM: 64x64 tile, k-steps of 16, 4x4 outputs per thread.
+struct GemmParamsF {
+  const float* x; int64_t ldx;
+  const float* w; int64_t ldw;
+  const float* bias;
+  const float* residual; int64_t ldr;
+  const float* gate;
+  float* y; int64_t ldy;
+  float* yt; int64_t ldyt;
+  int64_t split_col;
+  int m, n, k;
+};
+
+template <int EPI>
+__global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParamsF p) {
+  __shared__ float sX[16][64 + 4];
+  __shared__ float sW[16][64 + 4];
+  const int tid = threadIdx.x;
+  const int tok0 = blockIdx.y * 64, feat0 = blockIdx.x * 64;
+  const int ty = tid / 16, tx = tid % 16;
+  float acc[4][4] = {};
+  const int lr = tid / 4, lk = (tid % 4) * 4;
+  for (int k0 = 0; k0 < p.k; k0 += 16) {
+    {
+      const int t = tok0 + lr;
+      f32x4 v = (t < p.m) ? *reinterpret_cast<const f32x4*>(p.x + (int64_t)t * p.ldx + k0 + lk) : f32x4{0, 0, 0, 0};
+      const int f = feat0 + lr;
+      f32x4 u = (f < p.n) ? *reinterpret_cast<const f32x4*>(p.w + (int64_t)f * p.ldw + k0 + lk) : f32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) { sX[lk + e][lr] = v[e]; sW[lk + e][lr] = u[e]; }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      float a[4], b[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) { a[e] = sX[kk][ty * 4 + e]; b[e] = sW[kk][tx * 4 + e]; }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = tok0 + ty * 4 + i;
+    if (t >= p.m) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int f = feat0 + tx * 4 + j;
+      if (f >= p.n) continue;
+      float v = acc[i][j] + (p.bias ? p.bias[f] : 0.0f);
+      if ((int64_t)f >= p.split_col) {
+        p.yt[(int64_t)(f - p.split_col) * p.ldyt + t] = v;
+        continue;
+      }
+      if constexpr (EPI == kEpiGelu) v = gelu_tanh(v);
+      if constexpr (EPI == kEpiGatedResidual) v = p.residual[(int64_t)t * p.ldr + f] + p.gate[f] * v;
+      p.y[(int64_t)t * p.ldy + f] = v;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+template <int EPI, bool W8>
+static void launch_bf16(const LinearArgs& a, hipStream_t stream) {
+  GemmParams p;
+  p.x = (const bf16*)a.x; p.ldx = a.ldx;
+  p.w = a.w; p.ldw = a.ldw;
+  p.w_scale = a.w_scale;
+  p.bias = (const bf16*)a.bias;
+  p.residual = (const bf16*)a.residual; p.ldr = a.ldr;
+  p.gate = a.gate;
+  p.y = (bf16*)a.y; p.ldy = a.ldy;
+  p.yt = (bf16*)a.yt; p.ldyt = a.ldyt;
+  p.split_col = a.split_col;
+  p.m = (int)a.m; p.n = (int)a.n; p.k = (int)a.k;
+  p.tiles_m = (p.m + BM - 1) / BM;
+  p.tiles_n = (p.n + BN - 1) / BN;
+  gemm_bf16_kernel<EPI, W8><<<dim3(p.tiles_m * p.tiles_n), dim3(256), 0, stream>>>(p);
+}
+
+template <int EPI>
+static void launch_f32(const LinearArgs& a, hipStream_t stream) {
+  GemmParamsF p;
+  p.x = (const float*)a.x; p.ldx = a.ldx;
+  p.w = (const float*)a.w; p.ldw = a.ldw;
+  p.bias = (const float*)a.bias;
+  p.residual = (const float*)a.residual; p.ldr = a.ldr;
+  p.gate = a.gate;
+  p.y = (float*)a.y; p.ldy = a.ldy;
+  p.yt = (float*)a.yt; p.ldyt = a.ldyt;
+  p.split_col = a.split_col;
+  p.m = (int)a.m; p.n = (int)a.n; p.k = (int)a.k;
+  const dim3 grid((p.n + 63) / 64, (p.m + 63) / 64);
+  gemm_f32_kernel<EPI><<<grid, dim3(256), 0, stream>>>(p);
+}
+
+hipError_t launch_linear(const LinearArgs& a, hipStream_t stream) {
+  if (a.m == 0 || a.n == 0) return hipSuccess;
+  if (a.act == kF32) {
+    switch (a.epi) {
+      case kEpiBias: launch_f32<kEpiBias>(a, stream); break;
+      case kEpiGelu: launch_f32<kEpiGelu>(a, stream); break;
+      default: launch_f32<kEpiGatedResidual>(a, stream); break;
+    }
+  } else if (a.weight == kINT8) {
+    switch (a.epi) {
+      case kEpiBias: launch_bf16<kEpiBias, true>(a, stream); break;
+      case kEpiGelu: launch_bf16<kEpiGelu, true>(a, stream); break;
+      default: launch_bf16<kEpiGatedResidual, true>(a, stream); break;
+    }
+  } else {
+    switch (a.epi) {
+      case kEpiBias: launch_bf16<kEpiBias, false>(a, stream); break;
+      case kEpiGelu: launch_bf16<kEpiGelu, false>(a, stream); break;
+      default: launch_bf16<kEpiGatedResidual, false>(a, stream); break;
+    }
+  }
+  return hipGetLastError();
+}
+
+}  // namespace h3k

@@ -1,0 +1,51 @@
+// Host-side launchers of the gfx950 kernels.  Each launcher assumes its
+// arguments were validated by the C-ABI layer (h3k_api.cpp) and only
+// enqueues work on `stream`; it returns the launch status.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace h3k {
+
+enum DType : int32_t { kF32 = 0, kBF16 = 1, kINT8 = 2 };
+enum Epilogue : int32_t { kEpiBias = 0, kEpiGelu = 1, kEpiGatedResidual = 2 };
+
+// mod[rows] = W[rows, cols] c + b   (fp32 out)
+hipError_t launch_adaln_gemv(DType dt, int rows, int cols, const void* w, const void* b,
+                             const void* c, float* mod, hipStream_t stream);
+
+// out = LN(x) * (1 + scale) + shift, row-wise
+hipError_t launch_ln_modulate(DType dt, int n, int D, float eps, const void* x, int64_t ldx,
+                              const float* shift, const float* scale, void* out, int64_t ldo,
+                              hipStream_t stream);
+
+struct LinearArgs {
+  DType act, weight;
+  int64_t m, n, k;
+  const void* x; int64_t ldx;
+  const void* w; int64_t ldw;
+  const float* w_scale;
+  const void* bias;
+  Epilogue epi;
+  const void* residual; int64_t ldr;
+  const float* gate;
+  void* y; int64_t ldy;
+  void* yt; int64_t ldyt;
+  int64_t split_col;
+};
+hipError_t launch_linear(const LinearArgs& a, hipStream_t stream);
+
+struct AttentionArgs {
+  DType dt;
+  int n, n_heads, head_dim;
+  const void* q; int64_t ldq;
+  const void* k; int64_t ldk;
+  const void* vt; int64_t ldvt;
+  void* o; int64_t ldo;
+};
+hipError_t launch_attention(const AttentionArgs& a, hipStream_t stream);
+
+hipError_t launch_quantize_int8(DType dt, const void* w, int64_t rows, int64_t cols, int8_t* q,
+                                float* scales, hipStream_t stream);
+
+}  // namespace h3k
