@@ -209,7 +209,7 @@ def cpu_baseline(step_flops, L):
     hw = si.gen_block_weights(shape, 0)
     w = {k: v.values for k, v in hw.items()}
     n = shape.n_tokens
-    samples = (256, 1024)
+    samples = (1024, 4096)
     times = []
     for r in samples:
         rows = np.linspace(0, n - 1, r).astype(np.int64)
