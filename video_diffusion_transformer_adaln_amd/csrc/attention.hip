@@ -34,6 +34,7 @@ struct AttnParams {
 };
 
 constexpr int KT = 64;   // keys per tile
+constexpr float kRescaleLog2 = 8.0f;   // lazy-rescale threshold (log2 units)
 
 __device__ __forceinline__ f32x16 mfma32a(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -184,7 +185,11 @@ __global__ __launch_bounds__(256) void attention_bf16_kernel(AttnParams p) {
           }
         }
     }
-    // ---- online softmax (log2 domain), P rounded to bf16 for the MFMA
+    // ---- online softmax (log2 domain), P rounded to bf16 for the MFMA.
+    // The reference max m_run is raised (and O, l rescaled) only when some
+    // lane's tile maximum exceeds it by more than kRescaleLog2; otherwise the
+    // old reference is kept and p <= 2^kRescaleLog2.  O / l at the end is the
+    // same either way.
     bf16x8 P[2][2][QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -193,9 +198,16 @@ __global__ __launch_bounds__(256) void attention_bf16_kernel(AttnParams p) {
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[kb][qb][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-      const float m_new = fmaxf(m_run[qb], mx * p.scale_log2);
-      const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave)) * p.scale_log2;
+      if (__any(mx > m_run[qb] + kRescaleLog2)) {
+        const float m_new = fmaxf(m_run[qb], mx);
+        const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
+        l_run[qb] *= alpha;
+        m_run[qb] = m_new;
+#pragma unroll
+        for (int db = 0; db < HD / 32; ++db) O[db][qb] *= alpha;
+      }
+      const float m_ref = m_run[qb];
       float ls = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -203,14 +215,11 @@ __global__ __launch_bounds__(256) void attention_bf16_kernel(AttnParams p) {
         for (int m = 0; m < 2; ++m)
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
-            const float pr = __builtin_amdgcn_exp2f(fmaf(S[kb][qb][8 * m + j], p.scale_log2, -m_new));
+            const float pr = __builtin_amdgcn_exp2f(fmaf(S[kb][qb][8 * m + j], p.scale_log2, -m_ref));
             ls += pr;
             P[kb][m][qb][j] = static_cast<bf16>(pr);
           }
-      l_run[qb] = l_run[qb] * alpha + ls;
-      m_run[qb] = m_new;
-#pragma unroll
-      for (int db = 0; db < HD / 32; ++db) O[db][qb] *= alpha;
+      l_run[qb] += ls;
     }
     // ---- O^T[dv][query] += V^T[dv][keys] P^T[keys][query]
 #pragma unroll

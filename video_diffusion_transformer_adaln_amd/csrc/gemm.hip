@@ -1,11 +1,12 @@
 // Projection GEMMs of the DiT block: y = epilogue(x W^T), with x the
 // activations [m, k] and W the weight [n, k] (both k-contiguous).
 //
-//  * bf16 path: 256x256x64 workgroup tile, 4 waves in a 2x2 grid, each wave a
-//    128x128 sub-tile built from v_mfma_f32_32x32x16_bf16 (fp32 accumulate).
-//    Operands are staged through double-buffered, XOR-swizzled LDS
-//    (128 KiB of gfx950's 160 KiB), the next k-tile's global loads are in
-//    flight while the current one is multiplied.
+//  * bf16 path: 256x256x64 workgroup tile, 8 waves (two per SIMD, so one
+//    wave's memory instructions and waits overlap the other's MFMAs), each
+//    wave a 64x128 sub-tile of v_mfma_f32_32x32x16_bf16 (fp32 accumulators
+//    in VGPRs).  Operands are staged through double-buffered, swizzled LDS
+//    (128 KiB of gfx950's 160 KiB); the loads of k-tile t+2 are in flight
+//    while t is multiplied and t+1 is stored to LDS.
 //  * int8-weight path (W8A16): the weight tile is read as int8 (half the
 //    bytes), widened to bf16 exactly while it is staged into LDS, multiplied
 //    on the bf16 MFMA, and the per-output-channel scale is applied to the
@@ -87,10 +88,9 @@ __device__ __forceinline__ int plane_off(int ks, int r, int h) {
 }
 
 template <int EPI, bool W8>
-__global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmParams p) {
+__global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmParams p) {
   __shared__ __attribute__((aligned(16))) char lds[4 * kTileBytes];   // X0 W0 X1 W1
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
 
   // ---- tile order: XCD-contiguous ranges, then groups of kGroupM m-tiles
   const int nblk = p.tiles_m * p.tiles_n;
@@ -106,43 +106,43 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmParams p) {
   const bool trans = (int64_t)feat0 >= p.split_col;
   const int KT = p.k / BK;
 
-  // ---- global -> register staging.  bf16 tiles: per instruction a wave
-  // covers 8 full 128-byte rows; lane -> plane l/16, row (l%16)/2, half l%2.
-  // int8 weight tile: a wave covers 16 rows of 64 bytes; lane -> plane l/16,
-  // row l%16.
-  u32x4 rx[8];
-  u32x4 rw[W8 ? 4 : 8];
+  // ---- global -> register staging (8 waves).  bf16 tiles: per instruction a
+  // wave covers 8 full 128-byte rows; lane -> plane l/16, row (l%16)/2, half
+  // l%2.  int8 weight tile: a wave covers 16 rows of 64 bytes; lane -> plane
+  // l/16, row l%16.
+  constexpr int XL = 4;                 // bf16 chunks per thread per operand
+  constexpr int WL = W8 ? 2 : 4;
+  u32x4 rx[XL];
+  u32x4 rw[WL];
   const int ld_ks = lane >> 4;
   const int ld_rsub = (lane & 15) >> 1, ld_h = lane & 1;
   const __amdgpu_buffer_rsrc_t rsx = make_rsrc(p.x, (uint32_t)((uint64_t)p.m * p.ldx * 2));
   const __amdgpu_buffer_rsrc_t rsw = make_rsrc(p.w, (uint32_t)((uint64_t)p.n * p.ldw * (W8 ? 1 : 2)));
-  // byte offset of this thread's first row at k = 0; rows step by 32 (bf16)
-  // or 64 (int8) per staging instruction
   const uint32_t x_off0 = (uint32_t)((tok0 + wave * 8 + ld_rsub) * (uint32_t)p.ldx * 2u + (ld_ks * 16 + ld_h * 8) * 2);
-  const uint32_t x_step = 32u * (uint32_t)p.ldx * 2u;
+  const uint32_t x_step = 64u * (uint32_t)p.ldx * 2u;
   const uint32_t w_off0 = W8 ? (uint32_t)((feat0 + wave * 16 + (lane & 15)) * (uint32_t)p.ldw + ld_ks * 16)
                              : (uint32_t)((feat0 + wave * 8 + ld_rsub) * (uint32_t)p.ldw * 2u + (ld_ks * 16 + ld_h * 8) * 2);
-  const uint32_t w_step = W8 ? 64u * (uint32_t)p.ldw : 32u * (uint32_t)p.ldw * 2u;
+  const uint32_t w_step = W8 ? 128u * (uint32_t)p.ldw : 64u * (uint32_t)p.ldw * 2u;
 
   auto gload = [&](int kt) {
     const uint32_t kx = (uint32_t)kt * BK * 2u;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) rx[i] = buf_load16(rsx, x_off0 + i * x_step + kx);
+    for (int i = 0; i < XL; ++i) rx[i] = buf_load16(rsx, x_off0 + i * x_step + kx);
     const uint32_t kw = (uint32_t)kt * BK * (W8 ? 1u : 2u);
 #pragma unroll
-    for (int i = 0; i < (W8 ? 4 : 8); ++i) rw[i] = buf_load16(rsw, w_off0 + i * w_step + kw);
+    for (int i = 0; i < WL; ++i) rw[i] = buf_load16(rsw, w_off0 + i * w_step + kw);
   };
 
   auto lstore = [&](char* sx, char* sw) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = i * 32 + wave * 8 + ld_rsub;
+    for (int i = 0; i < XL; ++i) {
+      const int r = i * 64 + wave * 8 + ld_rsub;
       *reinterpret_cast<u32x4*>(sx + plane_off(ld_ks, r, ld_h)) = rx[i];
     }
     if constexpr (W8) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = i * 64 + wave * 16 + (lane & 15);
+      for (int i = 0; i < WL; ++i) {
+        const int r = i * 128 + wave * 16 + (lane & 15);
         u32x4 lo, hi;
         i8x16_to_bf16(rw[i], lo, hi);
         *reinterpret_cast<u32x4*>(sw + plane_off(ld_ks, r, 0)) = lo;
@@ -150,67 +150,81 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmParams p) {
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int r = i * 32 + wave * 8 + ld_rsub;
+      for (int i = 0; i < WL; ++i) {
+        const int r = i * 64 + wave * 8 + ld_rsub;
         *reinterpret_cast<u32x4*>(sw + plane_off(ld_ks, r, ld_h)) = rw[i];
       }
     }
   };
 
-  f32x16 acc[4][4];
+  // Each wave computes 64 A-rows x 128 B-rows: 2 x 4 tiles of 32x32.  A is
+  // the weight (row-major output) or the activation (transposed output).
+  f32x16 acc[2][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 
-  // MFMA A operand: weights (row-major output) or activations (transposed).
-  const int a_row0 = trans ? wm * 128 : wn * 128;
-  const int b_row0 = trans ? wn * 128 : wm * 128;
+  const int a_row0 = (wave & 3) * 64;
+  const int b_row0 = (wave >> 2) * 128;
   const int frag = (lane & 31) * 32 + (((lane >> 5) ^ half_swap(lane & 31)) << 4);
   const int a_off = (trans ? 0 : kTileBytes) + a_row0 * 32 + frag;
   const int b_off = (trans ? kTileBytes : 0) + b_row0 * 32 + frag;
 
-  auto compute = [&](const char* base) {
+  auto load_frags = [&](const char* base, int ks, bf16x8 (&fa)[2], bf16x8 (&fb)[4]) {
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      bf16x8 a[4], b[4];
+    for (int i = 0; i < 2; ++i)
+      fa[i] = *reinterpret_cast<const bf16x8*>(base + a_off + ks * kPlaneBytes + i * 1024);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        a[i] = *reinterpret_cast<const bf16x8*>(base + a_off + ks * kPlaneBytes + i * 1024);
+    for (int j = 0; j < 4; ++j)
+      fb[j] = *reinterpret_cast<const bf16x8*>(base + b_off + ks * kPlaneBytes + j * 1024);
+  };
+  auto mfmas = [&](const bf16x8 (&fa)[2], const bf16x8 (&fb)[4]) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        b[j] = *reinterpret_cast<const bf16x8*>(base + b_off + ks * kPlaneBytes + j * 1024);
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
-    }
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(fa[i], fb[j], acc[i][j]);
   };
 
+  bf16x8 f0a[2], f0b[4], f1a[2], f1b[4];
+  char* const buf0 = lds;
+  char* const buf1 = lds + 2 * kTileBytes;
   gload(0);
-  lstore(lds, lds + kTileBytes);
+  lstore(buf0, buf0 + kTileBytes);
   __syncthreads();
+  if (KT > 1) gload(1);
+  load_frags(buf0, 0, f0a, f0b);
   for (int kt = 0; kt < KT; ++kt) {
-    char* cur = lds + (kt & 1) * (2 * kTileBytes);
-    char* nxt = lds + ((kt + 1) & 1) * (2 * kTileBytes);
-    if (kt + 1 < KT) gload(kt + 1);
-    compute(cur);
+    const char* cur = (kt & 1) ? buf1 : buf0;
+    char* nxt = (kt & 1) ? buf0 : buf1;
+    load_frags(cur, 1, f1a, f1b);
+    mfmas(f0a, f0b);
+    __builtin_amdgcn_sched_barrier(0);
+    load_frags(cur, 2, f0a, f0b);
     if (kt + 1 < KT) lstore(nxt, nxt + kTileBytes);
+    mfmas(f1a, f1b);
+    __builtin_amdgcn_sched_barrier(0);
+    load_frags(cur, 3, f1a, f1b);
+    if (kt + 2 < KT) gload(kt + 2);
+    mfmas(f0a, f0b);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(f1a, f1b);
     __syncthreads();
+    if (kt + 1 < KT) load_frags(nxt, 0, f0a, f0b);
   }
 
   // ---- epilogue.  Accumulator register r of lane l in tile (i, j):
-  //      A-row = i*32 + 8*(r/4) + 4*(l/32) + r%4, B-row = j*32 + l%32.
+  //      A-row = a_row0 + i*32 + 8*(r/4) + 4*(l/32) + r%4, B-row = b_row0 + j*32 + l%32.
   const float* wsc = p.w_scale;
   if (!trans) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int f = feat0 + wn * 128 + i * 32 + 8 * g + 4 * (lane >> 5);
-          const int t = tok0 + wm * 128 + j * 32 + (lane & 31);
+          const int f = feat0 + a_row0 + i * 32 + 8 * g + 4 * (lane >> 5);
+          const int t = tok0 + b_row0 + j * 32 + (lane & 31);
           if (t >= p.m || f >= p.n) continue;
           float v[4];
 #pragma unroll
@@ -242,13 +256,13 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmParams p) {
         }
   } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int t0 = tok0 + wm * 128 + i * 32 + 8 * g + 4 * (lane >> 5);
-          const int f = feat0 + wn * 128 + j * 32 + (lane & 31);
+          const int t0 = tok0 + a_row0 + i * 32 + 8 * g + 4 * (lane >> 5);
+          const int f = feat0 + b_row0 + j * 32 + (lane & 31);
           if (f >= p.n || t0 >= p.m) continue;
           const float sc = W8 ? wsc[f] : 1.0f;
           const float bb = p.bias ? static_cast<float>(p.bias[f]) : 0.0f;
@@ -353,7 +367,7 @@ static void launch_bf16(const LinearArgs& a, hipStream_t stream) {
   p.m = (int)a.m; p.n = (int)a.n; p.k = (int)a.k;
   p.tiles_m = (p.m + BM - 1) / BM;
   p.tiles_n = (p.n + BN - 1) / BN;
-  gemm_bf16_kernel<EPI, W8><<<dim3(p.tiles_m * p.tiles_n), dim3(256), 0, stream>>>(p);
+  gemm_bf16_kernel<EPI, W8><<<dim3(p.tiles_m * p.tiles_n), dim3(512), 0, stream>>>(p);
 }
 
 template <int EPI>
