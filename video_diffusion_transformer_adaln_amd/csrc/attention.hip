@@ -21,6 +21,15 @@
 // workload.
 #include "common.hpp"
 #include "kernels.hpp"
+#ifndef H3K_ATTN_KT
+#define H3K_ATTN_KT 64
+#endif
+#ifndef H3K_QB
+#define H3K_QB 1
+#endif
+#ifndef H3K_NW
+#define H3K_NW 8
+#endif
 
 namespace h3k {
 
@@ -33,7 +42,6 @@ struct AttnParams {
   float scale_log2;   // log2(e) / sqrt(d)
 };
 
-constexpr int KT = 64;   // keys per tile
 constexpr float kRescaleLog2 = 8.0f;   // lazy-rescale threshold (log2 units)
 
 __device__ __forceinline__ f32x16 mfma32a(const bf16x8& a, const bf16x8& b, const f32x16& c) {
@@ -45,30 +53,46 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_
 __device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
+// 16-byte direct-to-LDS buffer load: lane l's 16 bytes land at lds_dst + 16 l.
+// (A plain device function: host compilation never instantiates its body.)
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, char* lds_dst, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_dst, 16, voff, 0, 0, 0);
+}
 // Row halves are swapped when bit 2 xor bit 3 of the row is set (LDS banks).
 __device__ __forceinline__ int hswap(int r) { return ((r >> 2) ^ (r >> 3)) & 1; }
 // Key permutation inside a 32-key block: swap bits 2 and 3.
 __device__ __forceinline__ int kperm(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
+// Chunk swizzle of a K row of CPR 16-byte chunks (CPR = 16 for d = 128, 8 for
+// d = 64): the fragment reads of rows kperm(0..7), kperm(8..15) and of any 16
+// consecutive rows each land on distinct banks (checked exhaustively offline).
+template <int CPR> __device__ __forceinline__ int kswz(int r);
+template <> __device__ __forceinline__ int kswz<16>(int r) { return (r & 15) ^ (((r >> 3) & 1) << 2); }
+template <> __device__ __forceinline__ int kswz<8>(int r) { return (r & 7) ^ (((r >> 3) & 1) * 5); }
 
-template <int HD, int QB>
-__global__ __launch_bounds__(256) void attention_bf16_kernel(AttnParams p) {
-  // K tile: HD/16 planes (one per 16-wide d-step) of [64 keys][32 B];
-  // V^T tile: 4 planes (one per 16-key step) of [HD rows][32 B].
-  constexpr int KPL = KT * 32, KBYTES = (HD / 16) * KPL;
-  constexpr int VPL = HD * 32, VBYTES = 4 * VPL;
-  constexpr int STAGE = KBYTES + VBYTES;
-  __shared__ __attribute__((aligned(16))) char lds[2 * STAGE];
+template <int HD, int KT, int QB, int NW>
+__global__ __launch_bounds__(NW * 64) void attention_bf16_kernel(AttnParams p) {
+  constexpr int KB = KT / 32;                  // 32-key blocks per tile
+  // K stage: [64 keys][HD dims] (HD*2-byte rows), 16-byte chunk c of row r at
+  // chunk c ^ kswz(r).  V^T stage: 4 planes (one per 16-key step) of [HD rows][32 B].
+  constexpr int KROW = HD * 2, KBYTES = KT * KROW;
+  constexpr int VPL = HD * 32, VBYTES = (KT / 16) * VPL;
+  __shared__ __attribute__((aligned(1024))) char lds[2 * KBYTES + 2 * VBYTES];
+  char* const kbuf0 = lds;
+  char* const kbuf1 = lds + KBYTES;
+  char* const vbuf0 = lds + 2 * KBYTES;
+  char* const vbuf1 = lds + 2 * KBYTES + VBYTES;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, l32 = lane & 31;
   const int nblk = p.q_tiles * p.n_heads;
   const int lin = xcd_remap(blockIdx.x, nblk);
-  const int head = lin / p.q_tiles;          // all q-tiles of a head on one XCD range
+  const int head = lin / p.q_tiles;
   const int qtile = lin - head * p.q_tiles;
   const int N = p.n;
-  const int q0 = qtile * (4 * QB * 32) + wave * (QB * 32);
+  const int T = (N + KT - 1) / KT;
+  const int q0 = qtile * (NW * QB * 32) + wave * (QB * 32);
 
-  // ---- Q fragments (B operand of S^T = K Q^T): query q0+qb*32+l32, dims ks*16+h*8..+7
+  // ---- Q fragments (B operand of S^T = K Q^T)
   bf16x8 qf[QB][HD / 16];
   {
     const __amdgpu_buffer_rsrc_t rq = rsrc(p.q, (uint32_t)((uint64_t)N * p.ldq * 2));
@@ -82,28 +106,43 @@ __global__ __launch_bounds__(256) void attention_bf16_kernel(AttnParams p) {
       }
   }
 
-  // ---- staging assignment (conflict-free LDS stores: 16 lanes fill 8 rows x 32 B of one plane)
+  // ---- K tiles: direct-to-LDS loads.  A wave instruction fills 1 KiB =
+  // KT*KROW/1024 ... rows (HD*2 bytes each); lane l -> row r0 + l/(KROW/16),
+  // physical chunk l%(KROW/16), fetching logical chunk phys ^ kswz(row).
+  constexpr int CPR = KROW / 16;               // chunks per K row
+  constexpr int RPI = 64 / CPR;                // rows per DMA instruction
+  constexpr int KDMA = KT / RPI / NW;          // DMA instructions per wave per tile
+  static_assert(KDMA >= 1 && KDMA * RPI * NW == KT, "K tile does not split over the waves");
   const __amdgpu_buffer_rsrc_t rk = rsrc(p.k, (uint32_t)((uint64_t)N * p.ldk * 2));
-  const int st_pl = lane >> 4, st_row = (lane & 15) >> 1, st_h = lane & 1;
-  constexpr int KLOADS = (KT * HD / 8) / 256;   // 16-byte chunks per thread per K tile
-  constexpr int VLOADS = (HD * KT / 8) / 256;
-  u32x4 rk_[KLOADS], rv_[VLOADS];
-
-  auto gload = [&](int t) {
-    const int k0 = t * KT;
+  uint32_t kdma_off[KDMA];
 #pragma unroll
-    for (int i = 0; i < KLOADS; ++i) {
-      // plane group (i % (HD/64)) * 4 + st_pl, key block (i / (HD/64)) * 32 + wave * 8 + st_row
-      const int pl = (i % (HD / 64)) * 4 + st_pl;
-      const int key = (i / (HD / 64)) * 32 + wave * 8 + st_row;
-      const uint32_t off = (uint32_t)(k0 + key) * (uint32_t)p.ldk * 2u + (head * HD + pl * 16 + st_h * 8) * 2;
-      rk_[i] = bload16(rk, off);
-    }
+  for (int j = 0; j < KDMA; ++j) {
+    const int row = (j * NW + wave) * RPI + lane / CPR;
+    const int c = (lane % CPR) ^ kswz<CPR>(row);
+    kdma_off[j] = (uint32_t)row * (uint32_t)p.ldk * 2u + (head * HD + c * 8) * 2;
+  }
+  auto kdma = [&](int t, char* dst) {
+    const uint32_t kofs = (uint32_t)t * KT * (uint32_t)p.ldk * 2u;
+#pragma unroll
+    for (int j = 0; j < KDMA; ++j)
+      lds_dma16(rk, dst + (j * NW + wave) * RPI * KROW, kdma_off[j] + kofs);
+  };
+
+  // ---- V^T tiles: register staging (keys >= N are zeroed here)
+  // a wave instruction covers (KT/16) planes x (64/(KT/16)/2) rows x 2 halves
+  constexpr int VPLN = KT / 16;                // planes per tile
+  constexpr int VRPW = 32 / VPLN;              // V^T rows per wave instruction
+  const int st_pl = lane / (64 / VPLN), st_row = (lane % (64 / VPLN)) >> 1, st_h = lane & 1;
+  constexpr int VLOADS = (HD * KT / 8) / (NW * 64);
+  static_assert(VLOADS >= 1 && VLOADS * NW * VRPW == HD, "V^T tile does not split over the waves");
+  u32x4 rv_[VLOADS];
+  auto vload = [&](int t) {
+    const int k0 = t * KT;
     const bool full = k0 + KT <= N;
 #pragma unroll
     for (int i = 0; i < VLOADS; ++i) {
-      const int row = i * 32 + wave * 8 + st_row;             // dv
-      const int key0 = k0 + st_pl * 16 + st_h * 8;            // first key of the chunk
+      const int row = i * (NW * VRPW) + wave * VRPW + st_row;
+      const int key0 = k0 + st_pl * 16 + st_h * 8;
       const bf16* src = p.vt + (int64_t)(head * HD + row) * p.ldvt + key0;
       if (full) {
         rv_[i] = *reinterpret_cast<const u32x4*>(src);
@@ -120,24 +159,22 @@ __global__ __launch_bounds__(256) void attention_bf16_kernel(AttnParams p) {
       }
     }
   };
-  auto lstore = [&](char* base) {
-#pragma unroll
-    for (int i = 0; i < KLOADS; ++i) {
-      const int pl = (i % (HD / 64)) * 4 + st_pl;
-      const int key = (i / (HD / 64)) * 32 + wave * 8 + st_row;
-      *reinterpret_cast<u32x4*>(base + pl * KPL + key * 32 + ((st_h ^ hswap(key)) << 4)) = rk_[i];
-    }
+  auto vstore = [&](char* base) {
 #pragma unroll
     for (int i = 0; i < VLOADS; ++i) {
-      const int row = i * 32 + wave * 8 + st_row;
-      *reinterpret_cast<u32x4*>(base + KBYTES + st_pl * VPL + row * 32 + ((st_h ^ hswap(row)) << 4)) = rv_[i];
+      const int row = i * (NW * VRPW) + wave * VRPW + st_row;
+      *reinterpret_cast<u32x4*>(base + st_pl * VPL + row * 32 + ((st_h ^ hswap(row)) << 4)) = rv_[i];
     }
   };
 
-  // fragment addresses: K row kperm(l32) (+ kb*32), V^T row l32 (+ db*32)
+  // ---- fragment addresses.  K: row kperm(l32) (+ kb*32), chunk 2ks+h;
+  // V^T: row l32 (+ db*32), plane = 16-key step.
   const int kr = kperm(l32);
-  const int k_frag = kr * 32 + ((h ^ hswap(kr)) << 4);
-  const int v_frag = KBYTES + l32 * 32 + ((h ^ hswap(l32)) << 4);
+  const int kq = kswz<CPR>(kr);
+  int k_off[HD / 16];
+#pragma unroll
+  for (int ks = 0; ks < HD / 16; ++ks) k_off[ks] = kr * KROW + (((2 * ks + h) ^ kq) << 4);
+  const int v_frag = l32 * 32 + ((h ^ hswap(l32)) << 4);
 
   f32x16 O[HD / 32][QB];
 #pragma unroll
@@ -148,54 +185,40 @@ __global__ __launch_bounds__(256) void attention_bf16_kernel(AttnParams p) {
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) { m_run[qb] = -INFINITY; l_run[qb] = 0.f; }
 
-  const int T = (N + KT - 1) / KT;
-  gload(0);
-  lstore(lds);
-  __syncthreads();
-  for (int t = 0; t < T; ++t) {
-    const char* cur = lds + (t & 1) * STAGE;
-    if (t + 1 < T) gload(t + 1);
-
-    // ---- S^T[key][query] for 64 keys x QB*32 queries
-    f32x16 S[2][QB];
+  auto scores = [&](const char* kb_base, f32x16 (&S)[KB][QB]) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) S[kb][qb] = f32x16{};
 #pragma unroll
-    for (int ks = 0; ks < HD / 16; ++ks) {
+    for (int ks = 0; ks < HD / 16; ++ks)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(cur + ks * KPL + kb * 1024 + k_frag);
+      for (int kb = 0; kb < KB; ++kb) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kb_base + kb * 32 * KROW + k_off[ks]);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) S[kb][qb] = mfma32a(a, qf[qb][ks], S[kb][qb]);
       }
-    }
-    // ---- mask keys >= N (last tile only).  Lane half h, register r of key
-    // block kb holds key kb*32 + 16*(r/8) + 8h + r%8.
-    if ((t + 1) * KT > N) {
+  };
+
+  // keys >= N of the last tile: lane half h, register r of key block kb holds
+  // key kb*32 + 16*(r/8) + 8h + r%8
+  auto mask_tail = [&](f32x16 (&S)[KB][QB], int t) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = t * KT + kb * 32 + 16 * (r >> 3) + 8 * h + (r & 7);
-          if (key >= N) {
+      for (int r = 0; r < 16; ++r) {
+        const bool out = t * KT + kb * 32 + 16 * (r >> 3) + 8 * h + (r & 7) >= N;
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb) S[kb][qb][r] = -INFINITY;
-          }
-        }
-    }
-    // ---- online softmax (log2 domain), P rounded to bf16 for the MFMA.
-    // The reference max m_run is raised (and O, l rescaled) only when some
-    // lane's tile maximum exceeds it by more than kRescaleLog2; otherwise the
-    // old reference is kept and p <= 2^kRescaleLog2.  O / l at the end is the
-    // same either way.
-    bf16x8 P[2][2][QB];
+        for (int qb = 0; qb < QB; ++qb) S[kb][qb][r] = out ? -INFINITY : S[kb][qb][r];
+      }
+  };
+  // softmax of one tile (scores S) -> P; rescales O and l when the reference max moves
+  auto softmax = [&](const f32x16 (&S)[KB][QB], bf16x8 (&P)[KB][2][QB]) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       float mx = -INFINITY;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[kb][qb][r]);
       mx = fmaxf(mx, __shfl_xor(mx, 32, kWave)) * p.scale_log2;
@@ -205,12 +228,15 @@ __global__ __launch_bounds__(256) void attention_bf16_kernel(AttnParams p) {
         l_run[qb] *= alpha;
         m_run[qb] = m_new;
 #pragma unroll
-        for (int db = 0; db < HD / 32; ++db) O[db][qb] *= alpha;
+        for (int db = 0; db < HD / 32; ++db) {   // one 16-register tile at a time
+          O[db][qb] *= alpha;
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
       const float m_ref = m_run[qb];
       float ls = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int m = 0; m < 2; ++m)
 #pragma unroll
@@ -221,20 +247,64 @@ __global__ __launch_bounds__(256) void attention_bf16_kernel(AttnParams p) {
           }
       l_run[qb] += ls;
     }
-    // ---- O^T[dv][query] += V^T[dv][keys] P^T[keys][query]
+  };
+
+  auto pv = [&](const char* vb, const bf16x8 (&P)[KB][2][QB]) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int m = 0; m < 2; ++m)
 #pragma unroll
         for (int db = 0; db < HD / 32; ++db) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(cur + (2 * kb + m) * VPL + db * 1024 + v_frag);
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(vb + (2 * kb + m) * VPL + db * 1024 + v_frag);
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) O[db][qb] = mfma32a(a, P[kb][m][qb], O[db][qb]);
         }
+  };
 
-    if (t + 1 < T) lstore(lds + ((t + 1) & 1) * STAGE);
+  // ---- prologue: K_0, K_1 and V_0 in LDS, S_0 computed
+  kdma(0, kbuf0);
+  if (T > 1) kdma(1, kbuf1);
+  vload(0);
+  vstore(vbuf0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);          // vmcnt = 0: the K loads have landed
+  __syncthreads();
+  f32x16 Sa[KB][QB], Sb[KB][QB];
+  bf16x8 P[KB][2][QB];
+  scores(kbuf0, Sa);
+  __syncthreads();                             // kbuf0 is refilled in iteration 0
+
+  // ---- iteration t: S_{t+1} = K_{t+1} Q^T runs alongside softmax(S_t);
+  // then O += V_t P_t.  K_{t+2} and V_{t+1} are staged meanwhile.  Past the
+  // last tile these loads and scores are harmless extra work (K rows >= N
+  // load as zero, V^T past N is zeroed, stale LDS stays finite) and keep the
+  // loop body free of branches.
+  auto step = [&](int t, f32x16 (&Scur)[KB][QB], f32x16 (&Snext)[KB][QB]) {
+    char* kdst = (t & 1) ? kbuf1 : kbuf0;       // held K_t (consumed in iteration t-1)
+    const char* ksrc = (t & 1) ? kbuf0 : kbuf1; // K_{t+1}
+    const char* vsrc = (t & 1) ? vbuf1 : vbuf0; // V_t
+    char* vdst = (t & 1) ? vbuf0 : vbuf1;       // V_{t+1}
+    kdma(t + 2, kdst);
+    vload(t + 1);
+    scores(ksrc, Snext);
+    softmax(Scur, P);
+    pv(vsrc, P);
+    vstore(vdst);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
+  };
+  int t = 0;
+  for (; t + 2 < T; t += 2) {                  // all but the last one or two tiles
+    step(t, Sa, Sb);
+    step(t + 1, Sb, Sa);
+  }
+  if (T - t == 2) {
+    step(t, Sa, Sb);
+    mask_tail(Sb, t + 1);
+    step(t + 1, Sb, Sa);
+  } else {
+    mask_tail(Sa, t);
+    step(t, Sa, Sb);
   }
 
   // ---- normalise and store: register r of tile db holds dv = db*32 + 8*(r/4) + 4h + r%4
@@ -326,7 +396,7 @@ __global__ __launch_bounds__(64) void attention_f32_kernel(AttnParamsF p) {
 }
 
 // ---------------------------------------------------------------------------
-template <int HD, int QB>
+template <int HD, int KT, int QB, int NW>
 static void launch_bf16_attn(const AttentionArgs& a, hipStream_t stream) {
   AttnParams p;
   p.q = (const bf16*)a.q; p.ldq = a.ldq;
@@ -334,9 +404,9 @@ static void launch_bf16_attn(const AttentionArgs& a, hipStream_t stream) {
   p.vt = (const bf16*)a.vt; p.ldvt = a.ldvt;
   p.o = (bf16*)a.o; p.ldo = a.ldo;
   p.n = a.n; p.n_heads = a.n_heads;
-  p.q_tiles = (a.n + 4 * QB * 32 - 1) / (4 * QB * 32);
+  p.q_tiles = (a.n + NW * QB * 32 - 1) / (NW * QB * 32);
   p.scale_log2 = 1.4426950408889634f / sqrtf((float)HD);
-  attention_bf16_kernel<HD, QB><<<dim3(p.q_tiles * p.n_heads), dim3(256), 0, stream>>>(p);
+  attention_bf16_kernel<HD, KT, QB, NW><<<dim3(p.q_tiles * p.n_heads), dim3(NW * 64), 0, stream>>>(p);
 }
 
 template <int HD>
@@ -357,15 +427,8 @@ hipError_t launch_attention(const AttentionArgs& a, hipStream_t stream) {
     if (a.head_dim == 64) launch_f32_attn<64>(a, stream);
     else launch_f32_attn<128>(a, stream);
   } else {
-    // Two query blocks per wave when there is enough work to fill the chip
-    // several times over; one otherwise (shorter tail).
-    const int64_t wg2 = (int64_t)((a.n + 255) / 256) * a.n_heads;
-    const bool qb2 = wg2 >= 4 * 256;
-    if (a.head_dim == 64) {
-      if (qb2) launch_bf16_attn<64, 2>(a, stream); else launch_bf16_attn<64, 1>(a, stream);
-    } else {
-      if (qb2) launch_bf16_attn<128, 2>(a, stream); else launch_bf16_attn<128, 1>(a, stream);
-    }
+    if (a.head_dim == 64) launch_bf16_attn<64, 64, H3K_QB, H3K_NW>(a, stream);
+    else launch_bf16_attn<128, H3K_ATTN_KT, H3K_QB, H3K_NW>(a, stream);
   }
   return hipGetLastError();
 }
