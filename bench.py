@@ -52,6 +52,30 @@ def ln_bytes(N, D, eb=2):
     return 2.0 * N * D * eb + 2.0 * D * 4
 
 
+COPY_BYTES = 512 * 2**20
+KERNEL_SOURCES = {"attention": "attention.hip", "qkv": "gemm.hip", "out_proj": "gemm.hip", "mlp_up": "gemm.hip",
+                  "mlp_down": "gemm.hip"}
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary (profiles/traffic.json), or None when the kernel's source file has
+    changed since the counters were taken (its sha256 no longer matches)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    src = os.path.join(ROOT, "video_diffusion_transformer_adaln_amd", "csrc", KERNEL_SOURCES.get(kernel, ""))
+    if not os.path.exists(path) or not os.path.isfile(src):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(kernel)
+    if not rec:
+        return None
+    with open(src, "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != rec.get("source_sha256"):
+            return None
+    return rec.get("hbm_bytes_per_launch")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -60,6 +84,8 @@ def main():
     ap.add_argument("--layers", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-layers45", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run one plain 512 MiB device copy first (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the DiT step runs on a single MI355X here "
@@ -95,6 +121,15 @@ def main():
     out = torch.empty_like(x)
     torch.cuda.synchronize()
     log(f"inputs ready in {time.time() - t0:.1f} s; workspace {stack.workspace.numel() / 2**30:.2f} GiB")
+
+    if args.calibrate_copy:
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log(f"calibration copy of {COPY_BYTES} bytes done")
 
     # ---- warmup
     for i in range(args.warmup):
@@ -155,7 +190,7 @@ def main():
     dom_avg = per_kernel[dom]["avg_ms"]
     achieved = fl[dom] / (dom_avg * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(dom),
                 "algorithmic_per_launch": f"{fl[dom] / 1e12:.3f} TFLOP"}
 
     cpu = None
