@@ -2,15 +2,20 @@
 // activations [m, k] and W the weight [n, k] (both k-contiguous).
 //
 //  * bf16 path: 256x256x64 workgroup tile, 8 waves (two per SIMD, so one
-//    wave's memory instructions and waits overlap the other's MFMAs), each
-//    wave a 64x128 sub-tile of v_mfma_f32_32x32x16_bf16 (fp32 accumulators
-//    in VGPRs).  Operands are staged through double-buffered, swizzled LDS
-//    (128 KiB of gfx950's 160 KiB); the loads of k-tile t+2 are in flight
-//    while t is multiplied and t+1 is stored to LDS.
+//    wave's waits overlap the other's MFMAs), each wave a 64x128 sub-tile of
+//    v_mfma_f32_32x32x16_bf16 (fp32 accumulators in VGPRs).  Operands go
+//    global -> LDS by direct-to-LDS loads (buffer_load ... lds) into a ring
+//    of five 32 KiB operand slots (all 160 KiB of gfx950's LDS), so the
+//    activation tile of k-tile t+2 and the weight tile of t+1 are in flight
+//    while t is multiplied.  Each load instruction moves 8 whole 128-byte
+//    rows: measured on MI355X, half-line (64-byte) row pieces halve the
+//    vector-memory return rate, and one k-tile of loads in flight per
+//    workgroup cannot cover the loaded L2/Infinity-Cache latency.
 //  * int8-weight path (W8A16): the weight tile is read as int8 (half the
-//    bytes), widened to bf16 exactly while it is staged into LDS, multiplied
-//    on the bf16 MFMA, and the per-output-channel scale is applied to the
-//    fp32 accumulator in the epilogue (it factors out of the k-sum).
+//    bytes) into registers, widened to bf16 exactly while it is stored into
+//    double-buffered LDS, multiplied on the bf16 MFMA, and the
+//    per-output-channel scale is applied to the fp32 accumulator in the
+//    epilogue (it factors out of the k-sum).
 //  * fp32 path: a plain LDS-tiled SIMT kernel for the small fp32 workload.
 //
 // Epilogues (fused, fp32 math, one rounding at the store): bias; bias + GELU
@@ -87,6 +92,85 @@ __device__ __forceinline__ int plane_off(int ks, int r, int h) {
   return ks * kPlaneBytes + r * 32 + ((h ^ half_swap(r)) << 4);
 }
 
+// Fused epilogue of one wave's 64x128 accumulator sub-tile.
+template <int EPI, bool W8>
+__device__ __forceinline__ void store_tile(const GemmParams& p, const f32x16 (&acc)[2][4], int a_row0, int b_row0,
+                                           int tok0, int feat0, bool trans, int lane) {
+  // ---- epilogue.  Accumulator register r of lane l in tile (i, j):
+  //      A-row = a_row0 + i*32 + 8*(r/4) + 4*(l/32) + r%4, B-row = b_row0 + j*32 + l%32.
+  const float* wsc = p.w_scale;
+  if (!trans) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int f = feat0 + a_row0 + i * 32 + 8 * g + 4 * (lane >> 5);
+          const int t = tok0 + b_row0 + j * 32 + (lane & 31);
+          if (t >= p.m || f >= p.n) continue;
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            v[e] = acc[i][j][4 * g + e];
+            if constexpr (W8) v[e] *= wsc[f + e];
+            if (p.bias) v[e] += static_cast<float>(p.bias[f + e]);
+          }
+          if ((int64_t)f >= p.split_col) {   // straddling tile: transposed part, bias only
+#pragma unroll
+            for (int e = 0; e < 4; ++e) p.yt[(int64_t)(f + e - p.split_col) * p.ldyt + t] = static_cast<bf16>(v[e]);
+            continue;
+          }
+          if constexpr (EPI == kEpiGelu) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = gelu_tanh(v[e]);
+          }
+          if constexpr (EPI == kEpiGatedResidual) {
+            const u32x2 rr = *reinterpret_cast<const u32x2*>(p.residual + (int64_t)t * p.ldr + f);
+            const bf16* re = reinterpret_cast<const bf16*>(&rr);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = static_cast<float>(re[e]) + p.gate[f + e] * v[e];
+          }
+          u32x2 out;
+          bf16* oe = reinterpret_cast<bf16*>(&out);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) oe[e] = static_cast<bf16>(v[e]);
+          *reinterpret_cast<u32x2*>(p.y + (int64_t)t * p.ldy + f) = out;
+        }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int t0 = tok0 + a_row0 + i * 32 + 8 * g + 4 * (lane >> 5);
+          const int f = feat0 + b_row0 + j * 32 + (lane & 31);
+          if (f >= p.n || t0 >= p.m) continue;
+          const float sc = W8 ? wsc[f] : 1.0f;
+          const float bb = p.bias ? static_cast<float>(p.bias[f]) : 0.0f;
+          u32x2 out;
+          bf16* oe = reinterpret_cast<bf16*>(&out);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float v = acc[i][j][4 * g + e];
+            if constexpr (W8) v *= sc;
+            oe[e] = static_cast<bf16>(v + bb);
+          }
+          bf16* dst = p.yt + (int64_t)(f - p.split_col) * p.ldyt + t0;
+          if (t0 + 3 < p.m) {
+            *reinterpret_cast<u32x2*>(dst) = out;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (t0 + e < p.m) dst[e] = oe[e];
+          }
+        }
+  }
+}
+
+// Register-staged kernel; launched for int8 weights (the widening happens
+// between the global load and the LDS store).
 template <int EPI, bool W8>
 __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmParams p) {
   __shared__ __attribute__((aligned(16))) char lds[4 * kTileBytes];   // X0 W0 X1 W1
@@ -213,77 +297,154 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmParams p) {
     if (kt + 1 < KT) load_frags(nxt, 0, f0a, f0b);
   }
 
-  // ---- epilogue.  Accumulator register r of lane l in tile (i, j):
-  //      A-row = a_row0 + i*32 + 8*(r/4) + 4*(l/32) + r%4, B-row = b_row0 + j*32 + l%32.
-  const float* wsc = p.w_scale;
-  if (!trans) {
+  store_tile<EPI, W8>(p, acc, a_row0, b_row0, tok0, feat0, trans, lane);
+}
+
+// ---------------------------------------------------------------------------
+// bf16-weight kernel with direct-to-LDS loads (buffer_load ... lds): no
+// staging registers and no LDS store instructions.  An operand's k-tile is
+// [256 rows][128 B], 16-byte chunk c of row r stored at chunk c ^ rswz(r)
+// (fragment reads of 8 or 16 consecutive rows hit distinct banks).  The
+// swizzle is applied on the source side: lane l of a load writes row
+// r0 + l/8, chunk l%8, and so fetches logical chunk (l%8) ^ rswz(row).
+//
+// Synchronisation: the workgroup barriers carry no memory fence.  A fence
+// makes the compiler wait for every outstanding vector-memory load (vmcnt(0)),
+// which would drain the ring at each k-tile; instead each wave waits
+// (vmcnt) for its own loads of the next k-tile, then all waves meet at
+// s_barrier, after which the whole tile is visible in LDS.
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, char* lds_dst, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_dst, 16, voff, 0, 0, 0);
+}
+// barrier without a fence; the empty asm statements keep the compiler from
+// moving memory accesses across it
+__device__ __forceinline__ void wg_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+// s_waitcnt vmcnt(N), expcnt and lgkmcnt left at their maxima
+template <int N> __device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+__device__ __forceinline__ int rswz(int r) { return (r ^ (r >> 3)) & 7; }
+constexpr int kSlot = 256 * 128;   // one operand's k-tile of 64: [256 rows][128 B]
+constexpr int kSlots = 5;          // 160 KiB
+
+template <int EPI>
+__global__ __launch_bounds__(512) void gemm_bf16_dma_kernel(GemmParams p) {
+  __shared__ __attribute__((aligned(1024))) char lds[kSlots * kSlot];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  const int nblk = p.tiles_m * p.tiles_n;
+  const int lin = xcd_remap(blockIdx.x, nblk);
+  const int per_group = kGroupM * p.tiles_n;
+  const int group = lin / per_group;
+  const int first_m = group * kGroupM;
+  const int gm = min(p.tiles_m - first_m, kGroupM);
+  const int in_group = lin - group * per_group;
+  const int tile_m = first_m + in_group % gm;
+  const int tile_n = in_group / gm;
+  const int tok0 = tile_m * BM, feat0 = tile_n * BN;
+  const bool trans = (int64_t)feat0 >= p.split_col;
+  const int KT = p.k / BK;
+
+  // Ring of 5 operand slots; position q holds operand q&1 (0: activations,
+  // 1: weights) of k-tile q>>1, in slot q%5.  Loads: instruction j (0..3)
+  // of wave w covers rows (8 j + w) * 8 .. +8; rswz(lrow + 64 j) == rswz(lrow).
+  const __amdgpu_buffer_rsrc_t rsx = make_rsrc(p.x, (uint32_t)((uint64_t)p.m * p.ldx * 2));
+  const __amdgpu_buffer_rsrc_t rsw = make_rsrc(p.w, (uint32_t)((uint64_t)p.n * p.ldw * 2));
+  const int lrow = wave * 8 + (lane >> 3);
+  const uint32_t c16 = (uint32_t)(((lane & 7) ^ rswz(lrow)) * 16);
+  const uint32_t xo0 = (uint32_t)(tok0 + lrow) * (uint32_t)p.ldx * 2u + c16;
+  const uint32_t wo0 = (uint32_t)(feat0 + lrow) * (uint32_t)p.ldw * 2u + c16;
+  const uint32_t xstep = 64u * (uint32_t)p.ldx * 2u, wstep = 64u * (uint32_t)p.ldw * 2u;
+  // half h (0/1) of position q: instructions 2h, 2h+1; past the end the last
+  // k-tile is re-loaded into the (unread) slot so the load counts stay uniform
+  auto issue = [&](int q, int h) {
+    int kt = q >> 1;
+    kt = kt < KT ? kt : KT - 1;
+    char* st = lds + (q % kSlots) * kSlot + wave * 1024;
+    const uint32_t kb = (uint32_t)kt * BK * 2u;
+    const bool isw = q & 1;
+    const __amdgpu_buffer_rsrc_t r = isw ? rsw : rsx;
+    const uint32_t o0 = (isw ? wo0 : xo0) + kb, step = isw ? wstep : xstep;
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      const int j = 2 * h + jj;
+      lds_dma16(r, st + j * 8192, o0 + j * step);
+    }
+  };
+
+  f32x16 acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+
+  // fragment of 32-row block i, k-step ks: row row0 + 32 i + rl, logical chunk
+  // 2 ks + h -> physical (2 ks) ^ 4 (i & 1) ^ q, q = h ^ rswz(rl)
+  const int a_row0 = (wave & 3) * 64;
+  const int b_row0 = (wave >> 2) * 128;
+  const int rl = lane & 31;
+  const int qq = (lane >> 5) ^ rswz(rl);
+  int lo[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) lo[c] = rl * 128 + (((2 * c) ^ qq) << 4);
+  // A is the weight (row-major output) or the activation (transposed output)
+  const int a_op = trans ? 0 : 1;
+  auto load_frags = [&](int t, int ks, bf16x8 (&fa)[2], bf16x8 (&fb)[4]) {
+    const char* sa = lds + ((2 * t + a_op) % kSlots) * kSlot + a_row0 * 128;
+    const char* sb = lds + ((2 * t + 1 - a_op) % kSlots) * kSlot + b_row0 * 128;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      fa[i] = *reinterpret_cast<const bf16x8*>(sa + i * 4096 + lo[((2 * ks) ^ (4 * (i & 1))) >> 1]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      fb[j] = *reinterpret_cast<const bf16x8*>(sb + j * 4096 + lo[((2 * ks) ^ (4 * (j & 1))) >> 1]);
+  };
+  auto mfmas = [&](const bf16x8 (&fa)[2], const bf16x8 (&fb)[4]) {
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int f = feat0 + a_row0 + i * 32 + 8 * g + 4 * (lane >> 5);
-          const int t = tok0 + b_row0 + j * 32 + (lane & 31);
-          if (t >= p.m || f >= p.n) continue;
-          float v[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            v[e] = acc[i][j][4 * g + e];
-            if constexpr (W8) v[e] *= wsc[f + e];
-            if (p.bias) v[e] += static_cast<float>(p.bias[f + e]);
-          }
-          if ((int64_t)f >= p.split_col) {   // straddling tile: transposed part, bias only
-#pragma unroll
-            for (int e = 0; e < 4; ++e) p.yt[(int64_t)(f + e - p.split_col) * p.ldyt + t] = static_cast<bf16>(v[e]);
-            continue;
-          }
-          if constexpr (EPI == kEpiGelu) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = gelu_tanh(v[e]);
-          }
-          if constexpr (EPI == kEpiGatedResidual) {
-            const u32x2 rr = *reinterpret_cast<const u32x2*>(p.residual + (int64_t)t * p.ldr + f);
-            const bf16* re = reinterpret_cast<const bf16*>(&rr);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = static_cast<float>(re[e]) + p.gate[f + e] * v[e];
-          }
-          u32x2 out;
-          bf16* oe = reinterpret_cast<bf16*>(&out);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) oe[e] = static_cast<bf16>(v[e]);
-          *reinterpret_cast<u32x2*>(p.y + (int64_t)t * p.ldy + f) = out;
-        }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int t0 = tok0 + a_row0 + i * 32 + 8 * g + 4 * (lane >> 5);
-          const int f = feat0 + b_row0 + j * 32 + (lane & 31);
-          if (f >= p.n || t0 >= p.m) continue;
-          const float sc = W8 ? wsc[f] : 1.0f;
-          const float bb = p.bias ? static_cast<float>(p.bias[f]) : 0.0f;
-          u32x2 out;
-          bf16* oe = reinterpret_cast<bf16*>(&out);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            float v = acc[i][j][4 * g + e];
-            if constexpr (W8) v *= sc;
-            oe[e] = static_cast<bf16>(v + bb);
-          }
-          bf16* dst = p.yt + (int64_t)(f - p.split_col) * p.ldyt + t0;
-          if (t0 + 3 < p.m) {
-            *reinterpret_cast<u32x2*>(dst) = out;
-          } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (t0 + e < p.m) dst[e] = oe[e];
-          }
-        }
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(fa[i], fb[j], acc[i][j]);
+  };
+
+  // prologue: positions 0, 1, 2 in flight; 0 and 1 (k-tile 0) must be complete
+  for (int q = 0; q < 3; ++q) {
+    issue(q, 0);
+    issue(q, 1);
   }
+  wait_vmcnt<4>();
+  wg_barrier();
+  bf16x8 f0a[2], f0b[4], f1a[2], f1b[4];
+  for (int t = 0; t < KT; ++t) {
+    // positions 2t+3 (weights of t+1) and 2t+4 (activations of t+2) go to the
+    // slots of k-tile t-1, whose readers all passed the last barrier
+    load_frags(t, 0, f0a, f0b);
+    issue(2 * t + 3, 0);
+    load_frags(t, 1, f1a, f1b);
+    issue(2 * t + 3, 1);
+    mfmas(f0a, f0b);
+    __builtin_amdgcn_sched_barrier(0);
+    load_frags(t, 2, f0a, f0b);
+    issue(2 * t + 4, 0);
+    mfmas(f1a, f1b);
+    __builtin_amdgcn_sched_barrier(0);
+    load_frags(t, 3, f1a, f1b);
+    issue(2 * t + 4, 1);
+    mfmas(f0a, f0b);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(f1a, f1b);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<4>();   // own loads of k-tile t+1 have landed; activations of t+2 may fly
+    wg_barrier();
+  }
+  wait_vmcnt<0>();
+  constexpr bool W8 = false;
+  store_tile<EPI, W8>(p, acc, a_row0, b_row0, tok0, feat0, trans, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -367,7 +528,10 @@ static void launch_bf16(const LinearArgs& a, hipStream_t stream) {
   p.m = (int)a.m; p.n = (int)a.n; p.k = (int)a.k;
   p.tiles_m = (p.m + BM - 1) / BM;
   p.tiles_n = (p.n + BN - 1) / BN;
-  gemm_bf16_kernel<EPI, W8><<<dim3(p.tiles_m * p.tiles_n), dim3(512), 0, stream>>>(p);
+  if constexpr (W8)
+    gemm_bf16_kernel<EPI, W8><<<dim3(p.tiles_m * p.tiles_n), dim3(512), 0, stream>>>(p);
+  else
+    gemm_bf16_dma_kernel<EPI><<<dim3(p.tiles_m * p.tiles_n), dim3(512), 0, stream>>>(p);
 }
 
 template <int EPI>
