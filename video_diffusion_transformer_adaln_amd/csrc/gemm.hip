@@ -331,6 +331,9 @@ template <int N> __device__ __forceinline__ void wait_vmcnt() {
 __device__ __forceinline__ int rswz(int r) { return (r ^ (r >> 3)) & 7; }
 constexpr int kSlot = 256 * 128;   // one operand's k-tile of 64: [256 rows][128 B]
 constexpr int kSlots = 5;          // 160 KiB
+// m-tiles per group in this kernel's tile order (the 32 workgroups resident
+// on one XCD then cover 2 m-tiles x 16 n-tiles); measured best of 1..32
+constexpr int kRingGroupM = 2;
 
 template <int EPI>
 __global__ __launch_bounds__(512) void gemm_bf16_dma_kernel(GemmParams p) {
@@ -340,10 +343,10 @@ __global__ __launch_bounds__(512) void gemm_bf16_dma_kernel(GemmParams p) {
 
   const int nblk = p.tiles_m * p.tiles_n;
   const int lin = xcd_remap(blockIdx.x, nblk);
-  const int per_group = kGroupM * p.tiles_n;
+  const int per_group = kRingGroupM * p.tiles_n;
   const int group = lin / per_group;
-  const int first_m = group * kGroupM;
-  const int gm = min(p.tiles_m - first_m, kGroupM);
+  const int first_m = group * kRingGroupM;
+  const int gm = min(p.tiles_m - first_m, kRingGroupM);
   const int in_group = lin - group * per_group;
   const int tile_m = first_m + in_group % gm;
   const int tile_n = in_group / gm;
