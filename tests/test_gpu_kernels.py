@@ -102,6 +102,9 @@ GEMM_CASES = [
     (1, 64, 64, 0, "bf16", False, None, True),
     (513, 768, 256, 0, "bf16", False, 512, True),     # Q|K row-major, V transposed (straddling tile)
     (300, 1536, 256, 0, "bf16", False, 1024, True),   # split on a tile boundary
+    (257, 328, 192, 2, "bf16", False, None, True),    # 3 k-tiles, ragged n
+    (129, 264, 320, 1, "bf16", False, None, True),    # 5 k-tiles: the operand ring wraps
+    (700, 520, 704, 0, "bf16", False, 264, True),     # 11 k-tiles, straddling transposed split
     (300, 320, 128, 0, "bf16", True, None, True),
     (300, 576, 192, 2, "bf16", True, None, True),
     (97, 1024, 256, 0, "bf16", True, 512, True),
