@@ -84,6 +84,8 @@ def main():
     ap.add_argument("--layers", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-layers45", action="store_true")
+    ap.add_argument("--no-extra-blocks", action="store_true",
+                    help="skip the int8-weight block and the 6144-token block timings")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one plain 512 MiB device copy first (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -193,6 +195,10 @@ def main():
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(dom),
                 "algorithmic_per_launch": f"{fl[dom] / 1e12:.3f} TFLOP"}
 
+    extra = {}
+    if not args.no_extra_blocks:
+        extra = extra_blocks(blocks[0], x, c)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(step_flops, L)
@@ -221,7 +227,99 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
+    result.update(extra)
     print(json.dumps(result), flush=True)
+
+
+def _time_block(cfg, tensors, x, c, reps=5):
+    """Mean ms of one block forward, and the per-kernel event summary."""
+    import torch
+    from video_diffusion_transformer_adaln_amd import binding as B
+    from video_diffusion_transformer_adaln_amd import runtime as R
+    st = R.DitStack(cfg, [tensors])
+    out = torch.empty_like(x)
+    st.forward(x, c, out)
+    torch.cuda.synchronize()
+    prof = B.Profiler(capacity=8 * reps + 16)
+    stats = prof.stats()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        st.forward(x, c, out, stats=stats)
+    e1.record()
+    torch.cuda.synchronize()
+    kern = prof.summary()
+    prof.close()
+    if not torch.isfinite(out.float()).all():
+        log("non-finite output in an extra block")
+        sys.exit(3)
+    return e0.elapsed_time(e1) / reps, kern
+
+
+def extra_blocks(b0, x, c):
+    """Two more measured units besides the step: the int8-weight block (the
+    four projection weights of block 0 quantised per output row by the
+    library's quantiser, W8A16 GEMMs) and one bf16 block at 6144 tokens,
+    D=3072 (512x512x22-frame latent).  Inputs as for the step."""
+    import torch
+    import seeded_inputs as si
+    from video_diffusion_transformer_adaln_amd import binding as B
+    from video_diffusion_transformer_adaln_amd import runtime as R
+    res = {}
+    # ---- int8 projection weights
+    sh = si.C4
+    N, D, F, C, H, d = sh.n_tokens, sh.hidden, sh.mlp_hidden, sh.cond_dim, sh.n_heads, sh.head_dim
+    t8 = {k: v for k, v in b0.items() if k in ("w_ada", "b_ada", "b_qkv", "b_out", "b_up", "b_down")}
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n_el = 0
+    e0.record()
+    for name in si.MATRIX_NAMES:
+        q, s = R.quantize_int8(b0[name])
+        t8[name], t8["s_" + name[2:]] = q, s
+        n_el += b0[name].numel()
+    e1.record()
+    torch.cuda.synchronize()
+    q_ms = e0.elapsed_time(e1)
+    rows = sum(b0[n].shape[0] for n in si.MATRIX_NAMES)
+    q_bytes = n_el * (2 + 1) + rows * 4
+    cfg8 = B.make_config(N, D, H, d, F, C, B.H3K_BF16, B.H3K_INT8, True)
+    ms8, kern8 = _time_block(cfg8, t8, x, c)
+    fl = block_flops(N, D, F, C)
+    k8 = {}
+    for name in ("qkv", "out_proj", "mlp_up", "mlp_down"):
+        v = kern8[name]
+        avg = v["total_ms"] / v["launches"]
+        k8[name] = {"avg_ms": round(avg, 4), "tflops": round(fl[name] / (avg * 1e-3) / 1e12, 1)}
+    res["int8_block"] = {
+        "workload": "one block at 22680 tokens with int8 QKV/out/up/down weights (per-row scales), "
+                    "bf16 activations, W8A16 GEMMs on the bf16 MFMA",
+        "ms_per_block": round(ms8, 3), "tflops": round(sum(fl.values()) / (ms8 * 1e-3) / 1e12, 1),
+        "gemm_kernels": k8,
+        "projection_weight_bytes": {"int8": int(n_el + rows * 4), "bf16": int(2 * n_el)},
+        "quantiser": {"ms_for_4_matrices": round(q_ms, 3), "gbs": round(q_bytes / (q_ms * 1e-3) / 1e9, 1)},
+    }
+    log(f"int8-weight block: {ms8:.2f} ms; quantiser {q_ms:.3f} ms")
+    del t8
+    # ---- 6144-token bf16 block
+    sh = si.C1
+    N, D, F, C, H, d = sh.n_tokens, sh.hidden, sh.mlp_hidden, sh.cond_dim, sh.n_heads, sh.head_dim
+    t1 = {}
+    for i, (name, shp) in enumerate(sh.weight_shapes().items()):
+        if name.startswith("b_"):
+            t1[name] = torch.zeros(shp, dtype=torch.bfloat16, device="cuda")
+        else:
+            t1[name] = si.torch_device_normal(shp, si.WEIGHT_STD, si.BASE_SEED, 500_000 + i, "cuda", torch.bfloat16)
+    x1 = si.torch_device_normal((N, D), 1.0, si.BASE_SEED, 599_000, "cuda", torch.bfloat16)
+    c1 = si.torch_device_normal((C,), 1.0, si.BASE_SEED, 599_001, "cuda", torch.bfloat16)
+    cfg1 = B.make_config(N, D, H, d, F, C, B.H3K_BF16, B.H3K_BF16, True)
+    ms1, _ = _time_block(cfg1, t1, x1, c1)
+    fl1 = sum(block_flops(N, D, F, C).values())
+    res["block_6144_tokens"] = {
+        "workload": "one bf16 block at 6144 tokens (6x32x32 latent of 512x512x22 frames), D=3072, "
+                    "24x128 heads, F=12288",
+        "ms_per_block": round(ms1, 3), "tflops": round(fl1 / (ms1 * 1e-3) / 1e12, 1)}
+    log(f"6144-token block: {ms1:.2f} ms")
+    return res
 
 
 def cpu_baseline(step_flops, L):

@@ -218,7 +218,8 @@ def test_attention(B, n, heads, hd, dtype, full):
 # ------------------------------------------------------------------ int8 quantiser
 
 @pytest.mark.parametrize("rows,cols,dtype", [(15360, 5120, "f32"), (5120, 13824, "f32"), (300, 77, "f32"),
-                                             (257, 1000, "bf16"), (3, 1, "f32")])
+                                             (257, 1000, "bf16"), (3, 1, "f32"), (5120, 13824, "bf16"),
+                                             (301, 8, "bf16"), (7, 20, "bf16")])
 def test_quantize_int8_bit_exact(B, rows, cols, dtype):
     import torch
     flush(f"quantize rows={rows} cols={cols} {dtype}")

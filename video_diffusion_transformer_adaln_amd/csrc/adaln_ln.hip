@@ -139,42 +139,91 @@ hipError_t launch_ln_modulate(DType dt, int n, int D, float eps, const void* x, 
 
 // ---------------------------------------------------------------------------
 // Per-row symmetric int8 quantiser: s = max|w| / 127, q = clamp(rint(w/s)).
-// One workgroup per row: absmax over the row (exact, order-independent), then
-// one correctly rounded fp32 division per element and round-half-to-even.
-template <typename T>
-__global__ __launch_bounds__(256) void quantize_int8_kernel(const T* __restrict__ w, int64_t cols,
-                                                            int8_t* __restrict__ q, float* __restrict__ scales) {
-  __shared__ float red[256 / kWave];
-  const int64_t row = blockIdx.x;
-  const T* wr = w + row * cols;
-  float mx = 0.f;
-  for (int64_t k = threadIdx.x; k < cols; k += blockDim.x) mx = fmaxf(mx, fabsf(to_f32(wr[k])));
-  mx = wave_max(mx);
-  if (threadIdx.x % kWave == 0) red[threadIdx.x / kWave] = mx;
-  __syncthreads();
-  mx = red[0];
+// One wave per row, four rows per workgroup.  Each lane handles groups of 8
+// consecutive elements (one 16-byte load for bf16, two for fp32; one 8-byte
+// store of 8 int8): pass 1 takes the absmax (exact, order-independent), pass 2
+// re-reads the row (mostly from L2) and does one correctly rounded fp32
+// division per element and round-half-to-even.  Rows whose length is not a
+// multiple of 8 (or not 16-byte aligned as a result) take a per-element path.
+template <typename T> struct Vec8;
+template <> struct Vec8<bf16> {
+  static __device__ __forceinline__ void load(const bf16* p, float (&v)[8]) {
+    const u32x4 r = *reinterpret_cast<const u32x4*>(p);
+    const bf16* e = reinterpret_cast<const bf16*>(&r);
 #pragma unroll
-  for (int i = 1; i < 256 / kWave; ++i) mx = fmaxf(mx, red[i]);
-  const float s = mx / 127.0f;
-  if (threadIdx.x == 0) scales[row] = s;
+    for (int i = 0; i < 8; ++i) v[i] = static_cast<float>(e[i]);
+  }
+};
+template <> struct Vec8<float> {
+  static __device__ __forceinline__ void load(const float* p, float (&v)[8]) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { v[i] = a[i]; v[4 + i] = b[i]; }
+  }
+};
+
+__device__ __forceinline__ int quant1(float v, float s) {
+  if (s == 0.f) return 0;
+  return (int)fminf(127.f, fmaxf(-127.f, rintf(v / s)));
+}
+
+template <typename T, bool VEC>
+__global__ __launch_bounds__(256) void quantize_int8_kernel(const T* __restrict__ w, int64_t rows, int64_t cols,
+                                                            int8_t* __restrict__ q, float* __restrict__ scales) {
+  const int lane = threadIdx.x % kWave;
+  const int64_t row = (int64_t)blockIdx.x * (256 / kWave) + threadIdx.x / kWave;
+  if (row >= rows) return;
+  const T* wr = w + row * cols;
   int8_t* qr = q + row * cols;
-  for (int64_t k = threadIdx.x; k < cols; k += blockDim.x) {
-    int qi = 0;
-    if (s != 0.f) {
-      const float t = rintf(to_f32(wr[k]) / s);
-      qi = (int)fminf(127.f, fmaxf(-127.f, t));
+  if constexpr (!VEC) {
+    float mx = 0.f;
+    for (int64_t k = lane; k < cols; k += kWave) mx = fmaxf(mx, fabsf(to_f32(wr[k])));
+    mx = wave_max(mx);
+    const float s = mx / 127.0f;
+    if (lane == 0) scales[row] = s;
+    for (int64_t k = lane; k < cols; k += kWave) qr[k] = (int8_t)quant1(to_f32(wr[k]), s);
+    return;
+  }
+  const int64_t groups = cols / 8;
+  float mx = 0.f;
+#pragma unroll 4
+  for (int64_t g = lane; g < groups; g += kWave) {
+    float v[8];
+    Vec8<T>::load(wr + g * 8, v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) mx = fmaxf(mx, fabsf(v[i]));
+  }
+  mx = wave_max(mx);
+  const float s = mx / 127.0f;
+  if (lane == 0) scales[row] = s;
+#pragma unroll 4
+  for (int64_t g = lane; g < groups; g += kWave) {
+    float v[8];
+    Vec8<T>::load(wr + g * 8, v);
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t b = (uint32_t)(quant1(v[i], s) & 0xff);
+      if (i < 4) lo |= b << (8 * i);
+      else hi |= b << (8 * (i - 4));
     }
-    qr[k] = (int8_t)qi;
+    *reinterpret_cast<u32x2*>(qr + g * 8) = u32x2{lo, hi};
   }
 }
 
 hipError_t launch_quantize_int8(DType dt, const void* w, int64_t rows, int64_t cols, int8_t* q, float* scales,
                                 hipStream_t stream) {
   if (rows == 0) return hipSuccess;
-  if (dt == kBF16)
-    quantize_int8_kernel<bf16><<<dim3((unsigned)rows), dim3(256), 0, stream>>>((const bf16*)w, cols, q, scales);
-  else
-    quantize_int8_kernel<float><<<dim3((unsigned)rows), dim3(256), 0, stream>>>((const float*)w, cols, q, scales);
+  const dim3 grid((unsigned)((rows + 3) / 4));
+  const bool vec = cols % 8 == 0;   // row starts then stay 16-byte aligned (w and q are)
+  if (dt == kBF16) {
+    if (vec) quantize_int8_kernel<bf16, true><<<grid, dim3(256), 0, stream>>>((const bf16*)w, rows, cols, q, scales);
+    else quantize_int8_kernel<bf16, false><<<grid, dim3(256), 0, stream>>>((const bf16*)w, rows, cols, q, scales);
+  } else {
+    if (vec) quantize_int8_kernel<float, true><<<grid, dim3(256), 0, stream>>>((const float*)w, rows, cols, q, scales);
+    else quantize_int8_kernel<float, false><<<grid, dim3(256), 0, stream>>>((const float*)w, rows, cols, q, scales);
+  }
   return hipGetLastError();
 }
 
