@@ -5,5 +5,5 @@ leg may import this package.  The product library never does.
 """
 from .dit_oracle import (  # noqa: F401
     LN_EPS, MOD_CHUNKS, adaln_modulation, attention, block_forward, dequantize_int8,
-    gelu_tanh, layer_norm, linear, modulate, quantize_int8, softmax_rows, stack_forward,
+    gelu_tanh, layer_norm, linear, linear_w8a8, modulate, quantize_int8, softmax_rows, stack_forward,
 )

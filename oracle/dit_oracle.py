@@ -27,7 +27,8 @@ Pins (tests/test_oracle_pins.py): textbook LayerNorm via torch on the CPU,
 pure-Python brute force of the whole block and of attention on tiny inputs,
 torch's scaled-dot-product attention and tanh-GELU, closed-form values,
 permutation equivariance, gate = 0 identity, softmax rows summing to one,
-the layer-prefix property of the stack, and a pure-Python fp32 quantiser.
+the layer-prefix property of the stack, a pure-Python fp32 quantiser, and
+pure-Python integer sums for the int8 x int8 projection.
 """
 from __future__ import annotations
 
@@ -141,6 +142,24 @@ def dequantize_int8(q: np.ndarray, s: np.ndarray) -> np.ndarray:
     return q.astype(f32) * s.astype(f32)[:, None]
 
 
+def linear_w8a8(qx: np.ndarray, sx: np.ndarray, qw: np.ndarray, sw: np.ndarray,
+                b: Optional[np.ndarray]) -> np.ndarray:
+    """Both operands int8: y[n, o] = sx[n] sw[o] sum_k qx[n, k] qw[o, k] + b[o].
+
+    The k-sum of int8 products is an exact integer (computed in float64,
+    which holds every integer below 2^53); it is rounded once to fp32, then
+    multiplied by the activation row scale and the weight channel scale,
+    and the bias is added, in fp32.  [H3-review] speed/quality section: the
+    row-quantised FC2 variant gives the MLP's second projection one
+    activation scale per token row.
+    """
+    acc = qx.astype(np.float64) @ qw.astype(np.float64).T
+    y = acc.astype(f32) * sx.astype(f32)[:, None] * sw.astype(f32)[None, :]
+    if b is not None:
+        y = y + b.astype(f32)
+    return y.astype(f32)
+
+
 def _weight(wts: Dict[str, np.ndarray], name: str) -> np.ndarray:
     """fp32 view of a projection matrix, dequantising int8 (q, s) pairs."""
     w = wts[name]
@@ -151,7 +170,7 @@ def _weight(wts: Dict[str, np.ndarray], name: str) -> np.ndarray:
 
 def block_forward(x: np.ndarray, c: np.ndarray, wts: Dict[str, np.ndarray], n_heads: int,
                   rows: Optional[Sequence[int]] = None, eps: float = LN_EPS,
-                  intermediates: Optional[dict] = None) -> np.ndarray:
+                  intermediates: Optional[dict] = None, int8_fc2_rows: bool = False) -> np.ndarray:
     """One AdaLN DiT block.
 
         mod = W_ada c + b_ada -> shift_a, scale_a, gate_a, shift_m, scale_m, gate_m
@@ -168,6 +187,12 @@ def block_forward(x: np.ndarray, c: np.ndarray, wts: Dict[str, np.ndarray], n_he
     per-token stages run only on those rows (each output row depends on its
     own row and on k, v of all rows).  Projection weights may be given as
     (q_int8, scale) pairs, which are dequantised in fp32.
+
+    ``int8_fc2_rows`` selects the row-quantised FC2 of [H3-review]'s
+    speed/quality section: u is quantised per token row with the same
+    symmetric rule as the weights (quantize_int8), and the MLP-down
+    projection is the int8 x int8 product of linear_w8a8 with the int8
+    w_down (which must then be a (q_int8, scale) pair).
     """
     x = x.astype(f32)
     D = x.shape[1]
@@ -187,14 +212,20 @@ def block_forward(x: np.ndarray, c: np.ndarray, wts: Dict[str, np.ndarray], n_he
     x1 = x[sel] + m["gate_a"] * linear(o, _weight(wts, "w_out"), wts.get("b_out"))
     h2 = modulate(layer_norm(x1, eps), m["shift_m"], m["scale_m"])
     u = gelu_tanh(linear(h2, _weight(wts, "w_up"), wts.get("b_up")))
-    y = x1 + m["gate_m"] * linear(u, _weight(wts, "w_down"), wts.get("b_down"))
+    if int8_fc2_rows:
+        q_down, s_down = wts["w_down"]
+        q_u, s_u = quantize_int8(u)
+        down = linear_w8a8(q_u, s_u, q_down, s_down, wts.get("b_down"))
+    else:
+        down = linear(u, _weight(wts, "w_down"), wts.get("b_down"))
+    y = x1 + m["gate_m"] * down
     if intermediates is not None:
         intermediates.update(mod=m, h=h, q=q, k=k, v=v, o=o, x1=x1, h2=h2, u=u)
     return y.astype(f32)
 
 
 def stack_forward(x: np.ndarray, c: np.ndarray, blocks: Sequence[Dict[str, np.ndarray]], n_heads: int,
-                  n_layers: Optional[int] = None, eps: float = LN_EPS) -> np.ndarray:
+                  n_layers: Optional[int] = None, eps: float = LN_EPS, int8_fc2_rows: bool = False) -> np.ndarray:
     """x_{l+1} = block_l(x_l, c) for the first ``n_layers`` blocks, one shared c.
 
     [H3-review] knob list: the layer count runs the first 50, 45 or 40 blocks.
@@ -202,5 +233,5 @@ def stack_forward(x: np.ndarray, c: np.ndarray, blocks: Sequence[Dict[str, np.nd
     """
     L = len(blocks) if n_layers is None else n_layers
     for l in range(L):
-        x = block_forward(x, c, blocks[l], n_heads, eps=eps)
+        x = block_forward(x, c, blocks[l], n_heads, eps=eps, int8_fc2_rows=int8_fc2_rows)
     return x

@@ -116,3 +116,18 @@ def quantize_row_int8(row):
         qi = int(round(t))
         q.append(max(-127, min(127, qi)))
     return q, s
+
+
+def fc2_int8_rows(u, q_w, s_w, b):
+    """int8 x int8 MLP-down on nested lists: each row of u quantised by
+    quantize_row_int8, then y[t][o] = s_u[t] s_w[o] sum_k q_u[t][k] q_w[o][k] + b[o]
+    with the integer sum exact and the scaling in Python floats."""
+    out = []
+    for row in u:
+        qu, su = quantize_row_int8(row)
+        r = []
+        for o in range(len(q_w)):
+            acc = sum(a * w for a, w in zip(qu, q_w[o]))      # exact integer
+            r.append(su * s_w[o] * acc + (b[o] if b is not None else 0.0))
+        out.append(r)
+    return out

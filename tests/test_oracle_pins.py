@@ -283,6 +283,54 @@ def test_int8_block_uses_dequantised_weights():
     assert rel_l2(got, ref) < 1e-5
 
 
+def test_w8a8_linear_is_the_exact_integer_sum():
+    rng = np.random.default_rng(37)
+    qx = rng.integers(-127, 128, size=(5, 96)).astype(np.int8)
+    qw = rng.integers(-127, 128, size=(7, 96)).astype(np.int8)
+    ones_x, ones_w = np.ones(5, np.float32), np.ones(7, np.float32)
+    got = oracle.linear_w8a8(qx, ones_x, qw, ones_w, None)
+    for n in range(5):
+        for o in range(7):
+            exact = sum(int(a) * int(w) for a, w in zip(qx[n], qw[o]))   # |sum| < 2^24: exact in fp32
+            assert float(got[n, o]) == float(exact)
+
+
+def test_w8a8_linear_matches_the_dequantised_product():
+    rng = np.random.default_rng(41)
+    x = rng.standard_normal((6, 128)).astype(np.float32)
+    w = (rng.standard_normal((9, 128)) * 0.02).astype(np.float32)
+    b = (rng.standard_normal(9) * 0.05).astype(np.float32)
+    qx, sx = oracle.quantize_int8(x)
+    qw, sw = oracle.quantize_int8(w)
+    got = oracle.linear_w8a8(qx, sx, qw, sw, b)
+    ref = (qx.astype(np.float64) * sx.astype(np.float64)[:, None]) @ \
+          (qw.astype(np.float64) * sw.astype(np.float64)[:, None]).T + b.astype(np.float64)
+    assert rel_l2(got, ref) < 1e-6
+
+
+def test_int8_fc2_block_stage_matches_brute_force():
+    """The row-quantised FC2 stage of the oracle block against the pure-Python
+    quantiser and integer sums, fed the same u (so every rounding decision
+    is taken on identical values); the residual and gate around it as in
+    the float block."""
+    shape, x, c, w = tiny_problem(n_tokens=6, n_heads=2, head_dim=4, mlp=40)
+    wq = dict(w)
+    for name in si.MATRIX_NAMES:
+        wq[name] = oracle.quantize_int8(w[name])
+    inter = {}
+    got = oracle.block_forward(x, c, wq, shape.n_heads, intermediates=inter, int8_fc2_rows=True)
+    q_down, s_down = wq["w_down"]
+    b_down = w.get("b_down")
+    down = bf.fc2_int8_rows(inter["u"].tolist(), q_down.astype(int).tolist(), s_down.tolist(),
+                            None if b_down is None else b_down.tolist())
+    gate_m = inter["mod"]["gate_m"].astype(np.float64)
+    ref = inter["x1"].astype(np.float64) + gate_m * np.array(down)
+    assert rel_l2(got, ref) < 1e-6
+    # and the int8 FC2 stays close to the dequantised-weight block (one quantisation of u)
+    plain = oracle.block_forward(x, c, wq, shape.n_heads)
+    assert rel_l2(got, plain) < 2e-2
+
+
 # ---------------------------------------------------------------- generator sanity
 
 def test_bf16_rounding_of_generator():
