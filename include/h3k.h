@@ -79,7 +79,14 @@ typedef int32_t h3k_dtype;
  * alias_activations: 1 lets the lifetime planner overlap intermediate buffers in
  * the workspace ([H3-memory] technique 2), 0 gives each its own region; the
  * output is bit-identical either way.  The environment variable
- * H3K_DISABLE_ACTIVATION_ALIAS=1 forces 0, as a diagnostic switch. */
+ * H3K_DISABLE_ACTIVATION_ALIAS=1 forces 0, as a diagnostic switch.
+ * int8_fc2_rows: 1 runs the MLP-down projection (FC2) with int8 activations as
+ * well ([H3-review] speed/quality section, the row-quantised FC2: one activation
+ * scale per token row): u is quantised per row by the rule of
+ * h3k_quantize_weights_int8, and FC2 is the int8 x int8 product with int32
+ * accumulation, scaled by the row and channel scales (h3k_linear_int8).
+ * Needs weight_dtype INT8, act_dtype BF16 and mlp_hidden a multiple of 128;
+ * 0 leaves FC2 as for the other projections. */
 typedef struct h3k_dit_config {
   int32_t n_tokens;
   int32_t hidden;
@@ -91,6 +98,7 @@ typedef struct h3k_dit_config {
   h3k_dtype act_dtype;
   h3k_dtype weight_dtype;
   int32_t alias_activations;
+  int32_t int8_fc2_rows;
 } h3k_dit_config;
 
 /* Weights of one block; all device pointers.
@@ -120,7 +128,8 @@ typedef struct h3k_profiler h3k_profiler;
 #define H3K_K_OUT        4  /* out-projection GEMM + gated residual      */
 #define H3K_K_UP         5  /* MLP up GEMM + GELU                        */
 #define H3K_K_DOWN       6  /* MLP down GEMM + gated residual            */
-#define H3K_K_COUNT      7
+#define H3K_K_ACT_QUANT  7  /* row quantiser of u (int8_fc2_rows only)   */
+#define H3K_K_COUNT      8
 
 /* Statistics of a forward call (host struct).  `profiler` is an input
  * (optional); the rest are outputs ([H3-memory], "verify it yourself": the
@@ -146,11 +155,13 @@ typedef struct h3k_dit_stats {
 #define H3K_T_X1   4   /* [N, D]      */
 #define H3K_T_H2   5   /* [N, D]      */
 #define H3K_T_U    6   /* [N, F]      */
-#define H3K_T_COUNT 7
+#define H3K_T_UQ   7   /* int8 [N, F] (int8_fc2_rows only, else 0 bytes) */
+#define H3K_T_US   8   /* fp32 [N]    (int8_fc2_rows only, else 0 bytes) */
+#define H3K_T_COUNT 9
 typedef struct h3k_dit_plan_info {
   uint64_t offset[H3K_T_COUNT];
   uint64_t bytes[H3K_T_COUNT];
-  int32_t  first_step[H3K_T_COUNT];  /* kernel step that writes it (0..7) */
+  int32_t  first_step[H3K_T_COUNT];  /* kernel step that writes it (0..8; step 7 quantises u) */
   int32_t  last_step[H3K_T_COUNT];   /* last kernel step that reads it    */
   uint64_t qkv_vt_offset;            /* byte offset of V^T inside the workspace */
   int64_t  vt_pitch;                 /* elements per V^T row */
@@ -189,7 +200,8 @@ h3k_status h3k_dit_stack_forward(const h3k_dit_config* cfg, const h3k_dit_block_
                                  void* workspace, uint64_t workspace_bytes,
                                  hipStream_t stream, h3k_dit_stats* stats);
 
-/* Per-output-channel symmetric int8 quantisation of w [rows, cols] (F32 or BF16):
+/* Per-output-channel symmetric int8 quantisation of w [rows, cols] (F32 or BF16);
+ * with int8_fc2_rows the forward calls apply the same rule to the rows of u:
  *   scales[o] = max_k |w[o,k]| / 127   (one fp32 division, correctly rounded)
  *   q[o,k]    = clamp(rint(w[o,k] / scales[o]), -127, 127)  (ties to even)
  * A zero row gives scale 0 and q 0.  Bit-exact with any IEEE fp32 implementation
@@ -230,6 +242,20 @@ h3k_status h3k_linear(h3k_dtype act_dtype, h3k_dtype weight_dtype, int64_t m, in
                       const void* bias, int32_t epilogue, const void* residual, int64_t ldr,
                       const float* gate, void* y, int64_t ldy, void* yt, int64_t ldyt,
                       int64_t split_col, hipStream_t stream);
+
+/* Both operands int8 (the row-quantised FC2 of [H3-review]'s speed/quality section):
+ *   z[i, j] = x_scale[i] * w_scale[j] * sum_k xq[i, k] wq[j, k]   (int32 sum, exact;
+ *             converted to fp32 once, then the two scale products in fp32)
+ *   y = epilogue(z + bias) as for h3k_linear (H3K_EPI_*), row-major only.
+ * xq [m, ldx] and wq [n, ldw] int8 with x_scale [m], w_scale [n] fp32 (e.g. from
+ * h3k_quantize_weights_int8 on the activations and on the weights); bias [n],
+ * residual [m, ldr] and y [m, ldy] BF16; gate [n] fp32.  k a multiple of 128 and
+ * k <= 2^17 (the int32 sum cannot overflow), ldx and ldw multiples of 16,
+ * n a multiple of 8.  y must not overlap the inputs. */
+h3k_status h3k_linear_int8(int64_t m, int64_t n, int64_t k, const int8_t* xq, int64_t ldx, const float* x_scale,
+                           const int8_t* wq, int64_t ldw, const float* w_scale, const void* bias,
+                           int32_t epilogue, const void* residual, int64_t ldr, const float* gate,
+                           void* y, int64_t ldy, hipStream_t stream);
 
 /* o[n, H*d] = per head softmax(q k^T / sqrt(d)) v, non-causal, no positional
  * terms; q [n, ldq], k [n, ldk] row-major (head j = columns j*d..j*d+d-1), v given

@@ -32,10 +32,10 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_struct_sizes_match_header_layout():
-    assert ctypes.sizeof(B.DitConfig) == 40
+    assert ctypes.sizeof(B.DitConfig) == 44
     assert ctypes.sizeof(B.DitBlockWeights) == 14 * 8
     assert ctypes.sizeof(B.DitStats) == 40
-    assert ctypes.sizeof(B.DitPlanInfo) == 7 * 8 * 2 + 7 * 4 * 2 + 8 * 5 + 8
+    assert ctypes.sizeof(B.DitPlanInfo) == 9 * 8 * 2 + 9 * 4 * 2 + 8 * 5 + 8
 
 
 def cfg_c2(**kw):
@@ -56,6 +56,10 @@ def _live(info, t, s):
     dict(n_tokens=512, hidden=256, n_heads=4, head_dim=64, mlp_hidden=1024, cond_dim=256, act_dtype=0),
     dict(n_tokens=1, hidden=128, n_heads=2, head_dim=64, mlp_hidden=64, cond_dim=8, act_dtype=1),
     dict(n_tokens=333, hidden=320, n_heads=5, head_dim=64, mlp_hidden=2048, cond_dim=64, act_dtype=1),
+    dict(n_tokens=22680, hidden=5120, n_heads=40, head_dim=128, mlp_hidden=13824, cond_dim=5120, act_dtype=1,
+         weight_dtype=2, int8_fc2_rows=True),
+    dict(n_tokens=37, hidden=256, n_heads=2, head_dim=128, mlp_hidden=384, cond_dim=64, act_dtype=1,
+         weight_dtype=2, int8_fc2_rows=True),
 ])
 def test_plan_no_live_overlap(shape, alias):
     cfg = B.make_config(alias=alias, **shape)
@@ -64,7 +68,7 @@ def test_plan_no_live_overlap(shape, alias):
     for t in range(n):
         assert info.offset[t] % 256 == 0
         assert info.offset[t] + info.bytes[t] <= info.workspace_bytes
-    for s in range(8):
+    for s in range(9):
         live = [t for t in range(n) if _live(info, t, s)]
         for i in live:
             for j in live:
@@ -145,6 +149,12 @@ def test_reject_bad_shapes_and_dtypes():
     assert _block(cfg_c2(act_dtype=7)) == B.H3K_ERR_DTYPE
     assert _block(cfg_c2(act_dtype=B.H3K_F32, weight_dtype=B.H3K_INT8)) == B.H3K_ERR_UNSUPPORTED
     assert _block(cfg_c2(ln_eps=0.0)) == B.H3K_ERR_SHAPE
+    # the row-quantised FC2 needs int8 weights, bf16 activations, F a multiple of 128
+    assert _block(cfg_c2(int8_fc2_rows=True)) == B.H3K_ERR_UNSUPPORTED
+    assert _block(cfg_c2(weight_dtype=B.H3K_INT8, mlp_hidden=13824 - 64, int8_fc2_rows=True)) == B.H3K_ERR_UNSUPPORTED
+    bad = cfg_c2(weight_dtype=B.H3K_INT8)
+    bad.int8_fc2_rows = 2
+    assert _block(bad) == B.H3K_ERR_SHAPE
 
 
 def test_reject_int8_without_scales():
@@ -184,6 +194,15 @@ def test_reject_bad_kernel_level_arguments():
     assert lib.h3k_quantize_weights_int8(FAKE, 2, 4, 64, FAKE + (1 << 32), FAKE + (2 << 32), None) == B.H3K_ERR_UNSUPPORTED
     assert lib.h3k_quantize_weights_int8(FAKE, 0, 4, 64, FAKE + 64, FAKE + (2 << 32), None) == B.H3K_ERR_OVERLAP
     assert lib.h3k_ln_modulate(1, 4, 100, 1e-6, FAKE, 100, FAKE, FAKE, FAKE + (1 << 32), 100, None) == B.H3K_ERR_SHAPE
+    # int8 x int8 linear: k not a multiple of 128, missing x_scale, misaligned xq, y overlapping wq
+    X, XS, W, WS, Y = FAKE, FAKE + (1 << 32), FAKE + (2 << 32), FAKE + (3 << 32), FAKE + (4 << 32)
+    assert lib.h3k_linear_int8(10, 64, 192, X, 192, XS, W, 192, WS, None, 0, None, 0, None, Y, 64, None) == B.H3K_ERR_SHAPE
+    assert lib.h3k_linear_int8(10, 64, 256, X, 256, None, W, 256, WS, None, 0, None, 0, None, Y, 64, None) == B.H3K_ERR_NULL
+    assert lib.h3k_linear_int8(10, 64, 256, X + 8, 256, XS, W, 256, WS, None, 0, None, 0, None, Y, 64, None) == B.H3K_ERR_ALIGN
+    assert lib.h3k_linear_int8(10, 64, 256, X, 256, XS, W, 256, WS, None, 0, None, 0, None, W + 256, 64, None) == B.H3K_ERR_OVERLAP
+    assert lib.h3k_linear_int8(10, 64, 256, X, 256, XS, W, 256, WS, None, 2, None, 0, None, Y, 64, None) == B.H3K_ERR_NULL
+    assert lib.h3k_linear_int8(10, 64, 1 << 18, X, 1 << 18, XS, W, 1 << 18, WS, None, 0, None, 0, None, Y, 64,
+                               None) == B.H3K_ERR_SHAPE
     assert lib.h3k_adaln_modulation(1, 10, 12, FAKE, None, FAKE, FAKE + (1 << 32), None) == B.H3K_ERR_SHAPE
 
 

@@ -33,10 +33,10 @@ def R():
     return runtime
 
 
-def _run_block(R, shape, dw, xd, cd, alias=True, poison=True, stats=None):
+def _run_block(R, shape, dw, xd, cd, alias=True, poison=True, stats=None, int8_fc2_rows=False):
     import torch
     from video_diffusion_transformer_adaln_amd import binding as B
-    cfg = config_for(shape, alias)
+    cfg = config_for(shape, alias, int8_fc2_rows)
     ws = R.alloc_workspace(cfg)
     if poison:
         ws.fill_(0xFF)
@@ -140,6 +140,32 @@ def test_block_c4_int8_sampled_rows(R):
     err = rel_l2(got[rows], ref)
     flush(f"  rel_l2 = {err:.3e}")
     assert err < TOL
+
+
+@pytest.mark.parametrize("case", ["c4", "small"])
+def test_block_int8_fc2_rows(R, case):
+    """The row-quantised FC2 (u quantised per token row, int8 x int8 MLP-down):
+    against the oracle's block with the same option, and byte-identical with
+    aliasing on and off."""
+    import torch
+    from video_diffusion_transformer_adaln_amd import binding as B
+    shape = si.C4 if case == "c4" else si.custom_shape("int8fc2", 971, 333, 2, 128, 640, "bf16", int8_weights=True)
+    flush(f"block {shape.name} int8_fc2_rows")
+    hx, hc, hw = _block_case(shape, bias_std=0.05)
+    dw, ow = upload_block(shape, hw)
+    xd, cd = dev(hx), dev(hc)
+    st = B.DitStats()
+    got_t = _run_block(R, shape, dw, xd, cd, stats=st, int8_fc2_rows=True)
+    assert st.dispatches == 9
+    got = to_np(got_t)
+    rows = sample_rows(shape.n_tokens) if case == "c4" else np.arange(shape.n_tokens)
+    ref = oracle.block_forward(hx.values, hc.values, ow, shape.n_heads, rows=rows, int8_fc2_rows=True)
+    err = rel_l2(got[rows], ref)
+    flush(f"  rel_l2 = {err:.3e}")
+    assert err < TOL
+    if case == "small":
+        off = _run_block(R, shape, dw, xd, cd, alias=False, int8_fc2_rows=True)
+        assert torch.equal(off.view(torch.int16), got_t.view(torch.int16))
 
 
 def test_stack50_reduced_width_vs_oracle(R):

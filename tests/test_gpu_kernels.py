@@ -171,6 +171,60 @@ def test_linear(B, m, n, k, epi, dtype, int8, split, full):
         assert np.isnan(to_np(yt)[:, m:]).all()                # padding columns untouched
 
 
+# ------------------------------------------------------------------ int8 x int8 linear
+
+LINEAR_INT8_CASES = [
+    # m, n, k, epilogue, full
+    (300, 320, 256, 0, True),
+    (300, 320, 256, 1, True),
+    (300, 320, 256, 2, True),
+    (1, 64, 128, 0, True),
+    (257, 328, 384, 2, True),      # 3 k-tiles, ragged n
+    (129, 264, 640, 1, True),      # 5 k-tiles: the operand ring wraps
+    (22680, 5120, 13824, 2, False),   # the MLP-down projection of the 864x480x56-frame block
+]
+
+
+@pytest.mark.parametrize("m,n,k,epi,full", LINEAR_INT8_CASES)
+def test_linear_int8(B, m, n, k, epi, full):
+    """Both operands quantised on the GPU (checked bit for bit against the
+    oracle's quantiser), then the int8 x int8 product against the oracle's
+    linear_w8a8 with the same epilogue."""
+    import torch
+    from video_diffusion_transformer_adaln_amd import runtime as R
+    flush(f"linear int8 m={m} n={n} k={k} epi={epi}")
+    cid = 840 + epi
+    x32 = _f32((m, k), 1.0, cid)
+    w32 = _f32((n, k), 0.02, cid, "w_up")
+    bias = _ht(_f32((n,), 0.05, cid, "b_up"), "bf16")
+    xq, xs = R.quantize_int8(torch.from_numpy(x32).cuda())
+    wq, ws = R.quantize_int8(torch.from_numpy(w32).cuda())
+    torch.cuda.synchronize()
+    rows = np.arange(m) if full else sample_rows(m)
+    qx_ref, sx_ref = oracle.quantize_int8(x32[rows])
+    qw_ref, sw_ref = oracle.quantize_int8(w32)
+    assert np.array_equal(xq.cpu().numpy()[rows], qx_ref) and np.array_equal(xs.cpu().numpy()[rows], sx_ref)
+    assert np.array_equal(wq.cpu().numpy(), qw_ref) and np.array_equal(ws.cpu().numpy(), sw_ref)
+    res = gate = resd = gated = None
+    if epi == 2:
+        res = _ht(_f32((m, n), 1.0, cid, "x", 1), "bf16")
+        gate = _f32((n,), 0.5, cid, "b_down")
+        resd, gated = dev(res), torch.from_numpy(gate).cuda()
+    y = torch.full((m, n), float("nan"), dtype=torch.bfloat16, device="cuda")
+    B.h3k_linear_int8(m, n, k, xq, k, xs, wq, k, ws, dev(bias), epi, resd, n, gated, y, n)
+    torch.cuda.synchronize()
+    z = oracle.linear_w8a8(qx_ref, sx_ref, qw_ref, sw_ref, bias.values)
+    if epi == 1:
+        ref = oracle.gelu_tanh(z)
+    elif epi == 2:
+        ref = res.values[rows] + gate * z
+    else:
+        ref = z
+    got = to_np(y)[rows]
+    assert np.isfinite(got).all()
+    assert rel_l2(got, ref) < BF16_TOL / 2
+
+
 # ------------------------------------------------------------------ attention
 
 ATTN_CASES = [

@@ -21,8 +21,8 @@ STATUS_NAMES = {0: "OK", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_DTYPE", 4: "ERR_
                 6: "ERR_OVERLAP", 7: "ERR_UNSUPPORTED", 8: "ERR_HIP"}
 H3K_F32, H3K_BF16, H3K_INT8 = 0, 1, 2
 H3K_EPI_BIAS, H3K_EPI_GELU, H3K_EPI_GATED_RESIDUAL = 0, 1, 2
-KERNEL_KINDS = ("adaln", "ln_mod", "qkv", "attention", "out_proj", "mlp_up", "mlp_down")
-TENSOR_NAMES = ("mod", "h", "qkv", "o", "x1", "h2", "u")
+KERNEL_KINDS = ("adaln", "ln_mod", "qkv", "attention", "out_proj", "mlp_up", "mlp_down", "act_quant")
+TENSOR_NAMES = ("mod", "h", "qkv", "o", "x1", "h2", "u", "uq", "us")
 
 c_int32, c_int64, c_uint64, c_float, c_void_p = (ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64,
                                                   ctypes.c_float, ctypes.c_void_p)
@@ -31,7 +31,7 @@ c_int32, c_int64, c_uint64, c_float, c_void_p = (ctypes.c_int32, ctypes.c_int64,
 class DitConfig(ctypes.Structure):
     _fields_ = [("n_tokens", c_int32), ("hidden", c_int32), ("n_heads", c_int32), ("head_dim", c_int32),
                 ("mlp_hidden", c_int32), ("cond_dim", c_int32), ("ln_eps", c_float), ("act_dtype", c_int32),
-                ("weight_dtype", c_int32), ("alias_activations", c_int32)]
+                ("weight_dtype", c_int32), ("alias_activations", c_int32), ("int8_fc2_rows", c_int32)]
 
 
 class DitBlockWeights(ctypes.Structure):
@@ -48,8 +48,8 @@ class DitStats(ctypes.Structure):
 
 
 class DitPlanInfo(ctypes.Structure):
-    _fields_ = [("offset", c_uint64 * 7), ("bytes", c_uint64 * 7), ("first_step", c_int32 * 7),
-                ("last_step", c_int32 * 7), ("qkv_vt_offset", c_uint64), ("vt_pitch", c_int64),
+    _fields_ = [("offset", c_uint64 * 9), ("bytes", c_uint64 * 9), ("first_step", c_int32 * 9),
+                ("last_step", c_int32 * 9), ("qkv_vt_offset", c_uint64), ("vt_pitch", c_int64),
                 ("workspace_bytes", c_uint64), ("peak_live_bytes", c_uint64), ("unaliased_bytes", c_uint64),
                 ("alias_activations", c_int32), ("_reserved", c_int32)]
 
@@ -82,6 +82,9 @@ _SIGNATURES = [
     ("h3k_linear", c_int32, [c_int32, c_int32, c_int64, c_int64, c_int64, c_void_p, c_int64, c_void_p, c_int64,
                              c_void_p, c_void_p, c_int32, c_void_p, c_int64, c_void_p, c_void_p, c_int64,
                              c_void_p, c_int64, c_int64, c_void_p]),
+    ("h3k_linear_int8", c_int32, [c_int64, c_int64, c_int64, c_void_p, c_int64, c_void_p, c_void_p, c_int64,
+                                  c_void_p, c_void_p, c_int32, c_void_p, c_int64, c_void_p, c_void_p, c_int64,
+                                  c_void_p]),
     ("h3k_attention", c_int32, [c_int32, c_int32, c_int32, c_int32, c_void_p, c_int64, c_void_p, c_int64,
                                 c_void_p, c_int64, c_void_p, c_int64, c_void_p]),
     ("h3k_profiler_create", c_int32, [c_int32, ctypes.POINTER(c_void_p)]),
@@ -138,9 +141,10 @@ def _stream(stream) -> Optional[int]:
 
 def make_config(n_tokens: int, hidden: int, n_heads: int, head_dim: int, mlp_hidden: int, cond_dim: int,
                 act_dtype: int, weight_dtype: Optional[int] = None, alias: bool = True,
-                ln_eps: float = 1e-6) -> DitConfig:
+                ln_eps: float = 1e-6, int8_fc2_rows: bool = False) -> DitConfig:
     return DitConfig(n_tokens, hidden, n_heads, head_dim, mlp_hidden, cond_dim, ln_eps, act_dtype,
-                     act_dtype if weight_dtype is None else weight_dtype, 1 if alias else 0)
+                     act_dtype if weight_dtype is None else weight_dtype, 1 if alias else 0,
+                     1 if int8_fc2_rows else 0)
 
 
 WEIGHT_FIELDS = ("w_ada", "b_ada", "w_qkv", "b_qkv", "s_qkv", "w_out", "b_out", "s_out",
@@ -204,6 +208,12 @@ def h3k_linear(act_dtype: int, weight_dtype: int, m: int, n: int, k: int, x, ldx
     check(lib().h3k_linear(act_dtype, weight_dtype, m, n, k, _ptr(x), ldx, _ptr(w), ldw, _ptr(w_scale), _ptr(bias),
                            epilogue, _ptr(residual), ldr, _ptr(gate), _ptr(y), ldy, _ptr(yt), ldyt,
                            n if split_col is None else split_col, _stream(stream)))
+
+
+def h3k_linear_int8(m: int, n: int, k: int, xq, ldx: int, x_scale, wq, ldw: int, w_scale, bias, epilogue: int,
+                    residual, ldr: int, gate, y, ldy: int, stream=None) -> None:
+    check(lib().h3k_linear_int8(m, n, k, _ptr(xq), ldx, _ptr(x_scale), _ptr(wq), ldw, _ptr(w_scale), _ptr(bias),
+                                epilogue, _ptr(residual), ldr, _ptr(gate), _ptr(y), ldy, _stream(stream)))
 
 
 def h3k_attention(dtype: int, n: int, n_heads: int, head_dim: int, q, ldq: int, k, ldk: int, vt, ldvt: int, o,

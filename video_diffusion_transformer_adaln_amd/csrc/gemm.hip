@@ -32,7 +32,8 @@
 namespace h3k {
 
 struct GemmParams {
-  const bf16* x; int64_t ldx;
+  const void* x; int64_t ldx;
+  const float* x_scale;   // int8 activations: per-row scales
   const void* w; int64_t ldw;
   const float* w_scale;
   const bf16* bias;
@@ -201,7 +202,7 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmParams p) {
   const int ld_ks = lane >> 4;
   const int ld_rsub = (lane & 15) >> 1, ld_h = lane & 1;
   const __amdgpu_buffer_rsrc_t rsx = make_rsrc(p.x, (uint32_t)((uint64_t)p.m * p.ldx * 2));
-  const __amdgpu_buffer_rsrc_t rsw = make_rsrc(p.w, (uint32_t)((uint64_t)p.n * p.ldw * (W8 ? 1 : 2)));
+  const __amdgpu_buffer_rsrc_t rsw = make_rsrc(p.w, (uint32_t)((uint64_t)p.n * p.ldw * (W8 ? 1 : 2)));   // activations bf16
   const uint32_t x_off0 = (uint32_t)((tok0 + wave * 8 + ld_rsub) * (uint32_t)p.ldx * 2u + (ld_ks * 16 + ld_h * 8) * 2);
   const uint32_t x_step = 64u * (uint32_t)p.ldx * 2u;
   const uint32_t w_off0 = W8 ? (uint32_t)((feat0 + wave * 16 + (lane & 15)) * (uint32_t)p.ldw + ld_ks * 16)
@@ -335,8 +336,8 @@ constexpr int kSlots = 5;          // 160 KiB
 // on one XCD then cover 2 m-tiles x 16 n-tiles); measured best of 1..32
 constexpr int kRingGroupM = 2;
 
-template <int EPI>
-__global__ __launch_bounds__(512) void gemm_bf16_dma_kernel(GemmParams p) {
+template <int EPI, bool I8>
+__global__ __launch_bounds__(512) void gemm_ring_kernel(GemmParams p) {
   __shared__ __attribute__((aligned(1024))) char lds[kSlots * kSlot];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -352,25 +353,27 @@ __global__ __launch_bounds__(512) void gemm_bf16_dma_kernel(GemmParams p) {
   const int tile_n = in_group / gm;
   const int tok0 = tile_m * BM, feat0 = tile_n * BN;
   const bool trans = (int64_t)feat0 >= p.split_col;
-  const int KT = p.k / BK;
+  // a k-tile is 128 bytes of every operand row: 64 bf16 or 128 int8 values
+  constexpr int ES = I8 ? 1 : 2;
+  const int KT = p.k / (128 / ES);
 
   // Ring of 5 operand slots; position q holds operand q&1 (0: activations,
   // 1: weights) of k-tile q>>1, in slot q%5.  Loads: instruction j (0..3)
   // of wave w covers rows (8 j + w) * 8 .. +8; rswz(lrow + 64 j) == rswz(lrow).
-  const __amdgpu_buffer_rsrc_t rsx = make_rsrc(p.x, (uint32_t)((uint64_t)p.m * p.ldx * 2));
-  const __amdgpu_buffer_rsrc_t rsw = make_rsrc(p.w, (uint32_t)((uint64_t)p.n * p.ldw * 2));
+  const __amdgpu_buffer_rsrc_t rsx = make_rsrc(p.x, (uint32_t)((uint64_t)p.m * p.ldx * ES));
+  const __amdgpu_buffer_rsrc_t rsw = make_rsrc(p.w, (uint32_t)((uint64_t)p.n * p.ldw * ES));
   const int lrow = wave * 8 + (lane >> 3);
   const uint32_t c16 = (uint32_t)(((lane & 7) ^ rswz(lrow)) * 16);
-  const uint32_t xo0 = (uint32_t)(tok0 + lrow) * (uint32_t)p.ldx * 2u + c16;
-  const uint32_t wo0 = (uint32_t)(feat0 + lrow) * (uint32_t)p.ldw * 2u + c16;
-  const uint32_t xstep = 64u * (uint32_t)p.ldx * 2u, wstep = 64u * (uint32_t)p.ldw * 2u;
+  const uint32_t xo0 = (uint32_t)(tok0 + lrow) * (uint32_t)p.ldx * ES + c16;
+  const uint32_t wo0 = (uint32_t)(feat0 + lrow) * (uint32_t)p.ldw * ES + c16;
+  const uint32_t xstep = 64u * (uint32_t)p.ldx * ES, wstep = 64u * (uint32_t)p.ldw * ES;
   // half h (0/1) of position q: instructions 2h, 2h+1; past the end the last
   // k-tile is re-loaded into the (unread) slot so the load counts stay uniform
   auto issue = [&](int q, int h) {
     int kt = q >> 1;
     kt = kt < KT ? kt : KT - 1;
     char* st = lds + (q % kSlots) * kSlot + wave * 1024;
-    const uint32_t kb = (uint32_t)kt * BK * 2u;
+    const uint32_t kb = (uint32_t)kt * 128u;
     const bool isw = q & 1;
     const __amdgpu_buffer_rsrc_t r = isw ? rsw : rsx;
     const uint32_t o0 = (isw ? wo0 : xo0) + kb, step = isw ? wstep : xstep;
@@ -381,14 +384,18 @@ __global__ __launch_bounds__(512) void gemm_bf16_dma_kernel(GemmParams p) {
     }
   };
 
-  f32x16 acc[2][4];
+  using Acc = typename std::conditional<I8, i32x16, f32x16>::type;
+  Acc acc[2][4];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < 4; ++j) acc[i][j] = Acc{};
 
   // fragment of 32-row block i, k-step ks: row row0 + 32 i + rl, logical chunk
-  // 2 ks + h -> physical (2 ks) ^ 4 (i & 1) ^ q, q = h ^ rswz(rl)
+  // 2 ks + h -> physical (2 ks) ^ 4 (i & 1) ^ q, q = h ^ rswz(rl).  A 16-byte
+  // chunk is 8 bf16 (v_mfma_f32_32x32x16_bf16, k-step 16) or 16 int8
+  // (v_mfma_i32_32x32x32_i8, k-step 32): both MFMAs take lane l's row l%32
+  // and the chunk selected by l/32.
   const int a_row0 = (wave & 3) * 64;
   const int b_row0 = (wave >> 2) * 128;
   const int rl = lane & 31;
@@ -412,7 +419,13 @@ __global__ __launch_bounds__(512) void gemm_bf16_dma_kernel(GemmParams p) {
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(fa[i], fb[j], acc[i][j]);
+      for (int j = 0; j < 4; ++j) {
+        if constexpr (I8)
+          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, fa[i]),
+                                                            __builtin_bit_cast(i32x4, fb[j]), acc[i][j], 0, 0, 0);
+        else
+          acc[i][j] = mfma32(fa[i], fb[j], acc[i][j]);
+      }
   };
 
   // prologue: positions 0, 1, 2 in flight; 0 and 1 (k-tile 0) must be complete
@@ -446,8 +459,24 @@ __global__ __launch_bounds__(512) void gemm_bf16_dma_kernel(GemmParams p) {
     wg_barrier();
   }
   wait_vmcnt<0>();
-  constexpr bool W8 = false;
-  store_tile<EPI, W8>(p, acc, a_row0, b_row0, tok0, feat0, trans, lane);
+  if constexpr (I8) {
+    // int32 -> fp32 (one rounding), times the activation row scale; the
+    // weight channel scale, bias and epilogue follow in store_tile.  The
+    // int8 path has no transposed part, so B-rows are tokens.
+    f32x16 accf[2][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int t = tok0 + b_row0 + j * 32 + (lane & 31);
+      const float xs = t < p.m ? p.x_scale[t] : 0.0f;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) accf[i][j][r] = static_cast<float>(acc[i][j][r]) * xs;
+    }
+    store_tile<EPI, true>(p, accf, a_row0, b_row0, tok0, feat0, false, lane);
+  } else {
+    store_tile<EPI, false>(p, acc, a_row0, b_row0, tok0, feat0, trans, lane);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -519,7 +548,8 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParamsF p) {
 template <int EPI, bool W8>
 static void launch_bf16(const LinearArgs& a, hipStream_t stream) {
   GemmParams p;
-  p.x = (const bf16*)a.x; p.ldx = a.ldx;
+  p.x = a.x; p.ldx = a.ldx;
+  p.x_scale = a.x_scale;
   p.w = a.w; p.ldw = a.ldw;
   p.w_scale = a.w_scale;
   p.bias = (const bf16*)a.bias;
@@ -531,10 +561,12 @@ static void launch_bf16(const LinearArgs& a, hipStream_t stream) {
   p.m = (int)a.m; p.n = (int)a.n; p.k = (int)a.k;
   p.tiles_m = (p.m + BM - 1) / BM;
   p.tiles_n = (p.n + BN - 1) / BN;
-  if constexpr (W8)
+  if (a.act == kINT8)
+    gemm_ring_kernel<EPI, true><<<dim3(p.tiles_m * p.tiles_n), dim3(512), 0, stream>>>(p);
+  else if constexpr (W8)
     gemm_bf16_kernel<EPI, W8><<<dim3(p.tiles_m * p.tiles_n), dim3(512), 0, stream>>>(p);
   else
-    gemm_bf16_dma_kernel<EPI><<<dim3(p.tiles_m * p.tiles_n), dim3(512), 0, stream>>>(p);
+    gemm_ring_kernel<EPI, false><<<dim3(p.tiles_m * p.tiles_n), dim3(512), 0, stream>>>(p);
 }
 
 template <int EPI>

@@ -101,6 +101,10 @@ h3k_status validate_config(const h3k_dit_config* c) {
   if (c->cond_dim % 8 != 0 || c->cond_dim > 8192)
     return fail(H3K_ERR_UNSUPPORTED, "cond_dim %d must be a multiple of 8 and <= 8192", c->cond_dim);
   if (!(c->ln_eps > 0.0f) || !(c->ln_eps < 1.0f)) return fail(H3K_ERR_SHAPE, "ln_eps must be in (0, 1)");
+  if (c->int8_fc2_rows != 0 && c->int8_fc2_rows != 1) return fail(H3K_ERR_SHAPE, "int8_fc2_rows must be 0 or 1");
+  if (c->int8_fc2_rows &&
+      (c->weight_dtype != H3K_INT8 || c->act_dtype != H3K_BF16 || c->mlp_hidden % 128 != 0))
+    return fail(H3K_ERR_UNSUPPORTED, "int8_fc2_rows needs INT8 weights, BF16 activations and mlp_hidden a multiple of 128");
   const int64_t eb = esize(c->act_dtype);
   const int64_t rows = (int64_t)c->n_tokens + 256;
   const int64_t widest = std::max<int64_t>(2 * (int64_t)c->hidden, c->mlp_hidden);
@@ -118,7 +122,7 @@ bool alias_enabled(const h3k_dit_config* c) {
 
 // ---------------------------------------------------------------- planner
 // Kernel steps of one block: 0 AdaLN, 1 LN, 2 QKV, 3 attention, 4 out-proj,
-// 5 LN, 6 MLP up, 7 MLP down.  A tensor is live from the step that writes it
+// 5 LN, 6 MLP up, 7 row quantiser of u (int8_fc2_rows only), 8 MLP down.  A tensor is live from the step that writes it
 // to the last step that reads it.  With aliasing, each tensor is placed
 // first-fit (lowest 256-aligned offset) among the already placed tensors
 // whose live ranges intersect its own, in a fixed order; without aliasing,
@@ -137,8 +141,11 @@ void make_plan(const h3k_dit_config* c, bool alias, h3k_dit_plan_info* P) {
   bytes[H3K_T_X1] = N * D * eb;
   bytes[H3K_T_H2] = N * D * eb;
   bytes[H3K_T_U] = N * F * eb;
-  const int first[H3K_T_COUNT] = {0, 1, 2, 3, 4, 5, 6};
-  const int last[H3K_T_COUNT] = {7, 2, 3, 4, 7, 6, 7};
+  const bool q8 = c->int8_fc2_rows != 0;
+  bytes[H3K_T_UQ] = q8 ? N * F : 0;
+  bytes[H3K_T_US] = q8 ? N * 4 : 0;
+  const int first[H3K_T_COUNT] = {0, 1, 2, 3, 4, 5, 6, 7, 7};
+  const int last[H3K_T_COUNT] = {8, 2, 3, 4, 8, 6, q8 ? 7 : 8, 8, 8};
   uint64_t off[H3K_T_COUNT];
   uint64_t unaliased = 0;
   for (int t = 0; t < H3K_T_COUNT; ++t) unaliased += align_up(bytes[t], kAlign);
@@ -162,7 +169,7 @@ void make_plan(const h3k_dit_config* c, bool alias, h3k_dit_plan_info* P) {
   }
   uint64_t ws = 0, peak = 0;
   for (int t = 0; t < H3K_T_COUNT; ++t) ws = std::max(ws, off[t] + align_up(bytes[t], kAlign));
-  for (int s = 0; s <= 7; ++s) {
+  for (int s = 0; s <= 8; ++s) {
     uint64_t live = 0;
     for (int t = 0; t < H3K_T_COUNT; ++t)
       if (first[t] <= s && s <= last[t]) live += align_up(bytes[t], kAlign);
@@ -288,8 +295,9 @@ h3k_status validate_forward(const h3k_dit_config* c, const h3k_dit_block_weights
   return H3K_OK;
 }
 
-// Enqueue the eight kernels of one block.  x may equal out (stack in place:
-// x is last read by the out-projection, out is first written by MLP down).
+// Enqueue the eight kernels of one block (nine with int8_fc2_rows).  x may
+// equal out (stack in place: x is last read by the out-projection, out is
+// first written by MLP down).
 h3k_status run_block(const h3k_dit_config* c, const h3k_dit_plan_info* P, const h3k_dit_block_weights* w,
                      const void* x, const void* cond, void* out, char* ws, hipStream_t s, Recorder& rec) {
   const DType act = (DType)c->act_dtype;
@@ -351,6 +359,13 @@ h3k_status run_block(const h3k_dit_config* c, const h3k_dit_plan_info* P, const 
   L.act = act; L.weight = wt;
   L.m = N; L.n = D; L.k = F;
   L.x = u; L.ldx = F; L.w = w->w_down; L.ldw = F; L.w_scale = w->s_down; L.bias = w->b_down;
+  if (c->int8_fc2_rows) {
+    int8_t* uq = reinterpret_cast<int8_t*>(ws + P->offset[H3K_T_UQ]);
+    float* us = reinterpret_cast<float*>(ws + P->offset[H3K_T_US]);
+    H3K_TRY(launched(launch_quantize_int8(act, u, N, F, uq, us, s), "row quantiser of u"));
+    rec.done(H3K_K_ACT_QUANT);
+    L.act = kINT8; L.x = uq; L.x_scale = us;
+  }
   L.epi = kEpiGatedResidual; L.residual = x1; L.ldr = D; L.gate = gate_m;
   L.y = out; L.ldy = D; L.split_col = D;
   H3K_TRY(launched(launch_linear(L, s), "MLP down"));
@@ -371,7 +386,7 @@ h3k_status forward(const h3k_dit_config* cfg, const h3k_dit_block_weights* block
     stats->workspace_bytes = plan.workspace_bytes;
     stats->peak_live_bytes = plan.peak_live_bytes;
     stats->unaliased_bytes = plan.unaliased_bytes;
-    stats->dispatches = 8 * n_blocks;
+    stats->dispatches = (cfg->int8_fc2_rows ? 9 : 8) * n_blocks;
     stats->alias_activations = plan.alias_activations;
   }
   return H3K_OK;
@@ -518,6 +533,42 @@ h3k_status h3k_linear(h3k_dtype act_dtype, h3k_dtype weight_dtype, int64_t m, in
   L.epi = (Epilogue)epilogue; L.residual = residual; L.ldr = ldr; L.gate = gate;
   L.y = y; L.ldy = ldy; L.yt = yt; L.ldyt = ldyt; L.split_col = split_col;
   return launched(launch_linear(L, stream), "linear");
+}
+
+h3k_status h3k_linear_int8(int64_t m, int64_t n, int64_t k, const int8_t* xq, int64_t ldx, const float* x_scale,
+                           const int8_t* wq, int64_t ldw, const float* w_scale, const void* bias, int32_t epilogue,
+                           const void* residual, int64_t ldr, const float* gate, void* y, int64_t ldy,
+                           hipStream_t stream) {
+  if (epilogue < H3K_EPI_BIAS || epilogue > H3K_EPI_GATED_RESIDUAL) return fail(H3K_ERR_SHAPE, "bad epilogue %d", epilogue);
+  if (m < 0 || n < 8 || n % 8 || k < 128 || k % 128 || k > (1 << 17))
+    return fail(H3K_ERR_SHAPE, "need m >= 0, n a multiple of 8, k a multiple of 128 and <= 2^17 (m=%lld n=%lld k=%lld)",
+                (long long)m, (long long)n, (long long)k);
+  if (ldx < k || ldw < k || ldx % 16 || ldw % 16 || ldy < n || ldy % 8)
+    return fail(H3K_ERR_SHAPE, "bad row pitches");
+  if (!xq || !x_scale || !wq || !w_scale || !y) return fail(H3K_ERR_NULL, "xq, x_scale, wq, w_scale and y must be non-NULL");
+  if (epilogue == H3K_EPI_GATED_RESIDUAL && (!residual || !gate || ldr < n || ldr % 8))
+    return fail(H3K_ERR_NULL, "gated residual needs residual (ldr >= n, multiple of 8) and gate");
+  const void* al[] = {xq, wq, bias, residual, y, x_scale, w_scale, gate};
+  for (const void* p : al)
+    if (p && !aligned(p, 16)) return fail(H3K_ERR_ALIGN, "pointers must be 16-byte aligned");
+  if ((m + 256) * ldx > kMaxOffset || (n + 256) * ldw > kMaxOffset)
+    return fail(H3K_ERR_UNSUPPORTED, "operand exceeds 2 GiB (32-bit offsets)");
+  const Range rx = rng(xq, span(m, k, ldx, 1), "xq"), rw = rng(wq, span(n, k, ldw, 1), "wq");
+  const Range rxs = rng(x_scale, m * 4, "x_scale"), rws = rng(w_scale, n * 4, "w_scale");
+  const Range ry = rng(y, span(m, n, ldy, 2), "y");
+  if (overlaps(ry, rx) || overlaps(ry, rw) || overlaps(ry, rxs) || overlaps(ry, rws))
+    return fail(H3K_ERR_OVERLAP, "y overlaps an input");
+  if (residual && residual != y && overlaps(ry, rng(residual, span(m, n, ldr, 2), "residual")))
+    return fail(H3K_ERR_OVERLAP, "y partially overlaps residual");
+  if (m == 0) return H3K_OK;
+  H3K_TRY(check_device());
+  LinearArgs L{};
+  L.act = kINT8; L.weight = kINT8;
+  L.m = m; L.n = n; L.k = k;
+  L.x = xq; L.ldx = ldx; L.x_scale = x_scale; L.w = wq; L.ldw = ldw; L.w_scale = w_scale; L.bias = bias;
+  L.epi = (Epilogue)epilogue; L.residual = residual; L.ldr = ldr; L.gate = gate;
+  L.y = y; L.ldy = ldy; L.split_col = n;
+  return launched(launch_linear(L, stream), "int8 linear");
 }
 
 h3k_status h3k_attention(h3k_dtype dtype, int32_t n, int32_t n_heads, int32_t head_dim, const void* q, int64_t ldq,

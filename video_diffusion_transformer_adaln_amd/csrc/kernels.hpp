@@ -32,6 +32,7 @@ struct LinearArgs {
   void* y; int64_t ldy;
   void* yt; int64_t ldyt;
   int64_t split_col;
+  const float* x_scale;   // per-row activation scales (act = kINT8 only)
 };
 hipError_t launch_linear(const LinearArgs& a, hipStream_t stream);
 
