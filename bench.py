@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 METRIC = "DiT step ms + TFLOP/s (MFMA util %) at 22.7k latent tokens, bf16, 1 GPU"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_INT8_TOPS = 5000.0        # MI355X dense int8 MFMA
 
 
 def log(*a):
@@ -299,6 +300,22 @@ def extra_blocks(b0, x, c):
         "quantiser": {"ms_for_4_matrices": round(q_ms, 3), "gbs": round(q_bytes / (q_ms * 1e-3) / 1e9, 1)},
     }
     log(f"int8-weight block: {ms8:.2f} ms; quantiser {q_ms:.3f} ms")
+    # ---- the same block with the row-quantised FC2 (int8 x int8 MLP-down)
+    cfgq = B.make_config(N, D, H, d, F, C, B.H3K_BF16, B.H3K_INT8, True, int8_fc2_rows=True)
+    msq, kq = _time_block(cfgq, t8, x, c)
+    fc2 = kq["mlp_down"]["total_ms"] / kq["mlp_down"]["launches"]
+    aq = kq["act_quant"]["total_ms"] / kq["act_quant"]["launches"]
+    fc2_tops = fl["mlp_down"] / (fc2 * 1e-3) / 1e12
+    res["int8_fc2_block"] = {
+        "workload": "the int8-weight block with the row-quantised FC2: u quantised per token row, MLP-down "
+                    "as int8 x int8 on v_mfma_i32_32x32x32_i8 (int32 accumulation)",
+        "ms_per_block": round(msq, 3), "tflops": round(sum(fl.values()) / (msq * 1e-3) / 1e12, 1),
+        "fc2": {"avg_ms": round(fc2, 4), "tops": round(fc2_tops, 1), "peak_tops": PEAK_INT8_TOPS,
+                "frac": round(fc2_tops / PEAK_INT8_TOPS, 4)},
+        "u_row_quantiser": {"avg_ms": round(aq, 4),
+                            "gbs": round((N * F * 3 + N * 4) / (aq * 1e-3) / 1e9, 1)},
+    }
+    log(f"int8-FC2 block: {msq:.2f} ms (FC2 {fc2:.3f} ms, u quantiser {aq:.3f} ms)")
     del t8
     # ---- 6144-token bf16 block
     sh = si.C1
