@@ -43,7 +43,7 @@ def _ht(a, dtype):
 
 # ------------------------------------------------------------------ AdaLN GEMV
 
-@pytest.mark.parametrize("rows,cols,dtype", [(6 * 5120, 5120, "bf16"), (6 * 256, 256, "f32"), (72, 24, "bf16"),
+@pytest.mark.parametrize("rows,cols,dtype", [(6 * 5120, 5120, "bf16"), (6 * 256, 256, "f32"), (72, 24, "bf16"), (30, 40, "bf16"), (42, 16, "f32"),
                                              (6 * 3072, 3072, "bf16")])
 def test_adaln_gemv(B, rows, cols, dtype):
     import torch

@@ -9,36 +9,56 @@
 namespace h3k {
 
 // ---------------------------------------------------------------------------
-// mod[row] = sum_k W[row, k] c[k] + b[row].  One wave per output row, 16-byte
-// loads along k; c is staged once per workgroup in LDS as fp32.  The sum
-// order is fixed by (lane, iteration), so results are deterministic.
+// mod[row] = sum_k W[row, k] c[k] + b[row].  One wave per four output rows,
+// 16-byte loads along k (the four rows' loads of several iterations in flight
+// per lane: one row per wave left the HBM stream latency-bound at ~3.7 TB/s);
+// c is staged once per workgroup in LDS as fp32.  The sum order is fixed by
+// (lane, iteration), so results are deterministic.
+constexpr int GEMV_ROWS = 4;
 template <typename T>
 __global__ __launch_bounds__(256) void adaln_gemv_kernel(const T* __restrict__ w, const T* __restrict__ b,
                                                          const T* __restrict__ c, float* __restrict__ mod,
                                                          int rows, int cols) {
+  constexpr int RW = GEMV_ROWS;
   extern __shared__ float c_lds[];
   for (int i = threadIdx.x; i < cols; i += blockDim.x) c_lds[i] = to_f32(c[i]);
   __syncthreads();
   const int lane = threadIdx.x % kWave;
-  const int row = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
-  if (row >= rows) return;
+  const int row0 = (blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave) * RW;
+  if (row0 >= rows) return;
   constexpr int V = 16 / sizeof(T);
-  const T* wr = w + (int64_t)row * cols;
-  float acc = 0.f;
-#pragma unroll 4
-  for (int k0 = lane * V; k0 < cols; k0 += kWave * V) {
-    const u32x4 raw = *reinterpret_cast<const u32x4*>(wr + k0);
-    const T* e = reinterpret_cast<const T*>(&raw);
+  const T* wr[RW];
+  float acc[RW];
 #pragma unroll
-    for (int j = 0; j < V; ++j) acc += to_f32(e[j]) * c_lds[k0 + j];
+  for (int r = 0; r < RW; ++r) {
+    wr[r] = w + (int64_t)min(row0 + r, rows - 1) * cols;
+    acc[r] = 0.f;
   }
-  acc = wave_sum(acc);
-  if (lane == 0) mod[row] = acc + (b ? to_f32(b[row]) : 0.f);
+#pragma unroll 8
+  for (int k0 = lane * V; k0 < cols; k0 += kWave * V) {
+    u32x4 raw[RW];
+#pragma unroll
+    for (int r = 0; r < RW; ++r) raw[r] = *reinterpret_cast<const u32x4*>(wr[r] + k0);
+    float cv[V];
+#pragma unroll
+    for (int j = 0; j < V; ++j) cv[j] = c_lds[k0 + j];
+#pragma unroll
+    for (int r = 0; r < RW; ++r) {
+      const T* e = reinterpret_cast<const T*>(&raw[r]);
+#pragma unroll
+      for (int j = 0; j < V; ++j) acc[r] += to_f32(e[j]) * cv[j];
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < RW; ++r) {
+    const float a = wave_sum(acc[r]);
+    if (lane == 0 && row0 + r < rows) mod[row0 + r] = a + (b ? to_f32(b[row0 + r]) : 0.f);
+  }
 }
 
 hipError_t launch_adaln_gemv(DType dt, int rows, int cols, const void* w, const void* b, const void* c,
                              float* mod, hipStream_t stream) {
-  const dim3 block(256), grid((rows + 3) / 4);
+  const dim3 block(256), grid((rows + 4 * GEMV_ROWS - 1) / (4 * GEMV_ROWS));
   const size_t lds = sizeof(float) * (size_t)cols;
   if (dt == kBF16)
     adaln_gemv_kernel<bf16><<<grid, block, lds, stream>>>((const bf16*)w, (const bf16*)b, (const bf16*)c, mod,
