@@ -269,6 +269,39 @@ def test_attention(B, n, heads, hd, dtype, full):
     assert rel_l2(got, ref) < (F32_TOL if dtype == "f32" else BF16_TOL)
 
 
+@pytest.mark.parametrize("n,hd,kind", [(700, 128, "ramp"), (2000, 128, "ramp"), (700, 64, "ramp"), (333, 128, "huge"),
+                                        (100, 64, "huge")])
+def test_attention_moving_reference(B, n, hd, kind):
+    """The kernel's softmax reference moves only when a tile's probabilities
+    would exceed a bound; these inputs make it move after the first tile.
+    ramp: key rows scaled by 1 + 6 j / n, so later keys score ever higher;
+    huge: queries scaled by 300 (logits of std ~100 in log2 units), where
+    exponentials taken without moving the reference would overflow."""
+    import torch
+    flush(f"attention moving reference n={n} d={hd} {kind}")
+    heads = 2
+    D = heads * hd
+    q = _f32((n, D), 1.0, 821, "x") * 0.6
+    k = _f32((n, D), 1.0, 821, "c") * 0.6
+    if kind == "ramp":
+        k = k * (1.0 + 6.0 * np.arange(n, dtype=np.float32)[:, None] / n)
+    else:
+        q = q * 300.0
+    q, k = _ht(q, "bf16"), _ht(k, "bf16")
+    v = _ht(_f32((n, D), 1.0, 821, "w_qkv"), "bf16")
+    ldvt = ((n + 7) // 8) * 8
+    vt = np.zeros((D, ldvt), dtype=np.float32)
+    vt[:, :n] = v.values.T
+    vtd = torch.from_numpy(vt).to(torch.bfloat16).cuda()
+    o = torch.full((n, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    B.h3k_attention(B.H3K_BF16, n, heads, hd, dev(q), D, dev(k), D, vtd, ldvt, o, D)
+    torch.cuda.synchronize()
+    ref = oracle.attention(q.values, k.values, v.values, heads)
+    got = to_np(o)
+    assert np.isfinite(got).all()
+    assert rel_l2(got, ref) < BF16_TOL
+
+
 # ------------------------------------------------------------------ int8 quantiser
 
 @pytest.mark.parametrize("rows,cols,dtype", [(15360, 5120, "f32"), (5120, 13824, "f32"), (300, 77, "f32"),

@@ -2,34 +2,45 @@
 // the middle stage of the block (h3.c memory-techniques page, technique 2).
 //
 // bf16 path (flash-style, fp32 online softmax, v_mfma_f32_32x32x16_bf16):
-//   * one workgroup = 4 waves = 4*QB*32 queries of one head; each wave keeps
-//     its queries' Q fragments in registers and loops over all keys in tiles
-//     of 64, staged (double-buffered) in LDS;
+//   * one workgroup = NW waves x 32 queries of one head (NW = 8 for d = 128,
+//     4 for d = 64); each wave keeps its queries' Q fragments in registers and
+//     walks all keys in tiles of 32;
 //   * scores are computed transposed, S^T = K Q^T, so that the accumulator's
-//     lane index is the query: every lane owns its query's running max and
-//     sum, and rescaling the output needs no cross-lane traffic except one
-//     xor-32 exchange for the tile maximum;
+//     lane index is the query: every lane owns its query's running reference
+//     and sum, and rescaling needs no cross-lane traffic except one xor-32
+//     exchange for a tile maximum;
 //   * K rows are read through a fixed key permutation (bits 2 and 3 of the
 //     key index swapped inside each 32-key block), so that the eight
 //     probabilities a lane holds per 16-key step are eight consecutive keys;
 //     they then serve directly as the B operand of O^T = V^T P^T;
 //   * V arrives transposed (V^T [H*d, ldvt], written so by the QKV projection),
 //     so the A operand of O^T = V^T P^T is a 16-byte read along the key axis;
-//   * keys beyond N contribute exactly zero: their K rows load as zero, their
-//     scores are set to -inf and their V^T entries to zero.
+//   * software pipeline: the step for tile t runs the scores of tile t+1 and
+//     the product with V of tile t-1 on the matrix cores while the vector
+//     ALUs take the exponentials of tile t.  The three are independent; the
+//     step is written as chunks (an LDS read two chunks ahead, one MFMA, a
+//     share of the exponentials) kept in order by sched_barrier, so that
+//     each wave alternates the two units;
+//   * lazy online softmax without a per-tile maximum: probabilities are
+//     exp2(s - m) against the running reference m.  When some lane's tile sum
+//     exceeds 2^8 (a probability above 2^8, or the first tile, where m is
+//     still -inf) the tile is redone: m moves to the maximum so far, O and the
+//     row sum l (which hold tiles up to t-1, all relative to the old m) are
+//     scaled by exp2(m_old - m_new), and the exponentials are recomputed.
+//     The result is the usual online-softmax recurrence with the reference
+//     updated only when a probability would otherwise exceed 2^8;
+//   * two tiles per workgroup barrier: K tiles arrive with direct-to-LDS
+//     loads, V^T tiles through registers (keys beyond N are zeroed there),
+//     both in rings of four 32-key slots; a pass over tiles (t0, t0+1) loads
+//     K_{t0+3}, K_{t0+4}, V_{t0+1}, V_{t0+2} into the slots the previous pass
+//     read, then waits for them and meets the other waves.  The barrier
+//     carries no fence: each wave waits for its own loads first.  Keys
+//     beyond N contribute exactly zero (their K rows load as zero, their
+//     scores are set to -inf and their V^T entries to zero).
 // fp32 path: one thread per query, K/V tiles in LDS, for the small fp32
 // workload.
 #include "common.hpp"
 #include "kernels.hpp"
-#ifndef H3K_ATTN_KT
-#define H3K_ATTN_KT 64
-#endif
-#ifndef H3K_QB
-#define H3K_QB 1
-#endif
-#ifndef H3K_NW
-#define H3K_NW 8
-#endif
 
 namespace h3k {
 
@@ -42,7 +53,7 @@ struct AttnParams {
   float scale_log2;   // log2(e) / sqrt(d)
 };
 
-constexpr float kRescaleLog2 = 8.0f;   // lazy-rescale threshold (log2 units)
+constexpr float kLazyBound = 256.0f;   // a tile is redone when a lane's probability sum exceeds this
 
 __device__ __forceinline__ f32x16 mfma32a(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -50,13 +61,8 @@ __device__ __forceinline__ f32x16 mfma32a(const bf16x8& a, const bf16x8& b, cons
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
-__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-}
-// 16-byte direct-to-LDS buffer load: lane l's 16 bytes land at lds_dst + 16 l.
-// (A plain device function: host compilation never instantiates its body.)
-__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, char* lds_dst, uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_dst, 16, voff, 0, 0, 0);
+__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff = 0) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, 0);
 }
 // Row halves are swapped when bit 2 xor bit 3 of the row is set (LDS banks).
 __device__ __forceinline__ int hswap(int r) { return ((r >> 2) ^ (r >> 3)) & 1; }
@@ -64,25 +70,30 @@ __device__ __forceinline__ int hswap(int r) { return ((r >> 2) ^ (r >> 3)) & 1; 
 __device__ __forceinline__ int kperm(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
 // Chunk swizzle of a K row of CPR 16-byte chunks (CPR = 16 for d = 128, 8 for
 // d = 64): the fragment reads of rows kperm(0..7), kperm(8..15) and of any 16
-// consecutive rows each land on distinct banks (checked exhaustively offline).
+// consecutive rows each land on distinct banks.
 template <int CPR> __device__ __forceinline__ int kswz(int r);
 template <> __device__ __forceinline__ int kswz<16>(int r) { return (r & 15) ^ (((r >> 3) & 1) << 2); }
 template <> __device__ __forceinline__ int kswz<8>(int r) { return (r & 7) ^ (((r >> 3) & 1) * 5); }
 
-template <int HD, int KT, int QB, int NW>
+template <int HD, int NW>
 __global__ __launch_bounds__(NW * 64) void attention_bf16_kernel(AttnParams p) {
-  constexpr int KB = KT / 32;                  // 32-key blocks per tile
-  // K stage: [64 keys][HD dims] (HD*2-byte rows), 16-byte chunk c of row r at
-  // chunk c ^ kswz(r).  V^T stage: 4 planes (one per 16-key step) of [HD rows][32 B].
+  constexpr int KT = 32;                       // keys per tile
+  constexpr int KS = HD / 16;                  // k-steps of the score product
+  constexpr int DB = HD / 32;                  // 32-row blocks of O^T
+  // K stage: [32 keys][HD dims] (HD*2-byte rows), 16-byte chunk c of row r at
+  // chunk c ^ kswz(r).  V^T stage: 2 planes (one per 16-key step) of
+  // [HD rows][32 B], the two 16-byte halves of row r swapped when hswap(r).
+  // Four slots of each; tile j lives in slot j % 4.
   constexpr int KROW = HD * 2, KBYTES = KT * KROW;
-  constexpr int VPL = HD * 32, VBYTES = (KT / 16) * VPL;
-  __shared__ __attribute__((aligned(1024))) char lds[2 * KBYTES + 2 * VBYTES];
-  char* const kbuf0 = lds;
-  char* const kbuf1 = lds + KBYTES;
-  char* const vbuf0 = lds + 2 * KBYTES;
-  char* const vbuf1 = lds + 2 * KBYTES + VBYTES;
+  constexpr int VPL = HD * 32, VBYTES = 2 * VPL;
+  static_assert(KBYTES == NW * 1024, "one K load instruction per wave and tile");
+  static_assert(HD == NW * 16, "one V^T load per lane and tile");
+  __shared__ __attribute__((aligned(1024))) char lds[4 * KBYTES + 4 * VBYTES];
+  char* const kbuf = lds;                      // slot u at kbuf + u * KBYTES
+  char* const vbuf = lds + 4 * KBYTES;         // slot u at vbuf + u * VBYTES
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, l32 = lane & 31;
   const int nblk = p.q_tiles * p.n_heads;
   const int lin = xcd_remap(blockIdx.x, nblk);
@@ -90,241 +101,268 @@ __global__ __launch_bounds__(NW * 64) void attention_bf16_kernel(AttnParams p) {
   const int qtile = lin - head * p.q_tiles;
   const int N = p.n;
   const int T = (N + KT - 1) / KT;
-  const int q0 = qtile * (NW * QB * 32) + wave * (QB * 32);
+  const int q0 = qtile * (NW * 32) + wave * 32;
+  const float sc = p.scale_log2;
 
-  // ---- Q fragments (B operand of S^T = K Q^T)
-  bf16x8 qf[QB][HD / 16];
+  // ---- Q fragments (B operand of S^T = K Q^T); queries >= N load as zero
+  bf16x8 qf[KS];
   {
     const __amdgpu_buffer_rsrc_t rq = rsrc(p.q, (uint32_t)((uint64_t)N * p.ldq * 2));
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-      for (int ks = 0; ks < HD / 16; ++ks) {
-        const uint32_t off = (uint32_t)(q0 + qb * 32 + l32) * (uint32_t)p.ldq * 2u + (head * HD + ks * 16 + h * 8) * 2;
-        const u32x4 v = bload16(rq, off);
-        qf[qb][ks] = *reinterpret_cast<const bf16x8*>(&v);
-      }
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint32_t off = (uint32_t)(q0 + l32) * (uint32_t)p.ldq * 2u + (head * HD + ks * 16 + h * 8) * 2;
+      const u32x4 v = bload16(rq, off);
+      qf[ks] = *reinterpret_cast<const bf16x8*>(&v);
+    }
   }
 
-  // ---- K tiles: direct-to-LDS loads.  A wave instruction fills 1 KiB =
-  // KT*KROW/1024 ... rows (HD*2 bytes each); lane l -> row r0 + l/(KROW/16),
-  // physical chunk l%(KROW/16), fetching logical chunk phys ^ kswz(row).
+  // ---- K tiles: direct-to-LDS loads, one 1 KiB instruction per wave: lane l
+  // -> row wave*RPI + l/CPR, physical chunk l%CPR, fetching logical chunk
+  // phys ^ kswz(row).  Rows >= N load as zero (buffer bounds); tiles past the
+  // last one re-load the last tile so that the load counts stay uniform.
   constexpr int CPR = KROW / 16;               // chunks per K row
-  constexpr int RPI = 64 / CPR;                // rows per DMA instruction
-  constexpr int KDMA = KT / RPI / NW;          // DMA instructions per wave per tile
-  static_assert(KDMA >= 1 && KDMA * RPI * NW == KT, "K tile does not split over the waves");
+  constexpr int RPI = 64 / CPR;                // rows per load instruction
   const __amdgpu_buffer_rsrc_t rk = rsrc(p.k, (uint32_t)((uint64_t)N * p.ldk * 2));
-  uint32_t kdma_off[KDMA];
-#pragma unroll
-  for (int j = 0; j < KDMA; ++j) {
-    const int row = (j * NW + wave) * RPI + lane / CPR;
+  uint32_t kdma_off;
+  {
+    const int row = wave * RPI + lane / CPR;
     const int c = (lane % CPR) ^ kswz<CPR>(row);
-    kdma_off[j] = (uint32_t)row * (uint32_t)p.ldk * 2u + (head * HD + c * 8) * 2;
+    kdma_off = (uint32_t)row * (uint32_t)p.ldk * 2u + (head * HD + c * 8) * 2;
   }
-  auto kdma = [&](int t, char* dst) {
-    const uint32_t kofs = (uint32_t)t * KT * (uint32_t)p.ldk * 2u;
-#pragma unroll
-    for (int j = 0; j < KDMA; ++j)
-      lds_dma16(rk, dst + (j * NW + wave) * RPI * KROW, kdma_off[j] + kofs);
+  const uint32_t ktile_bytes = (uint32_t)KT * (uint32_t)p.ldk * 2u;
+  auto kdma = [&](int t) {
+    const int tt = t < T ? t : T - 1;
+    lds_dma16(rk, kbuf + (t & 3) * KBYTES + wave * 1024, kdma_off, (uint32_t)tt * ktile_bytes);
   };
 
-  // ---- V^T tiles: register staging (keys >= N are zeroed here)
-  // a wave instruction covers (KT/16) planes x (64/(KT/16)/2) rows x 2 halves
-  constexpr int VPLN = KT / 16;                // planes per tile
-  constexpr int VRPW = 32 / VPLN;              // V^T rows per wave instruction
-  const int st_pl = lane / (64 / VPLN), st_row = (lane % (64 / VPLN)) >> 1, st_h = lane & 1;
-  constexpr int VLOADS = (HD * KT / 8) / (NW * 64);
-  static_assert(VLOADS >= 1 && VLOADS * NW * VRPW == HD, "V^T tile does not split over the waves");
-  u32x4 rv_[VLOADS];
-  auto vload = [&](int t) {
-    const int k0 = t * KT;
-    const bool full = k0 + KT <= N;
+  // ---- V^T tiles: one 16-byte load per lane: plane lane/32, row
+  // wave*16 + (lane%32)/2, half lane&1 (keys 16 plane + 8 half .. +8)
+  const int st_pl = lane >> 5, st_row = wave * 16 + ((lane & 31) >> 1), st_h = lane & 1;
+  const __amdgpu_buffer_rsrc_t rvt = rsrc(p.vt, (uint32_t)((uint64_t)p.n_heads * HD * p.ldvt * 2));
+  const uint32_t vld_off = ((uint32_t)(head * HD + st_row) * (uint32_t)p.ldvt + st_pl * 16 + st_h * 8) * 2u;
+  const int vst_off = st_pl * VPL + st_row * 32 + ((st_h ^ hswap(st_row)) << 4);
+  auto vload_full = [&](int t) { return bload16(rvt, vld_off, (uint32_t)t * (KT * 2)); };
+  auto vload_masked = [&](int t) {             // zero for keys >= N
+    const int key0 = t * KT + st_pl * 16 + st_h * 8;
+    u32x4 v = {0, 0, 0, 0};
+    if (key0 < N) {
+      v = bload16(rvt, vld_off, (uint32_t)t * (KT * 2));
+      uint16_t* e = reinterpret_cast<uint16_t*>(&v);
 #pragma unroll
-    for (int i = 0; i < VLOADS; ++i) {
-      const int row = i * (NW * VRPW) + wave * VRPW + st_row;
-      const int key0 = k0 + st_pl * 16 + st_h * 8;
-      const bf16* src = p.vt + (int64_t)(head * HD + row) * p.ldvt + key0;
-      if (full) {
-        rv_[i] = *reinterpret_cast<const u32x4*>(src);
-      } else {
-        u32x4 v = {0, 0, 0, 0};
-        if (key0 < N) {
-          v = *reinterpret_cast<const u32x4*>(src);
-          uint16_t* e = reinterpret_cast<uint16_t*>(&v);
-#pragma unroll
-          for (int j = 0; j < 8; ++j)
-            if (key0 + j >= N) e[j] = 0;
-        }
-        rv_[i] = v;
-      }
+      for (int j = 0; j < 8; ++j)
+        if (key0 + j >= N) e[j] = 0;
     }
+    return v;
   };
-  auto vstore = [&](char* base) {
-#pragma unroll
-    for (int i = 0; i < VLOADS; ++i) {
-      const int row = i * (NW * VRPW) + wave * VRPW + st_row;
-      *reinterpret_cast<u32x4*>(base + st_pl * VPL + row * 32 + ((st_h ^ hswap(row)) << 4)) = rv_[i];
-    }
-  };
+  auto vstore = [&](int t, const u32x4& v) { *reinterpret_cast<u32x4*>(vbuf + (t & 3) * VBYTES + vst_off) = v; };
 
-  // ---- fragment addresses.  K: row kperm(l32) (+ kb*32), chunk 2ks+h;
+  // ---- fragment addresses.  K: row kperm(l32), logical chunk 2ks+h;
   // V^T: row l32 (+ db*32), plane = 16-key step.
   const int kr = kperm(l32);
   const int kq = kswz<CPR>(kr);
-  int k_off[HD / 16];
+  int k_off[KS];
 #pragma unroll
-  for (int ks = 0; ks < HD / 16; ++ks) k_off[ks] = kr * KROW + (((2 * ks + h) ^ kq) << 4);
+  for (int ks = 0; ks < KS; ++ks) k_off[ks] = kr * KROW + (((2 * ks + h) ^ kq) << 4);
   const int v_frag = l32 * 32 + ((h ^ hswap(l32)) << 4);
 
-  f32x16 O[HD / 32][QB];
+  f32x16 O[DB];
 #pragma unroll
-  for (int db = 0; db < HD / 32; ++db)
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) O[db][qb] = f32x16{};
-  float m_run[QB], l_run[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) { m_run[qb] = -INFINITY; l_run[qb] = 0.f; }
+  for (int db = 0; db < DB; ++db) O[db] = f32x16{};
+  float m_ref = -INFINITY, l_run = 0.f;
+  f32x16 S[2];
+  bf16x8 P[2][2];
 
-  auto scores = [&](const char* kb_base, f32x16 (&S)[KB][QB]) {
+  auto scores = [&](const char* kb, f32x16& s) {
+    s = f32x16{};
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
+    for (int ks = 0; ks < KS; ++ks) s = mfma32a(*reinterpret_cast<const bf16x8*>(kb + k_off[ks]), qf[ks], s);
+  };
+  auto pv = [&](const char* vb, const bf16x8 (&pp)[2]) {
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) S[kb][qb] = f32x16{};
+    for (int m = 0; m < 2; ++m)
 #pragma unroll
-    for (int ks = 0; ks < HD / 16; ++ks)
+      for (int db = 0; db < DB; ++db)
+        O[db] = mfma32a(*reinterpret_cast<const bf16x8*>(vb + m * VPL + db * 1024 + v_frag), pp[m], O[db]);
+  };
+  // keys >= N of tile t: lane half h, register r holds key 16*(r/8) + 8h + r%8
+  auto mask_tail = [&](f32x16& s, int t) {
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kb_base + kb * 32 * KROW + k_off[ks]);
+    for (int r = 0; r < 16; ++r)
+      if (t * KT + 16 * (r >> 3) + 8 * h + (r & 7) >= N) s[r] = -INFINITY;
+  };
+  // probabilities against the current reference; returns the lane's sum
+  auto expo = [&](const f32x16& s, bf16x8 (&pp)[2]) {
+    float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) S[kb][qb] = mfma32a(a, qf[qb][ks], S[kb][qb]);
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float pr = __builtin_amdgcn_exp2f(fmaf(s[8 * m + j], sc, -m_ref));
+        if (j & 1) ls1 += pr; else ls0 += pr;
+        pp[m][j] = static_cast<bf16>(pr);
       }
+    return ls0 + ls1;
+  };
+  // move the reference to the maximum so far, rescale O and l, recompute
+  auto redo = [&](const f32x16& s, bf16x8 (&pp)[2]) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave)) * sc;
+    const float m_new = fmaxf(m_ref, mx);
+    const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+    l_run *= alpha;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) O[db] *= alpha;
+    m_ref = m_new;
+    return expo(s, pp);
   };
 
-  // keys >= N of the last tile: lane half h, register r of key block kb holds
-  // key kb*32 + 16*(r/8) + 8h + r%8
-  auto mask_tail = [&](f32x16 (&S)[KB][QB], int t) {
+  // ---- one tile's work, t with K_{t+1} in K slot KSL and V_{t-1} in V slot
+  // VSL: the scores of tile t+1 and the product with V of tile t-1 on the
+  // matrix cores, the exponentials of tile t on the vector ALUs.  Chunk i
+  // issues an LDS read two chunks ahead, MFMA i (even: score k-step i/2,
+  // odd: 16-key step m and row block db of the V product) and EPM of the
+  // exponentials; sched_barrier keeps the chunks in this order, so that each
+  // wave alternates the two units.
+  auto step = [&](int t, auto u_c, auto ksl_c, auto vsl_c, bool mask) {
+    constexpr int U = decltype(u_c)::value;
+    const char* kb = kbuf + decltype(ksl_c)::value * KBYTES;
+    const char* vb = vbuf + decltype(vsl_c)::value * VBYTES;
+    if (mask) mask_tail(S[U], t);
+    constexpr int NMF = KS + 2 * DB;           // MFMAs per tile (16 or 8)
+    constexpr int EPM = 16 / NMF;              // exponentials per MFMA
+    auto frag = [&](int i) {
+      const int j = i >> 1;
+      const char* a = (i & 1) ? vb + (j / DB) * VPL + (j % DB) * 1024 + v_frag : kb + k_off[j];
+      return *reinterpret_cast<const bf16x8*>(a);
+    };
+    bf16x8 fr[NMF];
+    fr[0] = frag(0);
+    fr[1] = frag(1);
+    float pe[16];
+    float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const bool out = t * KT + kb * 32 + 16 * (r >> 3) + 8 * h + (r & 7) >= N;
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) S[kb][qb][r] = out ? -INFINITY : S[kb][qb][r];
+    for (int i = 0; i < NMF; ++i) {
+      if (i + 2 < NMF) fr[i + 2] = frag(i + 2);
+      if (i & 1) {
+        const int j = i >> 1;
+        O[j % DB] = mfma32a(fr[i], P[1 - U][j / DB], O[j % DB]);
+      } else {
+        S[1 - U] = mfma32a(fr[i], qf[i >> 1], i == 0 ? f32x16{} : S[1 - U]);
       }
-  };
-  // softmax of one tile (scores S) -> P; rescales O and l when the reference max moves
-  auto softmax = [&](const f32x16 (&S)[KB][QB], bf16x8 (&P)[KB][2][QB]) {
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[kb][qb][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave)) * p.scale_log2;
-      if (__any(mx > m_run[qb] + kRescaleLog2)) {
-        const float m_new = fmaxf(m_run[qb], mx);
-        const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
-        l_run[qb] *= alpha;
-        m_run[qb] = m_new;
-#pragma unroll
-        for (int db = 0; db < HD / 32; ++db) {   // one 16-register tile at a time
-          O[db][qb] *= alpha;
-          __builtin_amdgcn_sched_barrier(0);
+      for (int e = 0; e < EPM; ++e) {
+        const int r = i * EPM + e;
+        pe[r] = __builtin_amdgcn_exp2f(fmaf(S[U][r], sc, -m_ref));
+        if (r & 1) {
+          ls1 += pe[r];
+          P[U][r >> 3][(r & 7) - 1] = static_cast<bf16>(pe[r - 1]);
+          P[U][r >> 3][r & 7] = static_cast<bf16>(pe[r]);
+        } else {
+          ls0 += pe[r];
         }
       }
-      const float m_ref = m_run[qb];
-      float ls = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int m = 0; m < 2; ++m)
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const float pr = __builtin_amdgcn_exp2f(fmaf(S[kb][qb][8 * m + j], p.scale_log2, -m_ref));
-            ls += pr;
-            P[kb][m][qb][j] = static_cast<bf16>(pr);
-          }
-      l_run[qb] += ls;
+      __builtin_amdgcn_sched_barrier(0);
     }
+    float ls = ls0 + ls1;
+    if (__any(!(ls <= kLazyBound))) ls = redo(S[U], P[U]);
+    l_run += ls;
   };
 
-  auto pv = [&](const char* vb, const bf16x8 (&P)[KB][2][QB]) {
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int m = 0; m < 2; ++m)
-#pragma unroll
-        for (int db = 0; db < HD / 32; ++db) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(vb + (2 * kb + m) * VPL + db * 1024 + v_frag);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) O[db][qb] = mfma32a(a, P[kb][m][qb], O[db][qb]);
-        }
+  // ---- two tiles per barrier.  Pass (t0, t0+1), t0 odd, with SL = t0 % 4:
+  // entry: S_{t0}, P_{t0-1} in registers; K_{t0+1}, K_{t0+2}, V_{t0-1}, V_{t0}
+  // in LDS.  It loads K_{t0+3}, K_{t0+4}, V_{t0+1}, V_{t0+2} (into the slots
+  // of the tiles read by the previous pass) and waits for them before the
+  // barrier.  TAIL passes mask the last tile and its V^T, and skip tiles >= T.
+  using C0 = std::integral_constant<int, 0>;
+  using C1 = std::integral_constant<int, 1>;
+  using C2 = std::integral_constant<int, 2>;
+  using C3 = std::integral_constant<int, 3>;
+  auto pass = [&](int t0, auto sl_c, auto tail_c) {
+    constexpr int SL = decltype(sl_c)::value;  // 1 or 3
+    constexpr bool TAIL = decltype(tail_c)::value;
+    using K1 = std::integral_constant<int, (SL + 1) & 3>;
+    using K2 = std::integral_constant<int, (SL + 2) & 3>;
+    using V0 = std::integral_constant<int, (SL + 3) & 3>;
+    using V1 = std::integral_constant<int, SL>;
+    kdma(t0 + 3);
+    kdma(t0 + 4);
+    u32x4 va = {0, 0, 0, 0}, vb = {0, 0, 0, 0};
+    if constexpr (!TAIL) {
+      va = vload_full(t0 + 1);
+      vb = vload_full(t0 + 2);
+    } else {
+      if (t0 + 1 < T) va = vload_masked(t0 + 1);
+      if (t0 + 2 < T) vb = vload_masked(t0 + 2);
+    }
+    step(t0, C1{}, K1{}, V0{}, TAIL && t0 == T - 1);
+    if (!TAIL || t0 + 1 < T) step(t0 + 1, C0{}, K2{}, V1{}, TAIL && t0 + 1 == T - 1);
+    wait_vmcnt<0>();
+    vstore(t0 + 1, va);
+    vstore(t0 + 2, vb);
+    wait_lgkm0();
+    wg_barrier();
   };
 
-  // ---- prologue: K_0, K_1 and V_0 in LDS, S_0 computed
-  kdma(0, kbuf0);
-  if (T > 1) kdma(1, kbuf1);
-  vload(0);
-  vstore(vbuf0);
-  __builtin_amdgcn_s_waitcnt(0x0F70);          // vmcnt = 0: the K loads have landed
-  __syncthreads();
-  f32x16 Sa[KB][QB], Sb[KB][QB];
-  bf16x8 P[KB][2][QB];
-  scores(kbuf0, Sa);
-  __syncthreads();                             // kbuf0 is refilled in iteration 0
-
-  // ---- iteration t: S_{t+1} = K_{t+1} Q^T runs alongside softmax(S_t);
-  // then O += V_t P_t.  K_{t+2} and V_{t+1} are staged meanwhile.  Past the
-  // last tile these loads and scores are harmless extra work (K rows >= N
-  // load as zero, V^T past N is zeroed, stale LDS stays finite) and keep the
-  // loop body free of branches.
-  auto step = [&](int t, f32x16 (&Scur)[KB][QB], f32x16 (&Snext)[KB][QB]) {
-    char* kdst = (t & 1) ? kbuf1 : kbuf0;       // held K_t (consumed in iteration t-1)
-    const char* ksrc = (t & 1) ? kbuf0 : kbuf1; // K_{t+1}
-    const char* vsrc = (t & 1) ? vbuf1 : vbuf0; // V_t
-    char* vdst = (t & 1) ? vbuf0 : vbuf1;       // V_{t+1}
-    kdma(t + 2, kdst);
-    vload(t + 1);
-    scores(ksrc, Snext);
-    softmax(Scur, P);
-    pv(vsrc, P);
-    vstore(vdst);
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    __syncthreads();
-  };
-  int t = 0;
-  for (; t + 2 < T; t += 2) {                  // all but the last one or two tiles
-    step(t, Sa, Sb);
-    step(t + 1, Sb, Sa);
+  // ---- prologue: K_0..K_3 and V_0, V_1 staged; S_0 -> P_0 (always through
+  // redo, the reference being -inf); S_1 computed
+  kdma(0);
+  kdma(1);
+  kdma(2);
+  kdma(3);
+  {
+    const u32x4 v0 = vload_masked(0);
+    const u32x4 v1 = T > 1 ? vload_masked(1) : u32x4{0, 0, 0, 0};
+    wait_vmcnt<0>();
+    vstore(0, v0);
+    vstore(1, v1);
   }
-  if (T - t == 2) {
-    step(t, Sa, Sb);
-    mask_tail(Sb, t + 1);
-    step(t + 1, Sb, Sa);
-  } else {
-    mask_tail(Sa, t);
-    step(t, Sa, Sb);
-  }
+  wait_lgkm0();
+  wg_barrier();
+  scores(kbuf, S[0]);
+  if (T == 1) mask_tail(S[0], 0);
+  l_run += redo(S[0], P[0]);
+  if (T > 1) scores(kbuf + KBYTES, S[1]);
+  wg_barrier();                                // K slots 0 and 1 are refilled next
 
-  // ---- normalise and store: register r of tile db holds dv = db*32 + 8*(r/4) + 4h + r%4
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int q = q0 + qb * 32 + l32;
-    const float lt = l_run[qb] + __shfl_xor(l_run[qb], 32, kWave);
+  using Full = std::integral_constant<bool, false>;
+  using Tail = std::integral_constant<bool, true>;
+  int t0 = 1;
+  for (; (t0 + 5) * KT <= N; t0 += 4) {        // V^T tiles up to t0+4 are full
+    pass(t0, C1{}, Full{});
+    pass(t0 + 2, C3{}, Full{});
+  }
+  // t0 % 4 == 1 here and fewer than six tiles remain
+  if (t0 < T) pass(t0, C1{}, Tail{});
+  if (t0 + 2 < T) pass(t0 + 2, C3{}, Tail{});
+  if (t0 + 4 < T) pass(t0 + 4, C1{}, Tail{});
+  // the last tile's product with V
+  {
+    const char* vl = vbuf + ((T - 1) & 3) * VBYTES;
+    if ((T - 1) & 1) pv(vl, P[1]);
+    else pv(vl, P[0]);
+  }
+  wait_vmcnt<0>();                             // no load left in flight at exit
+
+  // ---- normalise and store: register r of block db holds dv = db*32 + 8*(r/4) + 4h + r%4
+  {
+    const int q = q0 + l32;
+    const float lt = l_run + __shfl_xor(l_run, 32, kWave);
     const float inv = 1.0f / lt;
-    if (q >= N) continue;
-    bf16* orow = p.o + (int64_t)q * p.ldo + head * HD;
+    if (q < N) {
+      bf16* orow = p.o + (int64_t)q * p.ldo + head * HD;
 #pragma unroll
-    for (int db = 0; db < HD / 32; ++db)
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        u32x2 out;
-        bf16* oe = reinterpret_cast<bf16*>(&out);
+        for (int g = 0; g < 4; ++g) {
+          u32x2 out;
+          bf16* oe = reinterpret_cast<bf16*>(&out);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) oe[e] = static_cast<bf16>(O[db][qb][4 * g + e] * inv);
-        *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * g + 4 * h) = out;
-      }
+          for (int e = 0; e < 4; ++e) oe[e] = static_cast<bf16>(O[db][4 * g + e] * inv);
+          *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * g + 4 * h) = out;
+        }
+    }
   }
 }
 
@@ -396,17 +434,18 @@ __global__ __launch_bounds__(64) void attention_f32_kernel(AttnParamsF p) {
 }
 
 // ---------------------------------------------------------------------------
-template <int HD, int KT, int QB, int NW>
+template <int HD>
 static void launch_bf16_attn(const AttentionArgs& a, hipStream_t stream) {
+  constexpr int NW = HD / 16;
   AttnParams p;
   p.q = (const bf16*)a.q; p.ldq = a.ldq;
   p.k = (const bf16*)a.k; p.ldk = a.ldk;
   p.vt = (const bf16*)a.vt; p.ldvt = a.ldvt;
   p.o = (bf16*)a.o; p.ldo = a.ldo;
   p.n = a.n; p.n_heads = a.n_heads;
-  p.q_tiles = (a.n + NW * QB * 32 - 1) / (NW * QB * 32);
+  p.q_tiles = (a.n + NW * 32 - 1) / (NW * 32);
   p.scale_log2 = 1.4426950408889634f / sqrtf((float)HD);
-  attention_bf16_kernel<HD, KT, QB, NW><<<dim3(p.q_tiles * p.n_heads), dim3(NW * 64), 0, stream>>>(p);
+  attention_bf16_kernel<HD, NW><<<dim3(p.q_tiles * p.n_heads), dim3(NW * 64), 0, stream>>>(p);
 }
 
 template <int HD>
@@ -427,8 +466,8 @@ hipError_t launch_attention(const AttentionArgs& a, hipStream_t stream) {
     if (a.head_dim == 64) launch_f32_attn<64>(a, stream);
     else launch_f32_attn<128>(a, stream);
   } else {
-    if (a.head_dim == 64) launch_bf16_attn<64, 64, H3K_QB, H3K_NW>(a, stream);
-    else launch_bf16_attn<128, H3K_ATTN_KT, H3K_QB, H3K_NW>(a, stream);
+    if (a.head_dim == 64) launch_bf16_attn<64>(a, stream);
+    else launch_bf16_attn<128>(a, stream);
   }
   return hipGetLastError();
 }

@@ -50,6 +50,28 @@ __device__ __forceinline__ int swz8(int r, int c) { return c ^ ((r ^ (r >> 3)) &
 // Same for rows of 16 chunks (256 bytes).
 __device__ __forceinline__ int swz16(int r, int c) { return c ^ (r & 15); }
 
+// 16-byte direct-to-LDS buffer load: lane l's 16 bytes land at lds_dst + 16 l.
+// (A plain device function: host compilation never instantiates its body.)
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, char* lds_dst, uint32_t voff, uint32_t soff = 0) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_dst, 16, voff, soff, 0, 0);
+}
+// Workgroup barrier without a memory fence (__syncthreads would also wait
+// for every outstanding load, including direct-to-LDS loads meant to stay in
+// flight); the empty asm statements keep the compiler from moving memory
+// accesses across it.  Callers wait for what must be visible first.
+__device__ __forceinline__ void wg_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+// s_waitcnt vmcnt(N), expcnt and lgkmcnt left at their maxima
+template <int N> __device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+// s_waitcnt lgkmcnt(0): this wave's LDS reads and writes have completed
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
 // Remap a linear workgroup id so that each XCD receives one contiguous range
 // of logical tiles (neighbouring tiles then share that XCD's L2).
 __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {

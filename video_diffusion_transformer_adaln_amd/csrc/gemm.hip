@@ -314,21 +314,6 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmParams p) {
 // which would drain the ring at each k-tile; instead each wave waits
 // (vmcnt) for its own loads of the next k-tile, then all waves meet at
 // s_barrier, after which the whole tile is visible in LDS.
-__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, char* lds_dst, uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_dst, 16, voff, 0, 0, 0);
-}
-// barrier without a fence; the empty asm statements keep the compiler from
-// moving memory accesses across it
-__device__ __forceinline__ void wg_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-// s_waitcnt vmcnt(N), expcnt and lgkmcnt left at their maxima
-template <int N> __device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 16, "vmcnt field");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
-}
 __device__ __forceinline__ int rswz(int r) { return (r ^ (r >> 3)) & 7; }
 constexpr int kSlot = 256 * 128;   // one operand's k-tile of 64: [256 rows][128 B]
 constexpr int kSlots = 5;          // 160 KiB

@@ -584,7 +584,8 @@ h3k_status h3k_attention(h3k_dtype dtype, int32_t n, int32_t n_heads, int32_t he
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(vt, 16) || !aligned(o, 16))
     return fail(H3K_ERR_ALIGN, "pointers must be 16-byte aligned");
   const int64_t e = esize(dtype);
-  if (((int64_t)n + 256) * std::max(ldq, ldk) * e > kMaxOffset) return fail(H3K_ERR_UNSUPPORTED, "operand exceeds 2 GiB");
+  if (((int64_t)n + 256) * std::max(ldq, ldk) * e > kMaxOffset || D * ldvt * e > kMaxOffset)
+    return fail(H3K_ERR_UNSUPPORTED, "operand exceeds 2 GiB");
   const Range ro = rng(o, span(n, D, ldo, e), "o");
   if (overlaps(ro, rng(q, span(n, D, ldq, e), "q")) || overlaps(ro, rng(k, span(n, D, ldk, e), "k")) ||
       overlaps(ro, rng(vt, span(D, n, ldvt, e), "vt")))
