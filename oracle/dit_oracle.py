@@ -27,8 +27,9 @@ Pins (tests/test_oracle_pins.py): textbook LayerNorm via torch on the CPU,
 pure-Python brute force of the whole block and of attention on tiny inputs,
 torch's scaled-dot-product attention and tanh-GELU, closed-form values,
 permutation equivariance, gate = 0 identity, softmax rows summing to one,
-the layer-prefix property of the stack, a pure-Python fp32 quantiser, and
-pure-Python integer sums for the int8 x int8 projection.
+the layer-prefix property of the stack, a pure-Python fp32 quantiser (per
+channel and per group), and pure-Python integer sums for the int8 x int8
+projection.
 """
 from __future__ import annotations
 
@@ -139,7 +140,42 @@ def quantize_int8(w: np.ndarray):
 
 
 def dequantize_int8(q: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """q * s in fp32; s is [rows] (per-channel) or [rows, cols / G] (groups of G)."""
+    if s.ndim == 2:
+        return dequantize_int8_groups(q, s)
     return q.astype(f32) * s.astype(f32)[:, None]
+
+
+def quantize_int8_groups(w: np.ndarray, group: int):
+    """Group-wise symmetric int8: each output channel's input axis is cut into
+    consecutive blocks of ``group`` weights, and every block gets its own
+    scale, s[o, g] = max |w[o, gG:(g+1)G]| / 127, with
+    q = clip(rint(w / s), -127, 127), ties to even, one fp32 division per
+    element.  A block of zeros gets s = 0 and q = 0.
+
+    [H3-review] speed/quality section: the engine's default MLP path on the
+    M5 is int8 with group quantisation.  The page gives no group size; the
+    library takes G in {32, 64, 128}.  With G = cols this is quantize_int8.
+    """
+    w = np.ascontiguousarray(w, dtype=f32)
+    rows, cols = w.shape
+    if cols % group:
+        raise ValueError("cols must be a multiple of the group size")
+    wg = w.reshape(rows, cols // group, group)
+    s = (np.abs(wg).max(axis=2) / f32(127.0)).astype(f32)
+    safe = np.where(s == 0, f32(1.0), s).astype(f32)
+    q = np.rint(wg / safe[:, :, None])
+    q = np.clip(q, -127, 127)
+    q[s == 0] = 0
+    return q.reshape(rows, cols).astype(np.int8), s
+
+
+def dequantize_int8_groups(q: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """w[o, k] = q[o, k] * s[o, k // G] in fp32, G = cols / s.shape[1]."""
+    rows, cols = q.shape
+    ng = s.shape[1]
+    wg = q.astype(f32).reshape(rows, ng, cols // ng) * s.astype(f32)[:, :, None]
+    return wg.reshape(rows, cols)
 
 
 def linear_w8a8(qx: np.ndarray, sx: np.ndarray, qw: np.ndarray, sw: np.ndarray,
@@ -186,7 +222,9 @@ def block_forward(x: np.ndarray, c: np.ndarray, wts: Dict[str, np.ndarray], n_he
     to some token rows: keys and values still come from every token, the
     per-token stages run only on those rows (each output row depends on its
     own row and on k, v of all rows).  Projection weights may be given as
-    (q_int8, scale) pairs, which are dequantised in fp32.
+    (q_int8, scale) pairs, which are dequantised in fp32: scale [rows] per
+    output channel, or [rows, cols / G] for groups of G input channels
+    (quantize_int8_groups; the group-wise int8 MLP).
 
     ``int8_fc2_rows`` selects the row-quantised FC2 of [H3-review]'s
     speed/quality section: u is quantised per token row with the same

@@ -118,6 +118,18 @@ def quantize_row_int8(row):
     return q, s
 
 
+def quantize_groups_int8(row, group):
+    """Group-wise symmetric int8 of one row: each block of ``group`` consecutive
+    values is quantised by quantize_row_int8 on its own; returns the row's q
+    and its list of group scales."""
+    q, s = [], []
+    for g in range(0, len(row), group):
+        qg, sg = quantize_row_int8(row[g:g + group])
+        q.extend(qg)
+        s.append(sg)
+    return q, s
+
+
 def fc2_int8_rows(u, q_w, s_w, b):
     """int8 x int8 MLP-down on nested lists: each row of u quantised by
     quantize_row_int8, then y[t][o] = s_u[t] s_w[o] sum_k q_u[t][k] q_w[o][k] + b[o]

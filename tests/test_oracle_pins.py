@@ -283,6 +283,69 @@ def test_int8_block_uses_dequantised_weights():
     assert rel_l2(got, ref) < 1e-5
 
 
+def test_quantize_groups_golden():
+    g = _golden("quantize_int8_groups.json")
+    q, s = oracle.quantize_int8_groups(np.array(g["w"], dtype=np.float32), g["group"])
+    assert q.tolist() == g["q"]
+    assert s.tolist() == g["s"]
+
+
+@pytest.mark.parametrize("group", [4, 32, 64])
+def test_quantize_groups_matches_pure_python_fp32(group):
+    rng = np.random.default_rng(43)
+    w = (rng.standard_normal((7, 128)) * 0.02).astype(np.float32)
+    w[2] = 0.0                            # a zero row: every group zero
+    w[3, :group] = 0.0                    # one zero group inside a row
+    w[4, 5] = 1.0                         # one large value: its group's scale only
+    q, s = oracle.quantize_int8_groups(w, group)
+    assert s.shape == (7, 128 // group)
+    for o in range(w.shape[0]):
+        qr, sr = bf.quantize_groups_int8(w[o].tolist(), group)
+        assert q[o].tolist() == qr
+        assert s[o].tolist() == sr
+
+
+def test_quantize_groups_whole_row_is_per_channel():
+    rng = np.random.default_rng(47)
+    w = (rng.standard_normal((9, 96)) * 0.02).astype(np.float32)
+    qg, sg = oracle.quantize_int8_groups(w, 96)
+    q, s = oracle.quantize_int8(w)
+    assert np.array_equal(qg, q)
+    assert np.array_equal(sg[:, 0], s)
+
+
+def test_quantize_groups_bounds_error_and_dequantise():
+    rng = np.random.default_rng(53)
+    w = (rng.standard_normal((32, 256)) * 0.02).astype(np.float32)
+    q, s = oracle.quantize_int8_groups(w, 64)
+    qi = q.astype(np.int32).reshape(32, 4, 64)
+    assert np.abs(qi).max() <= 127
+    assert (np.abs(qi).max(axis=2) == 127).all()        # every group reaches the full range
+    deq = oracle.dequantize_int8(q, s)                   # 2-D scales select the group rule
+    for o in range(0, 32, 7):
+        for k in range(0, 256, 13):
+            assert deq[o, k] == np.float32(np.float32(q[o, k]) * s[o, k // 64])
+    err = np.abs(w.astype(np.float64) - deq.astype(np.float64))
+    bound = np.repeat(s.astype(np.float64), 64, axis=1) * (0.5 + 127 * 2.0 ** -24)
+    assert (err <= bound).all()
+    # group scales never exceed the row scale, so the group rule is at least as fine
+    _, s_row = oracle.quantize_int8(w)
+    assert (s <= s_row[:, None]).all()
+
+
+def test_int8_group_mlp_block_uses_dequantised_weights():
+    shape, x, c, w = tiny_problem(n_tokens=5, n_heads=2, head_dim=4, mlp=16)
+    wq = dict(w)
+    deq = dict(w)
+    for name in si.MATRIX_NAMES:
+        qs = oracle.quantize_int8_groups(w[name], 4) if name in ("w_up", "w_down") else oracle.quantize_int8(w[name])
+        wq[name] = qs
+        deq[name] = oracle.dequantize_int8(*qs)
+    got = oracle.block_forward(x, c, wq, shape.n_heads)
+    ref = bf.block(x.tolist(), c.tolist(), {k: v.tolist() for k, v in deq.items()}, shape.n_heads)
+    assert rel_l2(got, ref) < 1e-5
+
+
 def test_w8a8_linear_is_the_exact_integer_sum():
     rng = np.random.default_rng(37)
     qx = rng.integers(-127, 128, size=(5, 96)).astype(np.int8)
