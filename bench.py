@@ -258,10 +258,11 @@ def _time_block(cfg, tensors, x, c, reps=5):
 
 
 def extra_blocks(b0, x, c):
-    """Two more measured units besides the step: the int8-weight block (the
-    four projection weights of block 0 quantised per output row by the
-    library's quantiser, W8A16 GEMMs) and one bf16 block at 6144 tokens,
-    D=3072 (512x512x22-frame latent).  Inputs as for the step."""
+    """More measured units besides the step: the int8-weight block (the four
+    projection weights of block 0 quantised per output row by the library's
+    quantiser, W8A16 GEMMs), the same with the row-quantised FC2 and with
+    the group-wise int8 MLP, and one bf16 block at 6144 tokens, D=3072
+    (512x512x22-frame latent).  Inputs as for the step."""
     import torch
     import seeded_inputs as si
     from video_diffusion_transformer_adaln_amd import binding as B
@@ -316,7 +317,33 @@ def extra_blocks(b0, x, c):
                             "gbs": round((N * F * 3 + N * 4) / (aq * 1e-3) / 1e9, 1)},
     }
     log(f"int8-FC2 block: {msq:.2f} ms (FC2 {fc2:.3f} ms, u quantiser {aq:.3f} ms)")
-    del t8
+    # ---- the same block with the group-wise int8 MLP (w_up, w_down in groups of 128 input channels)
+    G = 128
+    tg = dict(t8)
+    e0.record()
+    for name in ("w_up", "w_down"):
+        tg[name], tg["s_" + name[2:]] = R.quantize_int8_groups(b0[name], G)
+    e1.record()
+    torch.cuda.synchronize()
+    qg_ms = e0.elapsed_time(e1)
+    g_el = b0["w_up"].numel() + b0["w_down"].numel()
+    cfgg = B.make_config(N, D, H, d, F, C, B.H3K_BF16, B.H3K_INT8, True, int8_mlp_group=G)
+    msg, kg = _time_block(cfgg, tg, x, c)
+    kgr = {}
+    for name in ("mlp_up", "mlp_down"):
+        v = kg[name]
+        avg = v["total_ms"] / v["launches"]
+        kgr[name] = {"avg_ms": round(avg, 4), "tflops": round(fl[name] / (avg * 1e-3) / 1e12, 1)}
+    res["int8_group_block"] = {
+        "workload": f"the int8-weight block with group-wise int8 MLP weights (one scale per {G} input "
+                    "channels, dequantised to bf16 on the way to the bf16 MFMA)",
+        "ms_per_block": round(msg, 3), "tflops": round(sum(fl.values()) / (msg * 1e-3) / 1e12, 1),
+        "mlp_kernels": kgr,
+        "group_quantiser": {"ms_for_2_matrices": round(qg_ms, 3),
+                            "gbs": round((g_el * 3 + g_el // G * 4) / (qg_ms * 1e-3) / 1e9, 1)},
+    }
+    log(f"int8 group-MLP block: {msg:.2f} ms; group quantiser {qg_ms:.3f} ms")
+    del t8, tg
     # ---- 6144-token bf16 block
     sh = si.C1
     N, D, F, C, H, d = sh.n_tokens, sh.hidden, sh.mlp_hidden, sh.cond_dim, sh.n_heads, sh.head_dim

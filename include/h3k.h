@@ -86,7 +86,14 @@ typedef int32_t h3k_dtype;
  * h3k_quantize_weights_int8, and FC2 is the int8 x int8 product with int32
  * accumulation, scaled by the row and channel scales (h3k_linear_int8).
  * Needs weight_dtype INT8, act_dtype BF16 and mlp_hidden a multiple of 128;
- * 0 leaves FC2 as for the other projections. */
+ * 0 leaves FC2 as for the other projections.
+ * int8_mlp_group: 0 gives every INT8 matrix per-row scales; G in {32, 64, 128}
+ * quantises the two MLP matrices in groups of G input channels instead
+ * ([H3-review] speed/quality section: the default MLP engine is int8 with group
+ * quantisation; the page gives no group size): s_up is then [F, D/G] and
+ * s_down [D, F/G] (h3k_quantize_weights_int8_groups), the QKV and output
+ * projections keep per-row scales.  Needs weight_dtype INT8, act_dtype BF16,
+ * hidden and mlp_hidden multiples of G, and int8_fc2_rows = 0. */
 typedef struct h3k_dit_config {
   int32_t n_tokens;
   int32_t hidden;
@@ -99,12 +106,15 @@ typedef struct h3k_dit_config {
   h3k_dtype weight_dtype;
   int32_t alias_activations;
   int32_t int8_fc2_rows;
+  int32_t int8_mlp_group;
 } h3k_dit_config;
 
 /* Weights of one block; all device pointers.
  * w_ada [6D, C] and b_ada [6D] in act_dtype.  Projection matrices
  * w_qkv [3D, D], w_out [D, D], w_up [F, D], w_down [D, F] in weight_dtype;
- * with INT8 weights, s_* are the fp32 per-row scales ([rows]), otherwise NULL.
+ * with INT8 weights, s_* are the fp32 per-row scales ([rows]), otherwise NULL;
+ * with int8_mlp_group = G, s_up and s_down hold one scale per group instead
+ * ([F, D/G] and [D, F/G], row-major).
  * Biases b_qkv [3D], b_out [D], b_up [F], b_down [D] in act_dtype; any bias may be
  * NULL, meaning zero. */
 typedef struct h3k_dit_block_weights {
@@ -211,6 +221,18 @@ h3k_status h3k_dit_stack_forward(const h3k_dit_config* cfg, const h3k_dit_block_
 h3k_status h3k_quantize_weights_int8(const void* w, h3k_dtype w_dtype, int64_t rows, int64_t cols,
                                      int8_t* q, float* scales, hipStream_t stream);
 
+/* Group-wise symmetric int8 quantisation of w [rows, cols] (F32 or BF16): each
+ * row's columns are cut into blocks of `group` (32, 64 or 128; cols a multiple
+ * of it), and every block gets its own scale by the rule above:
+ *   scales[o, g] = max_{k in block g} |w[o,k]| / 127
+ *   q[o,k]       = clamp(rint(w[o,k] / scales[o, k / group]), -127, 127)
+ * A zero block gives scale 0 and q 0.  Bit-exact like h3k_quantize_weights_int8
+ * ([H3-review] speed/quality section: the group-quantised int8 MLP; the group
+ * size is the caller's choice).  q [rows, cols] int8, scales [rows, cols/group]
+ * fp32, row-major; cols <= 2^20. */
+h3k_status h3k_quantize_weights_int8_groups(const void* w, h3k_dtype w_dtype, int64_t rows, int64_t cols,
+                                            int32_t group, int8_t* q, float* scales, hipStream_t stream);
+
 /* ---- building blocks of the block forward, exposed for testing and timing --- */
 
 /* mod[rows] (fp32) = W[rows, cols] c[cols] + b[rows] (b nullable), W, b, c in dtype.
@@ -256,6 +278,21 @@ h3k_status h3k_linear_int8(int64_t m, int64_t n, int64_t k, const int8_t* xq, in
                            const int8_t* wq, int64_t ldw, const float* w_scale, const void* bias,
                            int32_t epilogue, const void* residual, int64_t ldr, const float* gate,
                            void* y, int64_t ldy, hipStream_t stream);
+
+/* Group-wise int8 weights with BF16 activations (the group-quantised int8 MLP of
+ * [H3-review]'s speed/quality section):
+ *   z[i, j] = sum_k x[i, k] * bf16(wq[j, k] * w_scale[j, k / group])
+ *   y = epilogue(z + bias) as for h3k_linear (H3K_EPI_*), row-major only.
+ * Each weight is dequantised in fp32 and rounded to bf16 once, on its way to
+ * the bf16 matrix cores; the sum is fp32.  x [m, ldx], bias [n], residual
+ * [m, ldr] and y [m, ldy] BF16; wq [n, ldw] int8 with w_scale [n, k/group] fp32
+ * (e.g. from h3k_quantize_weights_int8_groups); gate [n] fp32.  group in
+ * {32, 64, 128}; k a multiple of 64 and of group; n a multiple of 8; ldx a
+ * multiple of 8 and ldw of 16.  y must not overlap the inputs. */
+h3k_status h3k_linear_int8_groups(int64_t m, int64_t n, int64_t k, int32_t group, const void* x, int64_t ldx,
+                                  const int8_t* wq, int64_t ldw, const float* w_scale, const void* bias,
+                                  int32_t epilogue, const void* residual, int64_t ldr, const float* gate, void* y,
+                                  int64_t ldy, hipStream_t stream);
 
 /* o[n, H*d] = per head softmax(q k^T / sqrt(d)) v, non-causal, no positional
  * terms; q [n, ldq], k [n, ldk] row-major (head j = columns j*d..j*d+d-1), v given

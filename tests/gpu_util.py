@@ -40,12 +40,12 @@ def act_code(shape):
     return B.H3K_F32 if shape.dtype == "f32" else B.H3K_BF16
 
 
-def config_for(shape, alias=True, int8_fc2_rows=False):
+def config_for(shape, alias=True, int8_fc2_rows=False, int8_mlp_group=0):
     from video_diffusion_transformer_adaln_amd import binding as B
     act = act_code(shape)
     return B.make_config(shape.n_tokens, shape.hidden, shape.n_heads, shape.head_dim, shape.mlp_hidden,
                          shape.cond_dim, act, B.H3K_INT8 if shape.int8_weights else act, alias,
-                         int8_fc2_rows=int8_fc2_rows)
+                         int8_fc2_rows=int8_fc2_rows, int8_mlp_group=int8_mlp_group)
 
 
 def sample_rows(n, count=ROWS_PER_SAMPLE, seed=5):
@@ -64,12 +64,13 @@ def to_np(t):
     return t.cpu().numpy()
 
 
-def upload_block(shape, hw):
+def upload_block(shape, hw, mlp_group=0):
     """Device tensors of one block; int8 matrices are quantised on the GPU.
 
     Returns (device dict, oracle weight dict).  For int8 the oracle gets its
     own quantisation of the same fp32 matrices; tests assert bit-equality of
-    the two quantisations separately."""
+    the two quantisations separately.  mlp_group > 0 quantises w_up and
+    w_down in groups of that many input channels."""
     import oracle
     from video_diffusion_transformer_adaln_amd import runtime as R
     d = {}
@@ -77,11 +78,12 @@ def upload_block(shape, hw):
     for name, ht in hw.items():
         if shape.int8_weights and name in si.MATRIX_NAMES:
             w32 = R.upload(ht.storage, "f32")
-            q, s = R.quantize_int8(w32)
+            grouped = mlp_group > 0 and name in ("w_up", "w_down")
+            q, s = R.quantize_int8_groups(w32, mlp_group) if grouped else R.quantize_int8(w32)
             del w32
             d[name] = q
             d["s_" + name[2:]] = s
-            ow[name] = oracle.quantize_int8(ht.values)
+            ow[name] = oracle.quantize_int8_groups(ht.values, mlp_group) if grouped else oracle.quantize_int8(ht.values)
         else:
             d[name] = dev(ht)
             ow[name] = ht.values

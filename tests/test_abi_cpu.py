@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_struct_sizes_match_header_layout():
-    assert ctypes.sizeof(B.DitConfig) == 44
+    assert ctypes.sizeof(B.DitConfig) == 48
     assert ctypes.sizeof(B.DitBlockWeights) == 14 * 8
     assert ctypes.sizeof(B.DitStats) == 40
     assert ctypes.sizeof(B.DitPlanInfo) == 9 * 8 * 2 + 9 * 4 * 2 + 8 * 5 + 8
@@ -155,6 +155,12 @@ def test_reject_bad_shapes_and_dtypes():
     bad = cfg_c2(weight_dtype=B.H3K_INT8)
     bad.int8_fc2_rows = 2
     assert _block(bad) == B.H3K_ERR_SHAPE
+    # group-wise int8 MLP: G in {32, 64, 128}, int8 weights with bf16 activations, D and F multiples of G,
+    # and not together with the row-quantised FC2
+    assert _block(cfg_c2(weight_dtype=B.H3K_INT8, int8_mlp_group=16)) == B.H3K_ERR_SHAPE
+    assert _block(cfg_c2(int8_mlp_group=64)) == B.H3K_ERR_UNSUPPORTED
+    assert _block(cfg_c2(weight_dtype=B.H3K_INT8, mlp_hidden=13824 - 64, int8_mlp_group=128)) == B.H3K_ERR_SHAPE
+    assert _block(cfg_c2(weight_dtype=B.H3K_INT8, int8_mlp_group=64, int8_fc2_rows=True)) == B.H3K_ERR_UNSUPPORTED
 
 
 def test_reject_int8_without_scales():
@@ -204,6 +210,21 @@ def test_reject_bad_kernel_level_arguments():
     assert lib.h3k_linear_int8(10, 64, 1 << 18, X, 1 << 18, XS, W, 1 << 18, WS, None, 0, None, 0, None, Y, 64,
                                None) == B.H3K_ERR_SHAPE
     assert lib.h3k_adaln_modulation(1, 10, 12, FAKE, None, FAKE, FAKE + (1 << 32), None) == B.H3K_ERR_SHAPE
+    # group quantiser: group 16, cols not a multiple of the group, scales overlapping q
+    Q, S = FAKE + (1 << 32), FAKE + (2 << 32)
+    assert lib.h3k_quantize_weights_int8_groups(FAKE, 1, 4, 128, 16, Q, S, None) == B.H3K_ERR_SHAPE
+    assert lib.h3k_quantize_weights_int8_groups(FAKE, 1, 4, 96, 64, Q, S, None) == B.H3K_ERR_SHAPE
+    assert lib.h3k_quantize_weights_int8_groups(FAKE, 1, 4, 128, 64, Q, Q + 256, None) == B.H3K_ERR_OVERLAP
+    assert lib.h3k_quantize_weights_int8_groups(FAKE, 2, 4, 128, 64, Q, S, None) == B.H3K_ERR_UNSUPPORTED
+    # group-wise int8 linear: k not a multiple of the group, no scales, y overlapping the scales, bad group
+    assert lib.h3k_linear_int8_groups(10, 64, 192, 128, X, 192, W, 192, WS, None, 0, None, 0, None, Y, 64,
+                                      None) == B.H3K_ERR_SHAPE
+    assert lib.h3k_linear_int8_groups(10, 64, 256, 64, X, 256, W, 256, None, None, 0, None, 0, None, Y, 64,
+                                      None) == B.H3K_ERR_NULL
+    assert lib.h3k_linear_int8_groups(10, 64, 256, 64, X, 256, W, 256, WS, None, 0, None, 0, None, WS + 64, 64,
+                                      None) == B.H3K_ERR_OVERLAP
+    assert lib.h3k_linear_int8_groups(10, 64, 256, 48, X, 256, W, 256, WS, None, 0, None, 0, None, Y, 64,
+                                      None) == B.H3K_ERR_SHAPE
 
 
 def _no_gpu():
@@ -215,3 +236,9 @@ def _no_gpu():
 def test_valid_arguments_without_device_report_hip_error():
     assert _block(cfg_c2()) == B.H3K_ERR_HIP
     assert "device" in h3k.last_error()
+    # group-wise int8 MLP: scales are [F, D/G] and [D, F/G]; everything valid, so only the device is missing
+    scales = {f: FAKE + (60 + i) * (1 << 32) for i, f in enumerate(("s_qkv", "s_out", "s_up", "s_down"))}
+    assert _block(cfg_c2(weight_dtype=B.H3K_INT8, int8_mlp_group=128), weights=_weights(**scales)) == B.H3K_ERR_HIP
+    lib = h3k.lib()
+    assert lib.h3k_quantize_weights_int8_groups(FAKE, 1, 4, 128, 64, FAKE + (1 << 32), FAKE + (2 << 32),
+                                                None) == B.H3K_ERR_HIP

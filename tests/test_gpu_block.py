@@ -33,10 +33,10 @@ def R():
     return runtime
 
 
-def _run_block(R, shape, dw, xd, cd, alias=True, poison=True, stats=None, int8_fc2_rows=False):
+def _run_block(R, shape, dw, xd, cd, alias=True, poison=True, stats=None, int8_fc2_rows=False, int8_mlp_group=0):
     import torch
     from video_diffusion_transformer_adaln_amd import binding as B
-    cfg = config_for(shape, alias, int8_fc2_rows)
+    cfg = config_for(shape, alias, int8_fc2_rows, int8_mlp_group)
     ws = R.alloc_workspace(cfg)
     if poison:
         ws.fill_(0xFF)
@@ -165,6 +165,34 @@ def test_block_int8_fc2_rows(R, case):
     assert err < TOL
     if case == "small":
         off = _run_block(R, shape, dw, xd, cd, alias=False, int8_fc2_rows=True)
+        assert torch.equal(off.view(torch.int16), got_t.view(torch.int16))
+
+
+@pytest.mark.parametrize("case,group", [("c4", 128), ("small", 32), ("small", 64)])
+def test_block_int8_mlp_groups(R, case, group):
+    """The group-wise int8 MLP (w_up and w_down with one scale per group of
+    input channels, dequantised to bf16 on the way to the matrix cores):
+    against the oracle's block with the same grouped weights, and
+    byte-identical with aliasing on and off."""
+    import torch
+    from video_diffusion_transformer_adaln_amd import binding as B
+    shape = si.C4 if case == "c4" else si.custom_shape("int8grp", 973, 333, 2, 128, 640, "bf16", int8_weights=True)
+    flush(f"block {shape.name} int8_mlp_group={group}")
+    hx, hc, hw = _block_case(shape, bias_std=0.05)
+    dw, ow = upload_block(shape, hw, mlp_group=group)
+    assert tuple(dw["s_up"].shape) == (shape.mlp_hidden, shape.hidden // group)
+    xd, cd = dev(hx), dev(hc)
+    st = B.DitStats()
+    got_t = _run_block(R, shape, dw, xd, cd, stats=st, int8_mlp_group=group)
+    assert st.dispatches == 8
+    got = to_np(got_t)
+    rows = sample_rows(shape.n_tokens) if case == "c4" else np.arange(shape.n_tokens)
+    ref = oracle.block_forward(hx.values, hc.values, ow, shape.n_heads, rows=rows)
+    err = rel_l2(got[rows], ref)
+    flush(f"  rel_l2 = {err:.3e}")
+    assert err < TOL
+    if case == "small":
+        off = _run_block(R, shape, dw, xd, cd, alias=False, int8_mlp_group=group)
         assert torch.equal(off.view(torch.int16), got_t.view(torch.int16))
 
 

@@ -225,6 +225,56 @@ def test_linear_int8(B, m, n, k, epi, full):
     assert rel_l2(got, ref) < BF16_TOL / 2
 
 
+LINEAR_GROUP_CASES = [
+    # m, n, k, group, epilogue, full
+    (300, 320, 256, 64, 0, True),
+    (300, 320, 256, 32, 1, True),
+    (257, 328, 384, 128, 2, True),     # 6 k-tiles, ragged m and n
+    (1, 64, 128, 128, 0, True),
+    (129, 264, 640, 64, 1, True),
+    (22680, 13824, 5120, 128, 1, False),   # the MLP-up projection of the 864x480x56-frame block
+    (22680, 5120, 13824, 128, 2, False),   # and its MLP-down
+]
+
+
+@pytest.mark.parametrize("m,n,k,group,epi,full", LINEAR_GROUP_CASES)
+def test_linear_int8_groups(B, m, n, k, group, epi, full):
+    """Weights quantised on the GPU in groups (checked bit for bit against the
+    oracle's group quantiser), bf16 activations, against the oracle's product
+    with the dequantised weights and the same epilogue."""
+    import torch
+    from video_diffusion_transformer_adaln_amd import runtime as R
+    flush(f"linear int8 groups m={m} n={n} k={k} group={group} epi={epi}")
+    cid = 850 + epi
+    x = _ht(_f32((m, k), 1.0, cid), "bf16")
+    w32 = _f32((n, k), 0.02, cid, "w_up")
+    w32[3, :group] = 0.0                               # a zero group
+    bias = _ht(_f32((n,), 0.05, cid, "b_up"), "bf16")
+    wq, ws = R.quantize_int8_groups(torch.from_numpy(w32).cuda(), group)
+    torch.cuda.synchronize()
+    qw_ref, sw_ref = oracle.quantize_int8_groups(w32, group)
+    assert np.array_equal(wq.cpu().numpy(), qw_ref) and np.array_equal(ws.cpu().numpy(), sw_ref)
+    res = gate = resd = gated = None
+    if epi == 2:
+        res = _ht(_f32((m, n), 1.0, cid, "x", 1), "bf16")
+        gate = _f32((n,), 0.5, cid, "b_down")
+        resd, gated = dev(res), torch.from_numpy(gate).cuda()
+    y = torch.full((m, n), float("nan"), dtype=torch.bfloat16, device="cuda")
+    B.h3k_linear_int8_groups(m, n, k, group, dev(x), k, wq, k, ws, dev(bias), epi, resd, n, gated, y, n)
+    torch.cuda.synchronize()
+    rows = np.arange(m) if full else sample_rows(m)
+    z = oracle.linear(x.values[rows], oracle.dequantize_int8(qw_ref, sw_ref), bias.values)
+    if epi == 1:
+        ref = oracle.gelu_tanh(z)
+    elif epi == 2:
+        ref = res.values[rows] + gate * z
+    else:
+        ref = z
+    got = to_np(y)[rows]
+    assert np.isfinite(got).all()
+    assert rel_l2(got, ref) < BF16_TOL / 2
+
+
 # ------------------------------------------------------------------ attention
 
 ATTN_CASES = [
@@ -303,6 +353,25 @@ def test_attention_moving_reference(B, n, hd, kind):
 
 
 # ------------------------------------------------------------------ int8 quantiser
+
+@pytest.mark.parametrize("rows,cols,group,dtype", [(13824, 5120, 128, "f32"), (5120, 13824, 128, "bf16"),
+                                                   (300, 256, 32, "f32"), (257, 1024, 64, "bf16"),
+                                                   (7, 64, 64, "bf16"), (3, 96, 32, "f32"), (64, 640, 128, "f32")])
+def test_quantize_int8_groups_bit_exact(B, rows, cols, group, dtype):
+    import torch
+    flush(f"quantize groups rows={rows} cols={cols} group={group} {dtype}")
+    w = _f32((rows, cols), 0.02, 831, "w_up")
+    w[min(1, rows - 1)] = 0.0                      # a zero row
+    w[rows - 1, group:2 * group] = 0.0             # a zero group inside a row
+    w[0, 3] = 0.5                                  # one large value: only its group's scale moves
+    ht = _ht(w, dtype)
+    from video_diffusion_transformer_adaln_amd import runtime as R
+    q, s = R.quantize_int8_groups(dev(ht), group)
+    torch.cuda.synchronize()
+    q_ref, s_ref = oracle.quantize_int8_groups(ht.values, group)
+    assert np.array_equal(s.cpu().numpy(), s_ref)
+    assert np.array_equal(q.cpu().numpy(), q_ref)
+
 
 @pytest.mark.parametrize("rows,cols,dtype", [(15360, 5120, "f32"), (5120, 13824, "f32"), (300, 77, "f32"),
                                              (257, 1000, "bf16"), (3, 1, "f32"), (5120, 13824, "bf16"),

@@ -31,7 +31,8 @@ c_int32, c_int64, c_uint64, c_float, c_void_p = (ctypes.c_int32, ctypes.c_int64,
 class DitConfig(ctypes.Structure):
     _fields_ = [("n_tokens", c_int32), ("hidden", c_int32), ("n_heads", c_int32), ("head_dim", c_int32),
                 ("mlp_hidden", c_int32), ("cond_dim", c_int32), ("ln_eps", c_float), ("act_dtype", c_int32),
-                ("weight_dtype", c_int32), ("alias_activations", c_int32), ("int8_fc2_rows", c_int32)]
+                ("weight_dtype", c_int32), ("alias_activations", c_int32), ("int8_fc2_rows", c_int32),
+                ("int8_mlp_group", c_int32)]
 
 
 class DitBlockWeights(ctypes.Structure):
@@ -75,6 +76,8 @@ _SIGNATURES = [
                                         c_void_p, c_void_p, c_void_p, c_void_p, c_uint64, c_void_p,
                                         ctypes.POINTER(DitStats)]),
     ("h3k_quantize_weights_int8", c_int32, [c_void_p, c_int32, c_int64, c_int64, c_void_p, c_void_p, c_void_p]),
+    ("h3k_quantize_weights_int8_groups", c_int32, [c_void_p, c_int32, c_int64, c_int64, c_int32, c_void_p, c_void_p,
+                                                   c_void_p]),
     ("h3k_adaln_modulation", c_int32, [c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
                                        c_void_p]),
     ("h3k_ln_modulate", c_int32, [c_int32, c_int32, c_int32, c_float, c_void_p, c_int64, c_void_p, c_void_p,
@@ -85,6 +88,9 @@ _SIGNATURES = [
     ("h3k_linear_int8", c_int32, [c_int64, c_int64, c_int64, c_void_p, c_int64, c_void_p, c_void_p, c_int64,
                                   c_void_p, c_void_p, c_int32, c_void_p, c_int64, c_void_p, c_void_p, c_int64,
                                   c_void_p]),
+    ("h3k_linear_int8_groups", c_int32, [c_int64, c_int64, c_int64, c_int32, c_void_p, c_int64, c_void_p, c_int64,
+                                         c_void_p, c_void_p, c_int32, c_void_p, c_int64, c_void_p, c_void_p, c_int64,
+                                         c_void_p]),
     ("h3k_attention", c_int32, [c_int32, c_int32, c_int32, c_int32, c_void_p, c_int64, c_void_p, c_int64,
                                 c_void_p, c_int64, c_void_p, c_int64, c_void_p]),
     ("h3k_profiler_create", c_int32, [c_int32, ctypes.POINTER(c_void_p)]),
@@ -141,10 +147,10 @@ def _stream(stream) -> Optional[int]:
 
 def make_config(n_tokens: int, hidden: int, n_heads: int, head_dim: int, mlp_hidden: int, cond_dim: int,
                 act_dtype: int, weight_dtype: Optional[int] = None, alias: bool = True,
-                ln_eps: float = 1e-6, int8_fc2_rows: bool = False) -> DitConfig:
+                ln_eps: float = 1e-6, int8_fc2_rows: bool = False, int8_mlp_group: int = 0) -> DitConfig:
     return DitConfig(n_tokens, hidden, n_heads, head_dim, mlp_hidden, cond_dim, ln_eps, act_dtype,
                      act_dtype if weight_dtype is None else weight_dtype, 1 if alias else 0,
-                     1 if int8_fc2_rows else 0)
+                     1 if int8_fc2_rows else 0, int8_mlp_group)
 
 
 WEIGHT_FIELDS = ("w_ada", "b_ada", "w_qkv", "b_qkv", "s_qkv", "w_out", "b_out", "s_out",
@@ -192,6 +198,12 @@ def h3k_quantize_weights_int8(w, w_dtype: int, rows: int, cols: int, q, scales, 
     check(lib().h3k_quantize_weights_int8(_ptr(w), w_dtype, rows, cols, _ptr(q), _ptr(scales), _stream(stream)))
 
 
+def h3k_quantize_weights_int8_groups(w, w_dtype: int, rows: int, cols: int, group: int, q, scales,
+                                     stream=None) -> None:
+    check(lib().h3k_quantize_weights_int8_groups(_ptr(w), w_dtype, rows, cols, group, _ptr(q), _ptr(scales),
+                                                 _stream(stream)))
+
+
 def h3k_adaln_modulation(dtype: int, rows: int, cols: int, w, b, c, mod, stream=None) -> None:
     check(lib().h3k_adaln_modulation(dtype, rows, cols, _ptr(w), _ptr(b), _ptr(c), _ptr(mod), _stream(stream)))
 
@@ -214,6 +226,12 @@ def h3k_linear_int8(m: int, n: int, k: int, xq, ldx: int, x_scale, wq, ldw: int,
                     residual, ldr: int, gate, y, ldy: int, stream=None) -> None:
     check(lib().h3k_linear_int8(m, n, k, _ptr(xq), ldx, _ptr(x_scale), _ptr(wq), ldw, _ptr(w_scale), _ptr(bias),
                                 epilogue, _ptr(residual), ldr, _ptr(gate), _ptr(y), ldy, _stream(stream)))
+
+
+def h3k_linear_int8_groups(m: int, n: int, k: int, group: int, x, ldx: int, wq, ldw: int, w_scale, bias,
+                           epilogue: int, residual, ldr: int, gate, y, ldy: int, stream=None) -> None:
+    check(lib().h3k_linear_int8_groups(m, n, k, group, _ptr(x), ldx, _ptr(wq), ldw, _ptr(w_scale), _ptr(bias),
+                                       epilogue, _ptr(residual), ldr, _ptr(gate), _ptr(y), ldy, _stream(stream)))
 
 
 def h3k_attention(dtype: int, n: int, n_heads: int, head_dim: int, q, ldq: int, k, ldk: int, vt, ldvt: int, o,

@@ -232,6 +232,64 @@ __global__ __launch_bounds__(256) void quantize_int8_kernel(const T* __restrict_
   }
 }
 
+// Group-wise variant: every block of G consecutive weights of a row (G in
+// {32, 64, 128}, cols a multiple of G) gets its own scale, s = max|w| / 127
+// over the block, and q = clamp(rint(w / s)) as above.  One wave per row;
+// lane l holds the 8 consecutive values of chunk (it*64 + l), so a group is
+// G/8 adjacent lanes and its maximum is a butterfly over those lanes.  The
+// values stay in registers: one pass over the row.
+template <typename T, int G>
+__global__ __launch_bounds__(256) void quantize_int8_groups_kernel(const T* __restrict__ w, int64_t rows,
+                                                                   int64_t cols, int8_t* __restrict__ q,
+                                                                   float* __restrict__ scales) {
+  constexpr int LG = G / 8;                    // lanes per group
+  const int lane = threadIdx.x % kWave;
+  const int64_t row = (int64_t)blockIdx.x * (256 / kWave) + threadIdx.x / kWave;
+  if (row >= rows) return;
+  const T* wr = w + row * cols;
+  int8_t* qr = q + row * cols;
+  float* sr = scales + row * (cols / G);
+  const int64_t chunks = cols / 8;             // a multiple of LG
+  for (int64_t c0 = 0; c0 < chunks; c0 += kWave) {
+    const int64_t c = c0 + lane;
+    if (c >= chunks) break;                    // whole groups drop out together
+    float v[8];
+    Vec8<T>::load(wr + c * 8, v);
+    float mx = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) mx = fmaxf(mx, fabsf(v[i]));
+#pragma unroll
+    for (int off = LG / 2; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, kWave));
+    const float sc = mx / 127.0f;
+    if (lane % LG == 0) sr[c / LG] = sc;
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t b = (uint32_t)(quant1(v[i], sc) & 0xff);
+      if (i < 4) lo |= b << (8 * i);
+      else hi |= b << (8 * (i - 4));
+    }
+    *reinterpret_cast<u32x2*>(qr + c * 8) = u32x2{lo, hi};
+  }
+}
+
+template <typename T>
+static void launch_groups(const T* w, int64_t rows, int64_t cols, int group, int8_t* q, float* scales,
+                          hipStream_t stream) {
+  const dim3 grid((unsigned)((rows + 3) / 4));
+  if (group == 32) quantize_int8_groups_kernel<T, 32><<<grid, dim3(256), 0, stream>>>(w, rows, cols, q, scales);
+  else if (group == 64) quantize_int8_groups_kernel<T, 64><<<grid, dim3(256), 0, stream>>>(w, rows, cols, q, scales);
+  else quantize_int8_groups_kernel<T, 128><<<grid, dim3(256), 0, stream>>>(w, rows, cols, q, scales);
+}
+
+hipError_t launch_quantize_int8_groups(DType dt, const void* w, int64_t rows, int64_t cols, int group, int8_t* q,
+                                       float* scales, hipStream_t stream) {
+  if (rows == 0) return hipSuccess;
+  if (dt == kBF16) launch_groups((const bf16*)w, rows, cols, group, q, scales, stream);
+  else launch_groups((const float*)w, rows, cols, group, q, scales, stream);
+  return hipGetLastError();
+}
+
 hipError_t launch_quantize_int8(DType dt, const void* w, int64_t rows, int64_t cols, int8_t* q, float* scales,
                                 hipStream_t stream) {
   if (rows == 0) return hipSuccess;

@@ -35,7 +35,8 @@ struct GemmParams {
   const void* x; int64_t ldx;
   const float* x_scale;   // int8 activations: per-row scales
   const void* w; int64_t ldw;
-  const float* w_scale;
+  const float* w_scale;   // int8 weights: [n] per channel, or [n, k / group] per group
+  int group_shift;        // log2 of the group size (group-wise int8 weights)
   const bf16* bias;
   const bf16* residual; int64_t ldr;
   const float* gate;
@@ -66,6 +67,21 @@ __device__ __forceinline__ void i8x16_to_bf16(const u32x4& src, u32x4& lo, u32x4
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       dst[e] = static_cast<bf16>(static_cast<float>((u >> (8 * e)) & 0xffu) - 128.0f);
+  }
+}
+// The same with a group scale: bf16(q * s), the product rounded once to fp32
+// (q has 8 significant bits, so q * s is exact unless s is subnormal) and
+// then to bf16.
+__device__ __forceinline__ void i8x16_to_bf16_scaled(const u32x4& src, float sc, u32x4& lo, u32x4& hi) {
+  bf16* l = reinterpret_cast<bf16*>(&lo);
+  bf16* h = reinterpret_cast<bf16*>(&hi);
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const uint32_t u = src[d] ^ 0x80808080u;
+    bf16* dst = d < 2 ? l + 4 * d : h + 4 * (d - 2);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      dst[e] = static_cast<bf16>((static_cast<float>((u >> (8 * e)) & 0xffu) - 128.0f) * sc);
   }
 }
 
@@ -171,8 +187,10 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, const f32x16 (&a
 }
 
 // Register-staged kernel; launched for int8 weights (the widening happens
-// between the global load and the LDS store).
-template <int EPI, bool W8>
+// between the global load and the LDS store).  GRP: group-wise scales, applied
+// while widening (each 16-weight chunk lies in one group), so the epilogue
+// takes no channel scale.
+template <int EPI, bool W8, bool GRP = false>
 __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmParams p) {
   __shared__ __attribute__((aligned(16))) char lds[4 * kTileBytes];   // X0 W0 X1 W1
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -209,6 +227,13 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmParams p) {
                              : (uint32_t)((feat0 + wave * 8 + ld_rsub) * (uint32_t)p.ldw * 2u + (ld_ks * 16 + ld_h * 8) * 2);
   const uint32_t w_step = W8 ? 128u * (uint32_t)p.ldw : 64u * (uint32_t)p.ldw * 2u;
 
+  // group scales: lane's weight row i of the tile and its 16-weight chunk's group
+  float rs[WL];
+  const int n_groups = GRP ? (p.k >> p.group_shift) : 0;
+  const __amdgpu_buffer_rsrc_t rss = make_rsrc(p.w_scale, GRP ? (uint32_t)((uint64_t)p.n * n_groups * 4) : 0u);
+  const uint32_t s_off0 = GRP ? (uint32_t)(feat0 + wave * 16 + (lane & 15)) * (uint32_t)n_groups * 4u : 0u;
+  const uint32_t s_step = GRP ? 128u * (uint32_t)n_groups * 4u : 0u;
+
   auto gload = [&](int kt) {
     const uint32_t kx = (uint32_t)kt * BK * 2u;
 #pragma unroll
@@ -216,6 +241,12 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmParams p) {
     const uint32_t kw = (uint32_t)kt * BK * (W8 ? 1u : 2u);
 #pragma unroll
     for (int i = 0; i < WL; ++i) rw[i] = buf_load16(rsw, w_off0 + i * w_step + kw);
+    if constexpr (GRP) {
+      const uint32_t g4 = (uint32_t)((kt * BK + ld_ks * 16) >> p.group_shift) * 4u;
+#pragma unroll
+      for (int i = 0; i < WL; ++i)
+        rs[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rss, s_off0 + i * s_step + g4, 0, 0));
+    }
   };
 
   auto lstore = [&](char* sx, char* sw) {
@@ -229,7 +260,8 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmParams p) {
       for (int i = 0; i < WL; ++i) {
         const int r = i * 128 + wave * 16 + (lane & 15);
         u32x4 lo, hi;
-        i8x16_to_bf16(rw[i], lo, hi);
+        if constexpr (GRP) i8x16_to_bf16_scaled(rw[i], rs[i], lo, hi);
+        else i8x16_to_bf16(rw[i], lo, hi);
         *reinterpret_cast<u32x4*>(sw + plane_off(ld_ks, r, 0)) = lo;
         *reinterpret_cast<u32x4*>(sw + plane_off(ld_ks, r, 1)) = hi;
       }
@@ -298,7 +330,7 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmParams p) {
     if (kt + 1 < KT) load_frags(nxt, 0, f0a, f0b);
   }
 
-  store_tile<EPI, W8>(p, acc, a_row0, b_row0, tok0, feat0, trans, lane);
+  store_tile<EPI, W8 && !GRP>(p, acc, a_row0, b_row0, tok0, feat0, trans, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -546,10 +578,15 @@ static void launch_bf16(const LinearArgs& a, hipStream_t stream) {
   p.m = (int)a.m; p.n = (int)a.n; p.k = (int)a.k;
   p.tiles_m = (p.m + BM - 1) / BM;
   p.tiles_n = (p.n + BN - 1) / BN;
+  p.group_shift = a.group > 0 ? __builtin_ctz((unsigned)a.group) : 0;
   if (a.act == kINT8)
     gemm_ring_kernel<EPI, true><<<dim3(p.tiles_m * p.tiles_n), dim3(512), 0, stream>>>(p);
-  else if constexpr (W8)
-    gemm_bf16_kernel<EPI, W8><<<dim3(p.tiles_m * p.tiles_n), dim3(512), 0, stream>>>(p);
+  else if constexpr (W8) {
+    if (a.group > 0)
+      gemm_bf16_kernel<EPI, true, true><<<dim3(p.tiles_m * p.tiles_n), dim3(512), 0, stream>>>(p);
+    else
+      gemm_bf16_kernel<EPI, true><<<dim3(p.tiles_m * p.tiles_n), dim3(512), 0, stream>>>(p);
+  }
   else
     gemm_ring_kernel<EPI, false><<<dim3(p.tiles_m * p.tiles_n), dim3(512), 0, stream>>>(p);
 }

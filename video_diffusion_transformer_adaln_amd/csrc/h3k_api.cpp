@@ -105,6 +105,14 @@ h3k_status validate_config(const h3k_dit_config* c) {
   if (c->int8_fc2_rows &&
       (c->weight_dtype != H3K_INT8 || c->act_dtype != H3K_BF16 || c->mlp_hidden % 128 != 0))
     return fail(H3K_ERR_UNSUPPORTED, "int8_fc2_rows needs INT8 weights, BF16 activations and mlp_hidden a multiple of 128");
+  const int g = c->int8_mlp_group;
+  if (g != 0 && g != 32 && g != 64 && g != 128) return fail(H3K_ERR_SHAPE, "int8_mlp_group must be 0, 32, 64 or 128");
+  if (g && (c->weight_dtype != H3K_INT8 || c->act_dtype != H3K_BF16))
+    return fail(H3K_ERR_UNSUPPORTED, "int8_mlp_group needs INT8 weights and BF16 activations");
+  if (g && (c->hidden % g || c->mlp_hidden % g))
+    return fail(H3K_ERR_SHAPE, "hidden and mlp_hidden must be multiples of int8_mlp_group %d", g);
+  if (g && c->int8_fc2_rows)
+    return fail(H3K_ERR_UNSUPPORTED, "int8_mlp_group and int8_fc2_rows cannot be combined (FC2 needs channel scales)");
   const int64_t eb = esize(c->act_dtype);
   const int64_t rows = (int64_t)c->n_tokens + 256;
   const int64_t widest = std::max<int64_t>(2 * (int64_t)c->hidden, c->mlp_hidden);
@@ -259,10 +267,11 @@ void weight_ranges(const h3k_dit_config* c, const h3k_dit_block_weights* w, std:
   out.push_back(rng(w->s_out, D * 4, "s_out"));
   out.push_back(rng(w->w_up, F * D * ew, "w_up"));
   out.push_back(rng(w->b_up, F * ea, "b_up"));
-  out.push_back(rng(w->s_up, F * 4, "s_up"));
+  const int64_t g = c->int8_mlp_group;
+  out.push_back(rng(w->s_up, F * (g ? D / g : 1) * 4, "s_up"));
   out.push_back(rng(w->w_down, D * F * ew, "w_down"));
   out.push_back(rng(w->b_down, D * ea, "b_down"));
-  out.push_back(rng(w->s_down, D * 4, "s_down"));
+  out.push_back(rng(w->s_down, D * (g ? F / g : 1) * 4, "s_down"));
 }
 
 h3k_status validate_forward(const h3k_dit_config* c, const h3k_dit_block_weights* blocks, int32_t n_blocks,
@@ -351,6 +360,7 @@ h3k_status run_block(const h3k_dit_config* c, const h3k_dit_plan_info* P, const 
   L.act = act; L.weight = wt;
   L.m = N; L.n = F; L.k = D;
   L.x = h2; L.ldx = D; L.w = w->w_up; L.ldw = D; L.w_scale = w->s_up; L.bias = w->b_up;
+  L.group = c->int8_mlp_group;
   L.epi = kEpiGelu; L.y = u; L.ldy = F; L.split_col = F;
   H3K_TRY(launched(launch_linear(L, s), "MLP up"));
   rec.done(H3K_K_UP);
@@ -359,6 +369,7 @@ h3k_status run_block(const h3k_dit_config* c, const h3k_dit_plan_info* P, const 
   L.act = act; L.weight = wt;
   L.m = N; L.n = D; L.k = F;
   L.x = u; L.ldx = F; L.w = w->w_down; L.ldw = F; L.w_scale = w->s_down; L.bias = w->b_down;
+  L.group = c->int8_mlp_group;
   if (c->int8_fc2_rows) {
     int8_t* uq = reinterpret_cast<int8_t*>(ws + P->offset[H3K_T_UQ]);
     float* us = reinterpret_cast<float*>(ws + P->offset[H3K_T_US]);
@@ -444,6 +455,27 @@ h3k_status h3k_quantize_weights_int8(const void* w, h3k_dtype w_dtype, int64_t r
   if (rows == 0) return H3K_OK;
   H3K_TRY(check_device());
   return launched(launch_quantize_int8((DType)w_dtype, w, rows, cols, q, scales, stream), "int8 quantiser");
+}
+
+h3k_status h3k_quantize_weights_int8_groups(const void* w, h3k_dtype w_dtype, int64_t rows, int64_t cols,
+                                            int32_t group, int8_t* q, float* scales, hipStream_t stream) {
+  if (w_dtype != H3K_F32 && w_dtype != H3K_BF16)
+    return fail(w_dtype == H3K_INT8 ? H3K_ERR_UNSUPPORTED : H3K_ERR_DTYPE, "w_dtype must be F32 or BF16");
+  if (group != 32 && group != 64 && group != 128) return fail(H3K_ERR_SHAPE, "group must be 32, 64 or 128 (got %d)", group);
+  if (rows < 0 || cols < group || cols % group || rows > 0x7fffffff || cols > (1 << 20))
+    return fail(H3K_ERR_SHAPE, "rows %lld / cols %lld out of range (cols a multiple of the group)", (long long)rows,
+                (long long)cols);
+  if (!w || !q || !scales) return fail(H3K_ERR_NULL, "w, q and scales must be non-NULL");
+  if (!aligned(w, 16) || !aligned(q, 16) || !aligned(scales, 16))
+    return fail(H3K_ERR_ALIGN, "w, q and scales must be 16-byte aligned");
+  const Range rw = rng(w, rows * cols * esize(w_dtype), "w"), rq = rng(q, rows * cols, "q"),
+              rs = rng(scales, rows * (cols / group) * 4, "scales");
+  if (overlaps(rq, rw) || overlaps(rs, rw) || overlaps(rq, rs))
+    return fail(H3K_ERR_OVERLAP, "q, scales and w must not overlap");
+  if (rows == 0) return H3K_OK;
+  H3K_TRY(check_device());
+  return launched(launch_quantize_int8_groups((DType)w_dtype, w, rows, cols, group, q, scales, stream),
+                  "int8 group quantiser");
 }
 
 h3k_status h3k_adaln_modulation(h3k_dtype dtype, int32_t rows, int32_t cols, const void* w, const void* b,
@@ -569,6 +601,40 @@ h3k_status h3k_linear_int8(int64_t m, int64_t n, int64_t k, const int8_t* xq, in
   L.epi = (Epilogue)epilogue; L.residual = residual; L.ldr = ldr; L.gate = gate;
   L.y = y; L.ldy = ldy; L.split_col = n;
   return launched(launch_linear(L, stream), "int8 linear");
+}
+
+h3k_status h3k_linear_int8_groups(int64_t m, int64_t n, int64_t k, int32_t group, const void* x, int64_t ldx,
+                                  const int8_t* wq, int64_t ldw, const float* w_scale, const void* bias,
+                                  int32_t epilogue, const void* residual, int64_t ldr, const float* gate, void* y,
+                                  int64_t ldy, hipStream_t stream) {
+  if (epilogue < H3K_EPI_BIAS || epilogue > H3K_EPI_GATED_RESIDUAL) return fail(H3K_ERR_SHAPE, "bad epilogue %d", epilogue);
+  if (group != 32 && group != 64 && group != 128) return fail(H3K_ERR_SHAPE, "group must be 32, 64 or 128 (got %d)", group);
+  if (m < 0 || n < 8 || n % 8 || k < 64 || k % 64 || k % group)
+    return fail(H3K_ERR_SHAPE, "need m >= 0, n a multiple of 8, k a multiple of 64 and of the group (m=%lld n=%lld k=%lld)",
+                (long long)m, (long long)n, (long long)k);
+  if (ldx < k || ldw < k || ldx % 8 || ldw % 16 || ldy < n || ldy % 8) return fail(H3K_ERR_SHAPE, "bad row pitches");
+  if (!x || !wq || !w_scale || !y) return fail(H3K_ERR_NULL, "x, wq, w_scale and y must be non-NULL");
+  if (epilogue == H3K_EPI_GATED_RESIDUAL && (!residual || !gate || ldr < n || ldr % 8))
+    return fail(H3K_ERR_NULL, "gated residual needs residual (ldr >= n, multiple of 8) and gate");
+  const void* al[] = {x, wq, bias, residual, y, w_scale, gate};
+  for (const void* p : al)
+    if (p && !aligned(p, 16)) return fail(H3K_ERR_ALIGN, "pointers must be 16-byte aligned");
+  if ((m + 256) * ldx * 2 > kMaxOffset || (n + 256) * ldw > kMaxOffset || (n + 256) * (k / group) * 4 > kMaxOffset)
+    return fail(H3K_ERR_UNSUPPORTED, "operand exceeds 2 GiB (32-bit offsets)");
+  const Range rx = rng(x, span(m, k, ldx, 2), "x"), rw = rng(wq, span(n, k, ldw, 1), "wq");
+  const Range rs = rng(w_scale, n * (k / group) * 4, "w_scale"), ry = rng(y, span(m, n, ldy, 2), "y");
+  if (overlaps(ry, rx) || overlaps(ry, rw) || overlaps(ry, rs)) return fail(H3K_ERR_OVERLAP, "y overlaps an input");
+  if (residual && residual != y && overlaps(ry, rng(residual, span(m, n, ldr, 2), "residual")))
+    return fail(H3K_ERR_OVERLAP, "y partially overlaps residual");
+  if (m == 0) return H3K_OK;
+  H3K_TRY(check_device());
+  LinearArgs L{};
+  L.act = kBF16; L.weight = kINT8; L.group = group;
+  L.m = m; L.n = n; L.k = k;
+  L.x = x; L.ldx = ldx; L.w = wq; L.ldw = ldw; L.w_scale = w_scale; L.bias = bias;
+  L.epi = (Epilogue)epilogue; L.residual = residual; L.ldr = ldr; L.gate = gate;
+  L.y = y; L.ldy = ldy; L.split_col = n;
+  return launched(launch_linear(L, stream), "int8 group linear");
 }
 
 h3k_status h3k_attention(h3k_dtype dtype, int32_t n, int32_t n_heads, int32_t head_dim, const void* q, int64_t ldq,

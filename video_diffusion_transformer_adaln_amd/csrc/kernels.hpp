@@ -33,6 +33,7 @@ struct LinearArgs {
   void* yt; int64_t ldyt;
   int64_t split_col;
   const float* x_scale;   // per-row activation scales (act = kINT8 only)
+  int group;              // int8 weights: 0 = w_scale per row [n]; else w_scale [n, k / group]
 };
 hipError_t launch_linear(const LinearArgs& a, hipStream_t stream);
 
@@ -48,5 +49,8 @@ hipError_t launch_attention(const AttentionArgs& a, hipStream_t stream);
 
 hipError_t launch_quantize_int8(DType dt, const void* w, int64_t rows, int64_t cols, int8_t* q,
                                 float* scales, hipStream_t stream);
+// group in {32, 64, 128}, cols a multiple of it; scales [rows, cols / group]
+hipError_t launch_quantize_int8_groups(DType dt, const void* w, int64_t rows, int64_t cols, int group, int8_t* q,
+                                       float* scales, hipStream_t stream);
 
 }  // namespace h3k

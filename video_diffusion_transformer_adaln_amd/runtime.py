@@ -52,6 +52,17 @@ def quantize_int8(w, stream=None):
     return q, s
 
 
+def quantize_int8_groups(w, group: int, stream=None):
+    """Group-wise symmetric int8 (blocks of `group` columns) of a 2-D fp32/bf16 device tensor."""
+    import torch
+    rows, cols = w.shape
+    q = torch.empty((rows, cols), dtype=torch.int8, device=w.device)
+    s = torch.empty((rows, cols // group), dtype=torch.float32, device=w.device)
+    code = B.H3K_F32 if w.dtype == torch.float32 else B.H3K_BF16
+    B.h3k_quantize_weights_int8_groups(w, code, rows, cols, group, q, s, stream)
+    return q, s
+
+
 class DitStack:
     """L blocks of weights on the device plus the shared workspace."""
 
