@@ -122,6 +122,64 @@ def gelu_tanh(z: np.ndarray) -> np.ndarray:
     return f32(0.5) * z * (f32(1.0) + np.tanh(c * (z + f32(0.044715) * z * z * z)))
 
 
+ROPE_BASE = 10000.0
+
+
+def rope_axis_dims(head_dim: int):
+    """Head dimensions given to the (time, height, width) axes: d/4, 3d/8, 3d/8
+    (each even, so d must be a multiple of 16)."""
+    if head_dim % 16:
+        raise ValueError("RoPE needs head_dim a multiple of 16")
+    dt = head_dim // 4
+    dh = (head_dim - dt) // 2
+    return dt, dh, head_dim - dt - dh
+
+
+def rope_positions(n_tokens: int, grid, half_spatial: bool = False) -> np.ndarray:
+    """[n_tokens, 3] (t, h, w) coordinates of tokens laid out frame by frame,
+    then row by row, then column by column over the latent grid (T, H, W);
+    the spatial two are halved under the native-256 rule."""
+    T, H, W = grid
+    if T * H * W != n_tokens:
+        raise ValueError("grid does not match the token count")
+    n = np.arange(n_tokens)
+    pos = np.stack([n // (H * W), (n // W) % H, n % W], axis=1).astype(np.float64)
+    if half_spatial:
+        pos[:, 1:] *= 0.5
+    return pos
+
+
+def rope_3d(x: np.ndarray, n_heads: int, grid, half_spatial: bool = False) -> np.ndarray:
+    """3D rotary position embedding of q or k ([n_tokens, n_heads * d]).
+
+    [H3-review], its note on native-256 RoPE: rotary position embedding
+    injects each token's position, and on 256 square canvases the spatial
+    RoPE coordinates are halved.  The page gives no more; the readings here
+    (listed again in the design notes) are the plainest ones for a video
+    latent: each head's d dimensions are split into a time, a height and a
+    width slice (rope_axis_dims), and within the slice of axis a the pair
+    (2i, 2i+1) is rotated by the angle pos_a * base^(-2i / d_a), base 10000:
+        (x, y) -> (x cos phi - y sin phi, x sin phi + y cos phi).
+    Angles and rotation in float64, result rounded to fp32.
+    """
+    N, D = x.shape
+    d = D // n_heads
+    pos = rope_positions(N, grid, half_spatial)
+    x = x.astype(np.float64).reshape(N, n_heads, d)
+    out = np.empty_like(x)
+    c0 = 0
+    for a, da in enumerate(rope_axis_dims(d)):
+        i = np.arange(da // 2, dtype=np.float64)
+        theta = ROPE_BASE ** (-2.0 * i / da)
+        phi = pos[:, a:a + 1] * theta[None, :]                 # [N, da/2]
+        cs, sn = np.cos(phi)[:, None, :], np.sin(phi)[:, None, :]
+        xe, xo = x[:, :, c0:c0 + da:2], x[:, :, c0 + 1:c0 + da:2]
+        out[:, :, c0:c0 + da:2] = xe * cs - xo * sn
+        out[:, :, c0 + 1:c0 + da:2] = xe * sn + xo * cs
+        c0 += da
+    return out.reshape(N, D).astype(f32)
+
+
 def quantize_int8(w: np.ndarray):
     """Per-output-channel symmetric int8: s[o] = max_k |w[o,k]| / 127,
     q = clip(rint(w / s), -127, 127) with ties to even.
@@ -206,7 +264,8 @@ def _weight(wts: Dict[str, np.ndarray], name: str) -> np.ndarray:
 
 def block_forward(x: np.ndarray, c: np.ndarray, wts: Dict[str, np.ndarray], n_heads: int,
                   rows: Optional[Sequence[int]] = None, eps: float = LN_EPS,
-                  intermediates: Optional[dict] = None, int8_fc2_rows: bool = False) -> np.ndarray:
+                  intermediates: Optional[dict] = None, int8_fc2_rows: bool = False,
+                  rope: Optional[tuple] = None) -> np.ndarray:
     """One AdaLN DiT block.
 
         mod = W_ada c + b_ada -> shift_a, scale_a, gate_a, shift_m, scale_m, gate_m
@@ -231,6 +290,10 @@ def block_forward(x: np.ndarray, c: np.ndarray, wts: Dict[str, np.ndarray], n_he
     symmetric rule as the weights (quantize_int8), and the MLP-down
     projection is the int8 x int8 product of linear_w8a8 with the int8
     w_down (which must then be a (q_int8, scale) pair).
+
+    ``rope`` = (T, H, W, half_spatial) rotates q and k after their bias by
+    rope_3d over the latent grid (T, H, W) (the native-256 note of
+    [H3-review]); None leaves attention without positional terms.
     """
     x = x.astype(f32)
     D = x.shape[1]
@@ -243,9 +306,13 @@ def block_forward(x: np.ndarray, c: np.ndarray, wts: Dict[str, np.ndarray], n_he
     bq = bk = bv = None
     if b_qkv is not None:
         bq, bk, bv = b_qkv[:D], b_qkv[D:2 * D], b_qkv[2 * D:]
-    q = linear(h[sel], w_qkv[:D], bq)
+    q = linear(h, w_qkv[:D], bq) if rope is not None else linear(h[sel], w_qkv[:D], bq)
     k = linear(h, w_qkv[D:2 * D], bk)
     v = linear(h, w_qkv[2 * D:], bv)
+    if rope is not None:
+        grid, half = tuple(rope[:3]), bool(rope[3])
+        q = rope_3d(q, n_heads, grid, half)[sel]
+        k = rope_3d(k, n_heads, grid, half)
     o = attention(q, k, v, n_heads)
     x1 = x[sel] + m["gate_a"] * linear(o, _weight(wts, "w_out"), wts.get("b_out"))
     h2 = modulate(layer_norm(x1, eps), m["shift_m"], m["scale_m"])
@@ -263,7 +330,8 @@ def block_forward(x: np.ndarray, c: np.ndarray, wts: Dict[str, np.ndarray], n_he
 
 
 def stack_forward(x: np.ndarray, c: np.ndarray, blocks: Sequence[Dict[str, np.ndarray]], n_heads: int,
-                  n_layers: Optional[int] = None, eps: float = LN_EPS, int8_fc2_rows: bool = False) -> np.ndarray:
+                  n_layers: Optional[int] = None, eps: float = LN_EPS, int8_fc2_rows: bool = False,
+                  rope: Optional[tuple] = None) -> np.ndarray:
     """x_{l+1} = block_l(x_l, c) for the first ``n_layers`` blocks, one shared c.
 
     [H3-review] knob list: the layer count runs the first 50, 45 or 40 blocks.
@@ -271,5 +339,5 @@ def stack_forward(x: np.ndarray, c: np.ndarray, blocks: Sequence[Dict[str, np.nd
     """
     L = len(blocks) if n_layers is None else n_layers
     for l in range(L):
-        x = block_forward(x, c, blocks[l], n_heads, eps=eps, int8_fc2_rows=int8_fc2_rows)
+        x = block_forward(x, c, blocks[l], n_heads, eps=eps, int8_fc2_rows=int8_fc2_rows, rope=rope)
     return x

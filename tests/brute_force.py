@@ -60,8 +60,30 @@ def attention_naive(q, k, v, n_heads):
     return out
 
 
-def block(x, c, w, n_heads, eps=1e-6):
-    """x: N x D nested lists, c: C list, w: dict of nested lists (biases may be None)."""
+def rope_rows(rows, n_heads, positions, split):
+    """Rotary embedding on nested lists: for every token, head and axis a, the
+    pair (2i, 2i+1) of the axis's slice (widths ``split`` = (d_t, d_h, d_w), in
+    that order inside the head) turns by positions[token][a] * 10000^(-2i/d_a)."""
+    out = []
+    for row, pos in zip(rows, positions):
+        d = len(row) // n_heads
+        new = list(row)
+        for hd in range(n_heads):
+            c0 = hd * d
+            for a, da in enumerate(split):
+                for i in range(da // 2):
+                    phi = pos[a] * 10000.0 ** (-2.0 * i / da)
+                    x, y = row[c0 + 2 * i], row[c0 + 2 * i + 1]
+                    new[c0 + 2 * i] = x * math.cos(phi) - y * math.sin(phi)
+                    new[c0 + 2 * i + 1] = x * math.sin(phi) + y * math.cos(phi)
+                c0 += da
+        out.append(new)
+    return out
+
+
+def block(x, c, w, n_heads, eps=1e-6, rope=None):
+    """x: N x D nested lists, c: C list, w: dict of nested lists (biases may be None).
+    rope = (positions, split) rotates q and k by rope_rows."""
     x = _mat(x)
     c = _vec(c)
     D = len(x[0])
@@ -81,6 +103,9 @@ def block(x, c, w, n_heads, eps=1e-6):
     q = [r[0:D] for r in qkv]
     k = [r[D:2 * D] for r in qkv]
     v = [r[2 * D:3 * D] for r in qkv]
+    if rope is not None:
+        q = rope_rows(q, n_heads, *rope)
+        k = rope_rows(k, n_heads, *rope)
     o = attention_naive(q, k, v, n_heads)
     proj = dense(o, W["w_out"], W.get("b_out"))
     x1 = [[x[t][i] + gate_a[i] * proj[t][i] for i in range(D)] for t in range(len(x))]

@@ -235,6 +235,100 @@ def test_stack_one_layer_is_block_and_prefix():
     assert np.array_equal(three, oracle.stack_forward(x, c, blocks[:3], shape.n_heads))
 
 
+# ---------------------------------------------------------------- 3D RoPE
+
+def _grid_positions(grid, half=False):
+    T, H, W = grid
+    return [(t, h * (0.5 if half else 1.0), w * (0.5 if half else 1.0))
+            for t in range(T) for h in range(H) for w in range(W)]
+
+
+@pytest.mark.parametrize("d,grid,half", [(16, (2, 3, 4), False), (32, (3, 2, 2), True), (64, (1, 4, 5), False)])
+def test_rope_matches_brute_force(d, grid, half):
+    n = grid[0] * grid[1] * grid[2]
+    heads = 2
+    rng = np.random.default_rng(61)
+    x = rng.standard_normal((n, heads * d)).astype(np.float32)
+    got = oracle.rope_3d(x, heads, grid, half)
+    ref = bf.rope_rows(x.astype(np.float64).tolist(), heads, _grid_positions(grid, half), oracle.rope_axis_dims(d))
+    assert np.allclose(got, np.array(ref), rtol=1e-6, atol=1e-6)
+
+
+def test_rope_axis_split_and_positions():
+    assert oracle.rope_axis_dims(128) == (32, 48, 48)
+    assert oracle.rope_axis_dims(64) == (16, 24, 24)
+    with pytest.raises(ValueError):
+        oracle.rope_axis_dims(8)
+    pos = oracle.rope_positions(2 * 3 * 5, (2, 3, 5))
+    assert pos[0].tolist() == [0, 0, 0] and pos[1].tolist() == [0, 0, 1] and pos[5].tolist() == [0, 1, 0]
+    assert pos[15].tolist() == [1, 0, 0] and pos[29].tolist() == [1, 2, 4]
+    assert oracle.rope_positions(30, (2, 3, 5), True)[29].tolist() == [1, 1.0, 2.0]
+    with pytest.raises(ValueError):
+        oracle.rope_positions(31, (2, 3, 5))
+
+
+def test_rope_identity_at_origin_and_pair_norms():
+    rng = np.random.default_rng(67)
+    grid = (2, 3, 4)
+    x = rng.standard_normal((24, 128)).astype(np.float32)
+    y = oracle.rope_3d(x, 1, grid)
+    assert np.array_equal(y[0], x[0])                         # token (0, 0, 0): every angle is 0
+    nx = np.hypot(x[:, 0::2].astype(np.float64), x[:, 1::2])
+    ny = np.hypot(y[:, 0::2].astype(np.float64), y[:, 1::2])
+    assert np.allclose(nx, ny, rtol=1e-6)
+
+
+def test_rope_scores_depend_on_relative_position_only():
+    """<R(p) q, R(p') k> is a function of p - p' for every axis: shifting both
+    tokens by the same offset leaves every head's score unchanged."""
+    rng = np.random.default_rng(71)
+    grid = (3, 4, 5)
+    n = 60
+    d, heads = 64, 2
+    qv = rng.standard_normal(heads * d)
+    kv = rng.standard_normal(heads * d)
+    X = np.tile(qv, (n, 1)).astype(np.float32)
+    K = np.tile(kv, (n, 1)).astype(np.float32)
+    rq, rk = oracle.rope_3d(X, heads, grid), oracle.rope_3d(K, heads, grid)
+    tok = lambda t, h, w: (t * 4 + h) * 5 + w
+    for h_ in range(heads):
+        sl = slice(h_ * d, (h_ + 1) * d)
+        s1 = float(rq[tok(0, 1, 1), sl].astype(np.float64) @ rk[tok(1, 0, 3), sl])
+        s2 = float(rq[tok(1, 3, 2), sl].astype(np.float64) @ rk[tok(2, 2, 4), sl])
+        assert abs(s1 - s2) < 1e-4 * max(1.0, abs(s1))
+        s3 = float(rq[tok(0, 1, 1), sl].astype(np.float64) @ rk[tok(1, 0, 4), sl])   # a different offset
+        assert abs(s1 - s3) > 1e-3
+
+
+def test_rope_axes_act_on_their_own_slices():
+    """Tokens in the same frame get the same time slice; tokens in the same
+    row the same height slice; tokens in the same column the same width slice."""
+    rng = np.random.default_rng(73)
+    grid = (2, 3, 4)
+    v = rng.standard_normal(64).astype(np.float32)
+    y = oracle.rope_3d(np.tile(v, (24, 1)), 1, grid)
+    dt, dh, dw = oracle.rope_axis_dims(64)
+    tok = lambda t, h, w: (t * 3 + h) * 4 + w
+    assert np.array_equal(y[tok(1, 0, 0), :dt], y[tok(1, 2, 3), :dt])
+    assert np.array_equal(y[tok(0, 2, 1), dt:dt + dh], y[tok(1, 2, 3), dt:dt + dh])
+    assert np.array_equal(y[tok(0, 0, 3), dt + dh:], y[tok(1, 2, 3), dt + dh:])
+    assert not np.array_equal(y[tok(0, 0, 0), :dt], y[tok(1, 0, 0), :dt])
+
+
+def test_block_with_rope_matches_brute_force():
+    shape, x, c, w = tiny_problem(n_tokens=6, n_heads=2, head_dim=16, mlp=12)
+    grid = (1, 2, 3)
+    got = oracle.block_forward(x, c, w, shape.n_heads, rope=(1, 2, 3, False))
+    ref = bf.block(x.tolist(), c.tolist(), {k: (v.tolist() if v is not None else None) for k, v in w.items()},
+                   shape.n_heads, rope=(_grid_positions(grid), oracle.rope_axis_dims(16)))
+    assert rel_l2(got, ref) < 1e-5
+    plain = oracle.block_forward(x, c, w, shape.n_heads)
+    assert rel_l2(got, plain) > 1e-3                    # the positions do change the block
+    rows = [1, 4]
+    part = oracle.block_forward(x, c, w, shape.n_heads, rows=rows, rope=(1, 2, 3, False))
+    assert np.allclose(part, got[rows], rtol=1e-5, atol=1e-6)
+
+
 # ---------------------------------------------------------------- int8 quantiser
 
 def test_quantize_golden_ties():
