@@ -261,8 +261,9 @@ def extra_blocks(b0, x, c):
     """More measured units besides the step: the int8-weight block (the four
     projection weights of block 0 quantised per output row by the library's
     quantiser, W8A16 GEMMs), the same with the row-quantised FC2 and with
-    the group-wise int8 MLP, and one bf16 block at 6144 tokens, D=3072
-    (512x512x22-frame latent).  Inputs as for the step."""
+    the group-wise int8 MLP, the bf16 block with 3D RoPE, and one bf16 block
+    at 6144 tokens, D=3072 (512x512x22-frame latent).  Inputs as for the
+    step."""
     import torch
     import seeded_inputs as si
     from video_diffusion_transformer_adaln_amd import binding as B
@@ -344,6 +345,20 @@ def extra_blocks(b0, x, c):
     }
     log(f"int8 group-MLP block: {msg:.2f} ms; group quantiser {qg_ms:.3f} ms")
     del t8, tg
+    # ---- the bf16 block with 3D RoPE of q and k (14 frames x 30 rows x 54 columns), fused into the QKV epilogue
+    cfgr = B.make_config(N, D, H, d, F, C, B.H3K_BF16, B.H3K_BF16, True, rope=(14, 30, 54, False))
+    msr, kr = _time_block(cfgr, b0, x, c)
+    cfgp = B.make_config(N, D, H, d, F, C, B.H3K_BF16, B.H3K_BF16, True)
+    msp, kp = _time_block(cfgp, b0, x, c)
+    qr = kr["qkv"]["total_ms"] / kr["qkv"]["launches"]
+    qp = kp["qkv"]["total_ms"] / kp["qkv"]["launches"]
+    res["rope_block"] = {
+        "workload": "one bf16 block at 22680 tokens with 3D RoPE of q and k over the 14x30x54 latent grid, "
+                    "rotated in the QKV projection's epilogue",
+        "ms_per_block": round(msr, 3), "tflops": round(sum(fl.values()) / (msr * 1e-3) / 1e12, 1),
+        "qkv_ms": round(qr, 4), "qkv_ms_without_rope": round(qp, 4), "block_ms_without_rope": round(msp, 3),
+    }
+    log(f"RoPE block: {msr:.2f} ms (QKV {qr:.3f} ms against {qp:.3f} ms without RoPE)")
     # ---- 6144-token bf16 block
     sh = si.C1
     N, D, F, C, H, d = sh.n_tokens, sh.hidden, sh.mlp_hidden, sh.cond_dim, sh.n_heads, sh.head_dim

@@ -93,7 +93,14 @@ typedef int32_t h3k_dtype;
  * quantisation; the page gives no group size): s_up is then [F, D/G] and
  * s_down [D, F/G] (h3k_quantize_weights_int8_groups), the QKV and output
  * projections keep per-row scales.  Needs weight_dtype INT8, act_dtype BF16,
- * hidden and mlp_hidden multiples of G, and int8_fc2_rows = 0. */
+ * hidden and mlp_hidden multiples of G, and int8_fc2_rows = 0.
+ * rope_frames, rope_height, rope_width: 0, 0, 0 leaves attention without
+ * positional terms (every workload of the pages' benchmark); a grid T x H x W
+ * with T*H*W = n_tokens (tokens laid out frame, row, column) rotates q and k
+ * after their bias by the 3D RoPE of h3k_rope_3d, fused into the QKV
+ * projection's epilogue ([H3-review], note on native-256 RoPE).  Needs BF16
+ * activations.  rope_half_spatial = 1 halves the spatial coordinates (the
+ * page's rule for native-256 generation on 256 square canvases). */
 typedef struct h3k_dit_config {
   int32_t n_tokens;
   int32_t hidden;
@@ -107,6 +114,10 @@ typedef struct h3k_dit_config {
   int32_t alias_activations;
   int32_t int8_fc2_rows;
   int32_t int8_mlp_group;
+  int32_t rope_frames;
+  int32_t rope_height;
+  int32_t rope_width;
+  int32_t rope_half_spatial;
 } h3k_dit_config;
 
 /* Weights of one block; all device pointers.
@@ -293,6 +304,19 @@ h3k_status h3k_linear_int8_groups(int64_t m, int64_t n, int64_t k, int32_t group
                                   const int8_t* wq, int64_t ldw, const float* w_scale, const void* bias,
                                   int32_t epilogue, const void* residual, int64_t ldr, const float* gate, void* y,
                                   int64_t ldy, hipStream_t stream);
+
+/* 3D rotary position embedding, in place, of x [n_tokens, ldx] BF16 whose first
+ * `cols` columns are heads of head_dim (e.g. the q and k columns of a QKV
+ * output).  Row n is the token at (t, h, w) = (n / (H W), (n / W) % H, n % W) of
+ * the grid frames x height x width; half_spatial = 1 halves h and w ([H3-review],
+ * note on native-256 RoPE: spatial coordinates halved on 256 square canvases).
+ * Each head is cut into a time, a height and a width slice of d/4, 3d/8, 3d/8
+ * dimensions, and the pair (2i, 2i+1) of the slice of axis a turns by
+ * pos_a * 10000^(-2i / d_a):  (x, y) -> (x cos - y sin, x sin + y cos).
+ * head_dim a multiple of 16 (<= 256), cols a multiple of head_dim, ldx >= cols
+ * and a multiple of 4, frames * height * width = n_tokens. */
+h3k_status h3k_rope_3d(int64_t n_tokens, int64_t cols, int32_t head_dim, int32_t frames, int32_t height,
+                       int32_t width, int32_t half_spatial, void* x, int64_t ldx, hipStream_t stream);
 
 /* o[n, H*d] = per head softmax(q k^T / sqrt(d)) v, non-causal, no positional
  * terms; q [n, ldq], k [n, ldk] row-major (head j = columns j*d..j*d+d-1), v given

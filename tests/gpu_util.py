@@ -40,12 +40,12 @@ def act_code(shape):
     return B.H3K_F32 if shape.dtype == "f32" else B.H3K_BF16
 
 
-def config_for(shape, alias=True, int8_fc2_rows=False, int8_mlp_group=0):
+def config_for(shape, alias=True, int8_fc2_rows=False, int8_mlp_group=0, rope=None):
     from video_diffusion_transformer_adaln_amd import binding as B
     act = act_code(shape)
     return B.make_config(shape.n_tokens, shape.hidden, shape.n_heads, shape.head_dim, shape.mlp_hidden,
                          shape.cond_dim, act, B.H3K_INT8 if shape.int8_weights else act, alias,
-                         int8_fc2_rows=int8_fc2_rows, int8_mlp_group=int8_mlp_group)
+                         int8_fc2_rows=int8_fc2_rows, int8_mlp_group=int8_mlp_group, rope=rope)
 
 
 def sample_rows(n, count=ROWS_PER_SAMPLE, seed=5):

@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_struct_sizes_match_header_layout():
-    assert ctypes.sizeof(B.DitConfig) == 48
+    assert ctypes.sizeof(B.DitConfig) == 64
     assert ctypes.sizeof(B.DitBlockWeights) == 14 * 8
     assert ctypes.sizeof(B.DitStats) == 40
     assert ctypes.sizeof(B.DitPlanInfo) == 9 * 8 * 2 + 9 * 4 * 2 + 8 * 5 + 8
@@ -161,6 +161,14 @@ def test_reject_bad_shapes_and_dtypes():
     assert _block(cfg_c2(int8_mlp_group=64)) == B.H3K_ERR_UNSUPPORTED
     assert _block(cfg_c2(weight_dtype=B.H3K_INT8, mlp_hidden=13824 - 64, int8_mlp_group=128)) == B.H3K_ERR_SHAPE
     assert _block(cfg_c2(weight_dtype=B.H3K_INT8, int8_mlp_group=64, int8_fc2_rows=True)) == B.H3K_ERR_UNSUPPORTED
+    # 3D RoPE: the grid must hold the tokens; bf16 activations; the halving flag needs a grid
+    assert _block(cfg_c2(rope=(14, 30, 53, False))) == B.H3K_ERR_SHAPE
+    assert _block(cfg_c2(rope=(14, 0, 54, False))) == B.H3K_ERR_SHAPE
+    f32 = dict(n_tokens=512, hidden=256, n_heads=4, head_dim=64, mlp_hidden=1024, cond_dim=256, act_dtype=B.H3K_F32)
+    assert _block(B.make_config(**f32, rope=(2, 16, 16, False))) == B.H3K_ERR_UNSUPPORTED
+    half_only = cfg_c2()
+    half_only.rope_half_spatial = 1
+    assert _block(half_only) == B.H3K_ERR_SHAPE
 
 
 def test_reject_int8_without_scales():
@@ -225,6 +233,12 @@ def test_reject_bad_kernel_level_arguments():
                                       None) == B.H3K_ERR_OVERLAP
     assert lib.h3k_linear_int8_groups(10, 64, 256, 48, X, 256, W, 256, WS, None, 0, None, 0, None, Y, 64,
                                       None) == B.H3K_ERR_SHAPE
+    # RoPE: head_dim not a multiple of 16, cols not a multiple of head_dim, grid / token mismatch, misaligned x
+    assert lib.h3k_rope_3d(24, 96, 24, 2, 3, 4, 0, X, 96, None) == B.H3K_ERR_SHAPE
+    assert lib.h3k_rope_3d(24, 96, 64, 2, 3, 4, 0, X, 96, None) == B.H3K_ERR_SHAPE
+    assert lib.h3k_rope_3d(24, 128, 64, 2, 3, 5, 0, X, 128, None) == B.H3K_ERR_SHAPE
+    assert lib.h3k_rope_3d(24, 128, 64, 2, 3, 4, 2, X, 128, None) == B.H3K_ERR_SHAPE
+    assert lib.h3k_rope_3d(24, 128, 64, 2, 3, 4, 0, X + 8, 128, None) == B.H3K_ERR_ALIGN
 
 
 def _no_gpu():
@@ -242,3 +256,5 @@ def test_valid_arguments_without_device_report_hip_error():
     lib = h3k.lib()
     assert lib.h3k_quantize_weights_int8_groups(FAKE, 1, 4, 128, 64, FAKE + (1 << 32), FAKE + (2 << 32),
                                                 None) == B.H3K_ERR_HIP
+    assert _block(cfg_c2(rope=(14, 30, 54, True))) == B.H3K_ERR_HIP
+    assert lib.h3k_rope_3d(24, 128, 64, 2, 3, 4, 1, FAKE, 128, None) == B.H3K_ERR_HIP

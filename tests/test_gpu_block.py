@@ -33,10 +33,11 @@ def R():
     return runtime
 
 
-def _run_block(R, shape, dw, xd, cd, alias=True, poison=True, stats=None, int8_fc2_rows=False, int8_mlp_group=0):
+def _run_block(R, shape, dw, xd, cd, alias=True, poison=True, stats=None, int8_fc2_rows=False, int8_mlp_group=0,
+               rope=None):
     import torch
     from video_diffusion_transformer_adaln_amd import binding as B
-    cfg = config_for(shape, alias, int8_fc2_rows, int8_mlp_group)
+    cfg = config_for(shape, alias, int8_fc2_rows, int8_mlp_group, rope)
     ws = R.alloc_workspace(cfg)
     if poison:
         ws.fill_(0xFF)
@@ -193,6 +194,45 @@ def test_block_int8_mlp_groups(R, case, group):
     assert err < TOL
     if case == "small":
         off = _run_block(R, shape, dw, xd, cd, alias=False, int8_mlp_group=group)
+        assert torch.equal(off.view(torch.int16), got_t.view(torch.int16))
+
+
+@pytest.mark.parametrize("case,grid,half", [("c2", (14, 30, 54), False), ("ragged", (3, 3, 37), False),
+                                             ("ragged", (3, 3, 37), True), ("d64", (2, 8, 16), True)])
+def test_block_rope(R, case, grid, half):
+    """3D RoPE of q and k fused into the QKV projection's epilogue, against the
+    oracle's block with the same grid; byte-identical with aliasing on and
+    off.  c2: the 864x480x56-frame latent (14 frames, 30 rows, 54 columns).
+    The QKV weights are scaled up so that the output depends on the
+    positions: the block without RoPE must be far from the reference."""
+    import torch
+    if case == "c2":
+        shape = si.C2
+    elif case == "ragged":
+        shape = si.custom_shape("rope", 974, 333, 2, 128, 640, "bf16")
+    else:
+        shape = si.custom_shape("rope64", 975, 256, 4, 64, 512, "bf16")
+    flush(f"block {shape.name} rope grid={grid} half={half}")
+    hx, hc, hw = _block_case(shape, bias_std=0.05)
+    # QKV weights scaled so that q and k have std ~1.4 (logits of std ~2) at every width, as the
+    # N(0, 0.02^2) weights give at D = 5120: attention, and the block, then depend on the positions
+    boost = max(1.0, 70.0 / np.sqrt(shape.hidden))
+    hw["w_qkv"] = si._finish(np.ascontiguousarray(hw["w_qkv"].values * boost, dtype=np.float32), shape.dtype)
+    dw, ow = upload_block(shape, hw)
+    xd, cd = dev(hx), dev(hc)
+    rope = (grid[0], grid[1], grid[2], half)
+    got_t = _run_block(R, shape, dw, xd, cd, rope=rope)
+    got = to_np(got_t)
+    rows = sample_rows(shape.n_tokens) if case == "c2" else np.arange(shape.n_tokens)
+    ref = oracle.block_forward(hx.values, hc.values, ow, shape.n_heads, rows=rows, rope=rope)
+    err = rel_l2(got[rows], ref)
+    flush(f"  rel_l2 = {err:.3e}")
+    assert err < TOL
+    plain = oracle.block_forward(hx.values, hc.values, ow, shape.n_heads, rows=rows)
+    flush(f"  rel_l2 to the block without RoPE = {rel_l2(got[rows], plain):.3e}")
+    assert rel_l2(got[rows], plain) > 5 * err          # the positions are in the output
+    if case != "c2":
+        off = _run_block(R, shape, dw, xd, cd, alias=False, rope=rope)
         assert torch.equal(off.view(torch.int16), got_t.view(torch.int16))
 
 

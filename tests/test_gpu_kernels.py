@@ -275,6 +275,31 @@ def test_linear_int8_groups(B, m, n, k, group, epi, full):
     assert rel_l2(got, ref) < BF16_TOL / 2
 
 
+# ------------------------------------------------------------------ 3D RoPE
+
+@pytest.mark.parametrize("grid,heads,hd,half", [((2, 3, 4), 2, 128, False), ((3, 3, 37), 4, 64, True),
+                                                ((1, 1, 1), 2, 64, False), ((14, 30, 54), 2, 128, False),
+                                                ((14, 30, 54), 2, 128, True), ((5, 7, 9), 3, 128, True)])
+def test_rope_3d(B, grid, heads, hd, half):
+    """In-place rotation of a [tokens, heads * d] bf16 matrix (with a wider
+    row pitch) against the oracle's float64 rope_3d of the same bf16 values."""
+    import torch
+    n = grid[0] * grid[1] * grid[2]
+    cols = heads * hd
+    flush(f"rope n={n} grid={grid} heads={heads} d={hd} half={half}")
+    x = _ht(_f32((n, cols), 1.0, 860, "x"), "bf16")
+    ld = cols + 8
+    xd = torch.full((n, ld), 7.0, dtype=torch.bfloat16, device="cuda")
+    xd[:, :cols] = dev(x)
+    B.h3k_rope_3d(n, cols, hd, grid[0], grid[1], grid[2], half, xd, ld)
+    torch.cuda.synchronize()
+    got = to_np(xd)
+    assert (got[:, cols:] == 7.0).all()                 # the pitch padding is untouched
+    ref = oracle.rope_3d(x.values, heads, grid, half)
+    assert rel_l2(got[:, :cols], ref) < 4e-3           # one bf16 rounding of the result
+    assert np.array_equal(got[0, :cols], x.values[0])   # token (0, 0, 0) is not rotated
+
+
 # ------------------------------------------------------------------ attention
 
 ATTN_CASES = [

@@ -32,7 +32,8 @@ class DitConfig(ctypes.Structure):
     _fields_ = [("n_tokens", c_int32), ("hidden", c_int32), ("n_heads", c_int32), ("head_dim", c_int32),
                 ("mlp_hidden", c_int32), ("cond_dim", c_int32), ("ln_eps", c_float), ("act_dtype", c_int32),
                 ("weight_dtype", c_int32), ("alias_activations", c_int32), ("int8_fc2_rows", c_int32),
-                ("int8_mlp_group", c_int32)]
+                ("int8_mlp_group", c_int32), ("rope_frames", c_int32), ("rope_height", c_int32),
+                ("rope_width", c_int32), ("rope_half_spatial", c_int32)]
 
 
 class DitBlockWeights(ctypes.Structure):
@@ -91,6 +92,8 @@ _SIGNATURES = [
     ("h3k_linear_int8_groups", c_int32, [c_int64, c_int64, c_int64, c_int32, c_void_p, c_int64, c_void_p, c_int64,
                                          c_void_p, c_void_p, c_int32, c_void_p, c_int64, c_void_p, c_void_p, c_int64,
                                          c_void_p]),
+    ("h3k_rope_3d", c_int32, [c_int64, c_int64, c_int32, c_int32, c_int32, c_int32, c_int32, c_void_p, c_int64,
+                              c_void_p]),
     ("h3k_attention", c_int32, [c_int32, c_int32, c_int32, c_int32, c_void_p, c_int64, c_void_p, c_int64,
                                 c_void_p, c_int64, c_void_p, c_int64, c_void_p]),
     ("h3k_profiler_create", c_int32, [c_int32, ctypes.POINTER(c_void_p)]),
@@ -147,10 +150,13 @@ def _stream(stream) -> Optional[int]:
 
 def make_config(n_tokens: int, hidden: int, n_heads: int, head_dim: int, mlp_hidden: int, cond_dim: int,
                 act_dtype: int, weight_dtype: Optional[int] = None, alias: bool = True,
-                ln_eps: float = 1e-6, int8_fc2_rows: bool = False, int8_mlp_group: int = 0) -> DitConfig:
+                ln_eps: float = 1e-6, int8_fc2_rows: bool = False, int8_mlp_group: int = 0,
+                rope: Optional[tuple] = None) -> DitConfig:
+    """rope = (frames, height, width, half_spatial) turns on the 3D RoPE of q and k."""
+    rt, rh, rw, rhalf = (0, 0, 0, 0) if rope is None else (rope[0], rope[1], rope[2], 1 if rope[3] else 0)
     return DitConfig(n_tokens, hidden, n_heads, head_dim, mlp_hidden, cond_dim, ln_eps, act_dtype,
                      act_dtype if weight_dtype is None else weight_dtype, 1 if alias else 0,
-                     1 if int8_fc2_rows else 0, int8_mlp_group)
+                     1 if int8_fc2_rows else 0, int8_mlp_group, rt, rh, rw, rhalf)
 
 
 WEIGHT_FIELDS = ("w_ada", "b_ada", "w_qkv", "b_qkv", "s_qkv", "w_out", "b_out", "s_out",
@@ -232,6 +238,12 @@ def h3k_linear_int8_groups(m: int, n: int, k: int, group: int, x, ldx: int, wq, 
                            epilogue: int, residual, ldr: int, gate, y, ldy: int, stream=None) -> None:
     check(lib().h3k_linear_int8_groups(m, n, k, group, _ptr(x), ldx, _ptr(wq), ldw, _ptr(w_scale), _ptr(bias),
                                        epilogue, _ptr(residual), ldr, _ptr(gate), _ptr(y), ldy, _stream(stream)))
+
+
+def h3k_rope_3d(n_tokens: int, cols: int, head_dim: int, frames: int, height: int, width: int, half_spatial: bool,
+                x, ldx: int, stream=None) -> None:
+    check(lib().h3k_rope_3d(n_tokens, cols, head_dim, frames, height, width, 1 if half_spatial else 0, _ptr(x), ldx,
+                            _stream(stream)))
 
 
 def h3k_attention(dtype: int, n: int, n_heads: int, head_dim: int, q, ldq: int, k, ldk: int, vt, ldvt: int, o,

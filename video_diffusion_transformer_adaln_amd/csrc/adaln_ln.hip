@@ -158,6 +158,39 @@ hipError_t launch_ln_modulate(DType dt, int n, int D, float eps, const void* x, 
 }
 
 // ---------------------------------------------------------------------------
+// In-place 3D RoPE of a bf16 matrix (rows = tokens): one thread per 4
+// consecutive columns (two rotation pairs), 8-byte loads and stores.
+__global__ __launch_bounds__(256) void rope_kernel(bf16* __restrict__ x, int64_t ldx, int64_t n, int64_t quads,
+                                                   RopeGeom g) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= n * quads) return;
+  const int64_t row = idx / quads;
+  const int c = (int)(idx - row * quads) * 4;
+  bf16* px = x + row * ldx + c;
+  u32x2 raw = *reinterpret_cast<const u32x2*>(px);
+  bf16* e = reinterpret_cast<bf16*>(&raw);
+  float v[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = static_cast<float>(e[i]);
+  const int j = c % g.head_dim;
+  rope_rotate(v[0], v[1], (int)row, j, g);
+  rope_rotate(v[2], v[3], (int)row, j + 2, g);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) e[i] = static_cast<bf16>(v[i]);
+  *reinterpret_cast<u32x2*>(px) = raw;
+}
+
+hipError_t launch_rope(int64_t n, int64_t cols, int head_dim, int height, int width, float spatial, void* x,
+                       int64_t ldx, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  const int64_t quads = cols / 4;
+  const int64_t blocks = (n * quads + 255) / 256;
+  rope_kernel<<<dim3((unsigned)blocks), dim3(256), 0, stream>>>((bf16*)x, ldx, n, quads,
+                                                                 RopeGeom{head_dim, height, width, spatial});
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Per-row symmetric int8 quantiser: s = max|w| / 127, q = clamp(rint(w/s)).
 // One wave per row, four rows per workgroup.  Each lane handles groups of 8
 // consecutive elements (one 16-byte load for bf16, two for fp32; one 8-byte

@@ -72,6 +72,42 @@ template <int N> __device__ __forceinline__ void wait_vmcnt() {
 // s_waitcnt lgkmcnt(0): this wave's LDS reads and writes have completed
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
+// 3D rotary position embedding over a (T, H, W) latent grid, tokens laid out
+// frame, row, column ([H3-review], note on native-256 RoPE, which halves the
+// spatial coordinates on 256 square canvases: spatial = 0.5, else 1).  A
+// head's d dimensions are cut into a time, a height and a width slice of
+// d/4, 3d/8, 3d/8; the pair (2i, 2i+1) of the slice of axis a turns by
+// pos_a * 10000^(-2i / d_a).
+struct RopeGeom {
+  int head_dim;          // 0: no rotation
+  int height, width;     // the grid's H and W (T = tokens / (H W))
+  float spatial;         // 1 or 0.5
+};
+// Rotate the pair (x, y) at even dimension j (0 <= j < head_dim) of a head of
+// token `tok`.
+__device__ __forceinline__ void rope_rotate(float& x, float& y, int tok, int j, const RopeGeom& g) {
+  const int d = g.head_dim, dt = d / 4, dh = (d - dt) / 2;
+  const int hw = g.height * g.width;
+  const int t = tok / hw, r = tok - t * hw;
+  const int h = r / g.width, w = r - h * g.width;
+  float pos;
+  int i, da;
+  if (j < dt) { pos = (float)t; i = j >> 1; da = dt; }
+  else if (j < dt + dh) { pos = (float)h * g.spatial; i = (j - dt) >> 1; da = dh; }
+  else { pos = (float)w * g.spatial; i = (j - dt - dh) >> 1; da = d - dt - dh; }
+  // 10000^(-2i/da) = 2^(-2i log2(10000) / da); the angle in turns, reduced to
+  // [0, 1) exactly (fract), for v_sin_f32 / v_cos_f32, which take turns.
+  // Positions are grid coordinates (< 2^16), so the angle's fp32 error stays
+  // far below bf16 resolution.
+  const float theta = __builtin_amdgcn_exp2f(-2.0f * 13.287712379549449f * (float)i / (float)da);
+  const float turns = pos * theta * 0.15915494309189535f;
+  const float fr = turns - floorf(turns);
+  const float sn = __builtin_amdgcn_sinf(fr), cs = __builtin_amdgcn_cosf(fr);
+  const float nx = x * cs - y * sn;
+  y = x * sn + y * cs;
+  x = nx;
+}
+
 // Remap a linear workgroup id so that each XCD receives one contiguous range
 // of logical tiles (neighbouring tiles then share that XCD's L2).
 __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {

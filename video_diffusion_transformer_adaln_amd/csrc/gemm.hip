@@ -37,6 +37,7 @@ struct GemmParams {
   const void* w; int64_t ldw;
   const float* w_scale;   // int8 weights: [n] per channel, or [n, k / group] per group
   int group_shift;        // log2 of the group size (group-wise int8 weights)
+  RopeGeom rope;          // kEpiBiasRope: rotation of the row-major columns
   const bf16* bias;
   const bf16* residual; int64_t ldr;
   const float* gate;
@@ -141,6 +142,11 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, const f32x16 (&a
           if constexpr (EPI == kEpiGelu) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) v[e] = gelu_tanh(v[e]);
+          }
+          if constexpr (EPI == kEpiBiasRope) {   // features f..f+3 are the pairs (j, j+1), (j+2, j+3) of a head
+            const int j = f % p.rope.head_dim;
+            rope_rotate(v[0], v[1], t, j, p.rope);
+            rope_rotate(v[2], v[3], t, j + 2, p.rope);
           }
           if constexpr (EPI == kEpiGatedResidual) {
             const u32x2 rr = *reinterpret_cast<const u32x2*>(p.residual + (int64_t)t * p.ldr + f);
@@ -579,6 +585,7 @@ static void launch_bf16(const LinearArgs& a, hipStream_t stream) {
   p.tiles_m = (p.m + BM - 1) / BM;
   p.tiles_n = (p.n + BN - 1) / BN;
   p.group_shift = a.group > 0 ? __builtin_ctz((unsigned)a.group) : 0;
+  p.rope = RopeGeom{a.rope_hd, a.rope_h, a.rope_w, a.rope_spatial};
   if (a.act == kINT8)
     gemm_ring_kernel<EPI, true><<<dim3(p.tiles_m * p.tiles_n), dim3(512), 0, stream>>>(p);
   else if constexpr (W8) {
@@ -613,19 +620,22 @@ hipError_t launch_linear(const LinearArgs& a, hipStream_t stream) {
     switch (a.epi) {
       case kEpiBias: launch_f32<kEpiBias>(a, stream); break;
       case kEpiGelu: launch_f32<kEpiGelu>(a, stream); break;
-      default: launch_f32<kEpiGatedResidual>(a, stream); break;
+      case kEpiGatedResidual: launch_f32<kEpiGatedResidual>(a, stream); break;
+      default: return hipErrorInvalidValue;   // no rotary epilogue on the fp32 path
     }
   } else if (a.weight == kINT8) {
     switch (a.epi) {
       case kEpiBias: launch_bf16<kEpiBias, true>(a, stream); break;
       case kEpiGelu: launch_bf16<kEpiGelu, true>(a, stream); break;
-      default: launch_bf16<kEpiGatedResidual, true>(a, stream); break;
+      case kEpiGatedResidual: launch_bf16<kEpiGatedResidual, true>(a, stream); break;
+      default: launch_bf16<kEpiBiasRope, true>(a, stream); break;
     }
   } else {
     switch (a.epi) {
       case kEpiBias: launch_bf16<kEpiBias, false>(a, stream); break;
       case kEpiGelu: launch_bf16<kEpiGelu, false>(a, stream); break;
-      default: launch_bf16<kEpiGatedResidual, false>(a, stream); break;
+      case kEpiGatedResidual: launch_bf16<kEpiGatedResidual, false>(a, stream); break;
+      default: launch_bf16<kEpiBiasRope, false>(a, stream); break;
     }
   }
   return hipGetLastError();

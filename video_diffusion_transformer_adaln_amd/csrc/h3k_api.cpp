@@ -113,6 +113,17 @@ h3k_status validate_config(const h3k_dit_config* c) {
     return fail(H3K_ERR_SHAPE, "hidden and mlp_hidden must be multiples of int8_mlp_group %d", g);
   if (g && c->int8_fc2_rows)
     return fail(H3K_ERR_UNSUPPORTED, "int8_mlp_group and int8_fc2_rows cannot be combined (FC2 needs channel scales)");
+  const bool rope = c->rope_frames || c->rope_height || c->rope_width;
+  if (c->rope_half_spatial != 0 && c->rope_half_spatial != 1) return fail(H3K_ERR_SHAPE, "rope_half_spatial must be 0 or 1");
+  if (rope) {
+    if (c->rope_frames < 1 || c->rope_height < 1 || c->rope_width < 1 ||
+        (int64_t)c->rope_frames * c->rope_height * c->rope_width != c->n_tokens)
+      return fail(H3K_ERR_SHAPE, "RoPE grid %d x %d x %d does not hold the %d tokens", c->rope_frames, c->rope_height,
+                  c->rope_width, c->n_tokens);
+    if (c->act_dtype != H3K_BF16) return fail(H3K_ERR_UNSUPPORTED, "RoPE needs BF16 activations");
+  } else if (c->rope_half_spatial) {
+    return fail(H3K_ERR_SHAPE, "rope_half_spatial without a RoPE grid");
+  }
   const int64_t eb = esize(c->act_dtype);
   const int64_t rows = (int64_t)c->n_tokens + 256;
   const int64_t widest = std::max<int64_t>(2 * (int64_t)c->hidden, c->mlp_hidden);
@@ -334,6 +345,11 @@ h3k_status run_block(const h3k_dit_config* c, const h3k_dit_plan_info* P, const 
   L.m = N; L.n = 3 * D; L.k = D;
   L.x = h; L.ldx = D; L.w = w->w_qkv; L.ldw = D; L.w_scale = w->s_qkv; L.bias = w->b_qkv;
   L.epi = kEpiBias; L.y = qkv; L.ldy = 2 * D; L.yt = vt; L.ldyt = P->vt_pitch; L.split_col = 2 * D;
+  if (c->rope_frames) {                        // q and k (the row-major part) rotated after the bias
+    L.epi = kEpiBiasRope;
+    L.rope_hd = c->head_dim; L.rope_h = c->rope_height; L.rope_w = c->rope_width;
+    L.rope_spatial = c->rope_half_spatial ? 0.5f : 1.0f;
+  }
   H3K_TRY(launched(launch_linear(L, s), "QKV projection"));
   rec.done(H3K_K_QKV);
 
@@ -635,6 +651,23 @@ h3k_status h3k_linear_int8_groups(int64_t m, int64_t n, int64_t k, int32_t group
   L.epi = (Epilogue)epilogue; L.residual = residual; L.ldr = ldr; L.gate = gate;
   L.y = y; L.ldy = ldy; L.split_col = n;
   return launched(launch_linear(L, stream), "int8 group linear");
+}
+
+h3k_status h3k_rope_3d(int64_t n_tokens, int64_t cols, int32_t head_dim, int32_t frames, int32_t height,
+                       int32_t width, int32_t half_spatial, void* x, int64_t ldx, hipStream_t stream) {
+  if (head_dim < 16 || head_dim % 16 || head_dim > 256) return fail(H3K_ERR_SHAPE, "head_dim must be a multiple of 16 in [16, 256]");
+  if (n_tokens < 0 || n_tokens > 0x7fffffff || cols < head_dim || cols % head_dim || ldx < cols || ldx % 4)
+    return fail(H3K_ERR_SHAPE, "need cols a multiple of head_dim and ldx >= cols, a multiple of 4");
+  if (frames < 1 || height < 1 || width < 1 || (int64_t)frames * height * width != n_tokens)
+    return fail(H3K_ERR_SHAPE, "grid %d x %d x %d does not hold the %lld tokens", frames, height, width,
+                (long long)n_tokens);
+  if (half_spatial != 0 && half_spatial != 1) return fail(H3K_ERR_SHAPE, "half_spatial must be 0 or 1");
+  if (!x) return fail(H3K_ERR_NULL, "x must be non-NULL");
+  if (!aligned(x, 16)) return fail(H3K_ERR_ALIGN, "x must be 16-byte aligned");
+  if (n_tokens == 0) return H3K_OK;
+  H3K_TRY(check_device());
+  return launched(launch_rope(n_tokens, cols, head_dim, height, width, half_spatial ? 0.5f : 1.0f, x, ldx, stream),
+                  "RoPE");
 }
 
 h3k_status h3k_attention(h3k_dtype dtype, int32_t n, int32_t n_heads, int32_t head_dim, const void* q, int64_t ldq,

@@ -8,7 +8,7 @@
 namespace h3k {
 
 enum DType : int32_t { kF32 = 0, kBF16 = 1, kINT8 = 2 };
-enum Epilogue : int32_t { kEpiBias = 0, kEpiGelu = 1, kEpiGatedResidual = 2 };
+enum Epilogue : int32_t { kEpiBias = 0, kEpiGelu = 1, kEpiGatedResidual = 2, kEpiBiasRope = 3 };
 
 // mod[rows] = W[rows, cols] c + b   (fp32 out)
 hipError_t launch_adaln_gemv(DType dt, int rows, int cols, const void* w, const void* b,
@@ -34,6 +34,8 @@ struct LinearArgs {
   int64_t split_col;
   const float* x_scale;   // per-row activation scales (act = kINT8 only)
   int group;              // int8 weights: 0 = w_scale per row [n]; else w_scale [n, k / group]
+  int rope_hd, rope_h, rope_w;   // kEpiBiasRope: head size and grid H, W (rows are tokens)
+  float rope_spatial;            // 1, or 0.5 to halve the spatial coordinates
 };
 hipError_t launch_linear(const LinearArgs& a, hipStream_t stream);
 
@@ -46,6 +48,11 @@ struct AttentionArgs {
   void* o; int64_t ldo;
 };
 hipError_t launch_attention(const AttentionArgs& a, hipStream_t stream);
+
+// in place: x[n, cols] (bf16, row pitch ldx), heads of head_dim consecutive
+// columns, rotated by the 3D RoPE of each row's token over the (T, H, W) grid
+hipError_t launch_rope(int64_t n, int64_t cols, int head_dim, int height, int width, float spatial, void* x,
+                       int64_t ldx, hipStream_t stream);
 
 hipError_t launch_quantize_int8(DType dt, const void* w, int64_t rows, int64_t cols, int8_t* q,
                                 float* scales, hipStream_t stream);
