@@ -329,15 +329,50 @@ def block_forward(x: np.ndarray, c: np.ndarray, wts: Dict[str, np.ndarray], n_he
     return y.astype(f32)
 
 
+def token_merge(x: np.ndarray) -> np.ndarray:
+    """Tokens (2m, 2m+1) -> their mean, in fp32: [N, D] -> [N/2, D].
+
+    [H3-review] knob list: token reduction pairs the video tokens two by two
+    along rows to shorten the sequence in the middle layers.  With tokens
+    laid out row by row and an even row length, tokens 2m and 2m+1 are such
+    row neighbours.  The mean is the reading for the merge (the page gives
+    no formula).
+    """
+    x = x.astype(f32)
+    if x.shape[0] % 2:
+        raise ValueError("token reduction needs an even token count")
+    return ((x[0::2] + x[1::2]) * f32(0.5)).astype(f32)
+
+
+def token_unmerge(entry: np.ndarray, merged_out: np.ndarray) -> np.ndarray:
+    """Back to N tokens: each token gets its own state from before the merge
+    plus the change the reduced layers made to its pair's mean,
+        y[2m + j] = entry[2m + j] + (merged_out[m] - token_merge(entry)[m]),
+    so reduced layers that change nothing give back ``entry`` exactly (the
+    reading for the restore; the page gives no formula)."""
+    delta = merged_out.astype(f32) - token_merge(entry)
+    return (entry.astype(f32) + np.repeat(delta, 2, axis=0)).astype(f32)
+
+
 def stack_forward(x: np.ndarray, c: np.ndarray, blocks: Sequence[Dict[str, np.ndarray]], n_heads: int,
                   n_layers: Optional[int] = None, eps: float = LN_EPS, int8_fc2_rows: bool = False,
-                  rope: Optional[tuple] = None) -> np.ndarray:
+                  rope: Optional[tuple] = None, token_reduction: Optional[tuple] = None) -> np.ndarray:
     """x_{l+1} = block_l(x_l, c) for the first ``n_layers`` blocks, one shared c.
 
     [H3-review] knob list: the layer count runs the first 50, 45 or 40 blocks.
     No final norm or unpatchify (they are outside the block).
+    ``token_reduction`` = (first, last) runs blocks first .. last-1 on the
+    merged tokens (token_merge before block first, token_unmerge after block
+    last-1); None runs every block on all tokens.
     """
     L = len(blocks) if n_layers is None else n_layers
+    first, last = token_reduction if token_reduction is not None else (0, 0)
+    entry = None
     for l in range(L):
+        if first < last and l == first:
+            entry = x
+            x = token_merge(x)
         x = block_forward(x, c, blocks[l], n_heads, eps=eps, int8_fc2_rows=int8_fc2_rows, rope=rope)
+        if first < last and l == last - 1:
+            x = token_unmerge(entry, x)
     return x

@@ -168,3 +168,24 @@ def fc2_int8_rows(u, q_w, s_w, b):
             r.append(su * s_w[o] * acc + (b[o] if b is not None else 0.0))
         out.append(r)
     return out
+
+
+def token_merge_rows(x):
+    """Pairs of consecutive rows -> their mean (nested lists)."""
+    return [[0.5 * (a + b) for a, b in zip(x[2 * m], x[2 * m + 1])] for m in range(len(x) // 2)]
+
+
+def reduced_stack(x, c, blocks, n_heads, first, last, eps=1e-6):
+    """Blocks first .. last-1 on the merged rows; on exit each row gets its own
+    entry state plus its pair's change."""
+    entry = None
+    for l, w in enumerate(blocks):
+        if l == first:
+            entry = x
+            x = token_merge_rows(x)
+        x = block(x, c, w, n_heads, eps)
+        if l == last - 1:
+            merged_in = token_merge_rows(entry)
+            x = [[e + (x[r // 2][i] - merged_in[r // 2][i]) for i, e in enumerate(entry[r])]
+                 for r in range(len(entry))]
+    return x

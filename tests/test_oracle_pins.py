@@ -329,6 +329,40 @@ def test_block_with_rope_matches_brute_force():
     assert np.allclose(part, got[rows], rtol=1e-5, atol=1e-6)
 
 
+# ---------------------------------------------------------------- token reduction
+
+def test_token_merge_pairs_and_identity_restore():
+    rng = np.random.default_rng(79)
+    x = rng.standard_normal((10, 6)).astype(np.float32)
+    m = oracle.token_merge(x)
+    ref = bf.token_merge_rows(x.astype(np.float64).tolist())
+    assert np.allclose(m, np.array(ref), rtol=1e-6, atol=1e-7)
+    dup = np.repeat(x[:5], 2, axis=0)                      # equal pairs merge to themselves
+    assert np.array_equal(oracle.token_merge(dup), x[:5])
+    assert np.array_equal(oracle.token_unmerge(x, m), x)   # reduced layers that change nothing
+    d = rng.standard_normal((5, 6)).astype(np.float32)     # a change of the merged stream reaches both tokens
+    assert np.allclose(oracle.token_unmerge(x, m + d), x + np.repeat(d, 2, axis=0), rtol=1e-6, atol=1e-6)
+    with pytest.raises(ValueError):
+        oracle.token_merge(x[:9])
+
+
+def test_reduced_stack_matches_brute_force_and_empty_range():
+    shape, x, c, w = tiny_problem(n_tokens=8, n_heads=2, head_dim=4, mlp=12)
+    blocks = [w, {k: (v * 0.9 if v is not None else None) for k, v in w.items()},
+              {k: (v * 1.1 if v is not None else None) for k, v in w.items()}, w]
+    got = oracle.stack_forward(x, c, blocks, shape.n_heads, token_reduction=(1, 3))
+    lists = [{k: (v.tolist() if v is not None else None) for k, v in b.items()} for b in blocks]
+    ref = bf.reduced_stack(x.tolist(), c.tolist(), lists, shape.n_heads, 1, 3)
+    assert rel_l2(got, ref) < 1e-5
+    plain = oracle.stack_forward(x, c, blocks, shape.n_heads)
+    assert np.array_equal(oracle.stack_forward(x, c, blocks, shape.n_heads, token_reduction=(2, 2)), plain)
+    assert rel_l2(got, plain) > 1e-3                       # the reduction does change the result
+    # reducing from the first block to the last is merge, the stack on N/2 tokens, restore
+    whole = oracle.stack_forward(x, c, blocks, shape.n_heads, token_reduction=(0, 4))
+    mid = oracle.stack_forward(oracle.token_merge(x), c, blocks, shape.n_heads)
+    assert np.allclose(whole, oracle.token_unmerge(x, mid), rtol=1e-6, atol=1e-6)
+
+
 # ---------------------------------------------------------------- int8 quantiser
 
 def test_quantize_golden_ties():
