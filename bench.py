@@ -199,6 +199,8 @@ def main():
     extra = {}
     if not args.no_extra_blocks:
         extra = extra_blocks(blocks[0], x, c)
+        if L >= 4:
+            extra["token_reduction_step"] = token_reduction_step(cfg, blocks, x, c, ms_step, fl, L)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -230,6 +232,44 @@ def main():
     }
     result.update(extra)
     print(json.dumps(result), flush=True)
+
+
+def token_reduction_step(cfg, blocks, x, c, ms_full, fl, L, reps=2):
+    """The same step with the middle half of the layers (L/4 .. L - L/4 - 1)
+    on merged tokens: adjacent tokens of a latent row (54 per row) averaged
+    before, restored after.  Reported besides the full step, not in `value`."""
+    import torch
+    from video_diffusion_transformer_adaln_amd import binding as B
+    from video_diffusion_transformer_adaln_amd import runtime as R
+    first, last = L // 4, L - L // 4
+    cfg_r = B.DitConfig.from_buffer_copy(cfg)
+    cfg_r.token_reduction_first, cfg_r.token_reduction_last = first, last
+    st = R.DitStack(cfg_r, blocks)
+    out = torch.empty_like(x)
+    st.forward(x, c, out)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        st.forward(x, c, out)
+    e1.record()
+    torch.cuda.synchronize()
+    if not torch.isfinite(out.float()).all():
+        log("non-finite output with token reduction")
+        sys.exit(3)
+    ms = e0.elapsed_time(e1) / reps
+    N = cfg.n_tokens
+    fl_half = block_flops(N // 2, cfg.hidden, cfg.mlp_hidden, cfg.cond_dim)
+    work = (L - (last - first)) * sum(fl.values()) + (last - first) * sum(fl_half.values())
+    del st
+    log(f"token reduction step (layers {first}..{last - 1} on {N // 2} tokens): {ms:.2f} ms")
+    return {
+        "workload": f"the denoising step with layers {first}..{last - 1} on merged token pairs "
+                    f"({N // 2} tokens), the rest on {N}",
+        "ms_per_step": round(ms, 2), "speedup_vs_full_step": round(ms_full / ms, 3),
+        "time_saved_frac": round(1.0 - ms / ms_full, 4),
+        "tflop_per_step": round(work / 1e12, 2), "tflops": round(work / (ms * 1e-3) / 1e12, 1),
+    }
 
 
 def _time_block(cfg, tensors, x, c, reps=5):

@@ -100,7 +100,17 @@ typedef int32_t h3k_dtype;
  * after their bias by the 3D RoPE of h3k_rope_3d, fused into the QKV
  * projection's epilogue ([H3-review], note on native-256 RoPE).  Needs BF16
  * activations.  rope_half_spatial = 1 halves the spatial coordinates (the
- * page's rule for native-256 generation on 256 square canvases). */
+ * page's rule for native-256 generation on 256 square canvases).
+ * token_reduction_first, token_reduction_last: for h3k_dit_stack_forward, a
+ * layer range [first, last) run on merged tokens ([H3-review] knob list: video
+ * tokens paired two by two along rows to shorten the sequence in the middle
+ * layers): before block `first` tokens 2m and 2m+1 become their mean
+ * (h3k_token_merge; row neighbours when rows have an even length, 54 for the
+ * 864x480 latent), the blocks of the range run on n_tokens/2 tokens, and after
+ * block last-1 each token gets its own state from before the merge plus the
+ * change the range made to its pair (h3k_token_unmerge).  0, 0 (or any empty
+ * range) runs every block on all tokens.  Needs an even n_tokens and no RoPE;
+ * the workspace then also holds the merged stream. */
 typedef struct h3k_dit_config {
   int32_t n_tokens;
   int32_t hidden;
@@ -118,6 +128,8 @@ typedef struct h3k_dit_config {
   int32_t rope_height;
   int32_t rope_width;
   int32_t rope_half_spatial;
+  int32_t token_reduction_first;
+  int32_t token_reduction_last;
 } h3k_dit_config;
 
 /* Weights of one block; all device pointers.
@@ -150,7 +162,9 @@ typedef struct h3k_profiler h3k_profiler;
 #define H3K_K_UP         5  /* MLP up GEMM + GELU                        */
 #define H3K_K_DOWN       6  /* MLP down GEMM + gated residual            */
 #define H3K_K_ACT_QUANT  7  /* row quantiser of u (int8_fc2_rows only)   */
-#define H3K_K_COUNT      8
+#define H3K_K_TOKEN_MERGE   8  /* token reduction: merge (once per stack) */
+#define H3K_K_TOKEN_UNMERGE 9  /* token reduction: restore (once per stack) */
+#define H3K_K_COUNT      10
 
 /* Statistics of a forward call (host struct).  `profiler` is an input
  * (optional); the rest are outputs ([H3-memory], "verify it yourself": the
@@ -304,6 +318,22 @@ h3k_status h3k_linear_int8_groups(int64_t m, int64_t n, int64_t k, int32_t group
                                   const int8_t* wq, int64_t ldw, const float* w_scale, const void* bias,
                                   int32_t epilogue, const void* residual, int64_t ldr, const float* gate, void* y,
                                   int64_t ldy, hipStream_t stream);
+
+/* Token reduction ([H3-review] knob list): xm[m] = (x[2m] + x[2m+1]) / 2 for
+ * m < n_tokens/2, in fp32, rounded once to dtype.  x [n_tokens, ldx], xm
+ * [n_tokens/2, ldxm] in dtype (F32 or BF16); n_tokens even; D, ldx and ldxm
+ * multiples of 8.  xm must not overlap x. */
+h3k_status h3k_token_merge(h3k_dtype dtype, int64_t n_tokens, int64_t D, const void* x, int64_t ldx, void* xm,
+                           int64_t ldxm, hipStream_t stream);
+
+/* The restore after the reduced layers:
+ *   out[2m+j] = entry[2m+j] + (xm[m] - merge(entry)[m]),  j = 0, 1,
+ * with merge(entry) recomputed exactly as h3k_token_merge rounds it, so an xm
+ * equal to h3k_token_merge(entry) gives back entry bit for bit.  entry, out
+ * [n_tokens, ld] and xm [n_tokens/2, ldxm] in dtype; out may be entry itself
+ * (with ldo == ld_entry) but must not otherwise overlap the inputs. */
+h3k_status h3k_token_unmerge(h3k_dtype dtype, int64_t n_tokens, int64_t D, const void* entry, int64_t ld_entry,
+                             const void* xm, int64_t ldxm, void* out, int64_t ldo, hipStream_t stream);
 
 /* 3D rotary position embedding, in place, of x [n_tokens, ldx] BF16 whose first
  * `cols` columns are heads of head_dim (e.g. the q and k columns of a QKV

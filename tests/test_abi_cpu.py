@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_struct_sizes_match_header_layout():
-    assert ctypes.sizeof(B.DitConfig) == 64
+    assert ctypes.sizeof(B.DitConfig) == 72
     assert ctypes.sizeof(B.DitBlockWeights) == 14 * 8
     assert ctypes.sizeof(B.DitStats) == 40
     assert ctypes.sizeof(B.DitPlanInfo) == 9 * 8 * 2 + 9 * 4 * 2 + 8 * 5 + 8
@@ -103,6 +103,14 @@ def test_plan_c2_sizes_and_layout():
     assert on.peak_live_bytes == on.workspace_bytes
 
 
+def test_token_reduction_adds_the_merged_stream_to_the_workspace():
+    plain = h3k.h3k_dit_workspace_size(cfg_c2())
+    red = h3k.h3k_dit_workspace_size(cfg_c2(token_reduction=(12, 38)))
+    assert red - plain == ((22680 // 2) * 5120 * 2 + 255) // 256 * 256
+    info = h3k.h3k_dit_plan(cfg_c2(token_reduction=(12, 38)))
+    assert max(info.offset[t] + info.bytes[t] for t in range(9)) <= info.workspace_bytes - (red - plain)
+
+
 def test_env_switch_disables_aliasing(monkeypatch):
     monkeypatch.setenv("H3K_DISABLE_ACTIVATION_ALIAS", "1")
     info = h3k.h3k_dit_plan(cfg_c2(alias=True))
@@ -169,6 +177,12 @@ def test_reject_bad_shapes_and_dtypes():
     half_only = cfg_c2()
     half_only.rope_half_spatial = 1
     assert _block(half_only) == B.H3K_ERR_SHAPE
+    # token reduction: an inverted range, an odd token count, together with RoPE, a range past the blocks
+    assert _block(cfg_c2(token_reduction=(3, 2))) == B.H3K_ERR_SHAPE
+    assert _block(cfg_c2(n_tokens=22679, token_reduction=(0, 1))) == B.H3K_ERR_SHAPE
+    assert _block(cfg_c2(token_reduction=(0, 1), rope=(14, 30, 54, False))) == B.H3K_ERR_UNSUPPORTED
+    assert _block(cfg_c2(token_reduction=(0, 2))) == B.H3K_ERR_SHAPE       # one block only
+    assert "beyond" in h3k.last_error()
 
 
 def test_reject_int8_without_scales():
@@ -239,6 +253,13 @@ def test_reject_bad_kernel_level_arguments():
     assert lib.h3k_rope_3d(24, 128, 64, 2, 3, 5, 0, X, 128, None) == B.H3K_ERR_SHAPE
     assert lib.h3k_rope_3d(24, 128, 64, 2, 3, 4, 2, X, 128, None) == B.H3K_ERR_SHAPE
     assert lib.h3k_rope_3d(24, 128, 64, 2, 3, 4, 0, X + 8, 128, None) == B.H3K_ERR_ALIGN
+    # token merge / unmerge: odd token count, xm overlapping x, out partially overlapping entry
+    assert lib.h3k_token_merge(1, 7, 64, X, 64, Y, 64, None) == B.H3K_ERR_SHAPE
+    assert lib.h3k_token_merge(1, 8, 64, X, 64, X + 256, 64, None) == B.H3K_ERR_OVERLAP
+    assert lib.h3k_token_merge(1, 8, 60, X, 64, Y, 64, None) == B.H3K_ERR_SHAPE
+    assert lib.h3k_token_unmerge(1, 8, 64, X, 64, Y, 64, X + 128, 64, None) == B.H3K_ERR_OVERLAP
+    assert lib.h3k_token_unmerge(1, 8, 64, X, 64, Y, 64, Y + 64, 64, None) == B.H3K_ERR_OVERLAP
+    assert lib.h3k_token_unmerge(1, 8, 64, X, 64, Y, 64, X, 72, None) == B.H3K_ERR_SHAPE
 
 
 def _no_gpu():
@@ -257,4 +278,7 @@ def test_valid_arguments_without_device_report_hip_error():
     assert lib.h3k_quantize_weights_int8_groups(FAKE, 1, 4, 128, 64, FAKE + (1 << 32), FAKE + (2 << 32),
                                                 None) == B.H3K_ERR_HIP
     assert _block(cfg_c2(rope=(14, 30, 54, True))) == B.H3K_ERR_HIP
+    assert _block(cfg_c2(token_reduction=(0, 1))) == B.H3K_ERR_HIP
+    assert lib.h3k_token_merge(1, 8, 64, FAKE, 64, FAKE + (1 << 32), 64, None) == B.H3K_ERR_HIP
+    assert lib.h3k_token_unmerge(1, 8, 64, FAKE, 64, FAKE + (1 << 32), 64, FAKE, 64, None) == B.H3K_ERR_HIP
     assert lib.h3k_rope_3d(24, 128, 64, 2, 3, 4, 1, FAKE, 128, None) == B.H3K_ERR_HIP

@@ -264,6 +264,67 @@ def test_stack50_reduced_width_vs_oracle(R):
     assert torch.equal(one.view(torch.int16), single.view(torch.int16))
 
 
+@pytest.mark.parametrize("n_blocks,rng_", [(6, (2, 5)), (4, (0, 4)), (3, (0, 1)), (5, (4, 5))])
+def test_stack_token_reduction(R, n_blocks, rng_):
+    """Token reduction over a layer range against the oracle's stack with the
+    same range: merge before the first reduced block, the range on N/2
+    tokens, restore after it.  Aliasing on and off give the same bytes, and
+    the stack makes two dispatches more than without the range."""
+    import torch
+    from video_diffusion_transformer_adaln_amd import binding as B
+    shape = si.custom_shape("tokred", 976, 334, 2, 128, 640, "bf16", n_blocks=n_blocks)
+    flush(f"stack of {n_blocks} with token reduction {rng_}")
+    hx, hc = si.gen_activation(shape)
+    blocks_h = [si.gen_block_weights(shape, l, bias_std=0.05) for l in range(n_blocks)]
+    up = [upload_block(shape, hw) for hw in blocks_h]
+    xd, cd = dev(hx), dev(hc)
+    outs = []
+    for alias in (True, False):
+        cfg = config_for(shape, alias)
+        cfg.token_reduction_first, cfg.token_reduction_last = rng_
+        stack = R.DitStack(cfg, [u[0] for u in up])
+        stack.workspace.fill_(0xFF)
+        out = torch.full_like(xd, float("nan"))
+        st = B.DitStats()
+        stack.forward(xd, cd, out, stats=st)
+        torch.cuda.synchronize()
+        assert st.dispatches == 8 * n_blocks + 2
+        outs.append(out)
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+    got = to_np(outs[0])
+    ref = oracle.stack_forward(hx.values, hc.values, [u[1] for u in up], shape.n_heads, token_reduction=rng_)
+    err = rel_l2(got, ref)
+    plain = oracle.stack_forward(hx.values, hc.values, [u[1] for u in up], shape.n_heads)
+    flush(f"  rel_l2 = {err:.3e}; to the stack without reduction {rel_l2(got, plain):.3e}")
+    assert err < TOL
+    assert rel_l2(got, plain) > 3 * err                   # the reduction is visible in the output
+
+
+def test_stack50_reduced_width_token_reduction(R):
+    """50 reduced-width blocks with the middle half (blocks 12..37) on merged tokens."""
+    import torch
+    from video_diffusion_transformer_adaln_amd import binding as B
+    shape = si.custom_shape("stack50", 960, 512, 4, 128, 2048, "bf16", n_blocks=50)
+    flush("stack of 50 reduced-width blocks, token reduction 12..37")
+    hx, hc = si.gen_activation(shape)
+    blocks_h = [si.gen_block_weights(shape, l) for l in range(50)]
+    up = [upload_block(shape, hw) for hw in blocks_h]
+    cfg = config_for(shape)
+    cfg.token_reduction_first, cfg.token_reduction_last = 12, 38
+    stack = R.DitStack(cfg, [u[0] for u in up])
+    stack.workspace.fill_(0xFF)
+    xd, cd = dev(hx), dev(hc)
+    out = torch.empty_like(xd)
+    st = B.DitStats()
+    stack.forward(xd, cd, out, stats=st)
+    torch.cuda.synchronize()
+    assert st.dispatches == 8 * 50 + 2
+    ref = oracle.stack_forward(hx.values, hc.values, [u[1] for u in up], shape.n_heads, token_reduction=(12, 38))
+    err = rel_l2(to_np(out), ref)
+    flush(f"  rel_l2 after 50 blocks = {err:.3e}")
+    assert err < TOL
+
+
 @pytest.fixture(scope="module")
 def c3_stack(R):
     """50 blocks at the full 864x480x56-frame shape, weights drawn on the device

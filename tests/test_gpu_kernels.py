@@ -275,6 +275,37 @@ def test_linear_int8_groups(B, m, n, k, group, epi, full):
     assert rel_l2(got, ref) < BF16_TOL / 2
 
 
+# ------------------------------------------------------------------ token reduction
+
+@pytest.mark.parametrize("n,D,dtype", [(22680, 5120, "bf16"), (334, 256, "bf16"), (2, 8, "f32"), (1000, 64, "f32")])
+def test_token_merge_unmerge(B, n, D, dtype):
+    """merge: bit-exact (the fp32 mean of two bf16 or fp32 values, rounded
+    once); unmerge of the unchanged merge: the entry back bit for bit, also
+    in place; unmerge after a change: the oracle's restore."""
+    import torch
+    flush(f"token merge/unmerge n={n} D={D} {dtype}")
+    code = B.H3K_F32 if dtype == "f32" else B.H3K_BF16
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    e = _ht(_f32((n, D), 1.0, 870, "x"), dtype)
+    ed = dev(e)
+    xm = torch.full((n // 2, D), float("nan"), dtype=tdt, device="cuda")
+    B.h3k_token_merge(code, n, D, ed, D, xm, D)
+    torch.cuda.synchronize()
+    ref_m = si._finish(oracle.token_merge(e.values), dtype).values       # exact fp32 mean, rounded like the store
+    assert np.array_equal(to_np(xm), ref_m)
+    out = torch.full_like(ed, float("nan"))
+    B.h3k_token_unmerge(code, n, D, ed, D, xm, D, out, D)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ed)
+    delta = _ht(_f32((n // 2, D), 0.3, 871, "c"), dtype)
+    xm2 = (xm.float() + dev(delta).float()).to(tdt)
+    inplace = ed.clone()
+    B.h3k_token_unmerge(code, n, D, inplace, D, xm2, D, inplace, D)
+    torch.cuda.synchronize()
+    ref = oracle.token_unmerge(e.values, to_np(xm2))
+    assert rel_l2(to_np(inplace), ref) < (F32_TOL if dtype == "f32" else BF16_TOL / 2)
+
+
 # ------------------------------------------------------------------ 3D RoPE
 
 @pytest.mark.parametrize("grid,heads,hd,half", [((2, 3, 4), 2, 128, False), ((3, 3, 37), 4, 64, True),

@@ -21,7 +21,8 @@ STATUS_NAMES = {0: "OK", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_DTYPE", 4: "ERR_
                 6: "ERR_OVERLAP", 7: "ERR_UNSUPPORTED", 8: "ERR_HIP"}
 H3K_F32, H3K_BF16, H3K_INT8 = 0, 1, 2
 H3K_EPI_BIAS, H3K_EPI_GELU, H3K_EPI_GATED_RESIDUAL = 0, 1, 2
-KERNEL_KINDS = ("adaln", "ln_mod", "qkv", "attention", "out_proj", "mlp_up", "mlp_down", "act_quant")
+KERNEL_KINDS = ("adaln", "ln_mod", "qkv", "attention", "out_proj", "mlp_up", "mlp_down", "act_quant",
+                "token_merge", "token_unmerge")
 TENSOR_NAMES = ("mod", "h", "qkv", "o", "x1", "h2", "u", "uq", "us")
 
 c_int32, c_int64, c_uint64, c_float, c_void_p = (ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64,
@@ -33,7 +34,8 @@ class DitConfig(ctypes.Structure):
                 ("mlp_hidden", c_int32), ("cond_dim", c_int32), ("ln_eps", c_float), ("act_dtype", c_int32),
                 ("weight_dtype", c_int32), ("alias_activations", c_int32), ("int8_fc2_rows", c_int32),
                 ("int8_mlp_group", c_int32), ("rope_frames", c_int32), ("rope_height", c_int32),
-                ("rope_width", c_int32), ("rope_half_spatial", c_int32)]
+                ("rope_width", c_int32), ("rope_half_spatial", c_int32), ("token_reduction_first", c_int32),
+                ("token_reduction_last", c_int32)]
 
 
 class DitBlockWeights(ctypes.Structure):
@@ -94,6 +96,9 @@ _SIGNATURES = [
                                          c_void_p]),
     ("h3k_rope_3d", c_int32, [c_int64, c_int64, c_int32, c_int32, c_int32, c_int32, c_int32, c_void_p, c_int64,
                               c_void_p]),
+    ("h3k_token_merge", c_int32, [c_int32, c_int64, c_int64, c_void_p, c_int64, c_void_p, c_int64, c_void_p]),
+    ("h3k_token_unmerge", c_int32, [c_int32, c_int64, c_int64, c_void_p, c_int64, c_void_p, c_int64, c_void_p,
+                                    c_int64, c_void_p]),
     ("h3k_attention", c_int32, [c_int32, c_int32, c_int32, c_int32, c_void_p, c_int64, c_void_p, c_int64,
                                 c_void_p, c_int64, c_void_p, c_int64, c_void_p]),
     ("h3k_profiler_create", c_int32, [c_int32, ctypes.POINTER(c_void_p)]),
@@ -151,12 +156,14 @@ def _stream(stream) -> Optional[int]:
 def make_config(n_tokens: int, hidden: int, n_heads: int, head_dim: int, mlp_hidden: int, cond_dim: int,
                 act_dtype: int, weight_dtype: Optional[int] = None, alias: bool = True,
                 ln_eps: float = 1e-6, int8_fc2_rows: bool = False, int8_mlp_group: int = 0,
-                rope: Optional[tuple] = None) -> DitConfig:
-    """rope = (frames, height, width, half_spatial) turns on the 3D RoPE of q and k."""
+                rope: Optional[tuple] = None, token_reduction: Optional[tuple] = None) -> DitConfig:
+    """rope = (frames, height, width, half_spatial) turns on the 3D RoPE of q and k;
+    token_reduction = (first, last) runs layers first .. last-1 of a stack on merged tokens."""
     rt, rh, rw, rhalf = (0, 0, 0, 0) if rope is None else (rope[0], rope[1], rope[2], 1 if rope[3] else 0)
+    tf, tl = (0, 0) if token_reduction is None else token_reduction
     return DitConfig(n_tokens, hidden, n_heads, head_dim, mlp_hidden, cond_dim, ln_eps, act_dtype,
                      act_dtype if weight_dtype is None else weight_dtype, 1 if alias else 0,
-                     1 if int8_fc2_rows else 0, int8_mlp_group, rt, rh, rw, rhalf)
+                     1 if int8_fc2_rows else 0, int8_mlp_group, rt, rh, rw, rhalf, tf, tl)
 
 
 WEIGHT_FIELDS = ("w_ada", "b_ada", "w_qkv", "b_qkv", "s_qkv", "w_out", "b_out", "s_out",
@@ -238,6 +245,16 @@ def h3k_linear_int8_groups(m: int, n: int, k: int, group: int, x, ldx: int, wq, 
                            epilogue: int, residual, ldr: int, gate, y, ldy: int, stream=None) -> None:
     check(lib().h3k_linear_int8_groups(m, n, k, group, _ptr(x), ldx, _ptr(wq), ldw, _ptr(w_scale), _ptr(bias),
                                        epilogue, _ptr(residual), ldr, _ptr(gate), _ptr(y), ldy, _stream(stream)))
+
+
+def h3k_token_merge(dtype: int, n_tokens: int, D: int, x, ldx: int, xm, ldxm: int, stream=None) -> None:
+    check(lib().h3k_token_merge(dtype, n_tokens, D, _ptr(x), ldx, _ptr(xm), ldxm, _stream(stream)))
+
+
+def h3k_token_unmerge(dtype: int, n_tokens: int, D: int, entry, ld_entry: int, xm, ldxm: int, out, ldo: int,
+                      stream=None) -> None:
+    check(lib().h3k_token_unmerge(dtype, n_tokens, D, _ptr(entry), ld_entry, _ptr(xm), ldxm, _ptr(out), ldo,
+                                  _stream(stream)))
 
 
 def h3k_rope_3d(n_tokens: int, cols: int, head_dim: int, frames: int, height: int, width: int, half_spatial: bool,

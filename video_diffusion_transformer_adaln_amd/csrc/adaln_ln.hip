@@ -338,4 +338,94 @@ hipError_t launch_quantize_int8(DType dt, const void* w, int64_t rows, int64_t c
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Token reduction ([H3-review] knob list: video tokens paired two by two along
+// rows in the middle layers).  merge: xm[m] = (x[2m] + x[2m+1]) / 2, exact in
+// fp32 for bf16 inputs, one rounding at the store.  unmerge: out[2m+j] =
+// entry[2m+j] + (xm[m] - merge(entry)[m]), where merge(entry) is recomputed
+// with the very same operations, so its rounded value equals what the merge
+// stored and unchanged reduced layers give back `entry` bit for bit.  One
+// thread per 8 columns of a token pair; out may alias entry (each thread
+// reads its own pair before writing it).
+template <typename T> struct Vec8Store;
+template <> struct Vec8Store<bf16> {
+  static __device__ __forceinline__ void store(bf16* p, const float (&v)[8]) {
+    u32x4 r;
+    bf16* e = reinterpret_cast<bf16*>(&r);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) e[i] = static_cast<bf16>(v[i]);
+    *reinterpret_cast<u32x4*>(p) = r;
+  }
+};
+template <> struct Vec8Store<float> {
+  static __device__ __forceinline__ void store(float* p, const float (&v)[8]) {
+    *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
+    *reinterpret_cast<f32x4*>(p + 4) = f32x4{v[4], v[5], v[6], v[7]};
+  }
+};
+template <typename T> __device__ __forceinline__ float round_to(float v) { return static_cast<float>(static_cast<T>(v)); }
+
+template <typename T>
+__global__ __launch_bounds__(256) void token_merge_kernel(const T* __restrict__ x, int64_t ldx, T* __restrict__ xm,
+                                                          int64_t ldm, int64_t pairs, int64_t oct) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= pairs * oct) return;
+  const int64_t m = idx / oct;
+  const int64_t c = (idx - m * oct) * 8;
+  float a[8], b[8], r[8];
+  Vec8<T>::load(x + (2 * m) * ldx + c, a);
+  Vec8<T>::load(x + (2 * m + 1) * ldx + c, b);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (a[i] + b[i]) * 0.5f;
+  Vec8Store<T>::store(xm + m * ldm + c, r);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void token_unmerge_kernel(const T* entry, int64_t lde, const T* __restrict__ xm,
+                                                            int64_t ldm, T* out, int64_t ldo, int64_t pairs,
+                                                            int64_t oct) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= pairs * oct) return;
+  const int64_t m = idx / oct;
+  const int64_t c = (idx - m * oct) * 8;
+  float a[8], b[8], y[8];
+  Vec8<T>::load(entry + (2 * m) * lde + c, a);
+  Vec8<T>::load(entry + (2 * m + 1) * lde + c, b);
+  Vec8<T>::load(xm + m * ldm + c, y);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float d = y[i] - round_to<T>((a[i] + b[i]) * 0.5f);
+    a[i] += d;
+    b[i] += d;
+  }
+  Vec8Store<T>::store(out + (2 * m) * ldo + c, a);
+  Vec8Store<T>::store(out + (2 * m + 1) * ldo + c, b);
+}
+
+hipError_t launch_token_merge(DType dt, int64_t n, int64_t D, const void* x, int64_t ldx, void* xm, int64_t ldm,
+                              hipStream_t stream) {
+  const int64_t pairs = n / 2, oct = D / 8;
+  if (pairs == 0) return hipSuccess;
+  const dim3 grid((unsigned)((pairs * oct + 255) / 256));
+  if (dt == kBF16)
+    token_merge_kernel<bf16><<<grid, dim3(256), 0, stream>>>((const bf16*)x, ldx, (bf16*)xm, ldm, pairs, oct);
+  else
+    token_merge_kernel<float><<<grid, dim3(256), 0, stream>>>((const float*)x, ldx, (float*)xm, ldm, pairs, oct);
+  return hipGetLastError();
+}
+
+hipError_t launch_token_unmerge(DType dt, int64_t n, int64_t D, const void* entry, int64_t lde, const void* xm,
+                                int64_t ldm, void* out, int64_t ldo, hipStream_t stream) {
+  const int64_t pairs = n / 2, oct = D / 8;
+  if (pairs == 0) return hipSuccess;
+  const dim3 grid((unsigned)((pairs * oct + 255) / 256));
+  if (dt == kBF16)
+    token_unmerge_kernel<bf16><<<grid, dim3(256), 0, stream>>>((const bf16*)entry, lde, (const bf16*)xm, ldm,
+                                                               (bf16*)out, ldo, pairs, oct);
+  else
+    token_unmerge_kernel<float><<<grid, dim3(256), 0, stream>>>((const float*)entry, lde, (const float*)xm, ldm,
+                                                                (float*)out, ldo, pairs, oct);
+  return hipGetLastError();
+}
+
 }  // namespace h3k

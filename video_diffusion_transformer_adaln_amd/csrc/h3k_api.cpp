@@ -124,6 +124,13 @@ h3k_status validate_config(const h3k_dit_config* c) {
   } else if (c->rope_half_spatial) {
     return fail(H3K_ERR_SHAPE, "rope_half_spatial without a RoPE grid");
   }
+  const int tf = c->token_reduction_first, tl = c->token_reduction_last;
+  if (tf < 0 || tl < 0 || (tl != 0 && tl < tf))
+    return fail(H3K_ERR_SHAPE, "token reduction range [%d, %d) is not a layer range", tf, tl);
+  if (tl > tf) {
+    if (c->n_tokens % 2) return fail(H3K_ERR_SHAPE, "token reduction needs an even token count (got %d)", c->n_tokens);
+    if (rope) return fail(H3K_ERR_UNSUPPORTED, "token reduction and RoPE cannot be combined");
+  }
   const int64_t eb = esize(c->act_dtype);
   const int64_t rows = (int64_t)c->n_tokens + 256;
   const int64_t widest = std::max<int64_t>(2 * (int64_t)c->hidden, c->mlp_hidden);
@@ -147,6 +154,13 @@ bool alias_enabled(const h3k_dit_config* c) {
 // whose live ranges intersect its own, in a fixed order; without aliasing,
 // each gets its own region.  The plan depends only on the config, so it is
 // deterministic, and no kernel reads workspace bytes it did not write first.
+// Token reduction keeps the merged stream ([N/2, D] in act_dtype) after the
+// block's tensors, at workspace_bytes - reduction_bytes.
+uint64_t reduction_bytes(const h3k_dit_config* c) {
+  if (c->token_reduction_last <= c->token_reduction_first) return 0;
+  return align_up((uint64_t)(c->n_tokens / 2) * c->hidden * esize(c->act_dtype), kAlign);
+}
+
 void make_plan(const h3k_dit_config* c, bool alias, h3k_dit_plan_info* P) {
   std::memset(P, 0, sizeof(*P));
   const uint64_t N = c->n_tokens, D = c->hidden, F = c->mlp_hidden, eb = esize(c->act_dtype);
@@ -202,9 +216,10 @@ void make_plan(const h3k_dit_config* c, bool alias, h3k_dit_plan_info* P) {
   }
   P->qkv_vt_offset = off[H3K_T_QKV] + qk_bytes;
   P->vt_pitch = (int64_t)vt_pitch;
-  P->workspace_bytes = ws;
-  P->peak_live_bytes = peak;
-  P->unaliased_bytes = unaliased;
+  const uint64_t red = reduction_bytes(c);
+  P->workspace_bytes = ws + red;
+  P->peak_live_bytes = peak + red;
+  P->unaliased_bytes = unaliased + red;
   P->alias_activations = alias ? 1 : 0;
 }
 
@@ -405,15 +420,48 @@ h3k_status forward(const h3k_dit_config* cfg, const h3k_dit_block_weights* block
                    h3k_dit_stats* stats) {
   h3k_dit_plan_info plan;
   H3K_TRY(validate_forward(cfg, blocks, n_blocks, x, c, out, workspace, workspace_bytes, &plan));
+  if (cfg->token_reduction_last > cfg->token_reduction_first && cfg->token_reduction_last > n_blocks)
+    return fail(H3K_ERR_SHAPE, "token reduction range [%d, %d) beyond the %d blocks", cfg->token_reduction_first,
+                cfg->token_reduction_last, n_blocks);
   H3K_TRY(check_device());
+  const int tf = cfg->token_reduction_first, tl = cfg->token_reduction_last;
+  const bool reduce = tl > tf;
   Recorder rec(stats ? stats->profiler : nullptr, stream);
-  for (int l = 0; l < n_blocks; ++l)
-    H3K_TRY(run_block(cfg, &plan, &blocks[l], l == 0 ? x : out, c, out, static_cast<char*>(workspace), stream, rec));
+  char* ws = static_cast<char*>(workspace);
+  // the reduced layers run on the merged stream, in place, with the plan of a
+  // config of N/2 tokens (it fits in the full plan's part of the workspace)
+  h3k_dit_config half = *cfg;
+  half.n_tokens = cfg->n_tokens / 2;
+  half.token_reduction_first = half.token_reduction_last = 0;
+  h3k_dit_plan_info plan_half;
+  void* xm = nullptr;
+  if (reduce) {
+    make_plan(&half, plan.alias_activations != 0, &plan_half);
+    xm = ws + plan.workspace_bytes - reduction_bytes(cfg);
+  }
+  const DType act = (DType)cfg->act_dtype;
+  const int64_t N = cfg->n_tokens, D = cfg->hidden;
+  for (int l = 0; l < n_blocks; ++l) {
+    const void* src = l == 0 ? x : out;
+    if (reduce && l == tf) {
+      H3K_TRY(launched(launch_token_merge(act, N, D, src, D, xm, D, stream), "token merge"));
+      rec.done(H3K_K_TOKEN_MERGE);
+    }
+    if (reduce && l >= tf && l < tl)
+      H3K_TRY(run_block(&half, &plan_half, &blocks[l], xm, c, xm, ws, stream, rec));
+    else
+      H3K_TRY(run_block(cfg, &plan, &blocks[l], src, c, out, ws, stream, rec));
+    if (reduce && l == tl - 1) {                // entry state: x if the range starts at block 0, else out
+      H3K_TRY(launched(launch_token_unmerge(act, N, D, tf == 0 ? x : out, D, xm, D, out, D, stream),
+                       "token unmerge"));
+      rec.done(H3K_K_TOKEN_UNMERGE);
+    }
+  }
   if (stats) {
     stats->workspace_bytes = plan.workspace_bytes;
     stats->peak_live_bytes = plan.peak_live_bytes;
     stats->unaliased_bytes = plan.unaliased_bytes;
-    stats->dispatches = (cfg->int8_fc2_rows ? 9 : 8) * n_blocks;
+    stats->dispatches = (cfg->int8_fc2_rows ? 9 : 8) * n_blocks + (reduce ? 2 : 0);
     stats->alias_activations = plan.alias_activations;
   }
   return H3K_OK;
@@ -651,6 +699,44 @@ h3k_status h3k_linear_int8_groups(int64_t m, int64_t n, int64_t k, int32_t group
   L.epi = (Epilogue)epilogue; L.residual = residual; L.ldr = ldr; L.gate = gate;
   L.y = y; L.ldy = ldy; L.split_col = n;
   return launched(launch_linear(L, stream), "int8 group linear");
+}
+
+h3k_status h3k_token_merge(h3k_dtype dtype, int64_t n_tokens, int64_t D, const void* x, int64_t ldx, void* xm,
+                           int64_t ldxm, hipStream_t stream) {
+  if (dtype != H3K_F32 && dtype != H3K_BF16) return fail(H3K_ERR_DTYPE, "dtype must be F32 or BF16");
+  if (n_tokens < 0 || n_tokens % 2 || n_tokens > 0x7fffffff || D < 8 || D % 8 || ldx < D || ldxm < D || ldx % 8 ||
+      ldxm % 8)
+    return fail(H3K_ERR_SHAPE, "need an even token count, D and the pitches multiples of 8");
+  if (!x || !xm) return fail(H3K_ERR_NULL, "x and xm must be non-NULL");
+  if (!aligned(x, 16) || !aligned(xm, 16)) return fail(H3K_ERR_ALIGN, "x and xm must be 16-byte aligned");
+  const int64_t e = esize(dtype);
+  if (overlaps(rng(xm, span(n_tokens / 2, D, ldxm, e), "xm"), rng(x, span(n_tokens, D, ldx, e), "x")))
+    return fail(H3K_ERR_OVERLAP, "xm overlaps x");
+  if (n_tokens == 0) return H3K_OK;
+  H3K_TRY(check_device());
+  return launched(launch_token_merge((DType)dtype, n_tokens, D, x, ldx, xm, ldxm, stream), "token merge");
+}
+
+h3k_status h3k_token_unmerge(h3k_dtype dtype, int64_t n_tokens, int64_t D, const void* entry, int64_t ld_entry,
+                             const void* xm, int64_t ldxm, void* out, int64_t ldo, hipStream_t stream) {
+  if (dtype != H3K_F32 && dtype != H3K_BF16) return fail(H3K_ERR_DTYPE, "dtype must be F32 or BF16");
+  if (n_tokens < 0 || n_tokens % 2 || n_tokens > 0x7fffffff || D < 8 || D % 8 || ld_entry < D || ldxm < D || ldo < D ||
+      ld_entry % 8 || ldxm % 8 || ldo % 8)
+    return fail(H3K_ERR_SHAPE, "need an even token count, D and the pitches multiples of 8");
+  if (!entry || !xm || !out) return fail(H3K_ERR_NULL, "entry, xm and out must be non-NULL");
+  if (!aligned(entry, 16) || !aligned(xm, 16) || !aligned(out, 16))
+    return fail(H3K_ERR_ALIGN, "entry, xm and out must be 16-byte aligned");
+  const int64_t e = esize(dtype);
+  const Range ro = rng(out, span(n_tokens, D, ldo, e), "out");
+  if (overlaps(ro, rng(xm, span(n_tokens / 2, D, ldxm, e), "xm")))
+    return fail(H3K_ERR_OVERLAP, "out overlaps xm");
+  if (out != entry && overlaps(ro, rng(entry, span(n_tokens, D, ld_entry, e), "entry")))
+    return fail(H3K_ERR_OVERLAP, "out partially overlaps entry (it may only be entry itself)");
+  if (out == entry && ldo != ld_entry) return fail(H3K_ERR_SHAPE, "in place needs ldo == ld_entry");
+  if (n_tokens == 0) return H3K_OK;
+  H3K_TRY(check_device());
+  return launched(launch_token_unmerge((DType)dtype, n_tokens, D, entry, ld_entry, xm, ldxm, out, ldo, stream),
+                  "token unmerge");
 }
 
 h3k_status h3k_rope_3d(int64_t n_tokens, int64_t cols, int32_t head_dim, int32_t frames, int32_t height,

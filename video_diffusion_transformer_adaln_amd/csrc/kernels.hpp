@@ -49,6 +49,13 @@ struct AttentionArgs {
 };
 hipError_t launch_attention(const AttentionArgs& a, hipStream_t stream);
 
+// token reduction: xm[m] = (x[2m] + x[2m+1]) / 2 for m < n/2 (D a multiple of 8)
+hipError_t launch_token_merge(DType dt, int64_t n, int64_t D, const void* x, int64_t ldx, void* xm, int64_t ldm,
+                              hipStream_t stream);
+// out[2m+j] = entry[2m+j] + xm[m] - merge(entry)[m]; out may alias entry
+hipError_t launch_token_unmerge(DType dt, int64_t n, int64_t D, const void* entry, int64_t lde, const void* xm,
+                                int64_t ldm, void* out, int64_t ldo, hipStream_t stream);
+
 // in place: x[n, cols] (bf16, row pitch ldx), heads of head_dim consecutive
 // columns, rotated by the 3D RoPE of each row's token over the (T, H, W) grid
 hipError_t launch_rope(int64_t n, int64_t cols, int head_dim, int height, int width, float spatial, void* x,
