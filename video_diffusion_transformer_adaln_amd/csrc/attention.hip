@@ -29,9 +29,10 @@
 //     scaled by exp2(m_old - m_new), and the exponentials are recomputed.
 //     The result is the usual online-softmax recurrence with the reference
 //     updated only when a probability would otherwise exceed 2^8;
-//   * two tiles per workgroup barrier: K tiles arrive with direct-to-LDS
-//     loads, V^T tiles through registers (keys beyond N are zeroed there),
-//     both in rings of four 32-key slots; a pass over tiles (t0, t0+1) loads
+//   * two tiles per workgroup barrier: K tiles and full V^T tiles arrive
+//     with direct-to-LDS loads, the V^T tiles of the last passes through
+//     registers (keys beyond N are zeroed there), all in rings of four
+//     32-key slots; a pass over tiles (t0, t0+1) loads
 //     K_{t0+3}, K_{t0+4}, V_{t0+1}, V_{t0+2} into the slots the previous pass
 //     read, then waits for them and meets the other waves.  The barrier
 //     carries no fence: each wave waits for its own loads first.  Keys
@@ -135,13 +136,13 @@ __global__ __launch_bounds__(NW * 64) void attention_bf16_kernel(AttnParams p) {
     lds_dma16(rk, kbuf + (t & 3) * KBYTES + wave * 1024, kdma_off, (uint32_t)tt * ktile_bytes);
   };
 
-  // ---- V^T tiles: one 16-byte load per lane: plane lane/32, row
-  // wave*16 + (lane%32)/2, half lane&1 (keys 16 plane + 8 half .. +8)
+  // ---- V^T tiles of the last passes, through registers: one 16-byte load
+  // per lane: plane lane/32, row wave*16 + (lane%32)/2, half lane&1 (keys
+  // 16 plane + 8 half .. +8)
   const int st_pl = lane >> 5, st_row = wave * 16 + ((lane & 31) >> 1), st_h = lane & 1;
   const __amdgpu_buffer_rsrc_t rvt = rsrc(p.vt, (uint32_t)((uint64_t)p.n_heads * HD * p.ldvt * 2));
   const uint32_t vld_off = ((uint32_t)(head * HD + st_row) * (uint32_t)p.ldvt + st_pl * 16 + st_h * 8) * 2u;
   const int vst_off = st_pl * VPL + st_row * 32 + ((st_h ^ hswap(st_row)) << 4);
-  auto vload_full = [&](int t) { return bload16(rvt, vld_off, (uint32_t)t * (KT * 2)); };
   auto vload_masked = [&](int t) {             // zero for keys >= N
     const int key0 = t * KT + st_pl * 16 + st_h * 8;
     u32x4 v = {0, 0, 0, 0};
@@ -155,6 +156,15 @@ __global__ __launch_bounds__(NW * 64) void attention_bf16_kernel(AttnParams p) {
     return v;
   };
   auto vstore = [&](int t, const u32x4& v) { *reinterpret_cast<u32x4*>(vbuf + (t & 3) * VBYTES + vst_off) = v; };
+  // full V^T tiles: direct-to-LDS, one 1 KiB instruction per wave: wave ->
+  // plane wave / (HD/32), rows 32 (wave % (HD/32)) + lane/2, physical half
+  // lane&1 (holding logical half (lane&1) ^ hswap(row))
+  constexpr int RB = HD / 32;
+  const int vd_row = 32 * (wave % RB) + (lane >> 1);
+  const uint32_t vdma_off = ((uint32_t)(head * HD + vd_row) * (uint32_t)p.ldvt + (wave / RB) * 16 +
+                             (((lane & 1) ^ hswap(vd_row)) * 8)) * 2u;
+  const int vdma_dst = (wave / RB) * VPL + 32 * (wave % RB) * 32;
+  auto vdma = [&](int t) { lds_dma16(rvt, vbuf + (t & 3) * VBYTES + vdma_dst, vdma_off, (uint32_t)t * (KT * 2)); };
 
   // ---- fragment addresses.  K: row kperm(l32), logical chunk 2ks+h;
   // V^T: row l32 (+ db*32), plane = 16-key step.
@@ -240,8 +250,22 @@ __global__ __launch_bounds__(NW * 64) void attention_bf16_kernel(AttnParams p) {
     bf16x8 fr[NMF];
     fr[0] = frag(0);
     fr[1] = frag(1);
-    float pe[16];
+    // The exponential chain is skewed by one: chunk i takes the scaled score
+    // of element r + 1, the exponential of element r (scaled in the previous
+    // chunk) and sums element r - 1 (exponentiated in the previous chunk), so
+    // no instruction waits on a result from its own chunk.
+    float xa[17], pe[16];
     float ls0 = 0.f, ls1 = 0.f;
+    auto sum_cvt = [&](int q) {
+      if (q & 1) {
+        ls1 += pe[q];
+        P[U][q >> 3][(q & 7) - 1] = static_cast<bf16>(pe[q - 1]);
+        P[U][q >> 3][q & 7] = static_cast<bf16>(pe[q]);
+      } else {
+        ls0 += pe[q];
+      }
+    };
+    xa[0] = fmaf(S[U][0], sc, -m_ref);
 #pragma unroll
     for (int i = 0; i < NMF; ++i) {
       if (i + 2 < NMF) fr[i + 2] = frag(i + 2);
@@ -254,17 +278,13 @@ __global__ __launch_bounds__(NW * 64) void attention_bf16_kernel(AttnParams p) {
 #pragma unroll
       for (int e = 0; e < EPM; ++e) {
         const int r = i * EPM + e;
-        pe[r] = __builtin_amdgcn_exp2f(fmaf(S[U][r], sc, -m_ref));
-        if (r & 1) {
-          ls1 += pe[r];
-          P[U][r >> 3][(r & 7) - 1] = static_cast<bf16>(pe[r - 1]);
-          P[U][r >> 3][r & 7] = static_cast<bf16>(pe[r]);
-        } else {
-          ls0 += pe[r];
-        }
+        if (r + 1 < 16) xa[r + 1] = fmaf(S[U][r + 1], sc, -m_ref);
+        pe[r] = __builtin_amdgcn_exp2f(xa[r]);
+        if (r >= 1) sum_cvt(r - 1);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    sum_cvt(15);
     float ls = ls0 + ls1;
     if (__any(!(ls <= kLazyBound))) ls = redo(S[U], P[U]);
     l_run += ls;
@@ -290,8 +310,8 @@ __global__ __launch_bounds__(NW * 64) void attention_bf16_kernel(AttnParams p) {
     kdma(t0 + 4);
     u32x4 va = {0, 0, 0, 0}, vb = {0, 0, 0, 0};
     if constexpr (!TAIL) {
-      va = vload_full(t0 + 1);
-      vb = vload_full(t0 + 2);
+      vdma(t0 + 1);
+      vdma(t0 + 2);
     } else {
       if (t0 + 1 < T) va = vload_masked(t0 + 1);
       if (t0 + 2 < T) vb = vload_masked(t0 + 2);
@@ -299,8 +319,10 @@ __global__ __launch_bounds__(NW * 64) void attention_bf16_kernel(AttnParams p) {
     step(t0, C1{}, K1{}, V0{}, TAIL && t0 == T - 1);
     if (!TAIL || t0 + 1 < T) step(t0 + 1, C0{}, K2{}, V1{}, TAIL && t0 + 1 == T - 1);
     wait_vmcnt<0>();
-    vstore(t0 + 1, va);
-    vstore(t0 + 2, vb);
+    if constexpr (TAIL) {
+      vstore(t0 + 1, va);
+      vstore(t0 + 2, vb);
+    }
     wait_lgkm0();
     wg_barrier();
   };
