@@ -201,6 +201,7 @@ def main():
         extra = extra_blocks(blocks[0], x, c)
         if L >= 4:
             extra["token_reduction_step"] = token_reduction_step(cfg, blocks, x, c, ms_step, fl, L)
+        extra["sp8_share_block"] = sp_share(blocks[0])
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -419,6 +420,82 @@ def extra_blocks(b0, x, c):
         "ms_per_block": round(ms1, 3), "tflops": round(fl1 / (ms1 * 1e-3) / 1e12, 1)}
     log(f"6144-token block: {ms1:.2f} ms")
     return res
+
+
+def sp_share(b0, P=8, reps=5):
+    """One GPU's share of a block under P-way sequence parallelism (the
+    split the design describes; the two all-to-alls around attention are
+    not built): LayerNorm + modulation and the four projection GEMMs on
+    N/P tokens, attention for H/P heads over all N tokens.  Each kernel is
+    timed through its own entry point on synthetic inputs of those shapes."""
+    import torch
+    import seeded_inputs as si
+    from video_diffusion_transformer_adaln_amd import binding as B
+    sh = si.C3
+    N, D, F, H, d = sh.n_tokens, sh.hidden, sh.mlp_hidden, sh.n_heads, sh.head_dim
+    M, Hs = N // P, H // P
+    bf = torch.bfloat16
+    g = lambda shp, std, sub: si.torch_device_normal(shp, std, si.BASE_SEED, 700_000 + sub, "cuda", bf)
+    x = g((M, D), 1.0, 0)
+    shift = si.torch_device_normal((D,), 0.1, si.BASE_SEED, 700_001, "cuda", torch.float32)
+    scale = si.torch_device_normal((D,), 0.1, si.BASE_SEED, 700_002, "cuda", torch.float32)
+    gate = si.torch_device_normal((D,), 0.1, si.BASE_SEED, 700_003, "cuda", torch.float32)
+    h = torch.empty(M, D, dtype=bf, device="cuda")
+    qk = torch.empty(M, 2 * D, dtype=bf, device="cuda")
+    ldvt = (M + 7) // 8 * 8
+    vt = torch.empty(D, ldvt, dtype=bf, device="cuda")
+    o = g((M, D), 1.0, 4)
+    y = torch.empty(M, D, dtype=bf, device="cuda")
+    u = torch.empty(M, F, dtype=bf, device="cuda")
+    # attention operands of H/P heads over all N tokens (after the all-to-all)
+    Ds = Hs * d
+    qa, ka = g((N, Ds), 0.6, 5), g((N, Ds), 0.6, 6)
+    vta = g((Ds, N), 1.0, 7)
+    oa = torch.empty(N, Ds, dtype=bf, device="cuda")
+    E = B.H3K_BF16
+    calls = {
+        "ln_mod": (None, lambda: B.h3k_ln_modulate(E, M, D, 1e-6, x, D, shift, scale, h, D)),
+        "qkv": (2.0 * M * D * 3 * D, lambda: B.h3k_linear(E, E, M, 3 * D, D, h, D, b0["w_qkv"], D, None, None,
+                                                            B.H3K_EPI_BIAS, None, 0, None, qk, 2 * D, vt, ldvt, 2 * D)),
+        "attention": (4.0 * N * N * Ds, lambda: B.h3k_attention(E, N, Hs, d, qa, Ds, ka, Ds, vta, N, oa, Ds)),
+        "out_proj": (2.0 * M * D * D, lambda: B.h3k_linear(E, E, M, D, D, o, D, b0["w_out"], D, None, None,
+                                                            B.H3K_EPI_GATED_RESIDUAL, x, D, gate, y, D)),
+        "mlp_up": (2.0 * M * D * F, lambda: B.h3k_linear(E, E, M, F, D, h, D, b0["w_up"], D, None, None,
+                                                          B.H3K_EPI_GELU, None, 0, None, u, F)),
+        "mlp_down": (2.0 * M * F * D, lambda: B.h3k_linear(E, E, M, D, F, u, F, b0["w_down"], F, None, None,
+                                                            B.H3K_EPI_GATED_RESIDUAL, x, D, gate, y, D)),
+    }
+    res, total = {}, 0.0
+    for name, (flops, fn) in calls.items():
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        n_calls = 2 if name == "ln_mod" else 1
+        total += n_calls * ms
+        e = {"avg_ms": round(ms, 4)}
+        if flops is not None:
+            e["tflops"] = round(flops / (ms * 1e-3) / 1e12, 1)
+        else:
+            e["gbs"] = round(ln_bytes(M, D) / (ms * 1e-3) / 1e9, 1)
+        res[name] = e
+    for t in (y, u, oa):
+        if not torch.isfinite(t.float()).all():
+            log("non-finite output in the per-GPU share")
+            sys.exit(3)
+    fl = sum(v for k, v in block_flops(M, D, F, D).items() if k not in ("adaln", "attention")) + calls["attention"][0]
+    log(f"one GPU's share of an {P}-way sequence-parallel block: {total:.3f} ms")
+    return {
+        "workload": f"one GPU's share of a block under {P}-way sequence parallelism: LayerNorm + modulation (x2) "
+                    f"and the QKV / out / MLP GEMMs on {M} tokens, attention for {Hs} of {H} heads over all "
+                    f"{N} tokens; all-to-alls not built",
+        "ms_per_block_share": round(total, 3), "tflops": round(fl / (total * 1e-3) / 1e12, 1), "kernels": res,
+    }
 
 
 def cpu_baseline(step_flops, L):

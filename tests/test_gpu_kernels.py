@@ -117,6 +117,8 @@ GEMM_CASES = [
     (22680, 5120, 13824, 2, "bf16", False, None, False),    # MLP down
     (22680, 13824, 5120, 1, "bf16", True, None, False),     # MLP up, int8 weights
     (22680, 15360, 5120, 0, "bf16", True, 10240, False),    # QKV, int8 weights
+    (2835, 15360, 5120, 0, "bf16", False, 10240, False),    # QKV on one GPU's 1/8 share of the tokens
+    (2835, 5120, 13824, 2, "bf16", False, None, False),     # MLP down on the same share
 ]
 
 
@@ -345,6 +347,7 @@ ATTN_CASES = [
     (6144, 24, 128, "bf16", False),
     (22680, 40, 128, "bf16", False),
     (9000, 40, 64, "bf16", False),
+    (22680, 5, 128, "bf16", False),    # one GPU's 5 of 40 heads over all tokens
 ]
 
 
