@@ -11,11 +11,13 @@
 //    rows: measured on MI355X, half-line (64-byte) row pieces halve the
 //    vector-memory return rate, and one k-tile of loads in flight per
 //    workgroup cannot cover the loaded L2/Infinity-Cache latency.
-//  * int8-weight path (W8A16): the weight tile is read as int8 (half the
-//    bytes) into registers, widened to bf16 exactly while it is stored into
-//    double-buffered LDS, multiplied on the bf16 MFMA, and the
+//  * int8-weight path (W8A16), same ring: the activation tiles arrive by
+//    direct-to-LDS loads, the weight tile is read as int8 (half the bytes)
+//    into registers one k-tile ahead, widened to bf16 exactly while it is
+//    stored into its slot, and multiplied on the bf16 MFMA.  The
 //    per-output-channel scale is applied to the fp32 accumulator in the
-//    epilogue (it factors out of the k-sum).
+//    epilogue (it factors out of the k-sum); group-wise scales are applied
+//    while widening (each 16-weight chunk lies in one group).
 //  * fp32 path: a plain LDS-tiled SIMT kernel for the small fp32 workload.
 //
 // Epilogues (fused, fp32 math, one rounding at the store): bias; bias + GELU
@@ -49,7 +51,6 @@ struct GemmParams {
 };
 
 constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int kGroupM = 8;
 
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -90,24 +91,6 @@ __device__ __forceinline__ void i8x16_to_bf16_scaled(const u32x4& src, float sc,
 // return zero, which masks the ragged edges of the token and feature axes.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-}
-
-// LDS tile of one operand: 4 "planes", one per 16-wide k-step of the 64-wide
-// k-tile; plane = [256 rows][32 bytes] (two 16-byte halves = the two lane
-// halves of a 32x32x16 MFMA fragment).  The halves of a row are swapped when
-// bit 2 xor bit 3 of the row is set, so that 8 (or 16) lanes reading 8 (16)
-// consecutive rows hit distinct banks; as row offsets of a wave's fragments
-// are multiples of 32, each lane's fragment address is one per-lane base plus
-// compile-time offsets.
-constexpr int kPlaneBytes = 256 * 32;
-constexpr int kTileBytes = 4 * kPlaneBytes;   // 32 KiB per operand per buffer
-
-__device__ __forceinline__ int half_swap(int r) { return ((r >> 2) ^ (r >> 3)) & 1; }
-__device__ __forceinline__ int plane_off(int ks, int r, int h) {
-  return ks * kPlaneBytes + r * 32 + ((h ^ half_swap(r)) << 4);
 }
 
 // Fused epilogue of one wave's 64x128 accumulator sub-tile.
@@ -192,156 +175,9 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, const f32x16 (&a
   }
 }
 
-// Register-staged kernel; launched for int8 weights (the widening happens
-// between the global load and the LDS store).  GRP: group-wise scales, applied
-// while widening (each 16-weight chunk lies in one group), so the epilogue
-// takes no channel scale.
-template <int EPI, bool W8, bool GRP = false>
-__global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmParams p) {
-  __shared__ __attribute__((aligned(16))) char lds[4 * kTileBytes];   // X0 W0 X1 W1
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-
-  // ---- tile order: XCD-contiguous ranges, then groups of kGroupM m-tiles
-  const int nblk = p.tiles_m * p.tiles_n;
-  const int lin = xcd_remap(blockIdx.x, nblk);
-  const int per_group = kGroupM * p.tiles_n;
-  const int group = lin / per_group;
-  const int first_m = group * kGroupM;
-  const int gm = min(p.tiles_m - first_m, kGroupM);
-  const int in_group = lin - group * per_group;
-  const int tile_m = first_m + in_group % gm;
-  const int tile_n = in_group / gm;
-  const int tok0 = tile_m * BM, feat0 = tile_n * BN;
-  const bool trans = (int64_t)feat0 >= p.split_col;
-  const int KT = p.k / BK;
-
-  // ---- global -> register staging (8 waves).  bf16 tiles: per instruction a
-  // wave covers 8 full 128-byte rows; lane -> plane l/16, row (l%16)/2, half
-  // l%2.  int8 weight tile: a wave covers 16 rows of 64 bytes; lane -> plane
-  // l/16, row l%16.
-  constexpr int XL = 4;                 // bf16 chunks per thread per operand
-  constexpr int WL = W8 ? 2 : 4;
-  u32x4 rx[XL];
-  u32x4 rw[WL];
-  const int ld_ks = lane >> 4;
-  const int ld_rsub = (lane & 15) >> 1, ld_h = lane & 1;
-  const __amdgpu_buffer_rsrc_t rsx = make_rsrc(p.x, (uint32_t)((uint64_t)p.m * p.ldx * 2));
-  const __amdgpu_buffer_rsrc_t rsw = make_rsrc(p.w, (uint32_t)((uint64_t)p.n * p.ldw * (W8 ? 1 : 2)));   // activations bf16
-  const uint32_t x_off0 = (uint32_t)((tok0 + wave * 8 + ld_rsub) * (uint32_t)p.ldx * 2u + (ld_ks * 16 + ld_h * 8) * 2);
-  const uint32_t x_step = 64u * (uint32_t)p.ldx * 2u;
-  const uint32_t w_off0 = W8 ? (uint32_t)((feat0 + wave * 16 + (lane & 15)) * (uint32_t)p.ldw + ld_ks * 16)
-                             : (uint32_t)((feat0 + wave * 8 + ld_rsub) * (uint32_t)p.ldw * 2u + (ld_ks * 16 + ld_h * 8) * 2);
-  const uint32_t w_step = W8 ? 128u * (uint32_t)p.ldw : 64u * (uint32_t)p.ldw * 2u;
-
-  // group scales: lane's weight row i of the tile and its 16-weight chunk's group
-  float rs[WL];
-  const int n_groups = GRP ? (p.k >> p.group_shift) : 0;
-  const __amdgpu_buffer_rsrc_t rss = make_rsrc(p.w_scale, GRP ? (uint32_t)((uint64_t)p.n * n_groups * 4) : 0u);
-  const uint32_t s_off0 = GRP ? (uint32_t)(feat0 + wave * 16 + (lane & 15)) * (uint32_t)n_groups * 4u : 0u;
-  const uint32_t s_step = GRP ? 128u * (uint32_t)n_groups * 4u : 0u;
-
-  auto gload = [&](int kt) {
-    const uint32_t kx = (uint32_t)kt * BK * 2u;
-#pragma unroll
-    for (int i = 0; i < XL; ++i) rx[i] = buf_load16(rsx, x_off0 + i * x_step + kx);
-    const uint32_t kw = (uint32_t)kt * BK * (W8 ? 1u : 2u);
-#pragma unroll
-    for (int i = 0; i < WL; ++i) rw[i] = buf_load16(rsw, w_off0 + i * w_step + kw);
-    if constexpr (GRP) {
-      const uint32_t g4 = (uint32_t)((kt * BK + ld_ks * 16) >> p.group_shift) * 4u;
-#pragma unroll
-      for (int i = 0; i < WL; ++i)
-        rs[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rss, s_off0 + i * s_step + g4, 0, 0));
-    }
-  };
-
-  auto lstore = [&](char* sx, char* sw) {
-#pragma unroll
-    for (int i = 0; i < XL; ++i) {
-      const int r = i * 64 + wave * 8 + ld_rsub;
-      *reinterpret_cast<u32x4*>(sx + plane_off(ld_ks, r, ld_h)) = rx[i];
-    }
-    if constexpr (W8) {
-#pragma unroll
-      for (int i = 0; i < WL; ++i) {
-        const int r = i * 128 + wave * 16 + (lane & 15);
-        u32x4 lo, hi;
-        if constexpr (GRP) i8x16_to_bf16_scaled(rw[i], rs[i], lo, hi);
-        else i8x16_to_bf16(rw[i], lo, hi);
-        *reinterpret_cast<u32x4*>(sw + plane_off(ld_ks, r, 0)) = lo;
-        *reinterpret_cast<u32x4*>(sw + plane_off(ld_ks, r, 1)) = hi;
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < WL; ++i) {
-        const int r = i * 64 + wave * 8 + ld_rsub;
-        *reinterpret_cast<u32x4*>(sw + plane_off(ld_ks, r, ld_h)) = rw[i];
-      }
-    }
-  };
-
-  // Each wave computes 64 A-rows x 128 B-rows: 2 x 4 tiles of 32x32.  A is
-  // the weight (row-major output) or the activation (transposed output).
-  f32x16 acc[2][4];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
-
-  const int a_row0 = (wave & 3) * 64;
-  const int b_row0 = (wave >> 2) * 128;
-  const int frag = (lane & 31) * 32 + (((lane >> 5) ^ half_swap(lane & 31)) << 4);
-  const int a_off = (trans ? 0 : kTileBytes) + a_row0 * 32 + frag;
-  const int b_off = (trans ? kTileBytes : 0) + b_row0 * 32 + frag;
-
-  auto load_frags = [&](const char* base, int ks, bf16x8 (&fa)[2], bf16x8 (&fb)[4]) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-      fa[i] = *reinterpret_cast<const bf16x8*>(base + a_off + ks * kPlaneBytes + i * 1024);
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      fb[j] = *reinterpret_cast<const bf16x8*>(base + b_off + ks * kPlaneBytes + j * 1024);
-  };
-  auto mfmas = [&](const bf16x8 (&fa)[2], const bf16x8 (&fb)[4]) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(fa[i], fb[j], acc[i][j]);
-  };
-
-  bf16x8 f0a[2], f0b[4], f1a[2], f1b[4];
-  char* const buf0 = lds;
-  char* const buf1 = lds + 2 * kTileBytes;
-  gload(0);
-  lstore(buf0, buf0 + kTileBytes);
-  __syncthreads();
-  if (KT > 1) gload(1);
-  load_frags(buf0, 0, f0a, f0b);
-  for (int kt = 0; kt < KT; ++kt) {
-    const char* cur = (kt & 1) ? buf1 : buf0;
-    char* nxt = (kt & 1) ? buf0 : buf1;
-    load_frags(cur, 1, f1a, f1b);
-    mfmas(f0a, f0b);
-    __builtin_amdgcn_sched_barrier(0);
-    load_frags(cur, 2, f0a, f0b);
-    if (kt + 1 < KT) lstore(nxt, nxt + kTileBytes);
-    mfmas(f1a, f1b);
-    __builtin_amdgcn_sched_barrier(0);
-    load_frags(cur, 3, f1a, f1b);
-    if (kt + 2 < KT) gload(kt + 2);
-    mfmas(f0a, f0b);
-    __builtin_amdgcn_sched_barrier(0);
-    mfmas(f1a, f1b);
-    __syncthreads();
-    if (kt + 1 < KT) load_frags(nxt, 0, f0a, f0b);
-  }
-
-  store_tile<EPI, W8 && !GRP>(p, acc, a_row0, b_row0, tok0, feat0, trans, lane);
-}
-
 // ---------------------------------------------------------------------------
-// bf16-weight kernel with direct-to-LDS loads (buffer_load ... lds): no
-// staging registers and no LDS store instructions.  An operand's k-tile is
+// Ring kernel.  bf16 operands arrive by direct-to-LDS loads (buffer_load ...
+// lds): no staging registers and no LDS store instructions.  An operand's k-tile is
 // [256 rows][128 B], 16-byte chunk c of row r stored at chunk c ^ rswz(r)
 // (fragment reads of 8 or 16 consecutive rows hit distinct banks).  The
 // swizzle is applied on the source side: lane l of a load writes row
@@ -359,8 +195,9 @@ constexpr int kSlots = 5;          // 160 KiB
 // on one XCD then cover 2 m-tiles x 16 n-tiles); measured best of 1..32
 constexpr int kRingGroupM = 2;
 
-template <int EPI, bool I8>
+template <int EPI, bool I8, bool W8 = false, bool GRP = false>
 __global__ __launch_bounds__(512) void gemm_ring_kernel(GemmParams p) {
+  static_assert(!(I8 && W8), "int8 activations take the int8 MFMA path");
   __shared__ __attribute__((aligned(1024))) char lds[kSlots * kSlot];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -384,7 +221,7 @@ __global__ __launch_bounds__(512) void gemm_ring_kernel(GemmParams p) {
   // 1: weights) of k-tile q>>1, in slot q%5.  Loads: instruction j (0..3)
   // of wave w covers rows (8 j + w) * 8 .. +8; rswz(lrow + 64 j) == rswz(lrow).
   const __amdgpu_buffer_rsrc_t rsx = make_rsrc(p.x, (uint32_t)((uint64_t)p.m * p.ldx * ES));
-  const __amdgpu_buffer_rsrc_t rsw = make_rsrc(p.w, (uint32_t)((uint64_t)p.n * p.ldw * ES));
+  const __amdgpu_buffer_rsrc_t rsw = make_rsrc(p.w, (uint32_t)((uint64_t)p.n * p.ldw * (W8 ? 1 : ES)));
   const int lrow = wave * 8 + (lane >> 3);
   const uint32_t c16 = (uint32_t)(((lane & 7) ^ rswz(lrow)) * 16);
   const uint32_t xo0 = (uint32_t)(tok0 + lrow) * (uint32_t)p.ldx * ES + c16;
@@ -406,6 +243,51 @@ __global__ __launch_bounds__(512) void gemm_ring_kernel(GemmParams p) {
       lds_dma16(r, st + j * 8192, o0 + j * step);
     }
   };
+
+  // int8 weights (W8): global -> registers, widened to bf16 (times the
+  // group scale with GRP) on the way into the weight slot, which then holds
+  // the same bf16 layout as a direct-to-LDS slot.  Load j (0, 1) of a lane:
+  // tile row w8_row + 16 j, int8 chunk lane%4 (16 values = logical
+  // bf16 chunks 2 (lane%4) and 2 (lane%4) + 1).  Lane group g = lane/4 takes
+  // row (g&1) + 8 ((g>>1)&1) + 2 (g>>2) of the wave's 16, so that the four
+  // rows of 16 consecutive lanes (two per 256-byte bank window) have
+  // swizzles of opposite parity and their stores hit distinct banks.
+  const int w8_g = lane >> 2;
+  const int w8_row = wave * 32 + (w8_g & 1) + (((w8_g >> 1) & 1) << 3) + ((w8_g >> 2) << 1), w8_c = lane & 3;
+  const uint32_t w8_off = (uint32_t)(feat0 + w8_row) * (uint32_t)p.ldw + w8_c * 16;
+  const uint32_t w8_step = 16u * (uint32_t)p.ldw;
+  const int n_groups = GRP ? (p.k >> p.group_shift) : 0;
+  const __amdgpu_buffer_rsrc_t rss = make_rsrc(p.w_scale, GRP ? (uint32_t)((uint64_t)p.n * n_groups * 4) : 0u);
+  const uint32_t s_off = GRP ? (uint32_t)(feat0 + w8_row) * (uint32_t)n_groups * 4u : 0u;
+  const uint32_t s_step = GRP ? 16u * (uint32_t)n_groups * 4u : 0u;
+  u32x4 wq[2];
+  float wsc[2];
+  auto wload = [&](int q) {
+    int kt = q >> 1;
+    kt = kt < KT ? kt : KT - 1;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) wq[j] = __builtin_amdgcn_raw_buffer_load_b128(rsw, w8_off + j * w8_step + kt * 64u, 0, 0);
+    if constexpr (GRP) {
+      const uint32_t g4 = (uint32_t)((kt * 64 + w8_c * 16) >> p.group_shift) * 4u;
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        wsc[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rss, s_off + j * s_step + g4, 0, 0));
+    }
+  };
+  auto wput = [&](int q) {
+    char* st = lds + (q % kSlots) * kSlot;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int r = w8_row + 16 * j;
+      u32x4 lo, hi;
+      if constexpr (GRP) i8x16_to_bf16_scaled(wq[j], wsc[j], lo, hi);
+      else i8x16_to_bf16(wq[j], lo, hi);
+      *reinterpret_cast<u32x4*>(st + r * 128 + (((2 * w8_c) ^ rswz(r)) << 4)) = lo;
+      *reinterpret_cast<u32x4*>(st + r * 128 + (((2 * w8_c + 1) ^ rswz(r)) << 4)) = hi;
+    }
+  };
+  // loads per k-tile after the weights' register loads, and before them
+  constexpr int kW8Loads = GRP ? 4 : 2;
 
   using Acc = typename std::conditional<I8, i32x16, f32x16>::type;
   Acc acc[2][4];
@@ -451,6 +333,46 @@ __global__ __launch_bounds__(512) void gemm_ring_kernel(GemmParams p) {
       }
   };
 
+  bf16x8 f0a[2], f0b[4], f1a[2], f1b[4];
+  if constexpr (W8) {
+    // prologue: k-tile 0 in LDS; the weights of k-tile 1 in registers and
+    // the activations of k-tile 1 (position 2) in flight
+    issue(0, 0);
+    issue(0, 1);
+    wload(1);
+    wait_vmcnt<0>();
+    wput(1);
+    issue(2, 0);
+    wload(3);
+    issue(2, 1);
+    wait_lgkm0();
+    wg_barrier();
+    for (int t = 0; t < KT; ++t) {
+      // the weights of t+1 (position 2t+3) go from registers to the slot of
+      // the activations of t-1, the activations of t+2 (2t+4) load into the
+      // slot of the weights of t-1: both slots' readers passed the last barrier
+      wait_vmcnt<2>();   // weights of t+1 in registers; the second half of the activations of t+1 may fly
+      wput(2 * t + 3);
+      load_frags(t, 0, f0a, f0b);
+      load_frags(t, 1, f1a, f1b);
+      issue(2 * t + 4, 0);
+      mfmas(f0a, f0b);
+      __builtin_amdgcn_sched_barrier(0);
+      wload(2 * t + 5);
+      load_frags(t, 2, f0a, f0b);
+      issue(2 * t + 4, 1);
+      mfmas(f1a, f1b);
+      __builtin_amdgcn_sched_barrier(0);
+      load_frags(t, 3, f1a, f1b);
+      mfmas(f0a, f0b);
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas(f1a, f1b);
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vmcnt<kW8Loads + 4>();   // activations of t+1 landed; this k-tile's loads may fly
+      wait_lgkm0();                 // this wave's widened weights of t+1 are in LDS
+      wg_barrier();
+    }
+  } else {
   // prologue: positions 0, 1, 2 in flight; 0 and 1 (k-tile 0) must be complete
   for (int q = 0; q < 3; ++q) {
     issue(q, 0);
@@ -458,7 +380,6 @@ __global__ __launch_bounds__(512) void gemm_ring_kernel(GemmParams p) {
   }
   wait_vmcnt<4>();
   wg_barrier();
-  bf16x8 f0a[2], f0b[4], f1a[2], f1b[4];
   for (int t = 0; t < KT; ++t) {
     // positions 2t+3 (weights of t+1) and 2t+4 (activations of t+2) go to the
     // slots of k-tile t-1, whose readers all passed the last barrier
@@ -481,6 +402,7 @@ __global__ __launch_bounds__(512) void gemm_ring_kernel(GemmParams p) {
     wait_vmcnt<4>();   // own loads of k-tile t+1 have landed; activations of t+2 may fly
     wg_barrier();
   }
+  }
   wait_vmcnt<0>();
   if constexpr (I8) {
     // int32 -> fp32 (one rounding), times the activation row scale; the
@@ -498,7 +420,7 @@ __global__ __launch_bounds__(512) void gemm_ring_kernel(GemmParams p) {
     }
     store_tile<EPI, true>(p, accf, a_row0, b_row0, tok0, feat0, false, lane);
   } else {
-    store_tile<EPI, false>(p, acc, a_row0, b_row0, tok0, feat0, trans, lane);
+    store_tile<EPI, W8 && !GRP>(p, acc, a_row0, b_row0, tok0, feat0, trans, lane);
   }
 }
 
@@ -590,9 +512,9 @@ static void launch_bf16(const LinearArgs& a, hipStream_t stream) {
     gemm_ring_kernel<EPI, true><<<dim3(p.tiles_m * p.tiles_n), dim3(512), 0, stream>>>(p);
   else if constexpr (W8) {
     if (a.group > 0)
-      gemm_bf16_kernel<EPI, true, true><<<dim3(p.tiles_m * p.tiles_n), dim3(512), 0, stream>>>(p);
+      gemm_ring_kernel<EPI, false, true, true><<<dim3(p.tiles_m * p.tiles_n), dim3(512), 0, stream>>>(p);
     else
-      gemm_bf16_kernel<EPI, true><<<dim3(p.tiles_m * p.tiles_n), dim3(512), 0, stream>>>(p);
+      gemm_ring_kernel<EPI, false, true><<<dim3(p.tiles_m * p.tiles_n), dim3(512), 0, stream>>>(p);
   }
   else
     gemm_ring_kernel<EPI, false><<<dim3(p.tiles_m * p.tiles_n), dim3(512), 0, stream>>>(p);
