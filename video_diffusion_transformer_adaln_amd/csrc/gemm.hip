@@ -93,12 +93,51 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-// Fused epilogue of one wave's 64x128 accumulator sub-tile.
+// Epilogue math, fp32, one bf16 rounding at the store.  Accumulator register
+// r of lane l in 32x32 tile (i, j) of a wave's 64x128 sub-tile:
+//   A-row = a_row0 + i*32 + 8*(r/4) + 4*(l/32) + r%4, B-row = b_row0 + j*32 + l%32.
+// Row-major output, first step: features f..f+3 of token t, channel scale and bias.
+template <bool W8>
+__device__ __forceinline__ void scale_bias4(const GemmParams& p, float (&v)[4], int f) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    if constexpr (W8) v[e] *= p.w_scale[f + e];
+    if (p.bias) v[e] += static_cast<float>(p.bias[f + e]);
+  }
+}
+// Second step: the activation, rotation or gated residual.
+template <int EPI>
+__device__ __forceinline__ void epilogue4(const GemmParams& p, float (&v)[4], int t, int f) {
+  if constexpr (EPI == kEpiGelu) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = gelu_tanh(v[e]);
+  }
+  if constexpr (EPI == kEpiBiasRope) {   // features f..f+3 are the pairs (j, j+1), (j+2, j+3) of a head
+    const int j = f % p.rope.head_dim;
+    rope_rotate(v[0], v[1], t, j, p.rope);
+    rope_rotate(v[2], v[3], t, j + 2, p.rope);
+  }
+  if constexpr (EPI == kEpiGatedResidual) {
+    const u32x2 rr = *reinterpret_cast<const u32x2*>(p.residual + (int64_t)t * p.ldr + f);
+    const bf16* re = reinterpret_cast<const bf16*>(&rr);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = static_cast<float>(re[e]) + p.gate[f + e] * v[e];
+  }
+}
+__device__ __forceinline__ u32x2 pack4(const float (&v)[4]) {
+  u32x2 out;
+  bf16* oe = reinterpret_cast<bf16*>(&out);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) oe[e] = static_cast<bf16>(v[e]);
+  return out;
+}
+
+// Fused epilogue of one wave's 64x128 accumulator sub-tile, stored straight
+// from the accumulator layout (8-byte pieces, 32 rows per instruction); used
+// for the tile that straddles split_col.
 template <int EPI, bool W8>
 __device__ __forceinline__ void store_tile(const GemmParams& p, const f32x16 (&acc)[2][4], int a_row0, int b_row0,
                                            int tok0, int feat0, bool trans, int lane) {
-  // ---- epilogue.  Accumulator register r of lane l in tile (i, j):
-  //      A-row = a_row0 + i*32 + 8*(r/4) + 4*(l/32) + r%4, B-row = b_row0 + j*32 + l%32.
   const float* wsc = p.w_scale;
   if (!trans) {
 #pragma unroll
@@ -112,36 +151,15 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, const f32x16 (&a
           if (t >= p.m || f >= p.n) continue;
           float v[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            v[e] = acc[i][j][4 * g + e];
-            if constexpr (W8) v[e] *= wsc[f + e];
-            if (p.bias) v[e] += static_cast<float>(p.bias[f + e]);
-          }
+          for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e];
+          scale_bias4<W8>(p, v, f);
           if ((int64_t)f >= p.split_col) {   // straddling tile: transposed part, bias only
 #pragma unroll
             for (int e = 0; e < 4; ++e) p.yt[(int64_t)(f + e - p.split_col) * p.ldyt + t] = static_cast<bf16>(v[e]);
             continue;
           }
-          if constexpr (EPI == kEpiGelu) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = gelu_tanh(v[e]);
-          }
-          if constexpr (EPI == kEpiBiasRope) {   // features f..f+3 are the pairs (j, j+1), (j+2, j+3) of a head
-            const int j = f % p.rope.head_dim;
-            rope_rotate(v[0], v[1], t, j, p.rope);
-            rope_rotate(v[2], v[3], t, j + 2, p.rope);
-          }
-          if constexpr (EPI == kEpiGatedResidual) {
-            const u32x2 rr = *reinterpret_cast<const u32x2*>(p.residual + (int64_t)t * p.ldr + f);
-            const bf16* re = reinterpret_cast<const bf16*>(&rr);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = static_cast<float>(re[e]) + p.gate[f + e] * v[e];
-          }
-          u32x2 out;
-          bf16* oe = reinterpret_cast<bf16*>(&out);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) oe[e] = static_cast<bf16>(v[e]);
-          *reinterpret_cast<u32x2*>(p.y + (int64_t)t * p.ldy + f) = out;
+          epilogue4<EPI>(p, v, t, f);
+          *reinterpret_cast<u32x2*>(p.y + (int64_t)t * p.ldy + f) = pack4(v);
         }
   } else {
 #pragma unroll
@@ -172,6 +190,75 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, const f32x16 (&a
               if (t0 + e < p.m) dst[e] = oe[e];
           }
         }
+  }
+}
+
+// The same epilogue for a tile that lies wholly on one side of split_col,
+// staged through LDS so that the global stores are whole 128-byte row
+// segments.  The wave's sub-tile, finished in registers as above, goes to
+// `stage` (16 KiB of the idle operand ring) as [128 B-rows][64 A-values] bf16,
+// 16-byte chunk c of row r at chunk c ^ ((r ^ r/8) % 8); each lane then stores
+// 16 bytes, 8 lanes per row.  Row-major output: B-rows are tokens and the 64
+// A-values features; transposed output (V^T): B-rows are features and the
+// A-values tokens.
+template <int EPI, bool W8>
+__device__ __forceinline__ void store_tile_staged(const GemmParams& p, const f32x16 (&acc)[2][4], int a_row0,
+                                                  int b_row0, int tok0, int feat0, bool trans, int lane,
+                                                  char* stage) {
+  auto swz = [](int r) { return (r ^ (r >> 3)) & 7; };
+  const int half = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int brow = j * 32 + (lane & 31);
+        const int ai = i * 32 + 8 * g + 4 * half;
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e];
+        if (!trans) {
+          const int f = feat0 + a_row0 + ai, t = tok0 + b_row0 + brow;
+          if (t < p.m && f < p.n) {
+            scale_bias4<W8>(p, v, f);
+            epilogue4<EPI>(p, v, t, f);
+          }
+        } else {
+          const int f = feat0 + b_row0 + brow;
+          if (f < p.n) {
+            const float sc = W8 ? p.w_scale[f] : 1.0f;
+            const float bb = p.bias ? static_cast<float>(p.bias[f]) : 0.0f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              if constexpr (W8) v[e] *= sc;
+              v[e] += bb;
+            }
+          }
+        }
+        *reinterpret_cast<u32x2*>(stage + brow * 128 + (((ai >> 3) ^ swz(brow)) << 4) + half * 8) = pack4(v);
+      }
+#pragma unroll
+  for (int s8 = 0; s8 < 16; ++s8) {
+    const int row = s8 * 8 + (lane >> 3), c = lane & 7;
+    const u32x4 val = *reinterpret_cast<const u32x4*>(stage + row * 128 + ((c ^ swz(row)) << 4));
+    if (!trans) {
+      const int t = tok0 + b_row0 + row, f = feat0 + a_row0 + 8 * c;
+      if (t < p.m && f < p.n) *reinterpret_cast<u32x4*>(p.y + (int64_t)t * p.ldy + f) = val;
+    } else {
+      const int f = feat0 + b_row0 + row, t0 = tok0 + a_row0 + 8 * c;
+      if (f < p.n && t0 < p.m) {
+        bf16* dst = p.yt + (int64_t)(f - p.split_col) * p.ldyt + t0;
+        if (t0 + 7 < p.m) {
+          *reinterpret_cast<u32x4*>(dst) = val;
+        } else {
+          const bf16* ve = reinterpret_cast<const bf16*>(&val);
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (t0 + e < p.m) dst[e] = ve[e];
+        }
+      }
+    }
   }
 }
 
@@ -404,6 +491,13 @@ __global__ __launch_bounds__(512) void gemm_ring_kernel(GemmParams p) {
   }
   }
   wait_vmcnt<0>();
+  // a tile wholly on one side of split_col (features >= n are never stored)
+  // stages its epilogue in the ring:
+  // every wave's loads (including the clamped re-loads past the last k-tile)
+  // have landed once all waves pass this barrier
+  const bool staged = trans || (int64_t)feat0 + BN <= p.split_col || p.split_col >= p.n;
+  if (staged) wg_barrier();
+  char* const stage = lds + wave * 16384;
   if constexpr (I8) {
     // int32 -> fp32 (one rounding), times the activation row scale; the
     // weight channel scale, bias and epilogue follow in store_tile.  The
@@ -418,9 +512,11 @@ __global__ __launch_bounds__(512) void gemm_ring_kernel(GemmParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) accf[i][j][r] = static_cast<float>(acc[i][j][r]) * xs;
     }
-    store_tile<EPI, true>(p, accf, a_row0, b_row0, tok0, feat0, false, lane);
+    if (staged) store_tile_staged<EPI, true>(p, accf, a_row0, b_row0, tok0, feat0, false, lane, stage);
+    else store_tile<EPI, true>(p, accf, a_row0, b_row0, tok0, feat0, false, lane);
   } else {
-    store_tile<EPI, W8 && !GRP>(p, acc, a_row0, b_row0, tok0, feat0, trans, lane);
+    if (staged) store_tile_staged<EPI, W8 && !GRP>(p, acc, a_row0, b_row0, tok0, feat0, trans, lane, stage);
+    else store_tile<EPI, W8 && !GRP>(p, acc, a_row0, b_row0, tok0, feat0, trans, lane);
   }
 }
 
