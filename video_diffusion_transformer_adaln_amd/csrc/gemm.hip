@@ -262,6 +262,57 @@ __device__ __forceinline__ void store_tile_staged(const GemmParams& p, const f32
   }
 }
 
+// Gated residual, row-major: the residual is read in the same coalesced
+// pattern as the output is written, so the wave stages z = acc (x scale) +
+// bias in fp32 instead, in two rounds of 64 B-rows (16 KiB each): row r holds
+// 64 fp32 values, 16-byte chunk c at chunk c ^ (r % 16).  Each lane then
+// finishes 8 consecutive features of one token: y = r + g * z, one rounding.
+template <bool W8>
+__device__ __forceinline__ void store_tile_staged_residual(const GemmParams& p, const f32x16 (&acc)[2][4],
+                                                           int a_row0, int b_row0, int tok0, int feat0, int lane,
+                                                           char* stage) {
+  const int half = lane >> 5;
+#pragma unroll
+  for (int rnd = 0; rnd < 2; ++rnd) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int j = 2 * rnd + jj;
+          const int brow = jj * 32 + (lane & 31);
+          const int ai = i * 32 + 8 * g + 4 * half;
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e];
+          const int f = feat0 + a_row0 + ai, t = tok0 + b_row0 + j * 32 + (lane & 31);
+          if (t < p.m && f < p.n) scale_bias4<W8>(p, v, f);
+          f32x4 z = {v[0], v[1], v[2], v[3]};
+          *reinterpret_cast<f32x4*>(stage + brow * 256 + (((ai >> 2) ^ (brow & 15)) << 4)) = z;
+        }
+#pragma unroll
+    for (int s8 = 0; s8 < 8; ++s8) {
+      const int row = s8 * 8 + (lane >> 3), c = lane & 7;
+      const int t = tok0 + b_row0 + rnd * 64 + row, f = feat0 + a_row0 + 8 * c;
+      const f32x4 z0 = *reinterpret_cast<const f32x4*>(stage + row * 256 + (((2 * c) ^ (row & 15)) << 4));
+      const f32x4 z1 = *reinterpret_cast<const f32x4*>(stage + row * 256 + (((2 * c + 1) ^ (row & 15)) << 4));
+      if (t < p.m && f < p.n) {
+        const u32x4 rr = *reinterpret_cast<const u32x4*>(p.residual + (int64_t)t * p.ldr + f);
+        const bf16* re = reinterpret_cast<const bf16*>(&rr);
+        u32x4 out;
+        bf16* oe = reinterpret_cast<bf16*>(&out);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          oe[e] = static_cast<bf16>(static_cast<float>(re[e]) + p.gate[f + e] * z0[e]);
+          oe[4 + e] = static_cast<bf16>(static_cast<float>(re[4 + e]) + p.gate[f + 4 + e] * z1[e]);
+        }
+        *reinterpret_cast<u32x4*>(p.y + (int64_t)t * p.ldy + f) = out;
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Ring kernel.  bf16 operands arrive by direct-to-LDS loads (buffer_load ...
 // lds): no staging registers and no LDS store instructions.  An operand's k-tile is
@@ -512,10 +563,14 @@ __global__ __launch_bounds__(512) void gemm_ring_kernel(GemmParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) accf[i][j][r] = static_cast<float>(acc[i][j][r]) * xs;
     }
-    if (staged) store_tile_staged<EPI, true>(p, accf, a_row0, b_row0, tok0, feat0, false, lane, stage);
+    if (staged && EPI == kEpiGatedResidual)
+      store_tile_staged_residual<true>(p, accf, a_row0, b_row0, tok0, feat0, lane, stage);
+    else if (staged) store_tile_staged<EPI, true>(p, accf, a_row0, b_row0, tok0, feat0, false, lane, stage);
     else store_tile<EPI, true>(p, accf, a_row0, b_row0, tok0, feat0, false, lane);
   } else {
-    if (staged) store_tile_staged<EPI, W8 && !GRP>(p, acc, a_row0, b_row0, tok0, feat0, trans, lane, stage);
+    if (staged && EPI == kEpiGatedResidual && !trans)
+      store_tile_staged_residual<W8 && !GRP>(p, acc, a_row0, b_row0, tok0, feat0, lane, stage);
+    else if (staged) store_tile_staged<EPI, W8 && !GRP>(p, acc, a_row0, b_row0, tok0, feat0, trans, lane, stage);
     else store_tile<EPI, W8 && !GRP>(p, acc, a_row0, b_row0, tok0, feat0, trans, lane);
   }
 }
