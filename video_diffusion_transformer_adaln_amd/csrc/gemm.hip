@@ -424,7 +424,7 @@ __global__ __launch_bounds__(512) void gemm_ring_kernel(GemmParams p) {
       *reinterpret_cast<u32x4*>(st + r * 128 + (((2 * w8_c + 1) ^ rswz(r)) << 4)) = hi;
     }
   };
-  // loads per k-tile after the weights' register loads, and before them
+  // vector-memory loads of one wload (two int8 chunks, and their two group scales)
   constexpr int kW8Loads = GRP ? 4 : 2;
 
   using Acc = typename std::conditional<I8, i32x16, f32x16>::type;
