@@ -196,66 +196,71 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, const f32x16 (&a
 // The same epilogue for a tile that lies wholly on one side of split_col,
 // staged through LDS so that the global stores are whole 128-byte row
 // segments.  The wave's sub-tile, finished in registers as above, goes to
-// `stage` (16 KiB of the idle operand ring) as [128 B-rows][64 A-values] bf16,
-// 16-byte chunk c of row r at chunk c ^ ((r ^ r/8) % 8); each lane then stores
-// 16 bytes, 8 lanes per row.  Row-major output: B-rows are tokens and the 64
-// A-values features; transposed output (V^T): B-rows are features and the
-// A-values tokens.
-template <int EPI, bool W8>
+// `stage` (idle operand-ring LDS) in rounds of JR 32-row blocks, each as
+// [32 JR B-rows][64 A-values] bf16 (4 JR KiB), 16-byte chunk c of row r at
+// chunk c ^ ((r ^ r/8) % 8); each lane then stores 16 bytes, 8 lanes per
+// row.  Row-major output: B-rows are tokens and the 64 A-values features;
+// transposed output (V^T): B-rows are features and the A-values tokens.
+template <int EPI, bool W8, int JR>
 __device__ __forceinline__ void store_tile_staged(const GemmParams& p, const f32x16 (&acc)[2][4], int a_row0,
                                                   int b_row0, int tok0, int feat0, bool trans, int lane,
                                                   char* stage) {
   auto swz = [](int r) { return (r ^ (r >> 3)) & 7; };
   const int half = lane >> 5;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int rnd = 0; rnd < 4 / JR; ++rnd) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int brow = j * 32 + (lane & 31);
-        const int ai = i * 32 + 8 * g + 4 * half;
-        float v[4];
+      for (int jj = 0; jj < JR; ++jj)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e];
-        if (!trans) {
-          const int f = feat0 + a_row0 + ai, t = tok0 + b_row0 + brow;
-          if (t < p.m && f < p.n) {
-            scale_bias4<W8>(p, v, f);
-            epilogue4<EPI>(p, v, t, f);
-          }
-        } else {
-          const int f = feat0 + b_row0 + brow;
-          if (f < p.n) {
-            const float sc = W8 ? p.w_scale[f] : 1.0f;
-            const float bb = p.bias ? static_cast<float>(p.bias[f]) : 0.0f;
+        for (int g = 0; g < 4; ++g) {
+          const int j = rnd * JR + jj;
+          const int brow = jj * 32 + (lane & 31);
+          const int ai = i * 32 + 8 * g + 4 * half;
+          float v[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              if constexpr (W8) v[e] *= sc;
-              v[e] += bb;
+          for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e];
+          if (!trans) {
+            const int f = feat0 + a_row0 + ai, t = tok0 + b_row0 + j * 32 + (lane & 31);
+            if (t < p.m && f < p.n) {
+              scale_bias4<W8>(p, v, f);
+              epilogue4<EPI>(p, v, t, f);
+            }
+          } else {
+            const int f = feat0 + b_row0 + j * 32 + (lane & 31);
+            if (f < p.n) {
+              const float sc = W8 ? p.w_scale[f] : 1.0f;
+              const float bb = p.bias ? static_cast<float>(p.bias[f]) : 0.0f;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                if constexpr (W8) v[e] *= sc;
+                v[e] += bb;
+              }
             }
           }
+          *reinterpret_cast<u32x2*>(stage + brow * 128 + (((ai >> 3) ^ swz(brow)) << 4) + half * 8) = pack4(v);
         }
-        *reinterpret_cast<u32x2*>(stage + brow * 128 + (((ai >> 3) ^ swz(brow)) << 4) + half * 8) = pack4(v);
-      }
 #pragma unroll
-  for (int s8 = 0; s8 < 16; ++s8) {
-    const int row = s8 * 8 + (lane >> 3), c = lane & 7;
-    const u32x4 val = *reinterpret_cast<const u32x4*>(stage + row * 128 + ((c ^ swz(row)) << 4));
-    if (!trans) {
-      const int t = tok0 + b_row0 + row, f = feat0 + a_row0 + 8 * c;
-      if (t < p.m && f < p.n) *reinterpret_cast<u32x4*>(p.y + (int64_t)t * p.ldy + f) = val;
-    } else {
-      const int f = feat0 + b_row0 + row, t0 = tok0 + a_row0 + 8 * c;
-      if (f < p.n && t0 < p.m) {
-        bf16* dst = p.yt + (int64_t)(f - p.split_col) * p.ldyt + t0;
-        if (t0 + 7 < p.m) {
-          *reinterpret_cast<u32x4*>(dst) = val;
-        } else {
-          const bf16* ve = reinterpret_cast<const bf16*>(&val);
+    for (int s8 = 0; s8 < 4 * JR; ++s8) {
+      const int row = s8 * 8 + (lane >> 3), c = lane & 7;
+      const int brow = rnd * JR * 32 + row;
+      const u32x4 val = *reinterpret_cast<const u32x4*>(stage + row * 128 + ((c ^ swz(row)) << 4));
+      if (!trans) {
+        const int t = tok0 + b_row0 + brow, f = feat0 + a_row0 + 8 * c;
+        if (t < p.m && f < p.n) *reinterpret_cast<u32x4*>(p.y + (int64_t)t * p.ldy + f) = val;
+      } else {
+        const int f = feat0 + b_row0 + brow, t0 = tok0 + a_row0 + 8 * c;
+        if (f < p.n && t0 < p.m) {
+          bf16* dst = p.yt + (int64_t)(f - p.split_col) * p.ldyt + t0;
+          if (t0 + 7 < p.m) {
+            *reinterpret_cast<u32x4*>(dst) = val;
+          } else {
+            const bf16* ve = reinterpret_cast<const bf16*>(&val);
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (t0 + e < p.m) dst[e] = ve[e];
+            for (int e = 0; e < 8; ++e)
+              if (t0 + e < p.m) dst[e] = ve[e];
+          }
         }
       }
     }
@@ -264,23 +269,24 @@ __device__ __forceinline__ void store_tile_staged(const GemmParams& p, const f32
 
 // Gated residual, row-major: the residual is read in the same coalesced
 // pattern as the output is written, so the wave stages z = acc (x scale) +
-// bias in fp32 instead, in two rounds of 64 B-rows (16 KiB each): row r holds
-// 64 fp32 values, 16-byte chunk c at chunk c ^ (r % 16).  Each lane then
-// finishes 8 consecutive features of one token: y = r + g * z, one rounding.
-template <bool W8>
+// bias in fp32 instead, in rounds of JR 32-row blocks (8 JR KiB): row r
+// holds 64 fp32 values, 16-byte chunk c at chunk c ^ (r % 16).  Each lane
+// then finishes 8 consecutive features of one token: y = r + g * z, one
+// rounding.
+template <bool W8, int JR>
 __device__ __forceinline__ void store_tile_staged_residual(const GemmParams& p, const f32x16 (&acc)[2][4],
                                                            int a_row0, int b_row0, int tok0, int feat0, int lane,
                                                            char* stage) {
   const int half = lane >> 5;
 #pragma unroll
-  for (int rnd = 0; rnd < 2; ++rnd) {
+  for (int rnd = 0; rnd < 4 / JR; ++rnd) {
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj)
+      for (int jj = 0; jj < JR; ++jj)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int j = 2 * rnd + jj;
+          const int j = rnd * JR + jj;
           const int brow = jj * 32 + (lane & 31);
           const int ai = i * 32 + 8 * g + 4 * half;
           float v[4];
@@ -292,9 +298,9 @@ __device__ __forceinline__ void store_tile_staged_residual(const GemmParams& p, 
           *reinterpret_cast<f32x4*>(stage + brow * 256 + (((ai >> 2) ^ (brow & 15)) << 4)) = z;
         }
 #pragma unroll
-    for (int s8 = 0; s8 < 8; ++s8) {
+    for (int s8 = 0; s8 < 4 * JR; ++s8) {
       const int row = s8 * 8 + (lane >> 3), c = lane & 7;
-      const int t = tok0 + b_row0 + rnd * 64 + row, f = feat0 + a_row0 + 8 * c;
+      const int t = tok0 + b_row0 + rnd * JR * 32 + row, f = feat0 + a_row0 + 8 * c;
       const f32x4 z0 = *reinterpret_cast<const f32x4*>(stage + row * 256 + (((2 * c) ^ (row & 15)) << 4));
       const f32x4 z1 = *reinterpret_cast<const f32x4*>(stage + row * 256 + (((2 * c + 1) ^ (row & 15)) << 4));
       if (t < p.m && f < p.n) {
@@ -564,13 +570,13 @@ __global__ __launch_bounds__(512) void gemm_ring_kernel(GemmParams p) {
         for (int r = 0; r < 16; ++r) accf[i][j][r] = static_cast<float>(acc[i][j][r]) * xs;
     }
     if (staged && EPI == kEpiGatedResidual)
-      store_tile_staged_residual<true>(p, accf, a_row0, b_row0, tok0, feat0, lane, stage);
-    else if (staged) store_tile_staged<EPI, true>(p, accf, a_row0, b_row0, tok0, feat0, false, lane, stage);
+      store_tile_staged_residual<true, 2>(p, accf, a_row0, b_row0, tok0, feat0, lane, stage);
+    else if (staged) store_tile_staged<EPI, true, 4>(p, accf, a_row0, b_row0, tok0, feat0, false, lane, stage);
     else store_tile<EPI, true>(p, accf, a_row0, b_row0, tok0, feat0, false, lane);
   } else {
     if (staged && EPI == kEpiGatedResidual && !trans)
-      store_tile_staged_residual<W8 && !GRP>(p, acc, a_row0, b_row0, tok0, feat0, lane, stage);
-    else if (staged) store_tile_staged<EPI, W8 && !GRP>(p, acc, a_row0, b_row0, tok0, feat0, trans, lane, stage);
+      store_tile_staged_residual<W8 && !GRP, 2>(p, acc, a_row0, b_row0, tok0, feat0, lane, stage);
+    else if (staged) store_tile_staged<EPI, W8 && !GRP, 4>(p, acc, a_row0, b_row0, tok0, feat0, trans, lane, stage);
     else store_tile<EPI, W8 && !GRP>(p, acc, a_row0, b_row0, tok0, feat0, trans, lane);
   }
 }
