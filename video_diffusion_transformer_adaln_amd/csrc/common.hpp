@@ -117,15 +117,16 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
 }
 
 // GELU, tanh form.  Uses the identity 0.5 (1 + tanh(y)) = 1 / (1 + exp(-2y)),
-// so gelu(z) = z / (1 + exp(-2y)) with y = sqrt(2/pi) (z + 0.044715 z^3);
-// exp through v_exp_f32 (exp2) and the reciprocal through v_rcp_f32.  For
-// z -> -inf the exponential overflows to +inf and the result is -0.
+// so gelu(z) = z / (1 + exp(-2y)) with y = sqrt(2/pi) (z + 0.044715 z^3).
+// The exponent -2 y log2(e) is folded to z (c1 + c2 z^2), c1 = -2 sqrt(2/pi)
+// log2(e), c2 = 0.044715 c1 (one multiply, one fma, one multiply), then
+// v_exp_f32 (exp2) and the reciprocal through v_rcp_f32; within 1e-6
+// relative of the exact function.  For z -> -inf the exponential overflows
+// to +inf and the result is -0.
 __device__ __forceinline__ float gelu_tanh(float z) {
-  const float k0 = 0.7978845608028654f;           // sqrt(2/pi)
-  const float k1 = 0.044715f;
-  const float m2log2e = -2.0f * 1.4426950408889634f;
-  const float y = k0 * (z + k1 * z * z * z);
-  const float e = __builtin_amdgcn_exp2f(m2log2e * y);
+  const float c1 = -2.3022082f;                   // -2 sqrt(2/pi) log2(e)
+  const float c2 = -0.10294324f;                  // 0.044715 c1
+  const float e = __builtin_amdgcn_exp2f(z * fmaf(z * z, c2, c1));
   return z * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
