@@ -71,8 +71,10 @@ hipError_t launch_adaln_gemv(DType dt, int rows, int cols, const void* w, const 
 
 // ---------------------------------------------------------------------------
 // out = LN(x) (1 + scale) + shift.  One wave per row; the row is held in
-// registers (MAXC 16-byte chunks per lane), so mean and the biased variance
-// are two exact passes over registers, each closed by a wave reduction.
+// registers (MAXC 16-byte chunks per lane, in its storage type, widened to
+// fp32 in each pass, which keeps the register count and so the number of
+// rows in flight per CU up), so mean and the biased variance are two exact
+// passes over registers, each closed by a wave reduction.
 template <typename T, int MAXC>
 __global__ __launch_bounds__(256) void ln_modulate_kernel(const T* __restrict__ x, int64_t ldx,
                                                           const float* __restrict__ shift,
@@ -84,19 +86,20 @@ __global__ __launch_bounds__(256) void ln_modulate_kernel(const T* __restrict__ 
   if (row >= n) return;
   const int chunks = D / V;
   const T* xr = x + (int64_t)row * ldx;
-  float v[MAXC][V];
+  u32x4 raw[MAXC];
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i) {
+    const int ch = lane + i * kWave;
+    raw[i] = ch < chunks ? *reinterpret_cast<const u32x4*>(xr + ch * V) : u32x4{0, 0, 0, 0};
+  }
+  auto elem = [&](int i, int j) { return to_f32(reinterpret_cast<const T*>(&raw[i])[j]); };
   float s = 0.f;
 #pragma unroll
   for (int i = 0; i < MAXC; ++i) {
     const int ch = lane + i * kWave;
     if (ch < chunks) {
-      const u32x4 raw = *reinterpret_cast<const u32x4*>(xr + ch * V);
-      const T* e = reinterpret_cast<const T*>(&raw);
 #pragma unroll
-      for (int j = 0; j < V; ++j) { v[i][j] = to_f32(e[j]); s += v[i][j]; }
-    } else {
-#pragma unroll
-      for (int j = 0; j < V; ++j) v[i][j] = 0.f;
+      for (int j = 0; j < V; ++j) s += elem(i, j);
     }
   }
   const float mean = wave_sum(s) / (float)D;
@@ -106,7 +109,7 @@ __global__ __launch_bounds__(256) void ln_modulate_kernel(const T* __restrict__ 
     const int ch = lane + i * kWave;
     if (ch < chunks) {
 #pragma unroll
-      for (int j = 0; j < V; ++j) { const float dlt = v[i][j] - mean; ss += dlt * dlt; }
+      for (int j = 0; j < V; ++j) { const float dlt = elem(i, j) - mean; ss += dlt * dlt; }
     }
   }
   const float var = wave_sum(ss) / (float)D;
@@ -117,12 +120,12 @@ __global__ __launch_bounds__(256) void ln_modulate_kernel(const T* __restrict__ 
     const int ch = lane + i * kWave;
     if (ch < chunks) {
       const int c0 = ch * V;
-      u32x4 raw;
-      T* e = reinterpret_cast<T*>(&raw);
+      u32x4 res;
+      T* e = reinterpret_cast<T*>(&res);
 #pragma unroll
       for (int j = 0; j < V; ++j)
-        e[j] = from_f32<T>((v[i][j] - mean) * rstd * (1.0f + scale[c0 + j]) + shift[c0 + j]);
-      *reinterpret_cast<u32x4*>(orow + c0) = raw;
+        e[j] = from_f32<T>((elem(i, j) - mean) * rstd * (1.0f + scale[c0 + j]) + shift[c0 + j]);
+      *reinterpret_cast<u32x4*>(orow + c0) = res;
     }
   }
 }
