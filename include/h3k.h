@@ -99,7 +99,7 @@ typedef int32_t h3k_dtype;
  * with T*H*W = n_tokens (tokens laid out frame, row, column) rotates q and k
  * after their bias by the 3D RoPE of h3k_rope_3d, fused into the QKV
  * projection's epilogue ([H3-review], note on native-256 RoPE).  Needs BF16
- * activations.  rope_half_spatial = 1 halves the spatial coordinates (the
+ * activations and n_tokens <= 2^24.  rope_half_spatial = 1 halves the spatial coordinates (the
  * page's rule for native-256 generation on 256 square canvases).
  * token_reduction_first, token_reduction_last: for h3k_dit_stack_forward, a
  * layer range [first, last) run on merged tokens ([H3-review] knob list: video
@@ -344,7 +344,8 @@ h3k_status h3k_token_unmerge(h3k_dtype dtype, int64_t n_tokens, int64_t D, const
  * dimensions, and the pair (2i, 2i+1) of the slice of axis a turns by
  * pos_a * 10000^(-2i / d_a):  (x, y) -> (x cos - y sin, x sin + y cos).
  * head_dim a multiple of 16 (<= 256), cols a multiple of head_dim, ldx >= cols
- * and a multiple of 4, frames * height * width = n_tokens. */
+ * and a multiple of 4, frames * height * width = n_tokens <= 2^24
+ * (H3K_ERR_UNSUPPORTED beyond). */
 h3k_status h3k_rope_3d(int64_t n_tokens, int64_t cols, int32_t head_dim, int32_t frames, int32_t height,
                        int32_t width, int32_t half_spatial, void* x, int64_t ldx, hipStream_t stream);
 

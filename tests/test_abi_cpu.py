@@ -214,6 +214,8 @@ def test_reject_bad_kernel_level_arguments():
     # transposed part with GELU is not supported
     assert lib.h3k_linear(1, 1, 10, 64, 64, FAKE, 64, FAKE + (1 << 32), 64, None, None, 1, None, 0, None,
                           FAKE + (2 << 32), 64, FAKE + (4 << 32), 16, 32, None) == B.H3K_ERR_UNSUPPORTED
+    # RoPE beyond 2^24 tokens (coordinates come from an exact fp32 quotient)
+    assert lib.h3k_rope_3d(1 << 25, 128, 128, 1 << 13, 1 << 6, 1 << 6, 0, FAKE, 128, None) == B.H3K_ERR_UNSUPPORTED
     # attention: head_dim 32, pitch too small
     assert lib.h3k_attention(1, 100, 2, 32, FAKE, 64, FAKE, 64, FAKE, 104, FAKE, 64, None) == B.H3K_ERR_UNSUPPORTED
     assert lib.h3k_attention(1, 100, 2, 64, FAKE, 128, FAKE + (1 << 32), 128, FAKE + (2 << 32), 96,

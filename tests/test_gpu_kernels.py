@@ -314,7 +314,8 @@ def test_token_merge_unmerge(B, n, D, dtype):
 
 @pytest.mark.parametrize("grid,heads,hd,half", [((2, 3, 4), 2, 128, False), ((3, 3, 37), 4, 64, True),
                                                 ((1, 1, 1), 2, 64, False), ((14, 30, 54), 2, 128, False),
-                                                ((14, 30, 54), 2, 128, True), ((5, 7, 9), 3, 128, True)])
+                                                ((14, 30, 54), 2, 128, True), ((5, 7, 9), 3, 128, True),
+                                                ((64, 127, 129), 1, 16, False)])
 def test_rope_3d(B, grid, heads, hd, half):
     """In-place rotation of a [tokens, heads * d] bf16 matrix (with a wider
     row pitch) against the oracle's float64 rope_3d of the same bf16 values."""
@@ -332,6 +333,9 @@ def test_rope_3d(B, grid, heads, hd, half):
     assert (got[:, cols:] == 7.0).all()                 # the pitch padding is untouched
     ref = oracle.rope_3d(x.values, heads, grid, half)
     assert rel_l2(got[:, :cols], ref) < 4e-3           # one bf16 rounding of the result
+    # every token at its own grid position: a wrong coordinate turns a pair by
+    # a wrong angle, far beyond one bf16 rounding (|values| < 8 here)
+    assert np.max(np.abs(got[:, :cols].astype(np.float64) - ref)) < 0.05
     assert np.array_equal(got[0, :cols], x.values[0])   # token (0, 0, 0) is not rotated
 
 

@@ -83,29 +83,85 @@ struct RopeGeom {
   int height, width;     // the grid's H and W (T = tokens / (H W))
   float spatial;         // 1 or 0.5
 };
+// cos and sin of the angle pos * 10000^(-2i/da) of rotation pair i of an
+// axis slice of width da.  10000^(-2i/da) = 2^(-2i log2(10000) / da); the
+// angle in turns, reduced to [0, 1) exactly (fract), for v_sin_f32 /
+// v_cos_f32, which take turns.  Positions are grid coordinates (< 2^16), so
+// the angle's fp32 error stays far below bf16 resolution.
+__device__ __forceinline__ void rope_cs(float pos, int i, int da, float& cs, float& sn) {
+  const float theta = __builtin_amdgcn_exp2f(-2.0f * 13.287712379549449f * (float)i / (float)da);
+  const float turns = pos * theta * 0.15915494309189535f;
+  const float fr = turns - floorf(turns);
+  sn = __builtin_amdgcn_sinf(fr);
+  cs = __builtin_amdgcn_cosf(fr);
+}
+__device__ __forceinline__ void rope_apply(float& x, float& y, float cs, float sn) {
+  const float nx = x * cs - y * sn;
+  y = x * sn + y * cs;
+  x = nx;
+}
+// Exact a / b for 0 <= a < 2^24, b > 0 through one fp32 multiply and one
+// correction step (the float quotient is off by at most one), instead of
+// the integer division sequence.
+__device__ __forceinline__ int div_small(int a, int b) {
+  int q = (int)((float)a * __builtin_amdgcn_rcpf((float)b));
+  const int r = a - q * b;
+  q += (r >= b) - (r < 0);
+  return q;
+}
+// Grid coordinates of token `tok` (frame-major, then rows, then columns).
+__device__ __forceinline__ void rope_coords(int tok, const RopeGeom& g, int& t, int& h, int& w) {
+  const int hw = g.height * g.width;
+  t = div_small(tok, hw);
+  const int r = tok - t * hw;
+  h = div_small(r, g.width);
+  w = r - h * g.width;
+}
 // Rotate the pair (x, y) at even dimension j (0 <= j < head_dim) of a head of
 // token `tok`.
 __device__ __forceinline__ void rope_rotate(float& x, float& y, int tok, int j, const RopeGeom& g) {
   const int d = g.head_dim, dt = d / 4, dh = (d - dt) / 2;
-  const int hw = g.height * g.width;
-  const int t = tok / hw, r = tok - t * hw;
-  const int h = r / g.width, w = r - h * g.width;
+  int t, h, w;
+  rope_coords(tok, g, t, h, w);
   float pos;
   int i, da;
   if (j < dt) { pos = (float)t; i = j >> 1; da = dt; }
   else if (j < dt + dh) { pos = (float)h * g.spatial; i = (j - dt) >> 1; da = dh; }
   else { pos = (float)w * g.spatial; i = (j - dt - dh) >> 1; da = d - dt - dh; }
-  // 10000^(-2i/da) = 2^(-2i log2(10000) / da); the angle in turns, reduced to
-  // [0, 1) exactly (fract), for v_sin_f32 / v_cos_f32, which take turns.
-  // Positions are grid coordinates (< 2^16), so the angle's fp32 error stays
-  // far below bf16 resolution.
-  const float theta = __builtin_amdgcn_exp2f(-2.0f * 13.287712379549449f * (float)i / (float)da);
-  const float turns = pos * theta * 0.15915494309189535f;
-  const float fr = turns - floorf(turns);
-  const float sn = __builtin_amdgcn_sinf(fr), cs = __builtin_amdgcn_cosf(fr);
-  const float nx = x * cs - y * sn;
-  y = x * sn + y * cs;
-  x = nx;
+  float cs, sn;
+  rope_cs(pos, i, da, cs, sn);
+  rope_apply(x, y, cs, sn);
+}
+// The same rotation from a table of (cos, sin) per axis position and pair:
+// frames x d/8 pairs, then height x 3d/16, then width x 3d/16 (rope_table_entry
+// fills entry e), so a tile's epilogue takes no transcendental per element.
+__device__ __forceinline__ int rope_table_size(const RopeGeom& g, int frames) {
+  const int d = g.head_dim, dt = d / 4, dh = (d - dt) / 2, dw = d - dt - dh;
+  return frames * (dt / 2) + g.height * (dh / 2) + g.width * (dw / 2);
+}
+__device__ __forceinline__ float2 rope_table_entry(int e, const RopeGeom& g, int frames) {
+  const int d = g.head_dim, dt = d / 4, dh = (d - dt) / 2, dw = d - dt - dh;
+  const int nt = dt / 2, nh = dh / 2, nw = dw / 2;
+  float pos;
+  int i, da;
+  if (e < frames * nt) { pos = (float)(e / nt); i = e % nt; da = dt; }
+  else if ((e -= frames * nt) < g.height * nh) { pos = (float)(e / nh) * g.spatial; i = e % nh; da = dh; }
+  else { e -= g.height * nh; pos = (float)(e / nw) * g.spatial; i = e % nw; da = dw; }
+  float2 r;
+  rope_cs(pos, i, da, r.x, r.y);
+  return r;
+}
+__device__ __forceinline__ void rope_rotate_table(float& x, float& y, int tok, int j, const RopeGeom& g, int frames,
+                                                  const float2* tab) {
+  const int d = g.head_dim, dt = d / 4, dh = (d - dt) / 2, dw = d - dt - dh;
+  int t, h, w;
+  rope_coords(tok, g, t, h, w);
+  int e;
+  if (j < dt) e = t * (dt / 2) + (j >> 1);
+  else if (j < dt + dh) e = frames * (dt / 2) + h * (dh / 2) + ((j - dt) >> 1);
+  else e = frames * (dt / 2) + g.height * (dh / 2) + w * (dw / 2) + ((j - dt - dh) >> 1);
+  const float2 cs = tab[e];
+  rope_apply(x, y, cs.x, cs.y);
 }
 
 // Remap a linear workgroup id so that each XCD receives one contiguous range

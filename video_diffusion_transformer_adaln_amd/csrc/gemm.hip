@@ -107,15 +107,22 @@ __device__ __forceinline__ void scale_bias4(const GemmParams& p, float (&v)[4], 
 }
 // Second step: the activation, rotation or gated residual.
 template <int EPI>
-__device__ __forceinline__ void epilogue4(const GemmParams& p, float (&v)[4], int t, int f) {
+__device__ __forceinline__ void epilogue4(const GemmParams& p, float (&v)[4], int t, int f,
+                                          const float2* rope_tab = nullptr) {
   if constexpr (EPI == kEpiGelu) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[e] = gelu_tanh(v[e]);
   }
   if constexpr (EPI == kEpiBiasRope) {   // features f..f+3 are the pairs (j, j+1), (j+2, j+3) of a head
     const int j = f % p.rope.head_dim;
-    rope_rotate(v[0], v[1], t, j, p.rope);
-    rope_rotate(v[2], v[3], t, j + 2, p.rope);
+    if (rope_tab) {
+      const int frames = p.m / (p.rope.height * p.rope.width);
+      rope_rotate_table(v[0], v[1], t, j, p.rope, frames, rope_tab);
+      rope_rotate_table(v[2], v[3], t, j + 2, p.rope, frames, rope_tab);
+    } else {
+      rope_rotate(v[0], v[1], t, j, p.rope);
+      rope_rotate(v[2], v[3], t, j + 2, p.rope);
+    }
   }
   if constexpr (EPI == kEpiGatedResidual) {
     const u32x2 rr = *reinterpret_cast<const u32x2*>(p.residual + (int64_t)t * p.ldr + f);
@@ -204,7 +211,7 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, const f32x16 (&a
 template <int EPI, bool W8, int JR>
 __device__ __forceinline__ void store_tile_staged(const GemmParams& p, const f32x16 (&acc)[2][4], int a_row0,
                                                   int b_row0, int tok0, int feat0, bool trans, int lane,
-                                                  char* stage) {
+                                                  char* stage, const float2* rope_tab = nullptr) {
   auto swz = [](int r) { return (r ^ (r >> 3)) & 7; };
   const int half = lane >> 5;
 #pragma unroll
@@ -225,7 +232,7 @@ __device__ __forceinline__ void store_tile_staged(const GemmParams& p, const f32
             const int f = feat0 + a_row0 + ai, t = tok0 + b_row0 + j * 32 + (lane & 31);
             if (t < p.m && f < p.n) {
               scale_bias4<W8>(p, v, f);
-              epilogue4<EPI>(p, v, t, f);
+              epilogue4<EPI>(p, v, t, f, rope_tab);
             }
           } else {
             const int f = feat0 + b_row0 + j * 32 + (lane & 31);
@@ -555,6 +562,20 @@ __global__ __launch_bounds__(512) void gemm_ring_kernel(GemmParams p) {
   const bool staged = trans || (int64_t)feat0 + BN <= p.split_col || p.split_col >= p.n;
   if (staged) wg_barrier();
   char* const stage = lds + wave * 16384;
+  // rotary epilogue: (cos, sin) per axis position and pair in the ring's
+  // fifth slot, which the staging (slots 0-3) leaves free
+  const float2* rope_tab = nullptr;
+  if constexpr (EPI == kEpiBiasRope) {
+    const int frames = p.m / (p.rope.height * p.rope.width);
+    const int n_ent = rope_table_size(p.rope, frames);
+    if (staged && !trans && n_ent * (int)sizeof(float2) <= kSlot) {
+      float2* tab = reinterpret_cast<float2*>(lds + 4 * kSlot);
+      for (int e = tid; e < n_ent; e += 512) tab[e] = rope_table_entry(e, p.rope, frames);
+      wait_lgkm0();
+      wg_barrier();
+      rope_tab = tab;
+    }
+  }
   if constexpr (I8) {
     // int32 -> fp32 (one rounding), times the activation row scale; the
     // weight channel scale, bias and epilogue follow in store_tile.  The
@@ -576,7 +597,8 @@ __global__ __launch_bounds__(512) void gemm_ring_kernel(GemmParams p) {
   } else {
     if (staged && EPI == kEpiGatedResidual && !trans)
       store_tile_staged_residual<W8 && !GRP, 2>(p, acc, a_row0, b_row0, tok0, feat0, lane, stage);
-    else if (staged) store_tile_staged<EPI, W8 && !GRP, 4>(p, acc, a_row0, b_row0, tok0, feat0, trans, lane, stage);
+    else if (staged)
+      store_tile_staged<EPI, W8 && !GRP, 4>(p, acc, a_row0, b_row0, tok0, feat0, trans, lane, stage, rope_tab);
     else store_tile<EPI, W8 && !GRP>(p, acc, a_row0, b_row0, tok0, feat0, trans, lane);
   }
 }

@@ -45,6 +45,7 @@ h3k_status fail(h3k_status code, const char* fmt, ...) {
 
 constexpr uint64_t kAlign = 256;
 constexpr int64_t kMaxOffset = (int64_t(1) << 31) - 1;   // 32-bit buffer offsets in the kernels
+constexpr int64_t kMaxRopeTokens = int64_t(1) << 24;       // token coordinates through an exact fp32 quotient
 
 uint64_t align_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
 int64_t esize(h3k_dtype d) { return d == H3K_F32 ? 4 : d == H3K_BF16 ? 2 : 1; }
@@ -121,6 +122,7 @@ h3k_status validate_config(const h3k_dit_config* c) {
       return fail(H3K_ERR_SHAPE, "RoPE grid %d x %d x %d does not hold the %d tokens", c->rope_frames, c->rope_height,
                   c->rope_width, c->n_tokens);
     if (c->act_dtype != H3K_BF16) return fail(H3K_ERR_UNSUPPORTED, "RoPE needs BF16 activations");
+    if (c->n_tokens > kMaxRopeTokens) return fail(H3K_ERR_UNSUPPORTED, "RoPE supports at most 2^24 tokens");
   } else if (c->rope_half_spatial) {
     return fail(H3K_ERR_SHAPE, "rope_half_spatial without a RoPE grid");
   }
@@ -747,6 +749,7 @@ h3k_status h3k_rope_3d(int64_t n_tokens, int64_t cols, int32_t head_dim, int32_t
   if (frames < 1 || height < 1 || width < 1 || (int64_t)frames * height * width != n_tokens)
     return fail(H3K_ERR_SHAPE, "grid %d x %d x %d does not hold the %lld tokens", frames, height, width,
                 (long long)n_tokens);
+  if (n_tokens > kMaxRopeTokens) return fail(H3K_ERR_UNSUPPORTED, "RoPE supports at most 2^24 tokens");
   if (half_spatial != 0 && half_spatial != 1) return fail(H3K_ERR_SHAPE, "half_spatial must be 0 or 1");
   if (!x) return fail(H3K_ERR_NULL, "x must be non-NULL");
   if (!aligned(x, 16)) return fail(H3K_ERR_ALIGN, "x must be 16-byte aligned");
