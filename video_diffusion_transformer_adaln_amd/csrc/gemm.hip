@@ -3,7 +3,9 @@
 //
 //  * bf16 path: 256x256x64 workgroup tile, 8 waves (two per SIMD, so one
 //    wave's waits overlap the other's MFMAs), each wave a 64x128 sub-tile of
-//    v_mfma_f32_32x32x16_bf16 (fp32 accumulators in VGPRs).  Operands go
+//    v_mfma_f32_16x16x32_bf16 (fp32 accumulators in VGPRs).  Measured on
+//    MI355X, streams of the 16x16x32 form hold a 10-14 % higher clock under
+//    the power limit than the 32x32x16 form for the same work.  Operands go
 //    global -> LDS by direct-to-LDS loads (buffer_load ... lds) into a ring
 //    of five 32 KiB operand slots (all 160 KiB of gfx950's LDS), so the
 //    activation tile of k-tile t+2 and the weight tile of t+1 are in flight
@@ -52,9 +54,6 @@ struct GemmParams {
 
 constexpr int BM = 256, BN = 256, BK = 64;
 
-__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
 
 // 16 int8 -> 16 bf16, exact (|q| <= 127 fits bf16's 8-bit significand):
 // flip the sign bit to get q + 128 as an unsigned byte, convert that byte to
@@ -93,9 +92,32 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-// Epilogue math, fp32, one bf16 rounding at the store.  Accumulator register
-// r of lane l in 32x32 tile (i, j) of a wave's 64x128 sub-tile:
-//   A-row = a_row0 + i*32 + 8*(r/4) + 4*(l/32) + r%4, B-row = b_row0 + j*32 + l%32.
+// Accumulator quads.  A wave's 64x128 sub-tile leaves each lane 32 quads:
+// four consecutive A-rows (features of the row-major output, tokens of the
+// transposed one) at one B-row.  Quad q (0..7) of 32-row B block jb lies at
+// A-row a_row0 + ai and B-row b_row0 + 32 jb + br:
+//  * v_mfma_f32_32x32x16 tiles acc[i][jb], registers 4g..4g+3 (i = q/4, g = q%4):
+//    ai = 32 i + 8 g + 4 (lane/32), br = lane%32;
+//  * v_mfma_f32_16x16x32 tiles acc[I][2 jb + h], registers 0..3 (I = q/2, h = q%2):
+//    ai = 16 I + 4 (lane/16), br = 16 h + lane%16.
+__device__ __forceinline__ void quad(const f32x16 (&acc)[2][4], int jb, int q, int lane, float (&v)[4], int& ai,
+                                     int& br) {
+  const int i = q >> 2, g = q & 3;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) v[e] = acc[i][jb][4 * g + e];
+  ai = 32 * i + 8 * g + 4 * (lane >> 5);
+  br = lane & 31;
+}
+__device__ __forceinline__ void quad(const f32x4 (&acc)[4][8], int jb, int q, int lane, float (&v)[4], int& ai,
+                                     int& br) {
+  const int I = q >> 1, h = q & 1;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) v[e] = acc[I][2 * jb + h][e];
+  ai = 16 * I + 4 * (lane >> 4);
+  br = 16 * h + (lane & 15);
+}
+
+// Epilogue math, fp32, one bf16 rounding at the store.
 // Row-major output, first step: features f..f+3 of token t, channel scale and bias.
 template <bool W8>
 __device__ __forceinline__ void scale_bias4(const GemmParams& p, float (&v)[4], int f) {
@@ -142,62 +164,53 @@ __device__ __forceinline__ u32x2 pack4(const float (&v)[4]) {
 // Fused epilogue of one wave's 64x128 accumulator sub-tile, stored straight
 // from the accumulator layout (8-byte pieces, 32 rows per instruction); used
 // for the tile that straddles split_col.
-template <int EPI, bool W8>
-__device__ __forceinline__ void store_tile(const GemmParams& p, const f32x16 (&acc)[2][4], int a_row0, int b_row0,
-                                           int tok0, int feat0, bool trans, int lane) {
+template <int EPI, bool W8, typename AccT>
+__device__ __forceinline__ void store_tile(const GemmParams& p, const AccT& acc, int a_row0, int b_row0, int tok0,
+                                           int feat0, bool trans, int lane) {
   const float* wsc = p.w_scale;
-  if (!trans) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+  for (int jb = 0; jb < 4; ++jb)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+    for (int q = 0; q < 8; ++q) {
+      float v[4];
+      int ai, br;
+      quad(acc, jb, q, lane, v, ai, br);
+      if (!trans) {
+        const int f = feat0 + a_row0 + ai;
+        const int t = tok0 + b_row0 + jb * 32 + br;
+        if (t >= p.m || f >= p.n) continue;
+        scale_bias4<W8>(p, v, f);
+        if ((int64_t)f >= p.split_col) {   // straddling tile: transposed part, bias only
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int f = feat0 + a_row0 + i * 32 + 8 * g + 4 * (lane >> 5);
-          const int t = tok0 + b_row0 + j * 32 + (lane & 31);
-          if (t >= p.m || f >= p.n) continue;
-          float v[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e];
-          scale_bias4<W8>(p, v, f);
-          if ((int64_t)f >= p.split_col) {   // straddling tile: transposed part, bias only
-#pragma unroll
-            for (int e = 0; e < 4; ++e) p.yt[(int64_t)(f + e - p.split_col) * p.ldyt + t] = static_cast<bf16>(v[e]);
-            continue;
-          }
-          epilogue4<EPI>(p, v, t, f);
-          *reinterpret_cast<u32x2*>(p.y + (int64_t)t * p.ldy + f) = pack4(v);
+          for (int e = 0; e < 4; ++e) p.yt[(int64_t)(f + e - p.split_col) * p.ldyt + t] = static_cast<bf16>(v[e]);
+          continue;
         }
-  } else {
+        epilogue4<EPI>(p, v, t, f);
+        *reinterpret_cast<u32x2*>(p.y + (int64_t)t * p.ldy + f) = pack4(v);
+      } else {
+        const int t0 = tok0 + a_row0 + ai;
+        const int f = feat0 + b_row0 + jb * 32 + br;
+        if (f >= p.n || t0 >= p.m) continue;
+        const float sc = W8 ? wsc[f] : 1.0f;
+        const float bb = p.bias ? static_cast<float>(p.bias[f]) : 0.0f;
+        u32x2 out;
+        bf16* oe = reinterpret_cast<bf16*>(&out);
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int t0 = tok0 + a_row0 + i * 32 + 8 * g + 4 * (lane >> 5);
-          const int f = feat0 + b_row0 + j * 32 + (lane & 31);
-          if (f >= p.n || t0 >= p.m) continue;
-          const float sc = W8 ? wsc[f] : 1.0f;
-          const float bb = p.bias ? static_cast<float>(p.bias[f]) : 0.0f;
-          u32x2 out;
-          bf16* oe = reinterpret_cast<bf16*>(&out);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            float v = acc[i][j][4 * g + e];
-            if constexpr (W8) v *= sc;
-            oe[e] = static_cast<bf16>(v + bb);
-          }
-          bf16* dst = p.yt + (int64_t)(f - p.split_col) * p.ldyt + t0;
-          if (t0 + 3 < p.m) {
-            *reinterpret_cast<u32x2*>(dst) = out;
-          } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (t0 + e < p.m) dst[e] = oe[e];
-          }
+        for (int e = 0; e < 4; ++e) {
+          float x = v[e];
+          if constexpr (W8) x *= sc;
+          oe[e] = static_cast<bf16>(x + bb);
         }
-  }
+        bf16* dst = p.yt + (int64_t)(f - p.split_col) * p.ldyt + t0;
+        if (t0 + 3 < p.m) {
+          *reinterpret_cast<u32x2*>(dst) = out;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (t0 + e < p.m) dst[e] = oe[e];
+        }
+      }
+    }
 }
 
 // The same epilogue for a tile that lies wholly on one side of split_col,
@@ -208,46 +221,43 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, const f32x16 (&a
 // chunk c ^ ((r ^ r/8) % 8); each lane then stores 16 bytes, 8 lanes per
 // row.  Row-major output: B-rows are tokens and the 64 A-values features;
 // transposed output (V^T): B-rows are features and the A-values tokens.
-template <int EPI, bool W8, int JR>
-__device__ __forceinline__ void store_tile_staged(const GemmParams& p, const f32x16 (&acc)[2][4], int a_row0,
-                                                  int b_row0, int tok0, int feat0, bool trans, int lane,
-                                                  char* stage, const float2* rope_tab = nullptr) {
+template <int EPI, bool W8, int JR, typename AccT>
+__device__ __forceinline__ void store_tile_staged(const GemmParams& p, const AccT& acc, int a_row0, int b_row0,
+                                                  int tok0, int feat0, bool trans, int lane, char* stage,
+                                                  const float2* rope_tab = nullptr) {
   auto swz = [](int r) { return (r ^ (r >> 3)) & 7; };
-  const int half = lane >> 5;
 #pragma unroll
   for (int rnd = 0; rnd < 4 / JR; ++rnd) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int jj = 0; jj < JR; ++jj)
 #pragma unroll
-      for (int jj = 0; jj < JR; ++jj)
+      for (int q = 0; q < 8; ++q) {
+        const int j = rnd * JR + jj;
+        float v[4];
+        int ai, br;
+        quad(acc, j, q, lane, v, ai, br);
+        const int brow = jj * 32 + br;
+        if (!trans) {
+          const int f = feat0 + a_row0 + ai, t = tok0 + b_row0 + j * 32 + br;
+          if (t < p.m && f < p.n) {
+            scale_bias4<W8>(p, v, f);
+            epilogue4<EPI>(p, v, t, f, rope_tab);
+          }
+        } else {
+          const int f = feat0 + b_row0 + j * 32 + br;
+          if (f < p.n) {
+            const float sc = W8 ? p.w_scale[f] : 1.0f;
+            const float bb = p.bias ? static_cast<float>(p.bias[f]) : 0.0f;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int j = rnd * JR + jj;
-          const int brow = jj * 32 + (lane & 31);
-          const int ai = i * 32 + 8 * g + 4 * half;
-          float v[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e];
-          if (!trans) {
-            const int f = feat0 + a_row0 + ai, t = tok0 + b_row0 + j * 32 + (lane & 31);
-            if (t < p.m && f < p.n) {
-              scale_bias4<W8>(p, v, f);
-              epilogue4<EPI>(p, v, t, f, rope_tab);
-            }
-          } else {
-            const int f = feat0 + b_row0 + j * 32 + (lane & 31);
-            if (f < p.n) {
-              const float sc = W8 ? p.w_scale[f] : 1.0f;
-              const float bb = p.bias ? static_cast<float>(p.bias[f]) : 0.0f;
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                if constexpr (W8) v[e] *= sc;
-                v[e] += bb;
-              }
+            for (int e = 0; e < 4; ++e) {
+              if constexpr (W8) v[e] *= sc;
+              v[e] += bb;
             }
           }
-          *reinterpret_cast<u32x2*>(stage + brow * 128 + (((ai >> 3) ^ swz(brow)) << 4) + half * 8) = pack4(v);
         }
+        *reinterpret_cast<u32x2*>(stage + brow * 128 + (((ai >> 3) ^ swz(brow)) << 4) + ((ai >> 2) & 1) * 8) =
+            pack4(v);
+      }
 #pragma unroll
     for (int s8 = 0; s8 < 4 * JR; ++s8) {
       const int row = s8 * 8 + (lane >> 3), c = lane & 7;
@@ -280,30 +290,25 @@ __device__ __forceinline__ void store_tile_staged(const GemmParams& p, const f32
 // holds 64 fp32 values, 16-byte chunk c at chunk c ^ (r % 16).  Each lane
 // then finishes 8 consecutive features of one token: y = r + g * z, one
 // rounding.
-template <bool W8, int JR>
-__device__ __forceinline__ void store_tile_staged_residual(const GemmParams& p, const f32x16 (&acc)[2][4],
-                                                           int a_row0, int b_row0, int tok0, int feat0, int lane,
-                                                           char* stage) {
-  const int half = lane >> 5;
+template <bool W8, int JR, typename AccT>
+__device__ __forceinline__ void store_tile_staged_residual(const GemmParams& p, const AccT& acc, int a_row0,
+                                                           int b_row0, int tok0, int feat0, int lane, char* stage) {
 #pragma unroll
   for (int rnd = 0; rnd < 4 / JR; ++rnd) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int jj = 0; jj < JR; ++jj)
 #pragma unroll
-      for (int jj = 0; jj < JR; ++jj)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int j = rnd * JR + jj;
-          const int brow = jj * 32 + (lane & 31);
-          const int ai = i * 32 + 8 * g + 4 * half;
-          float v[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e];
-          const int f = feat0 + a_row0 + ai, t = tok0 + b_row0 + j * 32 + (lane & 31);
-          if (t < p.m && f < p.n) scale_bias4<W8>(p, v, f);
-          f32x4 z = {v[0], v[1], v[2], v[3]};
-          *reinterpret_cast<f32x4*>(stage + brow * 256 + (((ai >> 2) ^ (brow & 15)) << 4)) = z;
-        }
+      for (int q = 0; q < 8; ++q) {
+        const int j = rnd * JR + jj;
+        float v[4];
+        int ai, br;
+        quad(acc, j, q, lane, v, ai, br);
+        const int brow = jj * 32 + br;
+        const int f = feat0 + a_row0 + ai, t = tok0 + b_row0 + j * 32 + br;
+        if (t < p.m && f < p.n) scale_bias4<W8>(p, v, f);
+        f32x4 z = {v[0], v[1], v[2], v[3]};
+        *reinterpret_cast<f32x4*>(stage + brow * 256 + (((ai >> 2) ^ (brow & 15)) << 4)) = z;
+      }
 #pragma unroll
     for (int s8 = 0; s8 < 4 * JR; ++s8) {
       const int row = s8 * 8 + (lane >> 3), c = lane & 7;
@@ -329,17 +334,24 @@ __device__ __forceinline__ void store_tile_staged_residual(const GemmParams& p, 
 // ---------------------------------------------------------------------------
 // Ring kernel.  bf16 operands arrive by direct-to-LDS loads (buffer_load ...
 // lds): no staging registers and no LDS store instructions.  An operand's k-tile is
-// [256 rows][128 B], 16-byte chunk c of row r stored at chunk c ^ rswz(r)
-// (fragment reads of 8 or 16 consecutive rows hit distinct banks).  The
-// swizzle is applied on the source side: lane l of a load writes row
+// [256 rows][128 B], 16-byte chunk c of row r stored at chunk c ^ rswz(r).
+// The swizzle is applied on the source side: lane l of a load writes row
 // r0 + l/8, chunk l%8, and so fetches logical chunk (l%8) ^ rswz(row).
 //
-// Synchronisation: the workgroup barriers carry no memory fence.  A fence
-// makes the compiler wait for every outstanding vector-memory load (vmcnt(0)),
-// which would drain the ring at each k-tile; instead each wave waits
-// (vmcnt) for its own loads of the next k-tile, then all waves meet at
-// s_barrier, after which the whole tile is visible in LDS.
-__device__ __forceinline__ int rswz(int r) { return (r ^ (r >> 3)) & 7; }
+// The swizzle depends on the fragment shape, since gfx950's LDS serves a
+// 16-byte read of 64 lanes in groups whose bank conflicts were measured on
+// MI355X (ds_read_b128 throughput per access pattern):
+//  * 32x32 fragments (lane l: row l%32, chunk selected by l/32):
+//    rswz(r) = (r ^ r/8) % 8 is conflict-free;
+//  * 16x16x32 fragments (lane l: row l%16, chunk selected by l/16): that
+//    swizzle leaves two-way conflicts, (r/2) % 8 is conflict-free.
+// Both are linear in the row bits, so a block at a multiple R of 16 (32)
+// adds the constant rswz(R) (zero for (r/2) % 8).
+template <bool M16>
+__device__ __forceinline__ int rswz(int r) {
+  if constexpr (M16) return (r >> 1) & 7;
+  else return (r ^ (r >> 3)) & 7;
+}
 constexpr int kSlot = 256 * 128;   // one operand's k-tile of 64: [256 rows][128 B]
 constexpr int kSlots = 5;          // 160 KiB
 // m-tiles per group in this kernel's tile order (the 32 workgroups resident
@@ -349,6 +361,8 @@ constexpr int kRingGroupM = 2;
 template <int EPI, bool I8, bool W8 = false, bool GRP = false>
 __global__ __launch_bounds__(512) void gemm_ring_kernel(GemmParams p) {
   static_assert(!(I8 && W8), "int8 activations take the int8 MFMA path");
+  constexpr bool M16 = !I8;   // bf16 MFMA: 16x16x32; int8 MFMA: 32x32x32
+  auto sw = [](int r) { return rswz<M16>(r); };
   __shared__ __attribute__((aligned(1024))) char lds[kSlots * kSlot];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -370,11 +384,11 @@ __global__ __launch_bounds__(512) void gemm_ring_kernel(GemmParams p) {
 
   // Ring of 5 operand slots; position q holds operand q&1 (0: activations,
   // 1: weights) of k-tile q>>1, in slot q%5.  Loads: instruction j (0..3)
-  // of wave w covers rows (8 j + w) * 8 .. +8; rswz(lrow + 64 j) == rswz(lrow).
+  // of wave w covers rows (8 j + w) * 8 .. +8; sw(lrow + 64 j) == sw(lrow).
   const __amdgpu_buffer_rsrc_t rsx = make_rsrc(p.x, (uint32_t)((uint64_t)p.m * p.ldx * ES));
   const __amdgpu_buffer_rsrc_t rsw = make_rsrc(p.w, (uint32_t)((uint64_t)p.n * p.ldw * (W8 ? 1 : ES)));
   const int lrow = wave * 8 + (lane >> 3);
-  const uint32_t c16 = (uint32_t)(((lane & 7) ^ rswz(lrow)) * 16);
+  const uint32_t c16 = (uint32_t)(((lane & 7) ^ sw(lrow)) * 16);
   const uint32_t xo0 = (uint32_t)(tok0 + lrow) * (uint32_t)p.ldx * ES + c16;
   const uint32_t wo0 = (uint32_t)(feat0 + lrow) * (uint32_t)p.ldw * ES + c16;
   const uint32_t xstep = 64u * (uint32_t)p.ldx * ES, wstep = 64u * (uint32_t)p.ldw * ES;
@@ -398,19 +412,18 @@ __global__ __launch_bounds__(512) void gemm_ring_kernel(GemmParams p) {
   // int8 weights (W8): global -> registers, widened to bf16 (times the
   // group scale with GRP) on the way into the weight slot, which then holds
   // the same bf16 layout as a direct-to-LDS slot.  Load j (0, 1) of a lane:
-  // tile row w8_row + 16 j, int8 chunk lane%4 (16 values = logical
+  // tile row w8_row + 8 j, int8 chunk lane%4 (16 values = logical
   // bf16 chunks 2 (lane%4) and 2 (lane%4) + 1).  Lane group g = lane/4 takes
-  // row (g&1) + 8 ((g>>1)&1) + 2 (g>>2) of the wave's 16, so that the four
-  // rows of 16 consecutive lanes (two per 256-byte bank window) have
-  // swizzles of opposite parity and their stores hit distinct banks.
+  // row (g&3) + 16 ((g>>2)&1) + 4 (g>>3) of the wave's 32 (with j, each of
+  // the wave's rows once).
   const int w8_g = lane >> 2;
-  const int w8_row = wave * 32 + (w8_g & 1) + (((w8_g >> 1) & 1) << 3) + ((w8_g >> 2) << 1), w8_c = lane & 3;
+  const int w8_row = wave * 32 + (w8_g & 3) + (((w8_g >> 2) & 1) << 4) + ((w8_g >> 3) << 2), w8_c = lane & 3;
   const uint32_t w8_off = (uint32_t)(feat0 + w8_row) * (uint32_t)p.ldw + w8_c * 16;
-  const uint32_t w8_step = 16u * (uint32_t)p.ldw;
+  const uint32_t w8_step = 8u * (uint32_t)p.ldw;
   const int n_groups = GRP ? (p.k >> p.group_shift) : 0;
   const __amdgpu_buffer_rsrc_t rss = make_rsrc(p.w_scale, GRP ? (uint32_t)((uint64_t)p.n * n_groups * 4) : 0u);
   const uint32_t s_off = GRP ? (uint32_t)(feat0 + w8_row) * (uint32_t)n_groups * 4u : 0u;
-  const uint32_t s_step = GRP ? 16u * (uint32_t)n_groups * 4u : 0u;
+  const uint32_t s_step = GRP ? 8u * (uint32_t)n_groups * 4u : 0u;
   u32x4 wq[2];
   float wsc[2];
   auto wload = [&](int q) {
@@ -429,62 +442,98 @@ __global__ __launch_bounds__(512) void gemm_ring_kernel(GemmParams p) {
     char* st = lds + (q % kSlots) * kSlot;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int r = w8_row + 16 * j;
+      const int r = w8_row + 8 * j;
       u32x4 lo, hi;
       if constexpr (GRP) i8x16_to_bf16_scaled(wq[j], wsc[j], lo, hi);
       else i8x16_to_bf16(wq[j], lo, hi);
-      *reinterpret_cast<u32x4*>(st + r * 128 + (((2 * w8_c) ^ rswz(r)) << 4)) = lo;
-      *reinterpret_cast<u32x4*>(st + r * 128 + (((2 * w8_c + 1) ^ rswz(r)) << 4)) = hi;
+      *reinterpret_cast<u32x4*>(st + r * 128 + (((2 * w8_c) ^ sw(r)) << 4)) = lo;
+      *reinterpret_cast<u32x4*>(st + r * 128 + (((2 * w8_c + 1) ^ sw(r)) << 4)) = hi;
     }
   };
   // vector-memory loads of one wload (two int8 chunks, and their two group scales)
   constexpr int kW8Loads = GRP ? 4 : 2;
 
-  using Acc = typename std::conditional<I8, i32x16, f32x16>::type;
-  Acc acc[2][4];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = Acc{};
-
-  // fragment of 32-row block i, k-step ks: row row0 + 32 i + rl, logical chunk
-  // 2 ks + h -> physical (2 ks) ^ 4 (i & 1) ^ q, q = h ^ rswz(rl).  A 16-byte
-  // chunk is 8 bf16 (v_mfma_f32_32x32x16_bf16, k-step 16) or 16 int8
-  // (v_mfma_i32_32x32x32_i8, k-step 32): both MFMAs take lane l's row l%32
-  // and the chunk selected by l/32.
+  // int8 fragment (v_mfma_i32_32x32x32_i8, k-step 32) of 32-row block i,
+  // k-step ks: lane l takes row row0 + 32 i + rl (rl = l%32) and the 16-int8
+  // chunk selected by l/32: logical chunk 2 ks + h -> physical
+  // (2 ks) ^ sw(32 i) ^ q, q = h ^ sw(rl).
   const int a_row0 = (wave & 3) * 64;
   const int b_row0 = (wave >> 2) * 128;
+  // A is the weight (row-major output) or the activation (transposed output)
+  const int a_op = trans ? 0 : 1;
+
+  using Acc32 = typename std::conditional<I8, i32x16, f32x16>::type;
+  Acc32 acc[2][4];
+  f32x4 acc16[4][8];
+  if constexpr (M16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc16[i][j] = f32x4{};
+  } else {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = Acc32{};
+  }
+
   const int rl = lane & 31;
-  const int qq = (lane >> 5) ^ rswz(rl);
+  const int qq = (lane >> 5) ^ sw(rl);
   int lo[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) lo[c] = rl * 128 + (((2 * c) ^ qq) << 4);
-  // A is the weight (row-major output) or the activation (transposed output)
-  const int a_op = trans ? 0 : 1;
   auto load_frags = [&](int t, int ks, bf16x8 (&fa)[2], bf16x8 (&fb)[4]) {
     const char* sa = lds + ((2 * t + a_op) % kSlots) * kSlot + a_row0 * 128;
     const char* sb = lds + ((2 * t + 1 - a_op) % kSlots) * kSlot + b_row0 * 128;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
-      fa[i] = *reinterpret_cast<const bf16x8*>(sa + i * 4096 + lo[((2 * ks) ^ (4 * (i & 1))) >> 1]);
+      fa[i] = *reinterpret_cast<const bf16x8*>(sa + i * 4096 + lo[((2 * ks) ^ sw(32 * i)) >> 1]);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      fb[j] = *reinterpret_cast<const bf16x8*>(sb + j * 4096 + lo[((2 * ks) ^ (4 * (j & 1))) >> 1]);
+      fb[j] = *reinterpret_cast<const bf16x8*>(sb + j * 4096 + lo[((2 * ks) ^ sw(32 * j)) >> 1]);
   };
   auto mfmas = [&](const bf16x8 (&fa)[2], const bf16x8 (&fb)[4]) {
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        if constexpr (I8)
-          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, fa[i]),
-                                                            __builtin_bit_cast(i32x4, fb[j]), acc[i][j], 0, 0, 0);
-        else
-          acc[i][j] = mfma32(fa[i], fb[j], acc[i][j]);
+        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, fa[i]),
+                                                          __builtin_bit_cast(i32x4, fb[j]), acc[i][j], 0, 0, 0);
       }
   };
 
+  // 16x16x32 fragments: 16-row block at row R (a multiple of 16), k-step ks
+  // (32 values): lane l reads row R + l%16, logical chunk 4 ks + l/16, at
+  // physical chunk (4 ks + l/16) ^ sw(l%16) ^ sw(R); sw(R) = sw(16 (block % 4))
+  // for the wave's A blocks (a_row0 % 64 == 0) and B blocks (b_row0 % 128 == 0).
+  const int xl = lane & 15;
+  int lo16[2][4];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) lo16[ks][b] = xl * 128 + ((((4 * ks + (lane >> 4)) ^ sw(xl)) ^ sw(16 * b)) << 4);
+  // A fragments of k-step ks (4 blocks of 16 rows), B fragments of k-step ks,
+  // blocks 4 hb .. 4 hb + 3
+  auto load_a16 = [&](int t, int ks, bf16x8 (&fa)[4]) {
+    const char* sa = lds + ((2 * t + a_op) % kSlots) * kSlot + a_row0 * 128;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[i] = *reinterpret_cast<const bf16x8*>(sa + i * 2048 + lo16[ks][i]);
+  };
+  auto load_b16 = [&](int t, int ks, int hb, bf16x8 (&fb)[4]) {
+    const char* sb = lds + ((2 * t + 1 - a_op) % kSlots) * kSlot + b_row0 * 128 + hb * 8192;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) fb[j] = *reinterpret_cast<const bf16x8*>(sb + j * 2048 + lo16[ks][j]);
+  };
+  auto mfmas16 = [&](const bf16x8 (&fa)[4], const bf16x8 (&fb)[4], int hb) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc16[i][4 * hb + j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc16[i][4 * hb + j], 0, 0, 0);
+  };
+
   bf16x8 f0a[2], f0b[4], f1a[2], f1b[4];
+  bf16x8 g0a[4], g1a[4], g0b[4], g1b[4];
   if constexpr (W8) {
     // prologue: k-tile 0 in LDS; the weights of k-tile 1 in registers and
     // the activations of k-tile 1 (position 2) in flight
@@ -504,20 +553,22 @@ __global__ __launch_bounds__(512) void gemm_ring_kernel(GemmParams p) {
       // slot of the weights of t-1: both slots' readers passed the last barrier
       wait_vmcnt<2>();   // weights of t+1 in registers; the second half of the activations of t+1 may fly
       wput(2 * t + 3);
-      load_frags(t, 0, f0a, f0b);
-      load_frags(t, 1, f1a, f1b);
+      load_a16(t, 0, g0a);
+      load_b16(t, 0, 0, g0b);
+      load_b16(t, 0, 1, g1b);
       issue(2 * t + 4, 0);
-      mfmas(f0a, f0b);
+      mfmas16(g0a, g0b, 0);
       __builtin_amdgcn_sched_barrier(0);
       wload(2 * t + 5);
-      load_frags(t, 2, f0a, f0b);
+      load_a16(t, 1, g1a);
+      load_b16(t, 1, 0, g0b);
       issue(2 * t + 4, 1);
-      mfmas(f1a, f1b);
+      mfmas16(g0a, g1b, 1);
       __builtin_amdgcn_sched_barrier(0);
-      load_frags(t, 3, f1a, f1b);
-      mfmas(f0a, f0b);
+      load_b16(t, 1, 1, g1b);
+      mfmas16(g1a, g0b, 0);
       __builtin_amdgcn_sched_barrier(0);
-      mfmas(f1a, f1b);
+      mfmas16(g1a, g1b, 1);
       __builtin_amdgcn_sched_barrier(0);
       wait_vmcnt<kW8Loads + 4>();   // activations of t+1 landed; this k-tile's loads may fly
       wait_lgkm0();                 // this wave's widened weights of t+1 are in LDS
@@ -534,22 +585,43 @@ __global__ __launch_bounds__(512) void gemm_ring_kernel(GemmParams p) {
   for (int t = 0; t < KT; ++t) {
     // positions 2t+3 (weights of t+1) and 2t+4 (activations of t+2) go to the
     // slots of k-tile t-1, whose readers all passed the last barrier
-    load_frags(t, 0, f0a, f0b);
-    issue(2 * t + 3, 0);
-    load_frags(t, 1, f1a, f1b);
-    issue(2 * t + 3, 1);
-    mfmas(f0a, f0b);
-    __builtin_amdgcn_sched_barrier(0);
-    load_frags(t, 2, f0a, f0b);
-    issue(2 * t + 4, 0);
-    mfmas(f1a, f1b);
-    __builtin_amdgcn_sched_barrier(0);
-    load_frags(t, 3, f1a, f1b);
-    issue(2 * t + 4, 1);
-    mfmas(f0a, f0b);
-    __builtin_amdgcn_sched_barrier(0);
-    mfmas(f1a, f1b);
-    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (M16) {
+      load_a16(t, 0, g0a);
+      load_b16(t, 0, 0, g0b);
+      issue(2 * t + 3, 0);
+      load_b16(t, 0, 1, g1b);
+      issue(2 * t + 3, 1);
+      mfmas16(g0a, g0b, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      load_a16(t, 1, g1a);
+      load_b16(t, 1, 0, g0b);
+      issue(2 * t + 4, 0);
+      mfmas16(g0a, g1b, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      load_b16(t, 1, 1, g1b);
+      issue(2 * t + 4, 1);
+      mfmas16(g1a, g0b, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas16(g1a, g1b, 1);
+      __builtin_amdgcn_sched_barrier(0);
+    } else {
+      load_frags(t, 0, f0a, f0b);
+      issue(2 * t + 3, 0);
+      load_frags(t, 1, f1a, f1b);
+      issue(2 * t + 3, 1);
+      mfmas(f0a, f0b);
+      __builtin_amdgcn_sched_barrier(0);
+      load_frags(t, 2, f0a, f0b);
+      issue(2 * t + 4, 0);
+      mfmas(f1a, f1b);
+      __builtin_amdgcn_sched_barrier(0);
+      load_frags(t, 3, f1a, f1b);
+      issue(2 * t + 4, 1);
+      mfmas(f0a, f0b);
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas(f1a, f1b);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     wait_vmcnt<4>();   // own loads of k-tile t+1 have landed; activations of t+2 may fly
     wg_barrier();
   }
@@ -595,11 +667,15 @@ __global__ __launch_bounds__(512) void gemm_ring_kernel(GemmParams p) {
     else if (staged) store_tile_staged<EPI, true, 4>(p, accf, a_row0, b_row0, tok0, feat0, false, lane, stage);
     else store_tile<EPI, true>(p, accf, a_row0, b_row0, tok0, feat0, false, lane);
   } else {
-    if (staged && EPI == kEpiGatedResidual && !trans)
-      store_tile_staged_residual<W8 && !GRP, 2>(p, acc, a_row0, b_row0, tok0, feat0, lane, stage);
-    else if (staged)
-      store_tile_staged<EPI, W8 && !GRP, 4>(p, acc, a_row0, b_row0, tok0, feat0, trans, lane, stage, rope_tab);
-    else store_tile<EPI, W8 && !GRP>(p, acc, a_row0, b_row0, tok0, feat0, trans, lane);
+    auto finish = [&](const auto& ac) {
+      if (staged && EPI == kEpiGatedResidual && !trans)
+        store_tile_staged_residual<W8 && !GRP, 2>(p, ac, a_row0, b_row0, tok0, feat0, lane, stage);
+      else if (staged)
+        store_tile_staged<EPI, W8 && !GRP, 4>(p, ac, a_row0, b_row0, tok0, feat0, trans, lane, stage, rope_tab);
+      else store_tile<EPI, W8 && !GRP>(p, ac, a_row0, b_row0, tok0, feat0, trans, lane);
+    };
+    if constexpr (M16) finish(acc16);
+    else finish(acc);
   }
 }
 
