@@ -1,17 +1,18 @@
 // Full (non-causal) multi-head self-attention over all video-latent tokens,
 // the middle stage of the block (h3.c memory-techniques page, technique 2).
 //
-// bf16 path (flash-style, fp32 online softmax, v_mfma_f32_32x32x16_bf16):
+// bf16 path (flash-style, fp32 online softmax, v_mfma_f32_16x16x32_bf16,
+// whose streams hold a 10-14 % higher clock under the power limit than the
+// 32x32x16 form on MI355X):
 //   * one workgroup = NW waves x 32 queries of one head (NW = 8 for d = 128,
-//     4 for d = 64); each wave keeps its queries' Q fragments in registers and
-//     walks all keys in tiles of 32;
+//     4 for d = 64); each wave keeps its queries' Q fragments (two 16-query
+//     blocks) in registers and walks all keys in tiles of 32;
 //   * scores are computed transposed, S^T = K Q^T, so that the accumulator's
-//     lane index is the query: every lane owns its query's running reference
-//     and sum, and rescaling needs no cross-lane traffic except one xor-32
-//     exchange for a tile maximum;
-//   * K rows are read through a fixed key permutation (bits 2 and 3 of the
-//     key index swapped inside each 32-key block), so that the eight
-//     probabilities a lane holds per 16-key step are eight consecutive keys;
+//     lane index is the query: a query's 32 keys per tile lie in the four
+//     lanes l%16 + 16 g (8 keys each), which share its running reference;
+//     the row sums are combined across them once at the end;
+//   * K rows are read through a fixed key permutation, so that the eight
+//     probabilities a lane holds per query block are eight consecutive keys;
 //     they then serve directly as the B operand of O^T = V^T P^T;
 //   * V arrives transposed (V^T [H*d, ldvt], written so by the QKV projection),
 //     so the A operand of O^T = V^T P^T is a 16-byte read along the key axis;
@@ -65,26 +66,25 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_
 __device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff = 0) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, 0);
 }
-// Row halves are swapped when bit 2 xor bit 3 of the row is set (LDS banks).
-__device__ __forceinline__ int hswap(int r) { return ((r >> 2) ^ (r >> 3)) & 1; }
-// Key permutation inside a 32-key block: swap bits 2 and 3.
-__device__ __forceinline__ int kperm(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
+// Key permutation inside a 32-key tile: the 16x16 score block kb of the
+// wave takes as its A-row x the key 8 (x/4) + 4 kb + x%4, so that the four
+// scores lane l holds per block (rows 4 (l/16) .. +3) are, over the two
+// blocks, the eight consecutive keys 8 (l/16) .. +7: the B operand of the
+// V^T P^T product that lane supplies.
+__device__ __forceinline__ int kperm(int kb, int x) { return 8 * (x >> 2) + 4 * kb + (x & 3); }
 // Chunk swizzle of a K row of CPR 16-byte chunks (CPR = 16 for d = 128, 8 for
-// d = 64): the fragment reads of rows kperm(0..7), kperm(8..15) and of any 16
-// consecutive rows each land on distinct banks.
-template <int CPR> __device__ __forceinline__ int kswz(int r);
-template <> __device__ __forceinline__ int kswz<16>(int r) { return (r & 15) ^ (((r >> 3) & 1) << 2); }
-template <> __device__ __forceinline__ int kswz<8>(int r) { return (r & 7) ^ (((r >> 3) & 1) * 5); }
+// d = 64).  Measured on MI355X (ds_read_b128 throughput per access pattern),
+// the 16x16 fragment reads of the permuted rows are conflict-free with it.
+template <int CPR> __device__ __forceinline__ int kswz(int r) { return (r ^ (r >> 2)) & (CPR - 1); }
 
 template <int HD, int NW>
 __global__ __launch_bounds__(NW * 64) void attention_bf16_kernel(AttnParams p) {
   constexpr int KT = 32;                       // keys per tile
-  constexpr int KS = HD / 16;                  // k-steps of the score product
-  constexpr int DB = HD / 32;                  // 32-row blocks of O^T
+  constexpr int KS = HD / 32;                  // k-steps of the score product (16x16x32)
+  constexpr int DB = HD / 16;                  // 16-row blocks of O^T
   // K stage: [32 keys][HD dims] (HD*2-byte rows), 16-byte chunk c of row r at
-  // chunk c ^ kswz(r).  V^T stage: 2 planes (one per 16-key step) of
-  // [HD rows][32 B], the two 16-byte halves of row r swapped when hswap(r).
-  // Four slots of each; tile j lives in slot j % 4.
+  // chunk c ^ kswz(r).  V^T stage: 2 planes (one per 16 keys) of
+  // [HD rows][32 B].  Four slots of each; tile j lives in slot j % 4.
   constexpr int KROW = HD * 2, KBYTES = KT * KROW;
   constexpr int VPL = HD * 32, VBYTES = 2 * VPL;
   static_assert(KBYTES == NW * 1024, "one K load instruction per wave and tile");
@@ -95,7 +95,7 @@ __global__ __launch_bounds__(NW * 64) void attention_bf16_kernel(AttnParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int h = lane >> 5, l32 = lane & 31;
+  const int g = lane >> 4, x16 = lane & 15;
   const int nblk = p.q_tiles * p.n_heads;
   const int lin = xcd_remap(blockIdx.x, nblk);
   const int head = lin / p.q_tiles;
@@ -105,16 +105,20 @@ __global__ __launch_bounds__(NW * 64) void attention_bf16_kernel(AttnParams p) {
   const int q0 = qtile * (NW * 32) + wave * 32;
   const float sc = p.scale_log2;
 
-  // ---- Q fragments (B operand of S^T = K Q^T); queries >= N load as zero
-  bf16x8 qf[KS];
+  // ---- Q fragments (B operand of S^T = K Q^T) of the wave's two 16-query
+  // blocks: lane l holds query q0 + 16 qb + l%16, dims 32 ks + 8 (l/16) .. +8;
+  // queries >= N load as zero
+  bf16x8 qf[2][KS];
   {
     const __amdgpu_buffer_rsrc_t rq = rsrc(p.q, (uint32_t)((uint64_t)N * p.ldq * 2));
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const uint32_t off = (uint32_t)(q0 + l32) * (uint32_t)p.ldq * 2u + (head * HD + ks * 16 + h * 8) * 2;
-      const u32x4 v = bload16(rq, off);
-      qf[ks] = *reinterpret_cast<const bf16x8*>(&v);
-    }
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint32_t off = (uint32_t)(q0 + 16 * qb + x16) * (uint32_t)p.ldq * 2u + (head * HD + ks * 32 + g * 8) * 2;
+        const u32x4 v = bload16(rq, off);
+        qf[qb][ks] = *reinterpret_cast<const bf16x8*>(&v);
+      }
   }
 
   // ---- K tiles: direct-to-LDS loads, one 1 KiB instruction per wave: lane l
@@ -142,7 +146,7 @@ __global__ __launch_bounds__(NW * 64) void attention_bf16_kernel(AttnParams p) {
   const int st_pl = lane >> 5, st_row = wave * 16 + ((lane & 31) >> 1), st_h = lane & 1;
   const __amdgpu_buffer_rsrc_t rvt = rsrc(p.vt, (uint32_t)((uint64_t)p.n_heads * HD * p.ldvt * 2));
   const uint32_t vld_off = ((uint32_t)(head * HD + st_row) * (uint32_t)p.ldvt + st_pl * 16 + st_h * 8) * 2u;
-  const int vst_off = st_pl * VPL + st_row * 32 + ((st_h ^ hswap(st_row)) << 4);
+  const int vst_off = st_pl * VPL + st_row * 32 + (st_h << 4);
   auto vload_masked = [&](int t) {             // zero for keys >= N
     const int key0 = t * KT + st_pl * 16 + st_h * 8;
     u32x4 v = {0, 0, 0, 0};
@@ -157,97 +161,123 @@ __global__ __launch_bounds__(NW * 64) void attention_bf16_kernel(AttnParams p) {
   };
   auto vstore = [&](int t, const u32x4& v) { *reinterpret_cast<u32x4*>(vbuf + (t & 3) * VBYTES + vst_off) = v; };
   // full V^T tiles: direct-to-LDS, one 1 KiB instruction per wave: wave ->
-  // plane wave / (HD/32), rows 32 (wave % (HD/32)) + lane/2, physical half
-  // lane&1 (holding logical half (lane&1) ^ hswap(row))
+  // plane wave / (HD/32), rows 32 (wave % (HD/32)) + lane/2, half lane&1
   constexpr int RB = HD / 32;
   const int vd_row = 32 * (wave % RB) + (lane >> 1);
-  const uint32_t vdma_off = ((uint32_t)(head * HD + vd_row) * (uint32_t)p.ldvt + (wave / RB) * 16 +
-                             (((lane & 1) ^ hswap(vd_row)) * 8)) * 2u;
+  const uint32_t vdma_off = ((uint32_t)(head * HD + vd_row) * (uint32_t)p.ldvt + (wave / RB) * 16 + (lane & 1) * 8) * 2u;
   const int vdma_dst = (wave / RB) * VPL + 32 * (wave % RB) * 32;
   auto vdma = [&](int t) { lds_dma16(rvt, vbuf + (t & 3) * VBYTES + vdma_dst, vdma_off, (uint32_t)t * (KT * 2)); };
 
-  // ---- fragment addresses.  K: row kperm(l32), logical chunk 2ks+h;
-  // V^T: row l32 (+ db*32), plane = 16-key step.
-  const int kr = kperm(l32);
-  const int kq = kswz<CPR>(kr);
-  int k_off[KS];
+  // ---- fragment addresses.  K block kb, k-step ks: row kperm(kb, l%16),
+  // logical chunk 4 ks + l/16.  V^T block db: row 16 db + l%16, keys
+  // 8 (l/16) .. +8 = plane (l/16)/2, half (l/16)%2.
+  int k_off[2][KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) k_off[ks] = kr * KROW + (((2 * ks + h) ^ kq) << 4);
-  const int v_frag = l32 * 32 + ((h ^ hswap(l32)) << 4);
+  for (int kb = 0; kb < 2; ++kb) {
+    const int kr = kperm(kb, x16);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) k_off[kb][ks] = kr * KROW + (((4 * ks + g) ^ kswz<CPR>(kr)) << 4);
+  }
+  const int v_frag = (g >> 1) * VPL + x16 * 32 + ((g & 1) << 4);
 
-  f32x16 O[DB];
+  // O^T block (db, qb): lane l holds dims 16 db + 4 (l/16) .. +4 of query
+  // q0 + 16 qb + l%16.  S block (kb, qb) likewise holds keys
+  // 8 (l/16) + 4 kb .. +4 of the tile.  Element r (0..15) of a lane's tile
+  // scores is query block r/8, key 8 (l/16) + r%8.
+  f32x4 O[DB][2];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) O[db] = f32x16{};
-  float m_ref = -INFINITY, l_run = 0.f;
-  f32x16 S[2];
-  bf16x8 P[2][2];
+  for (int db = 0; db < DB; ++db) O[db][0] = O[db][1] = f32x4{};
+  float m_ref[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+  f32x4 S[2][2][2];                            // [tile parity][kb][qb]
+  bf16x8 P[2][2];                              // [tile parity][qb]
+  auto sel = [&](const f32x4 (&s)[2][2], int r) __attribute__((always_inline)) -> float { return s[(r >> 2) & 1][r >> 3][r & 3]; };
+  auto mfma16 = [](const bf16x8& a, const bf16x8& b, const f32x4& c) __attribute__((always_inline)) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  };
 
-  auto scores = [&](const char* kb, f32x16& s) {
-    s = f32x16{};
+  auto scores = [&](const char* kb_, f32x4 (&s)[2][2]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) s = mfma32a(*reinterpret_cast<const bf16x8*>(kb + k_off[ks]), qf[ks], s);
-  };
-  auto pv = [&](const char* vb, const bf16x8 (&pp)[2]) {
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb][0] = s[kb][1] = f32x4{};
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-        O[db] = mfma32a(*reinterpret_cast<const bf16x8*>(vb + m * VPL + db * 1024 + v_frag), pp[m], O[db]);
-  };
-  // keys >= N of tile t: lane half h, register r holds key 16*(r/8) + 8h + r%8
-  auto mask_tail = [&](f32x16& s, int t) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r)
-      if (t * KT + 16 * (r >> 3) + 8 * h + (r & 7) >= N) s[r] = -INFINITY;
-  };
-  // probabilities against the current reference; returns the lane's sum
-  auto expo = [&](const f32x16& s, bf16x8 (&pp)[2]) {
-    float ls0 = 0.f, ls1 = 0.f;
-#pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float pr = __builtin_amdgcn_exp2f(fmaf(s[8 * m + j], sc, -m_ref));
-        if (j & 1) ls1 += pr; else ls0 += pr;
-        pp[m][j] = static_cast<bf16>(pr);
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kb_ + k_off[kb][ks]);
+        s[kb][0] = mfma16(a, qf[0][ks], s[kb][0]);
+        s[kb][1] = mfma16(a, qf[1][ks], s[kb][1]);
       }
-    return ls0 + ls1;
+    }
   };
-  // move the reference to the maximum so far, rescale O and l, recompute
-  auto redo = [&](const f32x16& s, bf16x8 (&pp)[2]) {
-    float mx = -INFINITY;
+  auto pv = [&](const char* vb, const bf16x8 (&pp)[2]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave)) * sc;
-    const float m_new = fmaxf(m_ref, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
-    l_run *= alpha;
+    for (int db = 0; db < DB; ++db) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(vb + db * 512 + v_frag);
+      O[db][0] = mfma16(a, pp[0], O[db][0]);
+      O[db][1] = mfma16(a, pp[1], O[db][1]);
+    }
+  };
+  // keys >= N of tile t
+  auto mask_tail = [&](f32x4 (&s)[2][2], int t) __attribute__((always_inline)) {
 #pragma unroll
-    for (int db = 0; db < DB; ++db) O[db] *= alpha;
-    m_ref = m_new;
-    return expo(s, pp);
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (t * KT + 8 * g + 4 * kb + j >= N) s[kb][0][j] = s[kb][1][j] = -INFINITY;
+  };
+  // probabilities against the current references; returns the lane's larger
+  // per-query-block sum
+  auto expo = [&](const f32x4 (&s)[2][2], bf16x8 (&pp)[2], float (&ls)[2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      float a = 0.f, b = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float pr = __builtin_amdgcn_exp2f(fmaf(s[e >> 2][qb][e & 3], sc, -m_ref[qb]));
+        if (e & 1) b += pr; else a += pr;
+        pp[qb][e] = static_cast<bf16>(pr);
+      }
+      ls[qb] = a + b;
+    }
+  };
+  // move each query's reference to its maximum so far (over the four lanes
+  // holding its keys), rescale O and l, recompute
+  auto redo = [&](const f32x4 (&s)[2][2], bf16x8 (&pp)[2], float (&ls)[2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, s[e >> 2][qb][e & 3]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave)) * sc;
+      const float m_new = fmaxf(m_ref[qb], mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_ref[qb] - m_new);
+      l_run[qb] *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) O[db][qb] *= alpha;
+      m_ref[qb] = m_new;
+    }
+    expo(s, pp, ls);
   };
 
   // ---- one tile's work, t with K_{t+1} in K slot KSL and V_{t-1} in V slot
   // VSL: the scores of tile t+1 and the product with V of tile t-1 on the
   // matrix cores, the exponentials of tile t on the vector ALUs.  Chunk i
-  // issues an LDS read two chunks ahead, MFMA i (even: score k-step i/2,
-  // odd: 16-key step m and row block db of the V product) and EPM of the
-  // exponentials; sched_barrier keeps the chunks in this order, so that each
-  // wave alternates the two units.
-  auto step = [&](int t, auto u_c, auto ksl_c, auto vsl_c, bool mask) {
+  // issues an LDS read two chunks ahead, the two MFMAs (one per query block)
+  // of fragment i (even: K block and k-step i/2, odd: V^T block i/2) and EPM
+  // of the exponentials; sched_barrier keeps the chunks in this order, so
+  // that each wave alternates the two units.
+  auto step = [&](int t, auto u_c, auto ksl_c, auto vsl_c, bool mask) __attribute__((always_inline)) {
     constexpr int U = decltype(u_c)::value;
-    const char* kb = kbuf + decltype(ksl_c)::value * KBYTES;
+    const char* kb_ = kbuf + decltype(ksl_c)::value * KBYTES;
     const char* vb = vbuf + decltype(vsl_c)::value * VBYTES;
     if (mask) mask_tail(S[U], t);
-    constexpr int NMF = KS + 2 * DB;           // MFMAs per tile (16 or 8)
-    constexpr int EPM = 16 / NMF;              // exponentials per MFMA
-    auto frag = [&](int i) {
+    constexpr int NCH = 2 * KS + DB;           // chunks (fragments) per tile (16 or 8)
+    constexpr int EPM = 16 / NCH;              // exponentials per chunk
+    auto frag = [&](int i) __attribute__((always_inline)) {
       const int j = i >> 1;
-      const char* a = (i & 1) ? vb + (j / DB) * VPL + (j % DB) * 1024 + v_frag : kb + k_off[j];
+      const char* a = (i & 1) ? vb + j * 512 + v_frag : kb_ + k_off[j / KS][j % KS];
       return *reinterpret_cast<const bf16x8*>(a);
     };
-    bf16x8 fr[NMF];
+    bf16x8 fr[NCH];
     fr[0] = frag(0);
     fr[1] = frag(1);
     // The exponential chain is skewed by one: chunk i takes the scaled score
@@ -255,39 +285,42 @@ __global__ __launch_bounds__(NW * 64) void attention_bf16_kernel(AttnParams p) {
     // chunk) and sums element r - 1 (exponentiated in the previous chunk), so
     // no instruction waits on a result from its own chunk.
     float xa[17], pe[16];
-    float ls0 = 0.f, ls1 = 0.f;
-    auto sum_cvt = [&](int q) {
+    float ls[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+    auto sum_cvt = [&](int q) __attribute__((always_inline)) {
+      ls[q >> 3][q & 1] += pe[q];
       if (q & 1) {
-        ls1 += pe[q];
         P[U][q >> 3][(q & 7) - 1] = static_cast<bf16>(pe[q - 1]);
         P[U][q >> 3][q & 7] = static_cast<bf16>(pe[q]);
-      } else {
-        ls0 += pe[q];
       }
     };
-    xa[0] = fmaf(S[U][0], sc, -m_ref);
+    xa[0] = fmaf(sel(S[U], 0), sc, -m_ref[0]);
 #pragma unroll
-    for (int i = 0; i < NMF; ++i) {
-      if (i + 2 < NMF) fr[i + 2] = frag(i + 2);
+    for (int i = 0; i < NCH; ++i) {
+      if (i + 2 < NCH) fr[i + 2] = frag(i + 2);
+      const int j = i >> 1;
       if (i & 1) {
-        const int j = i >> 1;
-        O[j % DB] = mfma32a(fr[i], P[1 - U][j / DB], O[j % DB]);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) O[j][qb] = mfma16(fr[i], P[1 - U][qb], O[j][qb]);
       } else {
-        S[1 - U] = mfma32a(fr[i], qf[i >> 1], i == 0 ? f32x16{} : S[1 - U]);
+        const int kb = j / KS, ks = j % KS;
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          S[1 - U][kb][qb] = mfma16(fr[i], qf[qb][ks], ks == 0 ? f32x4{} : S[1 - U][kb][qb]);
       }
 #pragma unroll
       for (int e = 0; e < EPM; ++e) {
         const int r = i * EPM + e;
-        if (r + 1 < 16) xa[r + 1] = fmaf(S[U][r + 1], sc, -m_ref);
+        if (r + 1 < 16) xa[r + 1] = fmaf(sel(S[U], r + 1), sc, -m_ref[(r + 1) >> 3]);
         pe[r] = __builtin_amdgcn_exp2f(xa[r]);
         if (r >= 1) sum_cvt(r - 1);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
     sum_cvt(15);
-    float ls = ls0 + ls1;
-    if (__any(!(ls <= kLazyBound))) ls = redo(S[U], P[U]);
-    l_run += ls;
+    float lt[2] = {ls[0][0] + ls[0][1], ls[1][0] + ls[1][1]};
+    if (__any(!(lt[0] <= kLazyBound) || !(lt[1] <= kLazyBound))) redo(S[U], P[U], lt);
+    l_run[0] += lt[0];
+    l_run[1] += lt[1];
   };
 
   // ---- two tiles per barrier.  Pass (t0, t0+1), t0 odd, with SL = t0 % 4:
@@ -344,7 +377,12 @@ __global__ __launch_bounds__(NW * 64) void attention_bf16_kernel(AttnParams p) {
   wg_barrier();
   scores(kbuf, S[0]);
   if (T == 1) mask_tail(S[0], 0);
-  l_run += redo(S[0], P[0]);
+  {
+    float ls[2];
+    redo(S[0], P[0], ls);
+    l_run[0] += ls[0];
+    l_run[1] += ls[1];
+  }
   if (T > 1) scores(kbuf + KBYTES, S[1]);
   wg_barrier();                                // K slots 0 and 1 are refilled next
 
@@ -367,23 +405,24 @@ __global__ __launch_bounds__(NW * 64) void attention_bf16_kernel(AttnParams p) {
   }
   wait_vmcnt<0>();                             // no load left in flight at exit
 
-  // ---- normalise and store: register r of block db holds dv = db*32 + 8*(r/4) + 4h + r%4
-  {
-    const int q = q0 + l32;
-    const float lt = l_run + __shfl_xor(l_run, 32, kWave);
+  // ---- normalise and store: a query's row sum is spread over the four lanes
+  // l%16 + 16 g that hold its keys
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    float lt = l_run[qb] + __shfl_xor(l_run[qb], 16, kWave);
+    lt += __shfl_xor(lt, 32, kWave);
     const float inv = 1.0f / lt;
+    const int q = q0 + 16 * qb + x16;
     if (q < N) {
-      bf16* orow = p.o + (int64_t)q * p.ldo + head * HD;
+      bf16* orow = p.o + (int64_t)q * p.ldo + head * HD + 4 * g;
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+      for (int db = 0; db < DB; ++db) {
+        u32x2 out;
+        bf16* oe = reinterpret_cast<bf16*>(&out);
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          u32x2 out;
-          bf16* oe = reinterpret_cast<bf16*>(&out);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) oe[e] = static_cast<bf16>(O[db][4 * g + e] * inv);
-          *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * g + 4 * h) = out;
-        }
+        for (int e = 0; e < 4; ++e) oe[e] = static_cast<bf16>(O[db][qb][e] * inv);
+        *reinterpret_cast<u32x2*>(orow + db * 16) = out;
+      }
     }
   }
 }
