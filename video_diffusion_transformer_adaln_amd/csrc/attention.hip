@@ -57,9 +57,6 @@ struct AttnParams {
 
 constexpr float kLazyBound = 256.0f;   // a tile is redone when a lane's probability sum exceeds this
 
-__device__ __forceinline__ f32x16 mfma32a(const bf16x8& a, const bf16x8& b, const f32x16& c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }

@@ -96,7 +96,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 // four consecutive A-rows (features of the row-major output, tokens of the
 // transposed one) at one B-row.  Quad q (0..7) of 32-row B block jb lies at
 // A-row a_row0 + ai and B-row b_row0 + 32 jb + br:
-//  * v_mfma_f32_32x32x16 tiles acc[i][jb], registers 4g..4g+3 (i = q/4, g = q%4):
+//  * 32x32 tiles (the int8 MFMA's, converted to fp32) acc[i][jb], registers 4g..4g+3 (i = q/4, g = q%4):
 //    ai = 32 i + 8 g + 4 (lane/32), br = lane%32;
 //  * v_mfma_f32_16x16x32 tiles acc[I][2 jb + h], registers 0..3 (I = q/2, h = q%2):
 //    ai = 16 I + 4 (lane/16), br = 16 h + lane%16.
