@@ -85,7 +85,8 @@ typedef int32_t h3k_dtype;
  * scale per token row): u is quantised per row by the rule of
  * h3k_quantize_weights_int8, and FC2 is the int8 x int8 product with int32
  * accumulation, scaled by the row and channel scales (h3k_linear_int8).
- * Needs weight_dtype INT8, act_dtype BF16 and mlp_hidden a multiple of 128;
+ * Needs weight_dtype INT8, act_dtype BF16 and mlp_hidden a multiple of 128 and
+ * <= 2^17 (so that the int32 sum of int8 products cannot overflow);
  * 0 leaves FC2 as for the other projections.
  * int8_mlp_group: 0 gives every INT8 matrix per-row scales; G in {32, 64, 128}
  * quantises the two MLP matrices in groups of G input channels instead

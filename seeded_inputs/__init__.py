@@ -163,6 +163,15 @@ def gen_block_weights(shape: DitShape, block: int = 0, seed: int = BASE_SEED,
     return out
 
 
+def block_weight_bf16_bits(shape: DitShape, block: int, name: str, seed: int = BASE_SEED) -> np.ndarray:
+    """The bf16 storage of one weight matrix of a block (``gen_block_weights(shape,
+    block, seed)[name].storage`` without the fp32 copy), for uploading many
+    blocks quickly.  Only for bf16 workloads."""
+    if shape.dtype != "bf16" or name not in shape.weight_shapes() or name.startswith("b_"):
+        raise ValueError(f"{name} of {shape.name}: bf16 weight matrices only")
+    return bf16_bits(normal_f32(shape.weight_shapes()[name], WEIGHT_STD, seed, shape.config_id, block, name))
+
+
 def custom_shape(name: str, config_id: int, n_tokens: int, n_heads: int, head_dim: int,
                  mlp_hidden: int, dtype: str, int8_weights: bool = False, n_blocks: int = 1,
                  cond_dim: Optional[int] = None) -> DitShape:

@@ -27,3 +27,14 @@ def tiny_problem(n_tokens=5, n_heads=2, head_dim=4, mlp=12, weight_std=0.3, bias
         if k.startswith("w_"):
             vals[k] = (vals[k] * np.float32(weight_std / si.WEIGHT_STD)).astype(np.float32)
     return shape, x.values, c.values, vals
+
+
+# (case, rel-L2, bound) of every parity comparison that calls ``record``; the
+# terminal summary (conftest.py) prints them, so a quiet run still shows how
+# far each result is from the oracle.
+PARITY = []
+
+
+def record(case: str, err: float, bound: float) -> float:
+    PARITY.append((case, float(err), float(bound)))
+    return err

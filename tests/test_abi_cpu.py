@@ -120,8 +120,29 @@ def test_env_switch_disables_aliasing(monkeypatch):
     assert h3k.h3k_dit_plan(cfg_c2(alias=True)).alias_activations == 1
 
 
+def test_config_rejects_int8_fc2_beyond_int32_range():
+    """The row-quantised FC2 sums mlp_hidden int8 products in int32: F <= 2^17."""
+    ok = B.make_config(8, 128, 2, 64, 1 << 17, 128, B.H3K_BF16, B.H3K_INT8, int8_fc2_rows=True)
+    assert h3k.h3k_dit_workspace_size(ok) > 0
+    bad = B.make_config(8, 128, 2, 64, (1 << 17) + 128, 128, B.H3K_BF16, B.H3K_INT8, int8_fc2_rows=True)
+    out = ctypes.c_uint64()
+    assert h3k.lib().h3k_dit_workspace_size(ctypes.byref(bad), 1, ctypes.byref(out)) == B.H3K_ERR_UNSUPPORTED
+    assert "2^17" in h3k.last_error()
+
+
 # ---------------------------------------------------------------- validation
 FAKE = 0x7f0000000000          # never dereferenced: every call below fails before a launch
+
+
+def _no_gpu():
+    import torch
+    return torch.cuda.device_count() == 0
+
+
+# The calls below pass never-mapped device addresses and rely on validation
+# rejecting them before any launch; they run only where no GPU is visible, so
+# a validation regression can never send a kernel to those addresses.
+fake_pointers = pytest.mark.skipif(not _no_gpu(), reason="fake device pointers: run only without a GPU")
 
 
 def _weights(**over):
@@ -140,6 +161,7 @@ def _block(cfg, weights=None, x=FAKE + (100 << 32), c=FAKE + (101 << 32), out=FA
     return lib.h3k_dit_block_forward(ctypes.byref(cfg), ctypes.byref(w), x, c, out, ws, ws_bytes, None, None)
 
 
+@fake_pointers
 def test_reject_null_config_and_pointers():
     lib = h3k.lib()
     assert lib.h3k_dit_block_forward(None, None, 0, 0, 0, 0, 0, None, None) == B.H3K_ERR_NULL
@@ -148,6 +170,7 @@ def test_reject_null_config_and_pointers():
     assert "w_qkv" in h3k.last_error()
 
 
+@fake_pointers
 def test_reject_bad_shapes_and_dtypes():
     assert _block(cfg_c2(hidden=5000)) == B.H3K_ERR_SHAPE                        # D != H*d
     assert _block(cfg_c2(n_tokens=0)) == B.H3K_ERR_SHAPE
@@ -185,12 +208,14 @@ def test_reject_bad_shapes_and_dtypes():
     assert "beyond" in h3k.last_error()
 
 
+@fake_pointers
 def test_reject_int8_without_scales():
     cfg = cfg_c2(weight_dtype=B.H3K_INT8)
     assert _block(cfg) == B.H3K_ERR_NULL
     assert "scale" in h3k.last_error()
 
 
+@fake_pointers
 def test_reject_misalignment_workspace_overlap():
     cfg = cfg_c2()
     assert _block(cfg, x=FAKE + (100 << 32) + 4) == B.H3K_ERR_ALIGN
@@ -203,6 +228,7 @@ def test_reject_misalignment_workspace_overlap():
     assert _block(cfg, weights=w) == B.H3K_ERR_OVERLAP
 
 
+@fake_pointers
 def test_reject_bad_kernel_level_arguments():
     lib = h3k.lib()
     # linear: k not a multiple of 64 for bf16
@@ -264,12 +290,7 @@ def test_reject_bad_kernel_level_arguments():
     assert lib.h3k_token_unmerge(1, 8, 64, X, 64, Y, 64, X, 72, None) == B.H3K_ERR_SHAPE
 
 
-def _no_gpu():
-    import torch
-    return torch.cuda.device_count() == 0
-
-
-@pytest.mark.skipif(not _no_gpu(), reason="only meaningful (and only safe) without a GPU")
+@fake_pointers
 def test_valid_arguments_without_device_report_hip_error():
     assert _block(cfg_c2()) == B.H3K_ERR_HIP
     assert "device" in h3k.last_error()

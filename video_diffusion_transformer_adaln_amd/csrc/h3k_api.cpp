@@ -46,6 +46,7 @@ h3k_status fail(h3k_status code, const char* fmt, ...) {
 constexpr uint64_t kAlign = 256;
 constexpr int64_t kMaxOffset = (int64_t(1) << 31) - 1;   // 32-bit buffer offsets in the kernels
 constexpr int64_t kMaxRopeTokens = int64_t(1) << 24;       // token coordinates through an exact fp32 quotient
+constexpr int64_t kMaxInt8K = int64_t(1) << 17;           // int8 x int8 k-sums stay below 2^31 in int32
 
 uint64_t align_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
 int64_t esize(h3k_dtype d) { return d == H3K_F32 ? 4 : d == H3K_BF16 ? 2 : 1; }
@@ -106,6 +107,9 @@ h3k_status validate_config(const h3k_dit_config* c) {
   if (c->int8_fc2_rows &&
       (c->weight_dtype != H3K_INT8 || c->act_dtype != H3K_BF16 || c->mlp_hidden % 128 != 0))
     return fail(H3K_ERR_UNSUPPORTED, "int8_fc2_rows needs INT8 weights, BF16 activations and mlp_hidden a multiple of 128");
+  if (c->int8_fc2_rows && c->mlp_hidden > kMaxInt8K)   // |sum| <= k * 127^2 must fit the int32 accumulator
+    return fail(H3K_ERR_UNSUPPORTED, "int8_fc2_rows needs mlp_hidden <= 2^17 (int32 accumulation), got %d",
+                c->mlp_hidden);
   const int g = c->int8_mlp_group;
   if (g != 0 && g != 32 && g != 64 && g != 128) return fail(H3K_ERR_SHAPE, "int8_mlp_group must be 0, 32, 64 or 128");
   if (g && (c->weight_dtype != H3K_INT8 || c->act_dtype != H3K_BF16))
@@ -638,7 +642,7 @@ h3k_status h3k_linear_int8(int64_t m, int64_t n, int64_t k, const int8_t* xq, in
                            const void* residual, int64_t ldr, const float* gate, void* y, int64_t ldy,
                            hipStream_t stream) {
   if (epilogue < H3K_EPI_BIAS || epilogue > H3K_EPI_GATED_RESIDUAL) return fail(H3K_ERR_SHAPE, "bad epilogue %d", epilogue);
-  if (m < 0 || n < 8 || n % 8 || k < 128 || k % 128 || k > (1 << 17))
+  if (m < 0 || n < 8 || n % 8 || k < 128 || k % 128 || k > kMaxInt8K)
     return fail(H3K_ERR_SHAPE, "need m >= 0, n a multiple of 8, k a multiple of 128 and <= 2^17 (m=%lld n=%lld k=%lld)",
                 (long long)m, (long long)n, (long long)k);
   if (ldx < k || ldw < k || ldx % 16 || ldw % 16 || ldy < n || ldy % 8)
