@@ -236,6 +236,22 @@ h3k_status h3k_dit_stack_forward(const h3k_dit_config* cfg, const h3k_dit_block_
                                  void* workspace, uint64_t workspace_bytes,
                                  hipStream_t stream, h3k_dit_stats* stats);
 
+/* One block without a caller workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments and result as h3k_dit_block_forward
+ * (byte-identical output), but the block's intermediates live in a static
+ * device array of the library of H3K_NOALLOC_SCRATCH_BYTES (128 MiB): each GPU
+ * the library runs on holds its own copy until the process ends.  A config
+ * whose workspace (h3k_dit_workspace_size) exceeds it is rejected with
+ * H3K_ERR_WORKSPACE before anything is enqueued.  The call allocates nothing;
+ * its first call on a device looks up the array's device address there.
+ * All calls on one GPU share the array, so calls that overlap in time on one
+ * GPU (e.g. on two streams) race on it; serialise them. */
+#define H3K_NOALLOC_SCRATCH_BYTES (128ull << 20)
+h3k_status h3k_dit_block_forward_noalloc(const h3k_dit_config* cfg, const h3k_dit_block_weights* weights,
+                                         const void* x, const void* c, void* out,
+                                         hipStream_t stream, h3k_dit_stats* stats);
+
 /* Per-output-channel symmetric int8 quantisation of w [rows, cols] (F32 or BF16);
  * with int8_fc2_rows the forward calls apply the same rule to the rows of u:
  *   scales[o] = max_k |w[o,k]| / 127   (one fp32 division, correctly rounded)

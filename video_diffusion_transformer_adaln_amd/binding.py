@@ -78,6 +78,8 @@ _SIGNATURES = [
     ("h3k_dit_stack_forward", c_int32, [ctypes.POINTER(DitConfig), ctypes.POINTER(DitBlockWeights), c_int32,
                                         c_void_p, c_void_p, c_void_p, c_void_p, c_uint64, c_void_p,
                                         ctypes.POINTER(DitStats)]),
+    ("h3k_dit_block_forward_noalloc", c_int32, [ctypes.POINTER(DitConfig), ctypes.POINTER(DitBlockWeights),
+                                                c_void_p, c_void_p, c_void_p, c_void_p, ctypes.POINTER(DitStats)]),
     ("h3k_quantize_weights_int8", c_int32, [c_void_p, c_int32, c_int64, c_int64, c_void_p, c_void_p, c_void_p]),
     ("h3k_quantize_weights_int8_groups", c_int32, [c_void_p, c_int32, c_int64, c_int64, c_int32, c_void_p, c_void_p,
                                                    c_void_p]),
@@ -205,6 +207,15 @@ def h3k_dit_stack_forward(cfg: DitConfig, blocks: Sequence[DitBlockWeights], x, 
     nbytes = workspace.numel() * workspace.element_size() if workspace_bytes is None else workspace_bytes
     check(lib().h3k_dit_stack_forward(ctypes.byref(cfg), arr, nb, _ptr(x), _ptr(c), _ptr(out), _ptr(workspace),
                                       nbytes, _stream(stream), ctypes.byref(stats) if stats is not None else None))
+
+
+NOALLOC_SCRATCH_BYTES = 128 << 20
+
+
+def h3k_dit_block_forward_noalloc(cfg: DitConfig, weights: DitBlockWeights, x, c, out, stream=None,
+                                  stats: Optional[DitStats] = None) -> None:
+    check(lib().h3k_dit_block_forward_noalloc(ctypes.byref(cfg), ctypes.byref(weights), _ptr(x), _ptr(c), _ptr(out),
+                                              _stream(stream), ctypes.byref(stats) if stats is not None else None))
 
 
 def h3k_quantize_weights_int8(w, w_dtype: int, rows: int, cols: int, q, scales, stream=None) -> None:

@@ -21,7 +21,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libh3k.so")
 ARCH = "gfx950"
 
-SOURCES = ["h3k_api.cpp", "adaln_ln.hip", "gemm.hip", "attention.hip"]
+SOURCES = ["h3k_api.cpp", "adaln_ln.hip", "gemm.hip", "attention.hip", "noalloc.hip"]
 
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",

@@ -18,6 +18,7 @@
 #include <string>
 #include <vector>
 
+#include "api_internal.hpp"
 #include "h3k.h"
 #include "kernels.hpp"
 
@@ -474,6 +475,26 @@ h3k_status forward(const h3k_dit_config* cfg, const h3k_dit_block_weights* block
 }
 
 }  // namespace
+
+namespace h3k {
+
+h3k_status api_fail(h3k_status code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+h3k_status api_forward(const h3k_dit_config* cfg, const h3k_dit_block_weights* blocks, int32_t n_blocks,
+                       const void* x, const void* c, void* out, void* workspace, uint64_t workspace_bytes,
+                       hipStream_t stream, h3k_dit_stats* stats) {
+  return forward(cfg, blocks, n_blocks, x, c, out, workspace, workspace_bytes, stream, stats);
+}
+
+}  // namespace h3k
 
 // ======================================================================== C ABI
 extern "C" {
