@@ -457,7 +457,8 @@ def sp_share(b0, P=8, reps=5):
         "ln_mod": (None, lambda: B.h3k_ln_modulate(E, M, D, 1e-6, x, D, shift, scale, h, D)),
         "qkv": (2.0 * M * D * 3 * D, lambda: B.h3k_linear(E, E, M, 3 * D, D, h, D, b0["w_qkv"], D, None, None,
                                                             B.H3K_EPI_BIAS, None, 0, None, qk, 2 * D, vt, ldvt, 2 * D)),
-        "attention": (4.0 * N * N * Ds, lambda: B.h3k_attention(E, N, Hs, d, qa, Ds, ka, Ds, vta, N, oa, Ds)),
+        "attention": (4.0 * N * N * Ds, lambda: B.h3k_attention(E, N, Hs, d, qa, Ds, ka, Ds, vta, N, oa, Ds,
+                                                                           q_prescaled=True)),
         "out_proj": (2.0 * M * D * D, lambda: B.h3k_linear(E, E, M, D, D, o, D, b0["w_out"], D, None, None,
                                                             B.H3K_EPI_GATED_RESIDUAL, x, D, gate, y, D)),
         "mlp_up": (2.0 * M * D * F, lambda: B.h3k_linear(E, E, M, F, D, h, D, b0["w_up"], D, None, None,

@@ -369,10 +369,15 @@ h3k_status h3k_rope_3d(int64_t n_tokens, int64_t cols, int32_t head_dim, int32_t
 /* o[n, H*d] = per head softmax(q k^T / sqrt(d)) v, non-causal, no positional
  * terms; q [n, ldq], k [n, ldk] row-major (head j = columns j*d..j*d+d-1), v given
  * transposed as vt [H*d, ldvt] with ldvt >= n rounded up to 8.  dtype F32 or BF16;
- * d in {64, 128}.  Full self-attention over all tokens ([H3-memory] technique 2). */
+ * d in {64, 128}.  Full self-attention over all tokens ([H3-memory] technique 2).
+ * q_prescaled = 1 (BF16 only): q is given already multiplied by log2(e)/sqrt(d),
+ * the layout the block's QKV projection writes (its epilogue folds the softmax
+ * scale of the base-2 exponentials into q, with the one rounding it makes
+ * anyway); the result is the same softmax.  0: q as above. */
 h3k_status h3k_attention(h3k_dtype dtype, int32_t n, int32_t n_heads, int32_t head_dim,
                          const void* q, int64_t ldq, const void* k, int64_t ldk,
-                         const void* vt, int64_t ldvt, void* o, int64_t ldo, hipStream_t stream);
+                         const void* vt, int64_t ldvt, void* o, int64_t ldo, int32_t q_prescaled,
+                         hipStream_t stream);
 
 /* ---- profiler ------------------------------------------------------------- */
 /* capacity: max kernel launches recorded between resets (events are created here). */

@@ -243,9 +243,14 @@ def test_reject_bad_kernel_level_arguments():
     # RoPE beyond 2^24 tokens (coordinates come from an exact fp32 quotient)
     assert lib.h3k_rope_3d(1 << 25, 128, 128, 1 << 13, 1 << 6, 1 << 6, 0, FAKE, 128, None) == B.H3K_ERR_UNSUPPORTED
     # attention: head_dim 32, pitch too small
-    assert lib.h3k_attention(1, 100, 2, 32, FAKE, 64, FAKE, 64, FAKE, 104, FAKE, 64, None) == B.H3K_ERR_UNSUPPORTED
+    assert lib.h3k_attention(1, 100, 2, 32, FAKE, 64, FAKE, 64, FAKE, 104, FAKE, 64, 0, None) == B.H3K_ERR_UNSUPPORTED
+    # prescaled q: bf16 only, flag 0 or 1
+    assert lib.h3k_attention(0, 100, 2, 64, FAKE, 128, FAKE + (1 << 32), 128, FAKE + (2 << 32), 104,
+                             FAKE + (3 << 32), 128, 1, None) == B.H3K_ERR_UNSUPPORTED
+    assert lib.h3k_attention(1, 100, 2, 64, FAKE, 128, FAKE + (1 << 32), 128, FAKE + (2 << 32), 104,
+                             FAKE + (3 << 32), 128, 2, None) == B.H3K_ERR_SHAPE
     assert lib.h3k_attention(1, 100, 2, 64, FAKE, 128, FAKE + (1 << 32), 128, FAKE + (2 << 32), 96,
-                             FAKE + (3 << 32), 128, None) == B.H3K_ERR_SHAPE
+                             FAKE + (3 << 32), 128, 0, None) == B.H3K_ERR_SHAPE
     # quantiser: int8 source, overlapping q / w
     assert lib.h3k_quantize_weights_int8(FAKE, 2, 4, 64, FAKE + (1 << 32), FAKE + (2 << 32), None) == B.H3K_ERR_UNSUPPORTED
     assert lib.h3k_quantize_weights_int8(FAKE, 0, 4, 64, FAKE + 64, FAKE + (2 << 32), None) == B.H3K_ERR_OVERLAP

@@ -362,14 +362,29 @@ ATTN_CASES = [
 ]
 
 
+def _prescaled_q(q32, hd):
+    """q in the kernel's prescaled form, bf16(q * log2(e) / sqrt(d)) (one rounding, as the
+    block's QKV epilogue writes it), and the fp32 q the oracle's softmax(q k^T / sqrt(d))
+    then sees: the stored value times sqrt(d) / log2(e), i.e. times sqrt(d) ln 2."""
+    c = np.float32(1.4426950408889634 / np.sqrt(hd))
+    qp = _ht((q32 * c).astype(np.float32), "bf16")
+    q_oracle = (qp.values.astype(np.float64) * np.sqrt(hd) * np.log(2.0)).astype(np.float32)
+    return qp, q_oracle
+
+
+@pytest.mark.parametrize("pre", [False, True])
 @pytest.mark.parametrize("n,heads,hd,dtype,full", ATTN_CASES)
-def test_attention(B, n, heads, hd, dtype, full):
+def test_attention(B, n, heads, hd, dtype, full, pre):
     import torch
-    flush(f"attention n={n} heads={heads} d={hd} {dtype}")
+    if pre and dtype != "bf16":
+        pytest.skip("prescaled q is a bf16 layout")
+    flush(f"attention n={n} heads={heads} d={hd} {dtype} prescaled={pre}")
     D = heads * hd
     # q and k entries ~ N(0, 3^2), so q.k / sqrt(d) has std 3^2 = 9: softmax rows as peaked as the
     # block's (its logits have std about 10), so the running reference moves through the key tiles
-    q = _ht(_f32((n, D), 1.0, 820, "x") * 3.0, dtype)
+    q32 = _f32((n, D), 1.0, 820, "x") * 3.0
+    q = _ht(q32, dtype)
+    q_in, q_ref = (q, q.values) if not pre else _prescaled_q(q32, hd)
     k = _ht(_f32((n, D), 1.0, 820, "c") * 3.0, dtype)
     v = _ht(_f32((n, D), 1.0, 820, "w_qkv"), dtype)
     ldvt = ((n + 7) // 8) * 8
@@ -381,28 +396,30 @@ def test_attention(B, n, heads, hd, dtype, full):
     if ldvt > n:
         vtd[:, n:] = float("nan")        # padding must never reach the output
     o = torch.full((n, D), float("nan"), dtype=tdt, device="cuda")
-    B.h3k_attention(code, n, heads, hd, dev(q), D, dev(k), D, vtd, ldvt, o, D)
+    B.h3k_attention(code, n, heads, hd, dev(q_in), D, dev(k), D, vtd, ldvt, o, D, q_prescaled=pre)
     torch.cuda.synchronize()
     rows = np.arange(n) if full else sample_rows(n)
-    ref = oracle.attention(q.values[rows], k.values, v.values, heads)
+    ref = oracle.attention(q_ref[rows], k.values, v.values, heads)
     got = to_np(o)[rows]
     assert np.isfinite(got).all()
     tol = F32_TOL if dtype == "f32" else BF16_TOL
     if not full:
-        record(f"attention N={n} {heads}x{hd} {dtype} (logit std 9)", rel_l2(got, ref), tol)
+        record(f"attention N={n} {heads}x{hd} {dtype}{' prescaled q' if pre else ''} (logit std 9)",
+               rel_l2(got, ref), tol)
     assert rel_l2(got, ref) < tol
 
 
+@pytest.mark.parametrize("pre", [False, True])
 @pytest.mark.parametrize("n,hd,kind", [(700, 128, "ramp"), (2000, 128, "ramp"), (700, 64, "ramp"), (333, 128, "huge"),
                                         (100, 64, "huge")])
-def test_attention_moving_reference(B, n, hd, kind):
+def test_attention_moving_reference(B, n, hd, kind, pre):
     """The kernel's softmax reference moves only when a tile's probabilities
     would exceed a bound; these inputs make it move after the first tile.
     ramp: key rows scaled by 1 + 6 j / n, so later keys score ever higher;
     huge: queries scaled by 300 (logits of std ~100 in log2 units), where
     exponentials taken without moving the reference would overflow."""
     import torch
-    flush(f"attention moving reference n={n} d={hd} {kind}")
+    flush(f"attention moving reference n={n} d={hd} {kind} prescaled={pre}")
     heads = 2
     D = heads * hd
     q = _f32((n, D), 1.0, 821, "x") * 0.6
@@ -411,16 +428,19 @@ def test_attention_moving_reference(B, n, hd, kind):
         k = k * (1.0 + 6.0 * np.arange(n, dtype=np.float32)[:, None] / n)
     else:
         q = q * 300.0
-    q, k = _ht(q, "bf16"), _ht(k, "bf16")
+    q_in, q_ref = (_ht(q, "bf16"), None) if not pre else _prescaled_q(q, hd)
+    if not pre:
+        q_ref = q_in.values
+    k = _ht(k, "bf16")
     v = _ht(_f32((n, D), 1.0, 821, "w_qkv"), "bf16")
     ldvt = ((n + 7) // 8) * 8
     vt = np.zeros((D, ldvt), dtype=np.float32)
     vt[:, :n] = v.values.T
     vtd = torch.from_numpy(vt).to(torch.bfloat16).cuda()
     o = torch.full((n, D), float("nan"), dtype=torch.bfloat16, device="cuda")
-    B.h3k_attention(B.H3K_BF16, n, heads, hd, dev(q), D, dev(k), D, vtd, ldvt, o, D)
+    B.h3k_attention(B.H3K_BF16, n, heads, hd, dev(q_in), D, dev(k), D, vtd, ldvt, o, D, q_prescaled=pre)
     torch.cuda.synchronize()
-    ref = oracle.attention(q.values, k.values, v.values, heads)
+    ref = oracle.attention(q_ref, k.values, v.values, heads)
     got = to_np(o)
     assert np.isfinite(got).all()
     assert rel_l2(got, ref) < BF16_TOL

@@ -102,7 +102,7 @@ _SIGNATURES = [
     ("h3k_token_unmerge", c_int32, [c_int32, c_int64, c_int64, c_void_p, c_int64, c_void_p, c_int64, c_void_p,
                                     c_int64, c_void_p]),
     ("h3k_attention", c_int32, [c_int32, c_int32, c_int32, c_int32, c_void_p, c_int64, c_void_p, c_int64,
-                                c_void_p, c_int64, c_void_p, c_int64, c_void_p]),
+                                c_void_p, c_int64, c_void_p, c_int64, c_int32, c_void_p]),
     ("h3k_profiler_create", c_int32, [c_int32, ctypes.POINTER(c_void_p)]),
     ("h3k_profiler_destroy", c_int32, [c_void_p]),
     ("h3k_profiler_reset", c_int32, [c_void_p]),
@@ -275,9 +275,9 @@ def h3k_rope_3d(n_tokens: int, cols: int, head_dim: int, frames: int, height: in
 
 
 def h3k_attention(dtype: int, n: int, n_heads: int, head_dim: int, q, ldq: int, k, ldk: int, vt, ldvt: int, o,
-                  ldo: int, stream=None) -> None:
+                  ldo: int, q_prescaled: bool = False, stream=None) -> None:
     check(lib().h3k_attention(dtype, n, n_heads, head_dim, _ptr(q), ldq, _ptr(k), ldk, _ptr(vt), ldvt, _ptr(o),
-                              ldo, _stream(stream)))
+                              ldo, 1 if q_prescaled else 0, _stream(stream)))
 
 
 class Profiler:

@@ -55,7 +55,7 @@ struct AttnParams {
   float scale_log2;   // log2(e) / sqrt(d)
 };
 
-constexpr float kLazyBound = 256.0f;   // a tile is redone when a lane's probability sum exceeds this
+constexpr float kLazyBound = 1024.0f;   // a tile is redone when a lane's probability sum exceeds this
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
@@ -74,7 +74,7 @@ __device__ __forceinline__ int kperm(int kb, int x) { return 8 * (x >> 2) + 4 * 
 // the 16x16 fragment reads of the permuted rows are conflict-free with it.
 template <int CPR> __device__ __forceinline__ int kswz(int r) { return (r ^ (r >> 2)) & (CPR - 1); }
 
-template <int HD, int NW>
+template <int HD, int NW, bool QPRE>
 __global__ __launch_bounds__(NW * 64) void attention_bf16_kernel(AttnParams p) {
   constexpr int KT = 32;                       // keys per tile
   constexpr int KS = HD / 32;                  // k-steps of the score product (16x16x32)
@@ -184,18 +184,37 @@ __global__ __launch_bounds__(NW * 64) void attention_bf16_kernel(AttnParams p) {
   f32x4 O[DB][2];
 #pragma unroll
   for (int db = 0; db < DB; ++db) O[db][0] = O[db][1] = f32x4{};
-  float m_ref[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+  // Running references m (log2 units).  With QPRE, q arrives multiplied by
+  // log2(e)/sqrt(d) and every score product starts from the accumulator
+  // value -m (minit), so the scores already are s - m and feed the
+  // exponential directly; a moved reference shifts the pending scores of the
+  // next tile by the same amount.  Without QPRE the scores are raw q.k and
+  // one fma per element applies the scale and the reference.
+  float m_ref[2] = {QPRE ? 0.f : -INFINITY, QPRE ? 0.f : -INFINITY}, l_run[2] = {0.f, 0.f};
+  f32x4 minit[2] = {f32x4{}, f32x4{}};
   f32x4 S[2][2][2];                            // [tile parity][kb][qb]
-  bf16x8 P[2][2];                              // [tile parity][qb]
+  u32x4 P[2][2];                               // [tile parity][qb]: eight bf16 probabilities, in pairs
+  const bf16x2 ones2 = {static_cast<bf16>(1.0f), static_cast<bf16>(1.0f)};
   auto sel = [&](const f32x4 (&s)[2][2], int r) __attribute__((always_inline)) -> float { return s[(r >> 2) & 1][r >> 3][r & 3]; };
+  // exponent of element r: s - m in log2 units
+  auto xval = [&](const f32x4 (&s)[2][2], int r) __attribute__((always_inline)) -> float {
+    if constexpr (QPRE) return sel(s, r);
+    else return fmaf(sel(s, r), sc, -m_ref[r >> 3]);
+  };
   auto mfma16 = [](const bf16x8& a, const bf16x8& b, const f32x4& c) __attribute__((always_inline)) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  };
+  auto pb = [](const u32x4& w) __attribute__((always_inline)) { return __builtin_bit_cast(bf16x8, w); };
+  auto sinit = [&](int qb) __attribute__((always_inline)) -> f32x4 {
+    if constexpr (QPRE) return minit[qb];
+    else return f32x4{};
   };
 
   auto scores = [&](const char* kb_, f32x4 (&s)[2][2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      s[kb][0] = s[kb][1] = f32x4{};
+      s[kb][0] = sinit(0);
+      s[kb][1] = sinit(1);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(kb_ + k_off[kb][ks]);
@@ -204,12 +223,12 @@ __global__ __launch_bounds__(NW * 64) void attention_bf16_kernel(AttnParams p) {
       }
     }
   };
-  auto pv = [&](const char* vb, const bf16x8 (&pp)[2]) __attribute__((always_inline)) {
+  auto pv = [&](const char* vb, const u32x4 (&pp)[2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       const bf16x8 a = *reinterpret_cast<const bf16x8*>(vb + db * 512 + v_frag);
-      O[db][0] = mfma16(a, pp[0], O[db][0]);
-      O[db][1] = mfma16(a, pp[1], O[db][1]);
+      O[db][0] = mfma16(a, pb(pp[0]), O[db][0]);
+      O[db][1] = mfma16(a, pb(pp[1]), O[db][1]);
     }
   };
   // keys >= N of tile t
@@ -220,37 +239,66 @@ __global__ __launch_bounds__(NW * 64) void attention_bf16_kernel(AttnParams p) {
       for (int j = 0; j < 4; ++j)
         if (t * KT + 8 * g + 4 * kb + j >= N) s[kb][0][j] = s[kb][1][j] = -INFINITY;
   };
-  // probabilities against the current references; returns the lane's larger
-  // per-query-block sum
-  auto expo = [&](const f32x4 (&s)[2][2], bf16x8 (&pp)[2], float (&ls)[2]) __attribute__((always_inline)) {
+  // a query's sum over the tile's 32 keys, from the matrix cores: ones (A) times P^T (B),
+  // every lane of the query gets the full sum
+  const u32x4 ones8 = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
+  auto tile_sums = [&](const u32x4 (&pp)[2], float (&ls)[2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) ls[qb] = mfma16(pb(ones8), pb(pp[qb]), f32x4{})[0];
+  };
+  // probabilities against the current references, rounded to bf16 in
+  // pairs; the lane's per-query-block sums are taken from the rounded pairs
+  // (v_dot2 with (1, 1)), the values the product with V uses
+  auto expo = [&](const f32x4 (&s)[2][2], u32x4 (&pp)[2], float (&ls)[2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      float a = 0.f, b = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float pr = __builtin_amdgcn_exp2f(fmaf(s[e >> 2][qb][e & 3], sc, -m_ref[qb]));
-        if (e & 1) b += pr; else a += pr;
-        pp[qb][e] = static_cast<bf16>(pr);
+      for (int e = 0; e < 8; e += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(xval(s, 8 * qb + e));
+        const float p1 = __builtin_amdgcn_exp2f(xval(s, 8 * qb + e + 1));
+        const bf16x2 pr = {static_cast<bf16>(p0), static_cast<bf16>(p1)};
+        pp[qb][e >> 1] = __builtin_bit_cast(uint32_t, pr);
       }
-      ls[qb] = a + b;
     }
+    tile_sums(pp, ls);
   };
   // move each query's reference to its maximum so far (over the four lanes
-  // holding its keys), rescale O and l, recompute
-  auto redo = [&](const f32x4 (&s)[2][2], bf16x8 (&pp)[2], float (&ls)[2]) __attribute__((always_inline)) {
+  // holding its keys), rescale O and l, recompute.  `first`: the first tile,
+  // whose maximum becomes the reference (O and l are still zero).  With
+  // QPRE the scores are relative to the reference, so the current tile's
+  // and, when `fix_next`, the next tile's pending scores shift with it.
+  auto redo = [&](f32x4 (&s)[2][2], f32x4 (&sn)[2][2], bool fix_next, u32x4 (&pp)[2], float (&ls)[2],
+                  bool first) __attribute__((always_inline)) {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       float mx = -INFINITY;
 #pragma unroll
       for (int e = 0; e < 8; ++e) mx = fmaxf(mx, s[e >> 2][qb][e & 3]);
       mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave)) * sc;
-      const float m_new = fmaxf(m_ref[qb], mx);
-      const float alpha = __builtin_amdgcn_exp2f(m_ref[qb] - m_new);
-      l_run[qb] *= alpha;
+      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+      if constexpr (QPRE) {
+        const float delta = first ? mx : fmaxf(0.f, mx);
+        if (!first) {
+          const float alpha = __builtin_amdgcn_exp2f(-delta);
+          l_run[qb] *= alpha;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) O[db][qb] *= alpha;
-      m_ref[qb] = m_new;
+          for (int db = 0; db < DB; ++db) O[db][qb] *= alpha;
+        }
+        m_ref[qb] += delta;
+        minit[qb] = f32x4{-m_ref[qb], -m_ref[qb], -m_ref[qb], -m_ref[qb]};
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          s[kb][qb] -= delta;
+          if (fix_next) sn[kb][qb] -= delta;
+        }
+      } else {
+        const float m_new = fmaxf(m_ref[qb], mx * sc);
+        const float alpha = __builtin_amdgcn_exp2f(m_ref[qb] - m_new);
+        l_run[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) O[db][qb] *= alpha;
+        m_ref[qb] = m_new;
+      }
     }
     expo(s, pp, ls);
   };
@@ -277,45 +325,46 @@ __global__ __launch_bounds__(NW * 64) void attention_bf16_kernel(AttnParams p) {
     bf16x8 fr[NCH];
     fr[0] = frag(0);
     fr[1] = frag(1);
-    // The exponential chain is skewed by one: chunk i takes the scaled score
-    // of element r + 1, the exponential of element r (scaled in the previous
-    // chunk) and sums element r - 1 (exponentiated in the previous chunk), so
-    // no instruction waits on a result from its own chunk.
+    // The exponential chain is skewed by one: chunk i takes the exponent of
+    // element r + 1, the exponential of element r (whose exponent the
+    // previous chunk took) and rounds and sums element r - 1 (exponentiated
+    // in the previous chunk), so no instruction waits on a result from its
+    // own chunk.  Elements are rounded to bf16 in pairs and the pair summed
+    // with one v_dot2 against (1, 1).
     float xa[17], pe[16];
-    float ls[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
     auto sum_cvt = [&](int q) __attribute__((always_inline)) {
-      ls[q >> 3][q & 1] += pe[q];
       if (q & 1) {
-        P[U][q >> 3][(q & 7) - 1] = static_cast<bf16>(pe[q - 1]);
-        P[U][q >> 3][q & 7] = static_cast<bf16>(pe[q]);
+        const bf16x2 pr = {static_cast<bf16>(pe[q - 1]), static_cast<bf16>(pe[q])};
+        P[U][q >> 3][(q & 7) >> 1] = __builtin_bit_cast(uint32_t, pr);
       }
     };
-    xa[0] = fmaf(sel(S[U], 0), sc, -m_ref[0]);
+    xa[0] = xval(S[U], 0);
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       if (i + 2 < NCH) fr[i + 2] = frag(i + 2);
       const int j = i >> 1;
       if (i & 1) {
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) O[j][qb] = mfma16(fr[i], P[1 - U][qb], O[j][qb]);
+        for (int qb = 0; qb < 2; ++qb) O[j][qb] = mfma16(fr[i], pb(P[1 - U][qb]), O[j][qb]);
       } else {
         const int kb = j / KS, ks = j % KS;
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
-          S[1 - U][kb][qb] = mfma16(fr[i], qf[qb][ks], ks == 0 ? f32x4{} : S[1 - U][kb][qb]);
+          S[1 - U][kb][qb] = mfma16(fr[i], qf[qb][ks], ks == 0 ? sinit(qb) : S[1 - U][kb][qb]);
       }
 #pragma unroll
       for (int e = 0; e < EPM; ++e) {
         const int r = i * EPM + e;
-        if (r + 1 < 16) xa[r + 1] = fmaf(sel(S[U], r + 1), sc, -m_ref[(r + 1) >> 3]);
+        if (r + 1 < 16) xa[r + 1] = xval(S[U], r + 1);
         pe[r] = __builtin_amdgcn_exp2f(xa[r]);
         if (r >= 1) sum_cvt(r - 1);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
     sum_cvt(15);
-    float lt[2] = {ls[0][0] + ls[0][1], ls[1][0] + ls[1][1]};
-    if (__any(!(lt[0] <= kLazyBound) || !(lt[1] <= kLazyBound))) redo(S[U], P[U], lt);
+    float lt[2];
+    tile_sums(P[U], lt);
+    if (__any(!(lt[0] <= kLazyBound) || !(lt[1] <= kLazyBound))) redo(S[U], S[1 - U], true, P[U], lt, false);
     l_run[0] += lt[0];
     l_run[1] += lt[1];
   };
@@ -376,7 +425,7 @@ __global__ __launch_bounds__(NW * 64) void attention_bf16_kernel(AttnParams p) {
   if (T == 1) mask_tail(S[0], 0);
   {
     float ls[2];
-    redo(S[0], P[0], ls);
+    redo(S[0], S[1], false, P[0], ls, true);   // before S_1 is computed: it starts from the new reference
     l_run[0] += ls[0];
     l_run[1] += ls[1];
   }
@@ -406,9 +455,7 @@ __global__ __launch_bounds__(NW * 64) void attention_bf16_kernel(AttnParams p) {
   // l%16 + 16 g that hold its keys
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    float lt = l_run[qb] + __shfl_xor(l_run[qb], 16, kWave);
-    lt += __shfl_xor(lt, 32, kWave);
-    const float inv = 1.0f / lt;
+    const float inv = 1.0f / l_run[qb];
     const int q = q0 + 16 * qb + x16;
     if (q < N) {
       bf16* orow = p.o + (int64_t)q * p.ldo + head * HD + 4 * g;
@@ -492,7 +539,7 @@ __global__ __launch_bounds__(64) void attention_f32_kernel(AttnParamsF p) {
 }
 
 // ---------------------------------------------------------------------------
-template <int HD>
+template <int HD, bool QPRE>
 static void launch_bf16_attn(const AttentionArgs& a, hipStream_t stream) {
   constexpr int NW = HD / 16;
   AttnParams p;
@@ -503,7 +550,7 @@ static void launch_bf16_attn(const AttentionArgs& a, hipStream_t stream) {
   p.n = a.n; p.n_heads = a.n_heads;
   p.q_tiles = (a.n + NW * 32 - 1) / (NW * 32);
   p.scale_log2 = 1.4426950408889634f / sqrtf((float)HD);
-  attention_bf16_kernel<HD, NW><<<dim3(p.q_tiles * p.n_heads), dim3(NW * 64), 0, stream>>>(p);
+  attention_bf16_kernel<HD, NW, QPRE><<<dim3(p.q_tiles * p.n_heads), dim3(NW * 64), 0, stream>>>(p);
 }
 
 template <int HD>
@@ -524,8 +571,13 @@ hipError_t launch_attention(const AttentionArgs& a, hipStream_t stream) {
     if (a.head_dim == 64) launch_f32_attn<64>(a, stream);
     else launch_f32_attn<128>(a, stream);
   } else {
-    if (a.head_dim == 64) launch_bf16_attn<64>(a, stream);
-    else launch_bf16_attn<128>(a, stream);
+    if (a.q_prescaled) {
+      if (a.head_dim == 64) launch_bf16_attn<64, true>(a, stream);
+      else launch_bf16_attn<128, true>(a, stream);
+    } else {
+      if (a.head_dim == 64) launch_bf16_attn<64, false>(a, stream);
+      else launch_bf16_attn<128, false>(a, stream);
+    }
   }
   return hipGetLastError();
 }

@@ -48,6 +48,8 @@ struct GemmParams {
   bf16* y; int64_t ldy;
   bf16* yt; int64_t ldyt;
   int64_t split_col;
+  int64_t scale_cols;     // columns < scale_cols are multiplied by col_scale after the bias
+  float col_scale;
   int m, n, k;
   int tiles_m, tiles_n;
 };
@@ -118,13 +120,17 @@ __device__ __forceinline__ void quad(const f32x4 (&acc)[4][8], int jb, int q, in
 }
 
 // Epilogue math, fp32, one bf16 rounding at the store.
-// Row-major output, first step: features f..f+3 of token t, channel scale and bias.
+// Row-major output, first step: features f..f+3 of token t, channel scale and
+// bias, then the column scale (the attention scale folded into q; f..f+3 lie
+// on one side of scale_cols, a multiple of 8).
 template <bool W8>
 __device__ __forceinline__ void scale_bias4(const GemmParams& p, float (&v)[4], int f) {
+  const float cs = (int64_t)f < p.scale_cols ? p.col_scale : 1.0f;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     if constexpr (W8) v[e] *= p.w_scale[f + e];
     if (p.bias) v[e] += static_cast<float>(p.bias[f + e]);
+    v[e] *= cs;
   }
 }
 // Second step: the activation, rotation or gated residual.
@@ -758,6 +764,8 @@ static void launch_bf16(const LinearArgs& a, hipStream_t stream) {
   p.y = (bf16*)a.y; p.ldy = a.ldy;
   p.yt = (bf16*)a.yt; p.ldyt = a.ldyt;
   p.split_col = a.split_col;
+  p.scale_cols = a.scale_cols;
+  p.col_scale = a.col_scale;
   p.m = (int)a.m; p.n = (int)a.n; p.k = (int)a.k;
   p.tiles_m = (p.m + BM - 1) / BM;
   p.tiles_n = (p.n + BN - 1) / BN;

@@ -11,6 +11,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -372,13 +373,20 @@ h3k_status run_block(const h3k_dit_config* c, const h3k_dit_plan_info* P, const 
     L.rope_hd = c->head_dim; L.rope_h = c->rope_height; L.rope_w = c->rope_width;
     L.rope_spatial = c->rope_half_spatial ? 0.5f : 1.0f;
   }
+  // bf16: q is stored times log2(e)/sqrt(d), the softmax scale in the base-2
+  // exponent the attention kernel takes, so its scores need no rescaling
+  const bool q_pre = act == kBF16;
+  if (q_pre) {
+    L.scale_cols = D;
+    L.col_scale = 1.4426950408889634f / std::sqrt((float)c->head_dim);
+  }
   H3K_TRY(launched(launch_linear(L, s), "QKV projection"));
   rec.done(H3K_K_QKV);
 
   AttentionArgs A{};
   A.dt = act; A.n = N; A.n_heads = c->n_heads; A.head_dim = c->head_dim;
   A.q = qkv; A.ldq = 2 * D; A.k = qkv + D * eb; A.ldk = 2 * D; A.vt = vt; A.ldvt = P->vt_pitch;
-  A.o = o; A.ldo = D;
+  A.o = o; A.ldo = D; A.q_prescaled = q_pre;
   H3K_TRY(launched(launch_attention(A, s), "attention"));
   rec.done(H3K_K_ATTENTION);
 
@@ -786,8 +794,10 @@ h3k_status h3k_rope_3d(int64_t n_tokens, int64_t cols, int32_t head_dim, int32_t
 
 h3k_status h3k_attention(h3k_dtype dtype, int32_t n, int32_t n_heads, int32_t head_dim, const void* q, int64_t ldq,
                          const void* k, int64_t ldk, const void* vt, int64_t ldvt, void* o, int64_t ldo,
-                         hipStream_t stream) {
+                         int32_t q_prescaled, hipStream_t stream) {
   if (dtype != H3K_F32 && dtype != H3K_BF16) return fail(H3K_ERR_DTYPE, "dtype must be F32 or BF16");
+  if (q_prescaled != 0 && q_prescaled != 1) return fail(H3K_ERR_SHAPE, "q_prescaled must be 0 or 1");
+  if (q_prescaled && dtype != H3K_BF16) return fail(H3K_ERR_UNSUPPORTED, "q_prescaled needs BF16");
   if (head_dim != 64 && head_dim != 128) return fail(H3K_ERR_UNSUPPORTED, "head_dim %d not supported", head_dim);
   const int64_t D = (int64_t)n_heads * head_dim;
   if (n < 0 || n_heads < 1 || ldq < D || ldk < D || ldo < D || ldq % 8 || ldk % 8 || ldo % 8 || ldvt < ((n + 7) / 8) * 8 ||
@@ -808,6 +818,7 @@ h3k_status h3k_attention(h3k_dtype dtype, int32_t n, int32_t n_heads, int32_t he
   AttentionArgs A{};
   A.dt = (DType)dtype; A.n = n; A.n_heads = n_heads; A.head_dim = head_dim;
   A.q = q; A.ldq = ldq; A.k = k; A.ldk = ldk; A.vt = vt; A.ldvt = ldvt; A.o = o; A.ldo = ldo;
+  A.q_prescaled = q_prescaled != 0;
   return launched(launch_attention(A, stream), "attention");
 }
 

@@ -36,6 +36,8 @@ struct LinearArgs {
   int group;              // int8 weights: 0 = w_scale per row [n]; else w_scale [n, k / group]
   int rope_hd, rope_h, rope_w;   // kEpiBiasRope: head size and grid H, W (rows are tokens)
   float rope_spatial;            // 1, or 0.5 to halve the spatial coordinates
+  int64_t scale_cols;            // bf16 row-major output: columns < scale_cols are multiplied by
+  float col_scale;               // col_scale after the bias (and rotation), before the rounding
 };
 hipError_t launch_linear(const LinearArgs& a, hipStream_t stream);
 
@@ -46,6 +48,7 @@ struct AttentionArgs {
   const void* k; int64_t ldk;
   const void* vt; int64_t ldvt;
   void* o; int64_t ldo;
+  bool q_prescaled;       // bf16: q already multiplied by log2(e) / sqrt(head_dim)
 };
 hipError_t launch_attention(const AttentionArgs& a, hipStream_t stream);
 
