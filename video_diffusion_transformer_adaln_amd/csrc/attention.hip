@@ -4,32 +4,43 @@
 // bf16 path (flash-style, fp32 online softmax, v_mfma_f32_16x16x32_bf16,
 // whose streams hold a 10-14 % higher clock under the power limit than the
 // 32x32x16 form on MI355X):
-//   * one workgroup = NW waves x 32 queries of one head (NW = 8 for d = 128,
-//     4 for d = 64); each wave keeps its queries' Q fragments (two 16-query
-//     blocks) in registers and walks all keys in tiles of 32;
+//   * one workgroup = NW waves x 16 QB queries of one head (d = 128: 8 waves
+//     of two 16-query blocks; d = 64: 4 waves of two); each wave keeps its
+//     queries' Q fragments in registers and walks all keys in tiles of 32.
+//     Measured on MI355X: 4 waves of three or four blocks (one wave per
+//     SIMD, so that each LDS fragment feeds more products) ran 25 % slower,
+//     and 4 waves of two blocks (two workgroups per CU) 3 % slower;
 //   * scores are computed transposed, S^T = K Q^T, so that the accumulator's
 //     lane index is the query: a query's 32 keys per tile lie in the four
 //     lanes l%16 + 16 g (8 keys each), which share its running reference;
-//     the row sums are combined across them once at the end;
 //   * K rows are read through a fixed key permutation, so that the eight
 //     probabilities a lane holds per query block are eight consecutive keys;
 //     they then serve directly as the B operand of O^T = V^T P^T;
 //   * V arrives transposed (V^T [H*d, ldvt], written so by the QKV projection),
 //     so the A operand of O^T = V^T P^T is a 16-byte read along the key axis;
+//   * the softmax scale is folded into q: q arrives multiplied by
+//     log2(e)/sqrt(d) (the QKV projection's epilogue writes it so), and each
+//     score product starts from the accumulator value -m, so the scores come
+//     out as s - m, the exponent of v_exp_f32 (exp2).  Unscaled q (the
+//     standalone entry point's default) takes one fma per score instead;
+//   * a query's sum over a tile's 32 keys comes from the matrix cores: one
+//     MFMA of a ones fragment with the bf16 probabilities (the values the
+//     product with V uses), which also reduces over the four lanes;
 //   * software pipeline: the step for tile t runs the scores of tile t+1 and
 //     the product with V of tile t-1 on the matrix cores while the vector
 //     ALUs take the exponentials of tile t.  The three are independent; the
-//     step is written as chunks (an LDS read two chunks ahead, one MFMA, a
-//     share of the exponentials) kept in order by sched_barrier, so that
-//     each wave alternates the two units;
+//     step is written as chunks (an LDS read two chunks ahead, the MFMAs of
+//     that fragment, a share of the exponentials) kept in order by
+//     sched_barrier, so that each wave alternates the two units;
 //   * lazy online softmax without a per-tile maximum: probabilities are
-//     exp2(s - m) against the running reference m.  When some lane's tile sum
-//     exceeds 2^8 (a probability above 2^8, or the first tile, where m is
-//     still -inf) the tile is redone: m moves to the maximum so far, O and the
-//     row sum l (which hold tiles up to t-1, all relative to the old m) are
-//     scaled by exp2(m_old - m_new), and the exponentials are recomputed.
-//     The result is the usual online-softmax recurrence with the reference
-//     updated only when a probability would otherwise exceed 2^8;
+//     exp2(s - m) against the running reference m.  When a query's tile sum
+//     exceeds 2^10 (some probability above 2^5, or the first tile) the tile
+//     is redone: m moves to the maximum so far, O and the row sum l (which
+//     hold tiles up to t-1, all relative to the old m) are scaled by
+//     exp2(m_old - m_new), the pending scores of the next tile shift with
+//     the reference, and the exponentials are recomputed.  The result is the
+//     usual online-softmax recurrence with the reference updated only when
+//     the probabilities would otherwise grow large;
 //   * two tiles per workgroup barrier: K tiles and full V^T tiles arrive
 //     with direct-to-LDS loads, the V^T tiles of the last passes through
 //     registers (keys beyond N are zeroed there), all in rings of four
@@ -55,7 +66,12 @@ struct AttnParams {
   float scale_log2;   // log2(e) / sqrt(d)
 };
 
-constexpr float kLazyBound = 1024.0f;   // a tile is redone when a lane's probability sum exceeds this
+// a tile is redone when a query's probability sum over the tile's 32 keys exceeds this
+constexpr float kLazyBound = 1024.0f;
+// bf16 kernel for head_dim 128: waves per workgroup, and 16-query blocks per
+// wave (head_dim 64 uses 4 waves of 2 blocks)
+constexpr int kAttnWaves128 = 8;
+constexpr int kAttnQBlocks128 = 2;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
@@ -74,8 +90,9 @@ __device__ __forceinline__ int kperm(int kb, int x) { return 8 * (x >> 2) + 4 * 
 // the 16x16 fragment reads of the permuted rows are conflict-free with it.
 template <int CPR> __device__ __forceinline__ int kswz(int r) { return (r ^ (r >> 2)) & (CPR - 1); }
 
-template <int HD, int NW, bool QPRE>
-__global__ __launch_bounds__(NW * 64) void attention_bf16_kernel(AttnParams p) {
+template <int HD, int NW, int QB, bool QPRE>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(QB > 2 ? 1 : 2, QB > 2 ? 1 : 2)))
+void attention_bf16_kernel(AttnParams p) {
   constexpr int KT = 32;                       // keys per tile
   constexpr int KS = HD / 32;                  // k-steps of the score product (16x16x32)
   constexpr int DB = HD / 16;                  // 16-row blocks of O^T
@@ -84,8 +101,9 @@ __global__ __launch_bounds__(NW * 64) void attention_bf16_kernel(AttnParams p) {
   // [HD rows][32 B].  Four slots of each; tile j lives in slot j % 4.
   constexpr int KROW = HD * 2, KBYTES = KT * KROW;
   constexpr int VPL = HD * 32, VBYTES = 2 * VPL;
-  static_assert(KBYTES == NW * 1024, "one K load instruction per wave and tile");
-  static_assert(HD == NW * 16, "one V^T load per lane and tile");
+  constexpr int LPW = HD / (16 * NW);          // K (and V^T) load instructions per wave and tile
+  static_assert(LPW >= 1 && KBYTES == NW * LPW * 1024, "whole 1 KiB K load instructions per wave and tile");
+  static_assert(HD == NW * LPW * 16, "whole V^T loads per lane and tile");
   __shared__ __attribute__((aligned(1024))) char lds[4 * KBYTES + 4 * VBYTES];
   char* const kbuf = lds;                      // slot u at kbuf + u * KBYTES
   char* const vbuf = lds + 4 * KBYTES;         // slot u at vbuf + u * VBYTES
@@ -99,17 +117,18 @@ __global__ __launch_bounds__(NW * 64) void attention_bf16_kernel(AttnParams p) {
   const int qtile = lin - head * p.q_tiles;
   const int N = p.n;
   const int T = (N + KT - 1) / KT;
-  const int q0 = qtile * (NW * 32) + wave * 32;
+  constexpr int QW = 16 * QB;                  // queries per wave
+  const int q0 = qtile * (NW * QW) + wave * QW;
   const float sc = p.scale_log2;
 
   // ---- Q fragments (B operand of S^T = K Q^T) of the wave's two 16-query
   // blocks: lane l holds query q0 + 16 qb + l%16, dims 32 ks + 8 (l/16) .. +8;
   // queries >= N load as zero
-  bf16x8 qf[2][KS];
+  bf16x8 qf[QB][KS];
   {
     const __amdgpu_buffer_rsrc_t rq = rsrc(p.q, (uint32_t)((uint64_t)N * p.ldq * 2));
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const uint32_t off = (uint32_t)(q0 + 16 * qb + x16) * (uint32_t)p.ldq * 2u + (head * HD + ks * 32 + g * 8) * 2;
@@ -118,52 +137,73 @@ __global__ __launch_bounds__(NW * 64) void attention_bf16_kernel(AttnParams p) {
       }
   }
 
-  // ---- K tiles: direct-to-LDS loads, one 1 KiB instruction per wave: lane l
-  // -> row wave*RPI + l/CPR, physical chunk l%CPR, fetching logical chunk
-  // phys ^ kswz(row).  Rows >= N load as zero (buffer bounds); tiles past the
-  // last one re-load the last tile so that the load counts stay uniform.
+  // ---- K tiles: direct-to-LDS loads, LPW 1 KiB instructions per wave;
+  // instruction u = wave + NW j: lane l -> row u*RPI + l/CPR, physical chunk
+  // l%CPR, fetching logical chunk phys ^ kswz(row).  Rows >= N load as zero
+  // (buffer bounds); tiles past the last one re-load the last tile so that
+  // the load counts stay uniform.
   constexpr int CPR = KROW / 16;               // chunks per K row
   constexpr int RPI = 64 / CPR;                // rows per load instruction
   const __amdgpu_buffer_rsrc_t rk = rsrc(p.k, (uint32_t)((uint64_t)N * p.ldk * 2));
-  uint32_t kdma_off;
-  {
-    const int row = wave * RPI + lane / CPR;
+  uint32_t kdma_off[LPW];
+#pragma unroll
+  for (int j = 0; j < LPW; ++j) {
+    const int row = (wave + NW * j) * RPI + lane / CPR;
     const int c = (lane % CPR) ^ kswz<CPR>(row);
-    kdma_off = (uint32_t)row * (uint32_t)p.ldk * 2u + (head * HD + c * 8) * 2;
+    kdma_off[j] = (uint32_t)row * (uint32_t)p.ldk * 2u + (head * HD + c * 8) * 2;
   }
   const uint32_t ktile_bytes = (uint32_t)KT * (uint32_t)p.ldk * 2u;
   auto kdma = [&](int t) {
     const int tt = t < T ? t : T - 1;
-    lds_dma16(rk, kbuf + (t & 3) * KBYTES + wave * 1024, kdma_off, (uint32_t)tt * ktile_bytes);
+#pragma unroll
+    for (int j = 0; j < LPW; ++j)
+      lds_dma16(rk, kbuf + (t & 3) * KBYTES + (wave + NW * j) * 1024, kdma_off[j], (uint32_t)tt * ktile_bytes);
   };
 
-  // ---- V^T tiles of the last passes, through registers: one 16-byte load
-  // per lane: plane lane/32, row wave*16 + (lane%32)/2, half lane&1 (keys
-  // 16 plane + 8 half .. +8)
-  const int st_pl = lane >> 5, st_row = wave * 16 + ((lane & 31) >> 1), st_h = lane & 1;
+  // ---- V^T tiles of the last passes, through registers: LPW 16-byte loads
+  // per lane; piece j: plane lane/32, row (wave + NW j)*16 + (lane%32)/2,
+  // half lane&1 (keys 16 plane + 8 half .. +8)
+  const int st_pl = lane >> 5, st_h = lane & 1;
   const __amdgpu_buffer_rsrc_t rvt = rsrc(p.vt, (uint32_t)((uint64_t)p.n_heads * HD * p.ldvt * 2));
-  const uint32_t vld_off = ((uint32_t)(head * HD + st_row) * (uint32_t)p.ldvt + st_pl * 16 + st_h * 8) * 2u;
-  const int vst_off = st_pl * VPL + st_row * 32 + (st_h << 4);
-  auto vload_masked = [&](int t) {             // zero for keys >= N
+  auto st_row = [&](int j) { return (wave + NW * j) * 16 + ((lane & 31) >> 1); };
+  auto vload_masked = [&](int t, u32x4 (&v)[LPW]) {   // zero for keys >= N
     const int key0 = t * KT + st_pl * 16 + st_h * 8;
-    u32x4 v = {0, 0, 0, 0};
-    if (key0 < N) {
-      v = bload16(rvt, vld_off, (uint32_t)t * (KT * 2));
-      uint16_t* e = reinterpret_cast<uint16_t*>(&v);
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        if (key0 + j >= N) e[j] = 0;
+    for (int j = 0; j < LPW; ++j) {
+      v[j] = u32x4{0, 0, 0, 0};
+      if (key0 < N) {
+        const uint32_t off = ((uint32_t)(head * HD + st_row(j)) * (uint32_t)p.ldvt + st_pl * 16 + st_h * 8) * 2u;
+        v[j] = bload16(rvt, off, (uint32_t)t * (KT * 2));
+        uint16_t* e = reinterpret_cast<uint16_t*>(&v[j]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (key0 + i >= N) e[i] = 0;
+      }
     }
-    return v;
   };
-  auto vstore = [&](int t, const u32x4& v) { *reinterpret_cast<u32x4*>(vbuf + (t & 3) * VBYTES + vst_off) = v; };
-  // full V^T tiles: direct-to-LDS, one 1 KiB instruction per wave: wave ->
-  // plane wave / (HD/32), rows 32 (wave % (HD/32)) + lane/2, half lane&1
+  auto vstore = [&](int t, const u32x4 (&v)[LPW]) {
+#pragma unroll
+    for (int j = 0; j < LPW; ++j)
+      *reinterpret_cast<u32x4*>(vbuf + (t & 3) * VBYTES + st_pl * VPL + st_row(j) * 32 + (st_h << 4)) = v[j];
+  };
+  // full V^T tiles: direct-to-LDS, LPW 1 KiB instructions per wave;
+  // instruction u = wave + NW j -> plane u / (HD/32), rows 32 (u % (HD/32)) +
+  // lane/2, half lane&1
   constexpr int RB = HD / 32;
-  const int vd_row = 32 * (wave % RB) + (lane >> 1);
-  const uint32_t vdma_off = ((uint32_t)(head * HD + vd_row) * (uint32_t)p.ldvt + (wave / RB) * 16 + (lane & 1) * 8) * 2u;
-  const int vdma_dst = (wave / RB) * VPL + 32 * (wave % RB) * 32;
-  auto vdma = [&](int t) { lds_dma16(rvt, vbuf + (t & 3) * VBYTES + vdma_dst, vdma_off, (uint32_t)t * (KT * 2)); };
+  uint32_t vdma_off[LPW];
+  int vdma_dst[LPW];
+#pragma unroll
+  for (int j = 0; j < LPW; ++j) {
+    const int u = wave + NW * j;
+    const int vd_row = 32 * (u % RB) + (lane >> 1);
+    vdma_off[j] = ((uint32_t)(head * HD + vd_row) * (uint32_t)p.ldvt + (u / RB) * 16 + (lane & 1) * 8) * 2u;
+    vdma_dst[j] = (u / RB) * VPL + 32 * (u % RB) * 32;
+  }
+  auto vdma = [&](int t) {
+#pragma unroll
+    for (int j = 0; j < LPW; ++j)
+      lds_dma16(rvt, vbuf + (t & 3) * VBYTES + vdma_dst[j], vdma_off[j], (uint32_t)t * (KT * 2));
+  };
 
   // ---- fragment addresses.  K block kb, k-step ks: row kperm(kb, l%16),
   // logical chunk 4 ks + l/16.  V^T block db: row 16 db + l%16, keys
@@ -181,23 +221,31 @@ __global__ __launch_bounds__(NW * 64) void attention_bf16_kernel(AttnParams p) {
   // q0 + 16 qb + l%16.  S block (kb, qb) likewise holds keys
   // 8 (l/16) + 4 kb .. +4 of the tile.  Element r (0..15) of a lane's tile
   // scores is query block r/8, key 8 (l/16) + r%8.
-  f32x4 O[DB][2];
+  f32x4 O[DB][QB];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) O[db][0] = O[db][1] = f32x4{};
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) O[db][qb] = f32x4{};
   // Running references m (log2 units).  With QPRE, q arrives multiplied by
   // log2(e)/sqrt(d) and every score product starts from the accumulator
   // value -m (minit), so the scores already are s - m and feed the
   // exponential directly; a moved reference shifts the pending scores of the
   // next tile by the same amount.  Without QPRE the scores are raw q.k and
   // one fma per element applies the scale and the reference.
-  float m_ref[2] = {QPRE ? 0.f : -INFINITY, QPRE ? 0.f : -INFINITY}, l_run[2] = {0.f, 0.f};
-  f32x4 minit[2] = {f32x4{}, f32x4{}};
-  f32x4 S[2][2][2];                            // [tile parity][kb][qb]
-  u32x4 P[2][2];                               // [tile parity][qb]: eight bf16 probabilities, in pairs
+  float m_ref[QB], l_run[QB];
+  f32x4 minit[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m_ref[qb] = QPRE ? 0.f : -INFINITY;
+    l_run[qb] = 0.f;
+    minit[qb] = f32x4{};
+  }
+  f32x4 S[2][2][QB];                           // [tile parity][kb][qb]
+  u32x4 P[2][QB];                              // [tile parity][qb]: eight bf16 probabilities, in pairs
   const bf16x2 ones2 = {static_cast<bf16>(1.0f), static_cast<bf16>(1.0f)};
-  auto sel = [&](const f32x4 (&s)[2][2], int r) __attribute__((always_inline)) -> float { return s[(r >> 2) & 1][r >> 3][r & 3]; };
+  auto sel = [&](const f32x4 (&s)[2][QB], int r) __attribute__((always_inline)) -> float { return s[(r >> 2) & 1][r >> 3][r & 3]; };
   // exponent of element r: s - m in log2 units
-  auto xval = [&](const f32x4 (&s)[2][2], int r) __attribute__((always_inline)) -> float {
+  auto xval = [&](const f32x4 (&s)[2][QB], int r) __attribute__((always_inline)) -> float {
     if constexpr (QPRE) return sel(s, r);
     else return fmaf(sel(s, r), sc, -m_ref[r >> 3]);
   };
@@ -210,48 +258,51 @@ __global__ __launch_bounds__(NW * 64) void attention_bf16_kernel(AttnParams p) {
     else return f32x4{};
   };
 
-  auto scores = [&](const char* kb_, f32x4 (&s)[2][2]) __attribute__((always_inline)) {
+  auto scores = [&](const char* kb_, f32x4 (&s)[2][QB]) __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      s[kb][0] = sinit(0);
-      s[kb][1] = sinit(1);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) s[kb][qb] = sinit(qb);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(kb_ + k_off[kb][ks]);
-        s[kb][0] = mfma16(a, qf[0][ks], s[kb][0]);
-        s[kb][1] = mfma16(a, qf[1][ks], s[kb][1]);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) s[kb][qb] = mfma16(a, qf[qb][ks], s[kb][qb]);
       }
     }
   };
-  auto pv = [&](const char* vb, const u32x4 (&pp)[2]) __attribute__((always_inline)) {
+  auto pv = [&](const char* vb, const u32x4 (&pp)[QB]) __attribute__((always_inline)) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       const bf16x8 a = *reinterpret_cast<const bf16x8*>(vb + db * 512 + v_frag);
-      O[db][0] = mfma16(a, pb(pp[0]), O[db][0]);
-      O[db][1] = mfma16(a, pb(pp[1]), O[db][1]);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) O[db][qb] = mfma16(a, pb(pp[qb]), O[db][qb]);
     }
   };
   // keys >= N of tile t
-  auto mask_tail = [&](f32x4 (&s)[2][2], int t) __attribute__((always_inline)) {
+  auto mask_tail = [&](f32x4 (&s)[2][QB], int t) __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        if (t * KT + 8 * g + 4 * kb + j >= N) s[kb][0][j] = s[kb][1][j] = -INFINITY;
+        if (t * KT + 8 * g + 4 * kb + j >= N) {
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) s[kb][qb][j] = -INFINITY;
+        }
   };
   // a query's sum over the tile's 32 keys, from the matrix cores: ones (A) times P^T (B),
   // every lane of the query gets the full sum
   const u32x4 ones8 = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
-  auto tile_sums = [&](const u32x4 (&pp)[2], float (&ls)[2]) __attribute__((always_inline)) {
+  auto tile_sums = [&](const u32x4 (&pp)[QB], float (&ls)[QB]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) ls[qb] = mfma16(pb(ones8), pb(pp[qb]), f32x4{})[0];
+    for (int qb = 0; qb < QB; ++qb) ls[qb] = mfma16(pb(ones8), pb(pp[qb]), f32x4{})[0];
   };
   // probabilities against the current references, rounded to bf16 in
   // pairs; the lane's per-query-block sums are taken from the rounded pairs
   // (v_dot2 with (1, 1)), the values the product with V uses
-  auto expo = [&](const f32x4 (&s)[2][2], u32x4 (&pp)[2], float (&ls)[2]) __attribute__((always_inline)) {
+  auto expo = [&](const f32x4 (&s)[2][QB], u32x4 (&pp)[QB], float (&ls)[QB]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
         const float p0 = __builtin_amdgcn_exp2f(xval(s, 8 * qb + e));
@@ -267,10 +318,10 @@ __global__ __launch_bounds__(NW * 64) void attention_bf16_kernel(AttnParams p) {
   // whose maximum becomes the reference (O and l are still zero).  With
   // QPRE the scores are relative to the reference, so the current tile's
   // and, when `fix_next`, the next tile's pending scores shift with it.
-  auto redo = [&](f32x4 (&s)[2][2], f32x4 (&sn)[2][2], bool fix_next, u32x4 (&pp)[2], float (&ls)[2],
+  auto redo = [&](f32x4 (&s)[2][QB], f32x4 (&sn)[2][QB], bool fix_next, u32x4 (&pp)[QB], float (&ls)[QB],
                   bool first) __attribute__((always_inline)) {
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < QB; ++qb) {
       float mx = -INFINITY;
 #pragma unroll
       for (int e = 0; e < 8; ++e) mx = fmaxf(mx, s[e >> 2][qb][e & 3]);
@@ -307,7 +358,7 @@ __global__ __launch_bounds__(NW * 64) void attention_bf16_kernel(AttnParams p) {
   // VSL: the scores of tile t+1 and the product with V of tile t-1 on the
   // matrix cores, the exponentials of tile t on the vector ALUs.  Chunk i
   // issues an LDS read two chunks ahead, the two MFMAs (one per query block)
-  // of fragment i (even: K block and k-step i/2, odd: V^T block i/2) and EPM
+  // of fragment i (even: K block and k-step i/2, odd: V^T block i/2) and its
   // of the exponentials; sched_barrier keeps the chunks in this order, so
   // that each wave alternates the two units.
   auto step = [&](int t, auto u_c, auto ksl_c, auto vsl_c, bool mask) __attribute__((always_inline)) {
@@ -316,7 +367,8 @@ __global__ __launch_bounds__(NW * 64) void attention_bf16_kernel(AttnParams p) {
     const char* vb = vbuf + decltype(vsl_c)::value * VBYTES;
     if (mask) mask_tail(S[U], t);
     constexpr int NCH = 2 * KS + DB;           // chunks (fragments) per tile (16 or 8)
-    constexpr int EPM = 16 / NCH;              // exponentials per chunk
+    constexpr int NE = 8 * QB;                 // scores per lane and tile
+    // chunk i takes the exponentials of elements NE i / NCH .. NE (i+1) / NCH - 1
     auto frag = [&](int i) __attribute__((always_inline)) {
       const int j = i >> 1;
       const char* a = (i & 1) ? vb + j * 512 + v_frag : kb_ + k_off[j / KS][j % KS];
@@ -331,7 +383,7 @@ __global__ __launch_bounds__(NW * 64) void attention_bf16_kernel(AttnParams p) {
     // in the previous chunk), so no instruction waits on a result from its
     // own chunk.  Elements are rounded to bf16 in pairs and the pair summed
     // with one v_dot2 against (1, 1).
-    float xa[17], pe[16];
+    float xa[NE + 1], pe[NE];
     auto sum_cvt = [&](int q) __attribute__((always_inline)) {
       if (q & 1) {
         const bf16x2 pr = {static_cast<bf16>(pe[q - 1]), static_cast<bf16>(pe[q])};
@@ -345,28 +397,30 @@ __global__ __launch_bounds__(NW * 64) void attention_bf16_kernel(AttnParams p) {
       const int j = i >> 1;
       if (i & 1) {
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) O[j][qb] = mfma16(fr[i], pb(P[1 - U][qb]), O[j][qb]);
+        for (int qb = 0; qb < QB; ++qb) O[j][qb] = mfma16(fr[i], pb(P[1 - U][qb]), O[j][qb]);
       } else {
         const int kb = j / KS, ks = j % KS;
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
+        for (int qb = 0; qb < QB; ++qb)
           S[1 - U][kb][qb] = mfma16(fr[i], qf[qb][ks], ks == 0 ? sinit(qb) : S[1 - U][kb][qb]);
       }
 #pragma unroll
-      for (int e = 0; e < EPM; ++e) {
-        const int r = i * EPM + e;
-        if (r + 1 < 16) xa[r + 1] = xval(S[U], r + 1);
+      for (int r = NE * i / NCH; r < NE * (i + 1) / NCH; ++r) {
+        if (r + 1 < NE) xa[r + 1] = xval(S[U], r + 1);
         pe[r] = __builtin_amdgcn_exp2f(xa[r]);
         if (r >= 1) sum_cvt(r - 1);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    sum_cvt(15);
-    float lt[2];
+    sum_cvt(NE - 1);
+    float lt[QB];
     tile_sums(P[U], lt);
-    if (__any(!(lt[0] <= kLazyBound) || !(lt[1] <= kLazyBound))) redo(S[U], S[1 - U], true, P[U], lt, false);
-    l_run[0] += lt[0];
-    l_run[1] += lt[1];
+    bool over = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) over = over || !(lt[qb] <= kLazyBound);
+    if (__any(over)) redo(S[U], S[1 - U], true, P[U], lt, false);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) l_run[qb] += lt[qb];
   };
 
   // ---- two tiles per barrier.  Pass (t0, t0+1), t0 odd, with SL = t0 % 4:
@@ -387,13 +441,15 @@ __global__ __launch_bounds__(NW * 64) void attention_bf16_kernel(AttnParams p) {
     using V1 = std::integral_constant<int, SL>;
     kdma(t0 + 3);
     kdma(t0 + 4);
-    u32x4 va = {0, 0, 0, 0}, vb = {0, 0, 0, 0};
+    u32x4 va[LPW], vb[LPW];
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) va[j] = vb[j] = u32x4{0, 0, 0, 0};
     if constexpr (!TAIL) {
       vdma(t0 + 1);
       vdma(t0 + 2);
     } else {
-      if (t0 + 1 < T) va = vload_masked(t0 + 1);
-      if (t0 + 2 < T) vb = vload_masked(t0 + 2);
+      if (t0 + 1 < T) vload_masked(t0 + 1, va);
+      if (t0 + 2 < T) vload_masked(t0 + 2, vb);
     }
     step(t0, C1{}, K1{}, V0{}, TAIL && t0 == T - 1);
     if (!TAIL || t0 + 1 < T) step(t0 + 1, C0{}, K2{}, V1{}, TAIL && t0 + 1 == T - 1);
@@ -413,8 +469,11 @@ __global__ __launch_bounds__(NW * 64) void attention_bf16_kernel(AttnParams p) {
   kdma(2);
   kdma(3);
   {
-    const u32x4 v0 = vload_masked(0);
-    const u32x4 v1 = T > 1 ? vload_masked(1) : u32x4{0, 0, 0, 0};
+    u32x4 v0[LPW], v1[LPW];
+    vload_masked(0, v0);
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) v1[j] = u32x4{0, 0, 0, 0};
+    if (T > 1) vload_masked(1, v1);
     wait_vmcnt<0>();
     vstore(0, v0);
     vstore(1, v1);
@@ -424,10 +483,10 @@ __global__ __launch_bounds__(NW * 64) void attention_bf16_kernel(AttnParams p) {
   scores(kbuf, S[0]);
   if (T == 1) mask_tail(S[0], 0);
   {
-    float ls[2];
+    float ls[QB];
     redo(S[0], S[1], false, P[0], ls, true);   // before S_1 is computed: it starts from the new reference
-    l_run[0] += ls[0];
-    l_run[1] += ls[1];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) l_run[qb] += ls[qb];
   }
   if (T > 1) scores(kbuf + KBYTES, S[1]);
   wg_barrier();                                // K slots 0 and 1 are refilled next
@@ -451,10 +510,9 @@ __global__ __launch_bounds__(NW * 64) void attention_bf16_kernel(AttnParams p) {
   }
   wait_vmcnt<0>();                             // no load left in flight at exit
 
-  // ---- normalise and store: a query's row sum is spread over the four lanes
-  // l%16 + 16 g that hold its keys
+  // ---- normalise and store (every lane holds its query's full row sum)
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < QB; ++qb) {
     const float inv = 1.0f / l_run[qb];
     const int q = q0 + 16 * qb + x16;
     if (q < N) {
@@ -541,16 +599,17 @@ __global__ __launch_bounds__(64) void attention_f32_kernel(AttnParamsF p) {
 // ---------------------------------------------------------------------------
 template <int HD, bool QPRE>
 static void launch_bf16_attn(const AttentionArgs& a, hipStream_t stream) {
-  constexpr int NW = HD / 16;
+  constexpr int NW = HD == 128 ? kAttnWaves128 : 4;
+  constexpr int QB = HD == 128 ? kAttnQBlocks128 : 2;
   AttnParams p;
   p.q = (const bf16*)a.q; p.ldq = a.ldq;
   p.k = (const bf16*)a.k; p.ldk = a.ldk;
   p.vt = (const bf16*)a.vt; p.ldvt = a.ldvt;
   p.o = (bf16*)a.o; p.ldo = a.ldo;
   p.n = a.n; p.n_heads = a.n_heads;
-  p.q_tiles = (a.n + NW * 32 - 1) / (NW * 32);
+  p.q_tiles = (a.n + NW * 16 * QB - 1) / (NW * 16 * QB);
   p.scale_log2 = 1.4426950408889634f / sqrtf((float)HD);
-  attention_bf16_kernel<HD, NW, QPRE><<<dim3(p.q_tiles * p.n_heads), dim3(NW * 64), 0, stream>>>(p);
+  attention_bf16_kernel<HD, NW, QB, QPRE><<<dim3(p.q_tiles * p.n_heads), dim3(NW * 64), 0, stream>>>(p);
 }
 
 template <int HD>
