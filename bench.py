@@ -12,7 +12,8 @@ The timed region is bracketed by torch.cuda.synchronize(); every kernel
 launch is also bracketed by hipEvents recorded by the library itself on the
 launch stream (h3k_profiler), which gives the per-kernel durations used for
 the roofline of the dominant kernel.  The CPU baseline times the plain numpy
-oracle on the host cores on a bounded sample (see `cpu_baseline.sample`).
+oracle on the host cores on one full block of the same shape (see
+`cpu_baseline.sample`).
 """
 from __future__ import annotations
 
@@ -84,6 +85,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--layers", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-breadth", action="store_true",
+                    help="also time the oracle on one 6144-token block and one int8-weight block")
     ap.add_argument("--no-layers45", action="store_true")
     ap.add_argument("--no-extra-blocks", action="store_true",
                     help="skip the int8-weight block and the 6144-token block timings")
@@ -205,7 +208,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(step_flops, L)
+        cpu = cpu_baseline(step_flops, L, breadth=args.cpu_breadth)
 
     result = {
         "metric": METRIC,
@@ -499,47 +502,64 @@ def sp_share(b0, P=8, reps=5):
     }
 
 
-def cpu_baseline(step_flops, L):
-    """Time the numpy oracle on the host for one full-shape block.
-
-    The oracle's block cost is affine in the number of query rows it
-    computes (k and v for all tokens once, then per-row attention and MLP),
-    so it is timed for two row samples and extrapolated to all 22680 rows;
-    the step time is L times that block time."""
+def _oracle_block_ms(shape, int8=False):
+    """Wall time (ms) of one oracle block forward over every token of `shape`
+    (inputs drawn and, for int8 weights, quantised by the oracle beforehand,
+    outside the timed call)."""
     import oracle  # test infrastructure: CPU baseline only
     import seeded_inputs as si
-    try:
-        from threadpoolctl import threadpool_info
-        blas_threads = max([p.get("num_threads", 0) for p in threadpool_info()] + [1])
-    except Exception:
-        blas_threads = len(os.sched_getaffinity(0))
-    shape = si.C2
-    log("cpu baseline: generating one full-shape block on the host")
     hx, hc = si.gen_activation(shape)
     hw = si.gen_block_weights(shape, 0)
     w = {k: v.values for k, v in hw.items()}
-    n = shape.n_tokens
-    samples = (1024, 4096)
-    times = []
-    for r in samples:
-        rows = np.linspace(0, n - 1, r).astype(np.int64)
-        t0 = time.perf_counter()
-        oracle.block_forward(hx.values, hc.values, w, shape.n_heads, rows=rows)
-        times.append(time.perf_counter() - t0)
-        log(f"cpu baseline: {r} rows in {times[-1]:.2f} s")
-    slope = (times[1] - times[0]) / (samples[1] - samples[0])
-    t_block = times[0] + slope * (n - samples[0])
-    t_step = L * t_block
+    if int8:
+        for name in si.MATRIX_NAMES:
+            w[name] = oracle.quantize_int8(w[name])
+    t0 = time.perf_counter()
+    oracle.block_forward(hx.values, hc.values, w, shape.n_heads)
+    return (time.perf_counter() - t0) * 1e3
+
+
+def cpu_baseline(step_flops, L, breadth=False):
+    """The numpy oracle timed on this host: one full block of the step's shape
+    (all 22680 tokens, every head, both projections and the MLP), measured,
+    not extrapolated; the step is L such blocks.  BLAS runs on every core in
+    the process's affinity mask.  With `breadth`, also one full block of the
+    6144-token workload and of the int8-weight workload."""
+    import seeded_inputs as si
+    cores = len(os.sched_getaffinity(0))
+    blas = "unknown"
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+        limiter = threadpool_limits(limits=cores, user_api="blas")
+        libs = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        if libs:
+            blas = ", ".join(f"{p.get('internal_api')} {p.get('version')} ({p.get('num_threads')} threads)" for p in libs)
+    except Exception:
+        limiter = None
+    try:
+        log(f"cpu baseline: one full 22680-token block on {cores} host cores ({blas})")
+        t_block = _oracle_block_ms(si.C2)
+        log(f"cpu baseline: {t_block / 1e3:.1f} s per block")
+        per_block = {"n22680_d5120_bf16_inputs": round(t_block, 1)}
+        if breadth:
+            per_block["n6144_d3072_bf16_inputs"] = round(_oracle_block_ms(si.C1), 1)
+            per_block["n22680_d5120_int8_weights"] = round(_oracle_block_ms(si.C4, int8=True), 1)
+            log(f"cpu baseline, other workloads: {per_block}")
+    finally:
+        if limiter is not None:
+            limiter.restore_original_limits()
+    t_step = L * t_block / 1e3
     return {
         "value": round(step_flops / t_step / 1e12, 4),
         "unit": "TFLOP/s",
         "ms_per_step": round(t_step * 1e3, 1),
-        "cores": int(blas_threads),
+        "cores": cores,
         "kind": "oracle",
-        "sample": (f"one 864x480x56-frame block (the step's unit) timed for {samples[0]} and {samples[1]} "
-                   f"query rows (k, v for all {n} tokens), extrapolated affinely to {n} rows and times {L} "
-                   f"blocks; measured {times[0]:.2f} s and {times[1]:.2f} s; numpy fp32, BLAS threads = "
-                   f"{blas_threads}"),
+        "blas": blas,
+        "per_block_ms": per_block,
+        "sample": (f"one full 864x480x56-frame block (all {si.C2.n_tokens} tokens, 40 heads, D=5120, F=13824), "
+                   f"the step's unit of work, measured once: {t_block / 1e3:.1f} s; the step is {L} such blocks; "
+                   f"numpy fp32 oracle on bf16-valued inputs, {cores} cores ({blas})"),
     }
 
 
