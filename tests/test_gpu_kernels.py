@@ -469,7 +469,11 @@ def test_quantize_int8_groups_bit_exact(B, rows, cols, group, dtype):
 
 @pytest.mark.parametrize("rows,cols,dtype", [(15360, 5120, "f32"), (5120, 13824, "f32"), (300, 77, "f32"),
                                              (257, 1000, "bf16"), (3, 1, "f32"), (5120, 13824, "bf16"),
-                                             (301, 8, "bf16"), (7, 20, "bf16")])
+                                             (301, 8, "bf16"), (7, 20, "bf16"),
+                                             (22680, 13824, "bf16"),   # the rows of u (row-quantised FC2)
+                                             (64, 4104, "bf16"),       # one wave per row, a part-filled chunk column
+                                             (33, 24576, "bf16"),      # a workgroup per row, 12 chunks per lane
+                                             (5, 34816, "f32")])       # longer rows: the two-pass kernel
 def test_quantize_int8_bit_exact(B, rows, cols, dtype):
     import torch
     flush(f"quantize rows={rows} cols={cols} {dtype}")
@@ -480,5 +484,48 @@ def test_quantize_int8_bit_exact(B, rows, cols, dtype):
     q, s = R.quantize_int8(dev(ht))
     torch.cuda.synchronize()
     q_ref, s_ref = oracle.quantize_int8(ht.values)
+    assert np.array_equal(s.cpu().numpy(), s_ref)
+    assert np.array_equal(q.cpu().numpy(), q_ref)
+
+
+@pytest.mark.parametrize("cols,dtype", [(4096, "bf16"), (13824, "bf16"), (5120, "f32")])
+def test_quantize_int8_exact_ties(B, cols, dtype):
+    """Rows of k + 1/2 values with scale 2^e, so that w / s lands exactly on
+    rounding ties: the reciprocal fast path must hand these to the correctly
+    rounded division and round them half to even, bit-exact with the oracle."""
+    import torch
+    flush(f"quantize ties cols={cols} {dtype}")
+    rng = np.random.default_rng(cols)
+    rows = 64
+    k = rng.integers(-127, 127, size=(rows, cols)).astype(np.float32) + np.float32(0.5)
+    k[:, 0] = 127.0                                 # max |w| / 127 = 2^e exactly
+    w = (k * np.exp2(rng.integers(-12, 4, size=(rows, 1)))).astype(np.float32)
+    ht = _ht(w, dtype)
+    assert np.array_equal(ht.values, w)             # exactly representable in bf16 as well
+    from video_diffusion_transformer_adaln_amd import runtime as R
+    q, s = R.quantize_int8(dev(ht))
+    torch.cuda.synchronize()
+    q_ref, s_ref = oracle.quantize_int8(ht.values)
+    assert np.array_equal(s.cpu().numpy(), s_ref)
+    assert np.array_equal(q.cpu().numpy(), q_ref)
+    assert (np.abs(q_ref[:, 1:]) % 2 == 0).all()    # every tie went to the even neighbour
+
+
+@pytest.mark.parametrize("group", [32, 128])
+def test_quantize_int8_groups_exact_ties(B, group):
+    """The group-wise quantiser on rows of k + 1/2 values whose every group
+    has max |w| = 127 * 2^e: all other entries are exact rounding ties."""
+    import torch
+    flush(f"group quantize ties G={group}")
+    rng = np.random.default_rng(group)
+    rows, cols = 48, 2048
+    k = rng.integers(-127, 127, size=(rows, cols)).astype(np.float32) + np.float32(0.5)
+    k[:, ::group] = -127.0
+    w = (k * np.exp2(rng.integers(-12, 4, size=(rows, 1)))).astype(np.float32)
+    ht = _ht(w, "f32")
+    from video_diffusion_transformer_adaln_amd import runtime as R
+    q, s = R.quantize_int8_groups(dev(ht), group)
+    torch.cuda.synchronize()
+    q_ref, s_ref = oracle.quantize_int8_groups(ht.values, group)
     assert np.array_equal(s.cpu().numpy(), s_ref)
     assert np.array_equal(q.cpu().numpy(), q_ref)

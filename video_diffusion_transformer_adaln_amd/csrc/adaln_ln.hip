@@ -9,20 +9,18 @@
 namespace h3k {
 
 // ---------------------------------------------------------------------------
-// mod[row] = sum_k W[row, k] c[k] + b[row].  One wave per four output rows,
-// 16-byte loads along k (the four rows' loads of several iterations in flight
-// per lane: one row per wave left the HBM stream latency-bound at ~3.7 TB/s);
-// c is staged once per workgroup in LDS as fp32.  The sum order is fixed by
-// (lane, iteration), so results are deterministic.
+// mod[row] = sum_k W[row, k] c[k] + b[row].  One wave per GEMV_ROWS output
+// rows, 16-byte loads along k (the rows' loads of several iterations in
+// flight per lane: one row per wave left the HBM stream latency-bound at
+// ~3.7 TB/s).  c is read straight from global memory (it is small and stays
+// in the L1/L2 caches), so a workgroup starts streaming W at once.  The sum
+// order is fixed by (lane, iteration), so results are deterministic.
 constexpr int GEMV_ROWS = 4;
 template <typename T>
 __global__ __launch_bounds__(256) void adaln_gemv_kernel(const T* __restrict__ w, const T* __restrict__ b,
                                                          const T* __restrict__ c, float* __restrict__ mod,
                                                          int rows, int cols) {
   constexpr int RW = GEMV_ROWS;
-  extern __shared__ float c_lds[];
-  for (int i = threadIdx.x; i < cols; i += blockDim.x) c_lds[i] = to_f32(c[i]);
-  __syncthreads();
   const int lane = threadIdx.x % kWave;
   const int row0 = (blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave) * RW;
   if (row0 >= rows) return;
@@ -39,14 +37,13 @@ __global__ __launch_bounds__(256) void adaln_gemv_kernel(const T* __restrict__ w
     u32x4 raw[RW];
 #pragma unroll
     for (int r = 0; r < RW; ++r) raw[r] = *reinterpret_cast<const u32x4*>(wr[r] + k0);
-    float cv[V];
-#pragma unroll
-    for (int j = 0; j < V; ++j) cv[j] = c_lds[k0 + j];
+    const u32x4 craw = *reinterpret_cast<const u32x4*>(c + k0);
+    const T* ce = reinterpret_cast<const T*>(&craw);
 #pragma unroll
     for (int r = 0; r < RW; ++r) {
       const T* e = reinterpret_cast<const T*>(&raw[r]);
 #pragma unroll
-      for (int j = 0; j < V; ++j) acc[r] += to_f32(e[j]) * cv[j];
+      for (int j = 0; j < V; ++j) acc[r] += to_f32(e[j]) * to_f32(ce[j]);
     }
   }
 #pragma unroll
@@ -59,73 +56,89 @@ __global__ __launch_bounds__(256) void adaln_gemv_kernel(const T* __restrict__ w
 hipError_t launch_adaln_gemv(DType dt, int rows, int cols, const void* w, const void* b, const void* c,
                              float* mod, hipStream_t stream) {
   const dim3 block(256), grid((rows + 4 * GEMV_ROWS - 1) / (4 * GEMV_ROWS));
-  const size_t lds = sizeof(float) * (size_t)cols;
   if (dt == kBF16)
-    adaln_gemv_kernel<bf16><<<grid, block, lds, stream>>>((const bf16*)w, (const bf16*)b, (const bf16*)c, mod,
-                                                          rows, cols);
+    adaln_gemv_kernel<bf16><<<grid, block, 0, stream>>>((const bf16*)w, (const bf16*)b, (const bf16*)c, mod, rows,
+                                                        cols);
   else
-    adaln_gemv_kernel<float><<<grid, block, lds, stream>>>((const float*)w, (const float*)b, (const float*)c,
-                                                           mod, rows, cols);
+    adaln_gemv_kernel<float><<<grid, block, 0, stream>>>((const float*)w, (const float*)b, (const float*)c, mod,
+                                                         rows, cols);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
-// out = LN(x) (1 + scale) + shift.  One wave per row; the row is held in
-// registers (MAXC 16-byte chunks per lane, in its storage type, widened to
-// fp32 in each pass, which keeps the register count and so the number of
-// rows in flight per CU up), so mean and the biased variance are two exact
-// passes over registers, each closed by a wave reduction.
+// out = LN(x) (1 + scale) + shift.  One wave per row (two rows per wave, for
+// fewer shift/scale reads, measured 7 % slower: half the waves fit); the row is
+// held in registers (MAXC 16-byte chunks per lane, in its storage type,
+// widened to fp32 in each pass, which keeps the register count and so the
+// number of rows in flight per CU up), so mean and the biased variance are
+// two exact passes over registers, each closed by a wave reduction.
+template <int MAXC> constexpr int ln_rows() { return 1; }   // rows per wave
 template <typename T, int MAXC>
 __global__ __launch_bounds__(256) void ln_modulate_kernel(const T* __restrict__ x, int64_t ldx,
                                                           const float* __restrict__ shift,
                                                           const float* __restrict__ scale, T* __restrict__ out,
                                                           int64_t ldo, int n, int D, float eps) {
   constexpr int V = 16 / sizeof(T);
+  constexpr int R = ln_rows<MAXC>();
   const int lane = threadIdx.x % kWave;
-  const int row = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
-  if (row >= n) return;
+  const int row0 = (blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave) * R;
+  if (row0 >= n) return;
   const int chunks = D / V;
-  const T* xr = x + (int64_t)row * ldx;
-  u32x4 raw[MAXC];
+  u32x4 raw[R][MAXC];
 #pragma unroll
-  for (int i = 0; i < MAXC; ++i) {
-    const int ch = lane + i * kWave;
-    raw[i] = ch < chunks ? *reinterpret_cast<const u32x4*>(xr + ch * V) : u32x4{0, 0, 0, 0};
-  }
-  auto elem = [&](int i, int j) { return to_f32(reinterpret_cast<const T*>(&raw[i])[j]); };
-  float s = 0.f;
+  for (int r = 0; r < R; ++r) {
+    const T* xr = x + (int64_t)min(row0 + r, n - 1) * ldx;
 #pragma unroll
-  for (int i = 0; i < MAXC; ++i) {
-    const int ch = lane + i * kWave;
-    if (ch < chunks) {
-#pragma unroll
-      for (int j = 0; j < V; ++j) s += elem(i, j);
+    for (int i = 0; i < MAXC; ++i) {
+      const int ch = lane + i * kWave;
+      raw[r][i] = ch < chunks ? *reinterpret_cast<const u32x4*>(xr + ch * V) : u32x4{0, 0, 0, 0};
     }
   }
-  const float mean = wave_sum(s) / (float)D;
-  float ss = 0.f;
+  auto elem = [&](int r, int i, int j) { return to_f32(reinterpret_cast<const T*>(&raw[r][i])[j]); };
+  float mean[R], rstd[R];
 #pragma unroll
-  for (int i = 0; i < MAXC; ++i) {
-    const int ch = lane + i * kWave;
-    if (ch < chunks) {
+  for (int r = 0; r < R; ++r) {
+    float s = 0.f;
 #pragma unroll
-      for (int j = 0; j < V; ++j) { const float dlt = elem(i, j) - mean; ss += dlt * dlt; }
+    for (int i = 0; i < MAXC; ++i) {
+      const int ch = lane + i * kWave;
+      if (ch < chunks) {
+#pragma unroll
+        for (int j = 0; j < V; ++j) s += elem(r, i, j);
+      }
     }
+    mean[r] = wave_sum(s) / (float)D;
   }
-  const float var = wave_sum(ss) / (float)D;
-  const float rstd = 1.0f / sqrtf(var + eps);
-  T* orow = out + (int64_t)row * ldo;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i) {
+      const int ch = lane + i * kWave;
+      if (ch < chunks) {
+#pragma unroll
+        for (int j = 0; j < V; ++j) { const float dlt = elem(r, i, j) - mean[r]; ss += dlt * dlt; }
+      }
+    }
+    rstd[r] = 1.0f / sqrtf(wave_sum(ss) / (float)D + eps);
+  }
 #pragma unroll
   for (int i = 0; i < MAXC; ++i) {
     const int ch = lane + i * kWave;
     if (ch < chunks) {
       const int c0 = ch * V;
-      u32x4 res;
-      T* e = reinterpret_cast<T*>(&res);
+      float sc[V], sh[V];
 #pragma unroll
-      for (int j = 0; j < V; ++j)
-        e[j] = from_f32<T>((elem(i, j) - mean) * rstd * (1.0f + scale[c0 + j]) + shift[c0 + j]);
-      *reinterpret_cast<u32x4*>(orow + c0) = res;
+      for (int j = 0; j < V; ++j) { sc[j] = 1.0f + scale[c0 + j]; sh[j] = shift[c0 + j]; }
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        if (row0 + r >= n) break;
+        u32x4 res;
+        T* e = reinterpret_cast<T*>(&res);
+#pragma unroll
+        for (int j = 0; j < V; ++j) e[j] = from_f32<T>((elem(r, i, j) - mean[r]) * rstd[r] * sc[j] + sh[j]);
+        *reinterpret_cast<u32x4*>(out + (int64_t)(row0 + r) * ldo + c0) = res;
+      }
     }
   }
 }
@@ -133,7 +146,8 @@ __global__ __launch_bounds__(256) void ln_modulate_kernel(const T* __restrict__ 
 template <typename T, int MAXC>
 static void ln_launch(int n, int D, float eps, const void* x, int64_t ldx, const float* shift,
                       const float* scale, void* out, int64_t ldo, hipStream_t stream) {
-  ln_modulate_kernel<T, MAXC><<<dim3((n + 3) / 4), dim3(256), 0, stream>>>(
+  const int rows_per_block = 4 * ln_rows<MAXC>();
+  ln_modulate_kernel<T, MAXC><<<dim3((n + rows_per_block - 1) / rows_per_block), dim3(256), 0, stream>>>(
       (const T*)x, ldx, shift, scale, (T*)out, ldo, n, D, eps);
 }
 
@@ -201,6 +215,8 @@ hipError_t launch_rope(int64_t n, int64_t cols, int head_dim, int height, int wi
 // re-reads the row (mostly from L2) and does one correctly rounded fp32
 // division per element and round-half-to-even.  Rows whose length is not a
 // multiple of 8 (or not 16-byte aligned as a result) take a per-element path.
+// The vector paths divide through the reciprocal with an exact fallback
+// (quant8), which gives the same bits as the division.
 template <typename T> struct Vec8;
 template <> struct Vec8<bf16> {
   static __device__ __forceinline__ void load(const bf16* p, float (&v)[8]) {
@@ -222,6 +238,42 @@ template <> struct Vec8<float> {
 __device__ __forceinline__ int quant1(float v, float s) {
   if (s == 0.f) return 0;
   return (int)fminf(127.f, fmaxf(-127.f, rintf(v / s)));
+}
+
+// The same value through the reciprocal, with a rounding test in the manner
+// of Ziv (exact result from a fast approximation unless it lies near a
+// rounding boundary): y = v * r with r = v_rcp_f32(s) (within 1 ulp of 1/s)
+// is within 2^-15 of v / s, and the correctly rounded quotient fl(v / s)
+// within 2^-18 of it, since |v / s| <= 127 (1 + 2^-23) < 128.  When y lies
+// more than 2^-12 from every k + 1/2, rint(y) = rint(fl(v / s)); otherwise
+// (or when y is not finite, e.g. for a subnormal s) it returns false and the
+// caller takes quant1's correctly rounded division.  For s > 0 only.
+__device__ __forceinline__ bool quant_fast(float v, float r, int& q) {
+  const float y = v * r;
+  const float f = y - floorf(y);
+  if (!(fabsf(f - 0.5f) > 0x1p-12f)) return false;
+  q = (int)fminf(127.f, fmaxf(-127.f, rintf(y)));
+  return true;
+}
+// eight values of one scale: the fast path, then the exact division for any
+// value the rounding test sends back (rare: about 2^-11 of them)
+__device__ __forceinline__ void quant8(const float (&v)[8], float s, uint32_t& lo, uint32_t& hi) {
+  int q[8];
+  bool ok = s > 0.f;
+  const float r = __builtin_amdgcn_rcpf(s);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ok = quant_fast(v[i], r, q[i]) && ok;
+  if (!ok) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q[i] = quant1(v[i], s);
+  }
+  lo = hi = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t b = (uint32_t)(q[i] & 0xff);
+    if (i < 4) lo |= b << (8 * i);
+    else hi |= b << (8 * (i - 4));
+  }
 }
 
 template <typename T, bool VEC>
@@ -257,13 +309,8 @@ __global__ __launch_bounds__(256) void quantize_int8_kernel(const T* __restrict_
   for (int64_t g = lane; g < groups; g += kWave) {
     float v[8];
     Vec8<T>::load(wr + g * 8, v);
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t b = (uint32_t)(quant1(v[i], s) & 0xff);
-      if (i < 4) lo |= b << (8 * i);
-      else hi |= b << (8 * (i - 4));
-    }
+    uint32_t lo, hi;
+    quant8(v, s, lo, hi);
     *reinterpret_cast<u32x2*>(qr + g * 8) = u32x2{lo, hi};
   }
 }
@@ -298,13 +345,8 @@ __global__ __launch_bounds__(256) void quantize_int8_groups_kernel(const T* __re
     for (int off = LG / 2; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, kWave));
     const float sc = mx / 127.0f;
     if (lane % LG == 0) sr[c / LG] = sc;
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t b = (uint32_t)(quant1(v[i], sc) & 0xff);
-      if (i < 4) lo |= b << (8 * i);
-      else hi |= b << (8 * (i - 4));
-    }
+    uint32_t lo, hi;
+    quant8(v, sc, lo, hi);
     *reinterpret_cast<u32x2*>(qr + c * 8) = u32x2{lo, hi};
   }
 }
@@ -326,15 +368,93 @@ hipError_t launch_quantize_int8_groups(DType dt, const void* w, int64_t rows, in
   return hipGetLastError();
 }
 
+// One-pass variants: the row stays in registers between the absmax and the
+// quantisation, so it is read from memory once (the two-pass kernel's second
+// read of a 27 KB row of u misses the L2 once many rows are in flight).  A
+// row of up to 64 MAXC chunks of 8 values takes one wave (WAVES = 1, four
+// rows per workgroup); longer rows take the four waves of a workgroup
+// (WAVES = 4, their maxima met in LDS), so that each lane holds at most 16
+// chunks and enough rows stay in flight per CU.
+template <typename T, int MAXC, int WAVES>
+__global__ __launch_bounds__(256) void quantize_int8_rows_kernel(const T* __restrict__ w, int64_t rows,
+                                                                 int64_t cols, int8_t* __restrict__ q,
+                                                                 float* __restrict__ scales) {
+  constexpr int W = 16 / sizeof(T);            // 16-byte words per 8 values
+  constexpr int LANES = WAVES * kWave;         // lanes per row
+  __shared__ float wmax[4];
+  const int lane = threadIdx.x % LANES;
+  const int64_t row = (int64_t)blockIdx.x * (256 / LANES) + threadIdx.x / LANES;
+  if (WAVES == 1 && row >= rows) return;       // (a 4-wave workgroup is one whole row)
+  const T* wr = w + row * cols;
+  int8_t* qr = q + row * cols;
+  const int groups = (int)(cols / 8);
+  u32x4 raw[MAXC][8 / W];
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i) {
+    const int g = lane + i * LANES;
+#pragma unroll
+    for (int h = 0; h < 8 / W; ++h)
+      raw[i][h] = g < groups ? *reinterpret_cast<const u32x4*>(wr + g * 8 + h * W) : u32x4{0, 0, 0, 0};
+  }
+  auto vals = [&](int i, float (&v)[8]) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = to_f32(reinterpret_cast<const T*>(&raw[i][j / W])[j % W]);
+  };
+  float mx = 0.f;
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i) {
+    float v[8];
+    vals(i, v);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) mx = fmaxf(mx, fabsf(v[j]));
+  }
+  mx = wave_max(mx);
+  if constexpr (WAVES > 1) {
+    if (threadIdx.x % kWave == 0) wmax[threadIdx.x / kWave] = mx;
+    __syncthreads();
+    mx = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  }
+  const float s = mx / 127.0f;
+  if (lane == 0) scales[row] = s;
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i) {
+    const int g = lane + i * LANES;
+    if (g < groups) {
+      float v[8];
+      vals(i, v);
+      uint32_t lo, hi;
+      quant8(v, s, lo, hi);
+      *reinterpret_cast<u32x2*>(qr + (int64_t)g * 8) = u32x2{lo, hi};
+    }
+  }
+}
+
+template <typename T>
+static bool launch_rows_one_pass(const T* w, int64_t rows, int64_t cols, int8_t* q, float* scales,
+                                 hipStream_t stream) {
+  if (cols % 8) return false;
+  const int64_t per_wave = (cols / 8 + kWave - 1) / kWave, per_wg = (cols / 8 + 255) / 256;
+  const dim3 g1((unsigned)((rows + 3) / 4)), g4((unsigned)rows);
+  if (per_wave <= 4) quantize_int8_rows_kernel<T, 4, 1><<<g1, dim3(256), 0, stream>>>(w, rows, cols, q, scales);
+  else if (per_wave <= 8) quantize_int8_rows_kernel<T, 8, 1><<<g1, dim3(256), 0, stream>>>(w, rows, cols, q, scales);
+  else if (per_wave <= 16) quantize_int8_rows_kernel<T, 16, 1><<<g1, dim3(256), 0, stream>>>(w, rows, cols, q, scales);
+  else if (per_wg <= 8) quantize_int8_rows_kernel<T, 8, 4><<<g4, dim3(256), 0, stream>>>(w, rows, cols, q, scales);
+  else if (per_wg <= 16) quantize_int8_rows_kernel<T, 16, 4><<<g4, dim3(256), 0, stream>>>(w, rows, cols, q, scales);
+  else return false;
+  return true;
+}
+
 hipError_t launch_quantize_int8(DType dt, const void* w, int64_t rows, int64_t cols, int8_t* q, float* scales,
                                 hipStream_t stream) {
   if (rows == 0) return hipSuccess;
   const dim3 grid((unsigned)((rows + 3) / 4));
   const bool vec = cols % 8 == 0;   // row starts then stay 16-byte aligned (w and q are)
   if (dt == kBF16) {
+    if (launch_rows_one_pass((const bf16*)w, rows, cols, q, scales, stream)) return hipGetLastError();
     if (vec) quantize_int8_kernel<bf16, true><<<grid, dim3(256), 0, stream>>>((const bf16*)w, rows, cols, q, scales);
     else quantize_int8_kernel<bf16, false><<<grid, dim3(256), 0, stream>>>((const bf16*)w, rows, cols, q, scales);
   } else {
+    if (launch_rows_one_pass((const float*)w, rows, cols, q, scales, stream)) return hipGetLastError();
     if (vec) quantize_int8_kernel<float, true><<<grid, dim3(256), 0, stream>>>((const float*)w, rows, cols, q, scales);
     else quantize_int8_kernel<float, false><<<grid, dim3(256), 0, stream>>>((const float*)w, rows, cols, q, scales);
   }
