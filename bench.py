@@ -57,6 +57,8 @@ def ln_bytes(N, D, eb=2):
 COPY_BYTES = 512 * 2**20
 KERNEL_SOURCES = {"attention": "attention.hip", "qkv": "gemm.hip", "out_proj": "gemm.hip", "mlp_up": "gemm.hip",
                   "mlp_down": "gemm.hip"}
+TRAFFIC_KEYS = {"attention": "attention", "qkv": "qkv:bf16", "out_proj": "out_proj:bf16", "mlp_up": "mlp_up:bf16",
+                "mlp_down": "mlp_down:bf16"}
 
 
 def measured_traffic(kernel):
@@ -69,7 +71,7 @@ def measured_traffic(kernel):
     if not os.path.exists(path) or not os.path.isfile(src):
         return None
     with open(path) as f:
-        rec = json.load(f).get(kernel)
+        rec = json.load(f).get(TRAFFIC_KEYS.get(kernel, kernel))
     if not rec:
         return None
     with open(src, "rb") as f:
@@ -78,7 +80,132 @@ def measured_traffic(kernel):
     return rec.get("hbm_bytes_per_launch")
 
 
+# ---------------------------------------------------------------- rocprofv3 summaries
+# Library kernels and what they are in a block; the gated-residual GEMM serves the
+# out-projection and MLP-down, told apart by their order within each block.
+def kernel_role(name):
+    n = name.replace(" ", "")
+    if "attention_bf16_kernel" in n:
+        return "attention"
+    if "gemm_ring_kernel<" in n:
+        args = n.split("gemm_ring_kernel<", 1)[1].split(">", 1)[0].split(",")
+        epi, i8 = args[0], args[1] == "true"
+        w8 = len(args) > 2 and args[2] == "true"
+        grp = len(args) > 3 and args[3] == "true"
+        kind = "int8xint8" if i8 else ("w8a16_group" if grp else ("w8a16" if w8 else "bf16"))
+        return {"0": "qkv", "1": "mlp_up", "2": "gated", "3": "qkv_rope"}.get(epi, "gemm") + ":" + kind
+    for key, role in (("ln_modulate_kernel", "ln_mod"), ("adaln_gemv_kernel", "adaln"),
+                      ("quantize_int8_rows_kernel", "quantize_rows"), ("quantize_int8_kernel", "quantize_rows"),
+                      ("quantize_int8_groups_kernel", "quantize_groups"), ("copyBuffer", "copy")):
+        if key in n:
+            return role
+    return None
+
+
+def _csv_rows(path):
+    import csv
+    import glob
+    files = sorted(glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True))
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {path}")
+    with open(files[0]) as f:
+        return list(csv.DictReader(f))
+
+
+def _per_dispatch(path):
+    """dispatch id -> (kernel name, grid size, {counter: value summed over instances})"""
+    out = {}
+    for r in _csv_rows(path):
+        d = out.setdefault(int(r["Dispatch_Id"]), [r["Kernel_Name"], int(r["Grid_Size"]), {}])
+        d[2][r["Counter_Name"]] = d[2].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        d[2]["_dur_ns"] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+    return dict(sorted(out.items()))
+
+
+def _label(dispatches):
+    """(dispatch id, role) for every library dispatch; 'gated' becomes out_proj or
+    mlp_down by its order in the block (the out-projection comes first)."""
+    labels, gated_seen = {}, 0
+    for did, (name, grid, _) in dispatches.items():
+        role = kernel_role(name)
+        if role is None:
+            continue
+        if role.startswith("gated:"):
+            role = ("out_proj:" if gated_seen % 2 == 0 else "mlp_down:") + role.split(":")[1]
+            gated_seen += 1
+        labels[did] = role
+    return labels
+
+
+def summarize_profiles(root, write_traffic=True):
+    """Turn the rocprofv3 outputs under `root` (trace/, fetch/, write/, mfma/
+    from the commands in profiles/*.md) into profiles/traffic.json and print the
+    per-kernel tables those summaries quote."""
+    import hashlib
+    import statistics
+    sources = {"attention": "attention.hip", "gemm": "gemm.hip", "other": "adaln_ln.hip"}
+
+    def src_sha(role):
+        key = "attention" if role.startswith("attention") else ("gemm" if ":" in role else "other")
+        with open(os.path.join(ROOT, "video_diffusion_transformer_adaln_amd", "csrc", sources[key]), "rb") as f:
+            return hashlib.sha256(f.read()).hexdigest()
+
+    fetch, write = _per_dispatch(os.path.join(root, "fetch")), _per_dispatch(os.path.join(root, "write"))
+    cf = [v[2]["FETCH_SIZE"] for v in fetch.values() if kernel_role(v[0]) == "copy"]
+    cw = [v[2]["WRITE_SIZE"] for v in write.values() if kernel_role(v[0]) == "copy"]
+    kib = COPY_BYTES / 1024.0
+    f_scale = kib / max(cf) if cf else 1.0        # the calibration copy is the largest copy dispatch
+    w_scale = kib / max(cw) if cw else 1.0
+    lf, lw = _label(fetch), _label(write)
+    roles = {}
+    for did, role in lf.items():
+        roles.setdefault(role, {"fetch": [], "write": []})["fetch"].append(fetch[did][2]["FETCH_SIZE"] * 1024 * f_scale)
+    for did, role in lw.items():
+        roles.setdefault(role, {"fetch": [], "write": []})["write"].append(write[did][2]["WRITE_SIZE"] * 1024 * w_scale)
+    traffic = {"_note": (f"bytes per launch = FETCH_SIZE x {f_scale:.4f} + WRITE_SIZE x {w_scale:.4f} (KiB x 1024), "
+                         "the factors from a plain 512 MiB device copy in the same runs; written by "
+                         "`bench.py --summarize-profiles`")}
+    print("| Kernel | Launches | Fetch (MB) | Write (MB) | HBM bytes / launch (MB) |")
+    print("|---|---:|---:|---:|---:|")
+    for role, v in sorted(roles.items()):
+        if role == "copy" or not v["fetch"] or not v["write"]:
+            continue
+        fm, wm = statistics.mean(v["fetch"]), statistics.mean(v["write"])
+        traffic[role] = {"hbm_bytes_per_launch": int(fm + wm), "fetch_bytes": int(fm), "write_bytes": int(wm),
+                         "launches": len(v["fetch"]), "source_sha256": src_sha(role)}
+        print(f"| {role} | {len(v['fetch'])} | {fm / 1e6:.1f} | {wm / 1e6:.1f} | {(fm + wm) / 1e6:.1f} |")
+    if write_traffic:
+        with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
+            json.dump(traffic, f, indent=1)
+    mfma_dir = os.path.join(root, "mfma")
+    if os.path.isdir(mfma_dir):
+        m = _per_dispatch(mfma_dir)
+        lm = _label(m)
+        agg = {}
+        for did, role in lm.items():
+            agg.setdefault(role, []).append(m[did][2])
+        print()
+        print("| Kernel | Launches | Clock (GHz) | MFMA busy | co-exec | wait | LDS bank conflicts / launch |")
+        print("|---|---:|---:|---:|---:|---:|---:|")
+        for role, lst in sorted(agg.items()):
+            if role == "copy":
+                continue
+            c = {k: statistics.mean(d.get(k, 0.0) for d in lst) for k in lst[0]}
+            gui = c.get("GRBM_GUI_ACTIVE", 0.0) / 8.0            # per XCD
+            busy = c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)
+            dur = statistics.mean(d.get("_dur_ns", 0.0) for d in lst)
+            clock = f"{gui / dur:.2f}" if dur else "-"
+            util = busy / (1024 * gui) if gui else 0.0
+            coex = c.get("SQ_VALU_MFMA_COEXEC_CYCLES", 0.0) / busy if busy else 0.0
+            wait = c.get("SQ_WAIT_INST_ANY", 0.0) / c["SQ_WAVE_CYCLES"] if c.get("SQ_WAVE_CYCLES") else 0.0
+            print(f"| {role} | {len(lst)} | {clock} | {100 * util:.1f} % | {100 * coex:.0f} % | {100 * wait:.0f} % | "
+                  f"{c.get('SQ_LDS_BANK_CONFLICT', 0.0):.3g} |")
+
+
 def main():
+    if len(sys.argv) >= 3 and sys.argv[1] == "--summarize-profiles":
+        summarize_profiles(sys.argv[2], write_traffic="--no-traffic-json" not in sys.argv[3:])
+        return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
