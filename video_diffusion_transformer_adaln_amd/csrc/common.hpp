@@ -65,10 +65,11 @@ __device__ __forceinline__ void wg_barrier() {
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
-// s_waitcnt vmcnt(N), expcnt and lgkmcnt left at their maxima
+// s_waitcnt vmcnt(N), expcnt and lgkmcnt left at their maxima (vmcnt is 6
+// bits: bits 3:0 and 15:14 of the immediate)
 template <int N> __device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 16, "vmcnt field");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 // s_waitcnt lgkmcnt(0): this wave's LDS reads and writes have completed
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }

@@ -15,8 +15,8 @@
 //    workgroup cannot cover the loaded L2/Infinity-Cache latency.
 //  * int8-weight path (W8A16), same ring: the activation tiles arrive by
 //    direct-to-LDS loads, the weight tile is read as int8 (half the bytes)
-//    into registers one k-tile ahead, widened to bf16 exactly while it is
-//    stored into its slot, and multiplied on the bf16 MFMA.  The
+//    into registers a step before it is widened to bf16 exactly and stored
+//    into its slot, one step before it is multiplied on the bf16 MFMA.  The
 //    per-output-channel scale is applied to the fp32 accumulator in the
 //    epilogue (it factors out of the k-sum); group-wise scales are applied
 //    while widening (each 16-weight chunk lies in one group).
@@ -57,35 +57,38 @@ struct GemmParams {
 constexpr int BM = 256, BN = 256, BK = 64;
 
 
-// 16 int8 -> 16 bf16, exact (|q| <= 127 fits bf16's 8-bit significand):
-// flip the sign bit to get q + 128 as an unsigned byte, convert that byte to
-// fp32 (v_cvt_f32_ubyte*), subtract 128, round to bf16 (no rounding occurs).
-__device__ __forceinline__ void i8x16_to_bf16(const u32x4& src, u32x4& lo, u32x4& hi) {
-  bf16* l = reinterpret_cast<bf16*>(&lo);
-  bf16* h = reinterpret_cast<bf16*>(&hi);
-#pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    const uint32_t u = src[d] ^ 0x80808080u;
-    bf16* dst = d < 2 ? l + 4 * d : h + 4 * (d - 2);
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      dst[e] = static_cast<bf16>(static_cast<float>((u >> (8 * e)) & 0xffu) - 128.0f);
-  }
+// Signed byte B of v as fp32 (one v_cvt_f32_i32 with a sign-extended SDWA
+// byte select).
+template <int B> __device__ __forceinline__ float sbyte_f32(uint32_t v) {
+  float r;
+  if constexpr (B == 0)
+    asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_0" : "=v"(r) : "v"(v));
+  else if constexpr (B == 1)
+    asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1" : "=v"(r) : "v"(v));
+  else if constexpr (B == 2)
+    asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_2" : "=v"(r) : "v"(v));
+  else
+    asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3" : "=v"(r) : "v"(v));
+  return r;
 }
-// The same with a group scale: bf16(q * s), the product rounded once to fp32
-// (q has 8 significant bits, so q * s is exact unless s is subnormal) and
-// then to bf16.
-__device__ __forceinline__ void i8x16_to_bf16_scaled(const u32x4& src, float sc, u32x4& lo, u32x4& hi) {
-  bf16* l = reinterpret_cast<bf16*>(&lo);
-  bf16* h = reinterpret_cast<bf16*>(&hi);
-#pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    const uint32_t u = src[d] ^ 0x80808080u;
-    bf16* dst = d < 2 ? l + 4 * d : h + 4 * (d - 2);
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      dst[e] = static_cast<bf16>((static_cast<float>((u >> (8 * e)) & 0xffu) - 128.0f) * sc);
-  }
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  const bf16x2 v = {static_cast<bf16>(a), static_cast<bf16>(b)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+// 8 int8 -> 8 bf16, exact (|q| <= 127 fits bf16's 8-bit significand): each
+// byte converted to fp32 and rounded to bf16 (no rounding occurs), 1.5
+// vector instructions per value.  With SCALED, bf16(q * s): the product is
+// rounded once to fp32 (q has 8 significant bits, so q * s is exact unless s
+// is subnormal) and then to bf16.
+template <bool SCALED>
+__device__ __forceinline__ u32x4 i8x8_to_bf16(const u32x2& q, float s) {
+  auto f = [&](float v) { return SCALED ? v * s : v; };
+  u32x4 o;
+  o[0] = pack_bf16(f(sbyte_f32<0>(q[0])), f(sbyte_f32<1>(q[0])));
+  o[1] = pack_bf16(f(sbyte_f32<2>(q[0])), f(sbyte_f32<3>(q[0])));
+  o[2] = pack_bf16(f(sbyte_f32<0>(q[1])), f(sbyte_f32<1>(q[1])));
+  o[3] = pack_bf16(f(sbyte_f32<2>(q[1])), f(sbyte_f32<3>(q[1])));
+  return o;
 }
 
 // Raw buffer resource over [base, base + bytes): loads at offsets >= bytes
@@ -417,47 +420,43 @@ __global__ __launch_bounds__(512) void gemm_ring_kernel(GemmParams p) {
 
   // int8 weights (W8): global -> registers, widened to bf16 (times the
   // group scale with GRP) on the way into the weight slot, which then holds
-  // the same bf16 layout as a direct-to-LDS slot.  Load j (0, 1) of a lane:
-  // tile row w8_row + 8 j, int8 chunk lane%4 (16 values = logical
-  // bf16 chunks 2 (lane%4) and 2 (lane%4) + 1).  Lane group g = lane/4 takes
-  // row (g&3) + 16 ((g>>2)&1) + 4 (g>>3) of the wave's 32 (with j, each of
-  // the wave's rows once).
-  const int w8_g = lane >> 2;
-  const int w8_row = wave * 32 + (w8_g & 3) + (((w8_g >> 2) & 1) << 4) + ((w8_g >> 3) << 2), w8_c = lane & 3;
-  const uint32_t w8_off = (uint32_t)(feat0 + w8_row) * (uint32_t)p.ldw + w8_c * 16;
+  // the same bf16 layout as a direct-to-LDS slot.  Load j (0..3) of a lane:
+  // tile row w8_row + 8 j, int8 values 8 (lane%8) .. +8 (logical bf16 chunk
+  // lane%8).  Each LDS store then writes 8 whole 128-byte rows, like a
+  // direct-to-LDS load: measured on MI355X, ds_write_b128 runs without bank
+  // conflicts when every 4 consecutive lanes fill one aligned 64-byte block,
+  // and takes 8 extra cycles per instruction when they write 16-byte pieces
+  // 32 bytes apart.
+  const int w8_row = wave * 32 + (lane >> 3), w8_c = lane & 7;
+  const uint32_t w8_off = (uint32_t)(feat0 + w8_row) * (uint32_t)p.ldw + w8_c * 8;
   const uint32_t w8_step = 8u * (uint32_t)p.ldw;
   const int n_groups = GRP ? (p.k >> p.group_shift) : 0;
   const __amdgpu_buffer_rsrc_t rss = make_rsrc(p.w_scale, GRP ? (uint32_t)((uint64_t)p.n * n_groups * 4) : 0u);
   const uint32_t s_off = GRP ? (uint32_t)(feat0 + w8_row) * (uint32_t)n_groups * 4u : 0u;
   const uint32_t s_step = GRP ? 8u * (uint32_t)n_groups * 4u : 0u;
-  u32x4 wq[2];
-  float wsc[2];
-  auto wload = [&](int q) {
-    int kt = q >> 1;
+  u32x2 wq[4];
+  float wsc[4];
+  auto wload = [&](int kt) {
     kt = kt < KT ? kt : KT - 1;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) wq[j] = __builtin_amdgcn_raw_buffer_load_b128(rsw, w8_off + j * w8_step + kt * 64u, 0, 0);
+    for (int j = 0; j < 4; ++j) wq[j] = __builtin_amdgcn_raw_buffer_load_b64(rsw, w8_off + j * w8_step + kt * 64u, 0, 0);
     if constexpr (GRP) {
-      const uint32_t g4 = (uint32_t)((kt * 64 + w8_c * 16) >> p.group_shift) * 4u;
+      const uint32_t g4 = (uint32_t)((kt * 64 + w8_c * 8) >> p.group_shift) * 4u;
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < 4; ++j)
         wsc[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rss, s_off + j * s_step + g4, 0, 0));
     }
   };
-  auto wput = [&](int q) {
-    char* st = lds + (q % kSlots) * kSlot;
+  auto wput = [&](int kt) {
+    char* st = lds + ((2 * kt + 1) % kSlots) * kSlot;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < 4; ++j) {
       const int r = w8_row + 8 * j;
-      u32x4 lo, hi;
-      if constexpr (GRP) i8x16_to_bf16_scaled(wq[j], wsc[j], lo, hi);
-      else i8x16_to_bf16(wq[j], lo, hi);
-      *reinterpret_cast<u32x4*>(st + r * 128 + (((2 * w8_c) ^ sw(r)) << 4)) = lo;
-      *reinterpret_cast<u32x4*>(st + r * 128 + (((2 * w8_c + 1) ^ sw(r)) << 4)) = hi;
+      *reinterpret_cast<u32x4*>(st + r * 128 + ((w8_c ^ sw(r)) << 4)) = i8x8_to_bf16<GRP>(wq[j], GRP ? wsc[j] : 1.0f);
     }
   };
-  // vector-memory loads of one wload (two int8 chunks, and their two group scales)
-  constexpr int kW8Loads = GRP ? 4 : 2;
+  // vector-memory loads of one wload (four int8 pieces, and their four group scales)
+  constexpr int kW8Loads = GRP ? 8 : 4;
 
   // int8 fragment (v_mfma_i32_32x32x32_i8, k-step 32) of 32-row block i,
   // k-step ks: lane l takes row row0 + 32 i + rl (rl = l%32) and the 16-int8
@@ -541,43 +540,56 @@ __global__ __launch_bounds__(512) void gemm_ring_kernel(GemmParams p) {
   bf16x8 f0a[2], f0b[4], f1a[2], f1b[4];
   bf16x8 g0a[4], g1a[4], g0b[4], g1b[4];
   if constexpr (W8) {
-    // prologue: k-tile 0 in LDS; the weights of k-tile 1 in registers and
-    // the activations of k-tile 1 (position 2) in flight
+    // prologue: k-tile 0 in LDS; the activations (position 2) and the
+    // weights of k-tile 1 in flight
     issue(0, 0);
     issue(0, 1);
-    wload(1);
+    wload(0);
     wait_vmcnt<0>();
-    wput(1);
+    wput(0);
     issue(2, 0);
-    wload(3);
     issue(2, 1);
+    wload(1);
     wait_lgkm0();
     wg_barrier();
+    // Widening step: the weights of t+1 (loaded a step earlier) go from
+    // registers to the slot of the activations of t-1 while MFMAs of t run,
+    // and the registers take the weights of t+2.  It runs in the second
+    // group of MFMAs, or in the third with group scales (more vector work,
+    // measured faster there).  Loads issued after the weights of t+1: the
+    // activation loads of one step (4).
+    auto widen = [&](int t) {
+      wait_vmcnt<4>();
+      wput(t + 1);
+      wload(t + 2);
+    };
+    // loads issued after the activations of t+1 by the end of step t: one
+    // wload and 4 activation loads, or (group scales) two wloads and 4
+    constexpr int kAfterActs = GRP ? 2 * kW8Loads + 4 : kW8Loads + 4;
     for (int t = 0; t < KT; ++t) {
-      // the weights of t+1 (position 2t+3) go from registers to the slot of
-      // the activations of t-1, the activations of t+2 (2t+4) load into the
-      // slot of the weights of t-1: both slots' readers passed the last barrier
-      wait_vmcnt<2>();   // weights of t+1 in registers; the second half of the activations of t+1 may fly
-      wput(2 * t + 3);
+      // the activations of t+2 load into the slot of the weights of t-1 and
+      // the widened weights of t+1 go to the slot of the activations of t-1:
+      // both slots' readers passed the last barrier
       load_a16(t, 0, g0a);
       load_b16(t, 0, 0, g0b);
       load_b16(t, 0, 1, g1b);
       issue(2 * t + 4, 0);
       mfmas16(g0a, g0b, 0);
       __builtin_amdgcn_sched_barrier(0);
-      wload(2 * t + 5);
+      if constexpr (!GRP) widen(t);
       load_a16(t, 1, g1a);
       load_b16(t, 1, 0, g0b);
       issue(2 * t + 4, 1);
       mfmas16(g0a, g1b, 1);
       __builtin_amdgcn_sched_barrier(0);
+      if constexpr (GRP) widen(t);
       load_b16(t, 1, 1, g1b);
       mfmas16(g1a, g0b, 0);
       __builtin_amdgcn_sched_barrier(0);
       mfmas16(g1a, g1b, 1);
       __builtin_amdgcn_sched_barrier(0);
-      wait_vmcnt<kW8Loads + 4>();   // activations of t+1 landed; this k-tile's loads may fly
-      wait_lgkm0();                 // this wave's widened weights of t+1 are in LDS
+      wait_vmcnt<kAfterActs>();   // activations of t+1 landed; this step's loads may fly
+      wait_lgkm0();               // this wave's widened weights of t+1 are in LDS
       wg_barrier();
     }
   } else {
