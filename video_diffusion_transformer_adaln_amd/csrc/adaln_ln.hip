@@ -36,7 +36,7 @@ __global__ __launch_bounds__(256) void adaln_gemv_kernel(const T* __restrict__ w
   for (int k0 = lane * V; k0 < cols; k0 += kWave * V) {
     u32x4 raw[RW];
 #pragma unroll
-    for (int r = 0; r < RW; ++r) raw[r] = *reinterpret_cast<const u32x4*>(wr[r] + k0);
+    for (int r = 0; r < RW; ++r) raw[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wr[r] + k0));
     const u32x4 craw = *reinterpret_cast<const u32x4*>(c + k0);
     const T* ce = reinterpret_cast<const T*>(&craw);
 #pragma unroll
@@ -91,10 +91,25 @@ __global__ __launch_bounds__(256) void ln_modulate_kernel(const T* __restrict__ 
 #pragma unroll
     for (int i = 0; i < MAXC; ++i) {
       const int ch = lane + i * kWave;
-      raw[r][i] = ch < chunks ? *reinterpret_cast<const u32x4*>(xr + ch * V) : u32x4{0, 0, 0, 0};
+      raw[r][i] = ch < chunks ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xr + ch * V))
+                              : u32x4{0, 0, 0, 0};
     }
   }
-  auto elem = [&](int r, int i, int j) { return to_f32(reinterpret_cast<const T*>(&raw[r][i])[j]); };
+  // element j of chunk i, widened to fp32.  For bf16 the widening (a shift or
+  // a mask of the 32-bit word) is an opaque instruction, so each pass redoes
+  // it instead of keeping a widened copy of the row live: 120 -> about 60
+  // registers for D = 5120, twice the rows in flight per CU.
+  auto elem = [&](int r, int i, int j) {
+    if constexpr (sizeof(T) == 2) {
+      const uint32_t w = raw[r][i][j >> 1];
+      float v;
+      if (j & 1) asm volatile("v_and_b32 %0, 0xffff0000, %1" : "=v"(v) : "v"(w));
+      else asm volatile("v_lshlrev_b32 %0, 16, %1" : "=v"(v) : "v"(w));
+      return v;
+    } else {
+      return to_f32(reinterpret_cast<const T*>(&raw[r][i])[j]);
+    }
+  };
   float mean[R], rstd[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
@@ -137,7 +152,7 @@ __global__ __launch_bounds__(256) void ln_modulate_kernel(const T* __restrict__ 
         T* e = reinterpret_cast<T*>(&res);
 #pragma unroll
         for (int j = 0; j < V; ++j) e[j] = from_f32<T>((elem(r, i, j) - mean[r]) * rstd[r] * sc[j] + sh[j]);
-        *reinterpret_cast<u32x4*>(out + (int64_t)(row0 + r) * ldo + c0) = res;
+        __builtin_nontemporal_store(res, reinterpret_cast<u32x4*>(out + (int64_t)(row0 + r) * ldo + c0));
       }
     }
   }
@@ -394,7 +409,8 @@ __global__ __launch_bounds__(256) void quantize_int8_rows_kernel(const T* __rest
     const int g = lane + i * LANES;
 #pragma unroll
     for (int h = 0; h < 8 / W; ++h)
-      raw[i][h] = g < groups ? *reinterpret_cast<const u32x4*>(wr + g * 8 + h * W) : u32x4{0, 0, 0, 0};
+      raw[i][h] = g < groups ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wr + g * 8 + h * W))
+                             : u32x4{0, 0, 0, 0};
   }
   auto vals = [&](int i, float (&v)[8]) {
 #pragma unroll
@@ -424,7 +440,7 @@ __global__ __launch_bounds__(256) void quantize_int8_rows_kernel(const T* __rest
       vals(i, v);
       uint32_t lo, hi;
       quant8(v, s, lo, hi);
-      *reinterpret_cast<u32x2*>(qr + (int64_t)g * 8) = u32x2{lo, hi};
+      __builtin_nontemporal_store(u32x2{lo, hi}, reinterpret_cast<u32x2*>(qr + (int64_t)g * 8));
     }
   }
 }
