@@ -110,6 +110,9 @@ GEMM_CASES = [
     (300, 320, 128, 0, "bf16", True, None, True),
     (300, 576, 192, 2, "bf16", True, None, True),
     (97, 1024, 256, 0, "bf16", True, 512, True),
+    (1, 64, 64, 0, "bf16", True, None, True),         # int8 weights, one k-tile
+    (257, 328, 320, 2, "bf16", True, None, True),     # int8 weights, 5 k-tiles (the ring wraps), ragged m and n
+    (700, 520, 704, 0, "bf16", True, 264, True),      # int8 weights, 11 k-tiles, straddling transposed split
     (512, 768, 256, 0, "f32", False, 512, True),
     (512, 1024, 256, 1, "f32", False, None, True),
     (512, 256, 1024, 2, "f32", False, None, True),
