@@ -213,7 +213,8 @@ def main():
     ap.add_argument("--layers", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-breadth", action="store_true",
-                    help="also time the oracle on one 6144-token block and one int8-weight block")
+                    help="also time the oracle on one 512-token fp32 block, one 6144-token block and one "
+                         "int8-weight block")
     ap.add_argument("--no-layers45", action="store_true")
     ap.add_argument("--no-extra-blocks", action="store_true",
                     help="skip the int8-weight block and the 6144-token block timings")
@@ -651,7 +652,8 @@ def cpu_baseline(step_flops, L, breadth=False):
     (all 22680 tokens, every head, both projections and the MLP), measured,
     not extrapolated; the step is L such blocks.  BLAS runs on every core in
     the process's affinity mask.  With `breadth`, also one full block of the
-    6144-token workload and of the int8-weight workload."""
+    512-token fp32 workload, of the 6144-token workload and of the
+    int8-weight workload."""
     import seeded_inputs as si
     cores = len(os.sched_getaffinity(0))
     blas = "unknown"
@@ -669,6 +671,7 @@ def cpu_baseline(step_flops, L, breadth=False):
         log(f"cpu baseline: {t_block / 1e3:.1f} s per block")
         per_block = {"n22680_d5120_bf16_inputs": round(t_block, 1)}
         if breadth:
+            per_block["n512_d256_f32"] = round(_oracle_block_ms(si.C0), 1)
             per_block["n6144_d3072_bf16_inputs"] = round(_oracle_block_ms(si.C1), 1)
             per_block["n22680_d5120_int8_weights"] = round(_oracle_block_ms(si.C4, int8=True), 1)
             log(f"cpu baseline, other workloads: {per_block}")
