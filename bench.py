@@ -482,7 +482,7 @@ def extra_blocks(b0, x, c):
     fc2_tops = fl["mlp_down"] / (fc2 * 1e-3) / 1e12
     res["int8_fc2_block"] = {
         "workload": "the int8-weight block with the row-quantised FC2: u quantised per token row, MLP-down "
-                    "as int8 x int8 on v_mfma_i32_32x32x32_i8 (int32 accumulation)",
+                    "as int8 x int8 on v_mfma_i32_16x16x64_i8 (int32 accumulation)",
         "ms_per_block": round(msq, 3), "tflops": round(sum(fl.values()) / (msq * 1e-3) / 1e12, 1),
         "fc2": {"avg_ms": round(fc2, 4), "tops": round(fc2_tops, 1), "peak_tops": PEAK_INT8_TOPS,
                 "frac": round(fc2_tops / PEAK_INT8_TOPS, 4)},
