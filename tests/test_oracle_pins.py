@@ -433,6 +433,13 @@ def test_quantize_bounds_and_error():
     err = np.abs(w.astype(np.float64) - q.astype(np.float64) * s.astype(np.float64)[:, None])
     # |w - q s| <= s (1/2 + 127 * 2^-24): half a step plus the fp32 rounding of w/s
     assert (err <= s.astype(np.float64)[:, None] * (0.5 + 127 * 2.0 ** -24)).all()
+    # the oracle's per-channel dequantisation lands within the same step of w
+    # (plus the fp32 rounding of q s); a dropped, transposed or wrong-row scale
+    # fails this on the non-square matrix
+    deq = oracle.dequantize_int8(q, s)
+    assert deq.dtype == np.float32 and deq.shape == w.shape
+    err_d = np.abs(w.astype(np.float64) - deq.astype(np.float64))
+    assert (err_d <= s.astype(np.float64)[:, None] * (0.5 + 2 * 127 * 2.0 ** -24)).all()
 
 
 def test_int8_block_uses_dequantised_weights():
