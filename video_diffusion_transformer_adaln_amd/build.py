@@ -32,6 +32,12 @@ COMMON_FLAGS = [
 ]
 
 
+# Per-source flags.  The projection GEMMs' kernels are scheduled with the
+# backend's max-ilp strategy: measured on MI355X, QKV and MLP-up 2-2.5 %
+# faster (the same bits; the W8A16 kernels within 1 %).
+FILE_FLAGS = {"gemm.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
+
+
 def _hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -42,7 +48,7 @@ def _hipcc() -> str:
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
-    cmd = [_hipcc()] + COMMON_FLAGS + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc()] + COMMON_FLAGS + FILE_FLAGS.get(src, []) + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
