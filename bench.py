@@ -630,10 +630,12 @@ def sp_share(b0, P=8, reps=5):
     }
 
 
-def _oracle_block_ms(shape, int8=False):
+def _oracle_block_ms(shape, int8=False, parity=False):
     """Wall time (ms) of one oracle block forward over every token of `shape`
     (inputs drawn and, for int8 weights, quantised by the oracle beforehand,
-    outside the timed call)."""
+    outside the timed call).  With `parity`, also the relative L2 distance of
+    the library's block on the same host-seeded inputs from the oracle's
+    output, over every token (bf16 workloads only)."""
     import oracle  # test infrastructure: CPU baseline only
     import seeded_inputs as si
     hx, hc = si.gen_activation(shape)
@@ -643,8 +645,25 @@ def _oracle_block_ms(shape, int8=False):
         for name in si.MATRIX_NAMES:
             w[name] = oracle.quantize_int8(w[name])
     t0 = time.perf_counter()
-    oracle.block_forward(hx.values, hc.values, w, shape.n_heads)
-    return (time.perf_counter() - t0) * 1e3
+    y = oracle.block_forward(hx.values, hc.values, w, shape.n_heads)
+    ms = (time.perf_counter() - t0) * 1e3
+    if not parity:
+        return ms, None
+    import torch
+    from video_diffusion_transformer_adaln_amd import binding as B
+    from video_diffusion_transformer_adaln_amd import runtime as R
+    cfg = B.make_config(shape.n_tokens, shape.hidden, shape.n_heads, shape.head_dim, shape.mlp_hidden,
+                        shape.cond_dim, B.H3K_BF16, B.H3K_BF16, True)
+    stack = R.DitStack(cfg, [{k: R.upload(v.storage, v.dtype) for k, v in hw.items()}])
+    x, c = R.upload(hx.storage, hx.dtype), R.upload(hc.storage, hc.dtype)
+    out = torch.empty_like(x)
+    stack.forward(x, c, out)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().astype(np.float64)
+    ref = y.astype(np.float64)
+    del stack, x, c, out
+    torch.cuda.empty_cache()
+    return ms, float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
 
 
 def cpu_baseline(step_flops, L, breadth=False):
@@ -667,13 +686,14 @@ def cpu_baseline(step_flops, L, breadth=False):
         limiter = None
     try:
         log(f"cpu baseline: one full 22680-token block on {cores} host cores ({blas})")
-        t_block = _oracle_block_ms(si.C2)
-        log(f"cpu baseline: {t_block / 1e3:.1f} s per block")
+        t_block, parity = _oracle_block_ms(si.C2, parity=True)
+        log(f"cpu baseline: {t_block / 1e3:.1f} s per block; the library's block on the same inputs: "
+            f"rel-L2 {parity:.3e} over all {si.C2.n_tokens} tokens")
         per_block = {"n22680_d5120_bf16_inputs": round(t_block, 1)}
         if breadth:
-            per_block["n512_d256_f32"] = round(_oracle_block_ms(si.C0), 1)
-            per_block["n6144_d3072_bf16_inputs"] = round(_oracle_block_ms(si.C1), 1)
-            per_block["n22680_d5120_int8_weights"] = round(_oracle_block_ms(si.C4, int8=True), 1)
+            per_block["n512_d256_f32"] = round(_oracle_block_ms(si.C0)[0], 1)
+            per_block["n6144_d3072_bf16_inputs"] = round(_oracle_block_ms(si.C1)[0], 1)
+            per_block["n22680_d5120_int8_weights"] = round(_oracle_block_ms(si.C4, int8=True)[0], 1)
             log(f"cpu baseline, other workloads: {per_block}")
     finally:
         if limiter is not None:
@@ -687,6 +707,7 @@ def cpu_baseline(step_flops, L, breadth=False):
         "kind": "oracle",
         "blas": blas,
         "per_block_ms": per_block,
+        "block_rel_l2_vs_oracle": round(parity, 6),
         "sample": (f"one full 864x480x56-frame block (all {si.C2.n_tokens} tokens, 40 heads, D=5120, F=13824), "
                    f"the step's unit of work, measured once: {t_block / 1e3:.1f} s; the step is {L} such blocks; "
                    f"numpy fp32 oracle on bf16-valued inputs, {cores} cores ({blas})"),
