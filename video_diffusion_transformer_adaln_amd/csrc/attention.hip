@@ -9,7 +9,8 @@
 //     queries' Q fragments in registers and walks all keys in tiles of 32.
 //     Measured on MI355X: 4 waves of three or four blocks (one wave per
 //     SIMD, so that each LDS fragment feeds more products) ran 25 % slower,
-//     and 4 waves of two blocks (two workgroups per CU) 3 % slower;
+//     and 4 waves of two blocks (two workgroups per CU) 3 % slower at 22680
+//     tokens x 40 heads (they serve short sequences; see the launcher);
 //   * scores are computed transposed, S^T = K Q^T, so that the accumulator's
 //     lane index is the query: a query's 32 keys per tile lie in the four
 //     lanes l%16 + 16 g (8 keys each), which share its running reference;
@@ -602,10 +603,8 @@ __global__ __launch_bounds__(64) void attention_f32_kernel(AttnParamsF p) {
 }
 
 // ---------------------------------------------------------------------------
-template <int HD, bool QPRE>
-static void launch_bf16_attn(const AttentionArgs& a, hipStream_t stream) {
-  constexpr int NW = HD == 128 ? kAttnWaves128 : 4;
-  constexpr int QB = HD == 128 ? kAttnQBlocks128 : 2;
+template <int HD, int NW, int QB, bool QPRE>
+static void launch_bf16_attn_nw(const AttentionArgs& a, hipStream_t stream) {
   AttnParams p;
   p.q = (const bf16*)a.q; p.ldq = a.ldq;
   p.k = (const bf16*)a.k; p.ldk = a.ldk;
@@ -615,6 +614,23 @@ static void launch_bf16_attn(const AttentionArgs& a, hipStream_t stream) {
   p.q_tiles = (a.n + NW * 16 * QB - 1) / (NW * 16 * QB);
   p.scale_log2 = 1.4426950408889634f / sqrtf((float)HD);
   attention_bf16_kernel<HD, NW, QB, QPRE><<<dim3(p.q_tiles * p.n_heads), dim3(NW * 64), 0, stream>>>(p);
+}
+// head_dim 128: 8-wave workgroups (256 queries), or 4-wave ones (128 queries,
+// two per CU) for short sequences with few workgroups, where the last round
+// of workgroups is then spread over twice as many CUs.  Measured on MI355X
+// (same bits): 6144 tokens x 24 heads 452 -> 417 us, 2000 x 40 108 -> 91 us;
+// but 22680 tokens x 5 heads (as few workgroups, a long key loop) 1055 ->
+// 1177 us, so the long sequences keep 8 waves.
+template <int HD, bool QPRE>
+static void launch_bf16_attn(const AttentionArgs& a, hipStream_t stream) {
+  if constexpr (HD == 128) {
+    const int64_t wg8 = (int64_t)((a.n + 16 * kAttnWaves128 * kAttnQBlocks128 - 1) /
+                                  (16 * kAttnWaves128 * kAttnQBlocks128)) * a.n_heads;
+    if (wg8 < 4 * 256 && a.n <= 8192) launch_bf16_attn_nw<128, 4, kAttnQBlocks128, QPRE>(a, stream);
+    else launch_bf16_attn_nw<128, kAttnWaves128, kAttnQBlocks128, QPRE>(a, stream);
+  } else {
+    launch_bf16_attn_nw<HD, 4, 2, QPRE>(a, stream);
+  }
 }
 
 template <int HD>
