@@ -32,6 +32,23 @@ METRIC = "DiT step ms + TFLOP/s (MFMA util %) at 22.7k latent tokens, bf16, 1 GP
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_INT8_TOPS = 5000.0        # MI355X dense int8 MFMA
+# dense FLOP per clock per CU of v_mfma_f32_16x16x32_bf16 (16x16x32 multiply-adds per 16 cycles per
+# SIMD, 4 SIMDs); int8 (16x16x64 in the same cycles) doubles it
+BF16_FLOP_PER_CLK_CU = 4 * 16 * 16 * 32 * 2 // 16
+
+
+def device_block():
+    """The GPU this run measured on, from the library's device query, with the dense peaks its
+    compute units and peak clock imply (the roofline keeps the published peaks)."""
+    import torch
+    from video_diffusion_transformer_adaln_amd import binding as B
+    d = B.h3k_get_device_info(torch.cuda.current_device())
+    per_s = d["compute_units"] * d["peak_clock_khz"] * 1e3
+    return {"name": torch.cuda.get_device_name(), "arch": d["arch"], "compute_units": d["compute_units"],
+            "peak_clock_mhz": round(d["peak_clock_khz"] / 1e3, 1), "lds_kib_per_cu": d["lds_bytes_per_cu"] // 1024,
+            "hbm_gib": round(d["hbm_bytes"] / 2**30, 1),
+            "bf16_peak_from_cus_and_clock_tflops": round(per_s * BF16_FLOP_PER_CLK_CU / 1e12, 1),
+            "int8_peak_from_cus_and_clock_tops": round(2 * per_s * BF16_FLOP_PER_CLK_CU / 1e12, 1)}
 
 
 def log(*a):
@@ -361,6 +378,7 @@ def main():
         "kernels": per_kernel,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "device": device_block(),
     }
     result.update(extra)
     print(json.dumps(result), flush=True)

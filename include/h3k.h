@@ -389,6 +389,23 @@ h3k_status h3k_profiler_reset(h3k_profiler* p);
  * H3K_ERR_SHAPE if more launches were made than the capacity. */
 h3k_status h3k_profiler_read(h3k_profiler* p, int32_t kernel_kind, double* total_ms, int32_t* launches);
 
+/* ---- device ------------------------------------------------------------- */
+/* The GPU a measurement ran on ([H3-memory], "verify it yourself": figures are
+ * taken on the machine at hand), from the HIP device properties of `device`,
+ * so that a harness can derive a peak rate from the compute units and the
+ * clock and set it beside the published one (host struct). */
+typedef struct h3k_device_info {
+  int32_t  compute_units;      /* CUs                                       */
+  int32_t  peak_clock_khz;     /* peak shader clock                         */
+  int32_t  lds_bytes_per_cu;   /* LDS a workgroup can use                   */
+  int32_t  wavefront_size;     /* lanes per wave                            */
+  uint64_t hbm_bytes;          /* device memory                             */
+  char     arch[64];           /* architecture name, NUL-terminated         */
+} h3k_device_info;
+/* Fills *out for device `device` (0 .. count-1).  H3K_ERR_NULL for a NULL out,
+ * H3K_ERR_HIP if the runtime has no such device (out untouched).  Enqueues nothing. */
+h3k_status h3k_get_device_info(int32_t device, h3k_device_info* out /* host */);
+
 #ifdef __cplusplus
 }
 #endif

@@ -212,6 +212,19 @@ void profiler() {
   CHECK(h3k_profiler_destroy(p) == H3K_OK);
 }
 
+void device_info() {
+  CHECK(h3k_get_device_info(0, nullptr) == H3K_ERR_NULL);
+  h3k_device_info d;
+  std::memset(&d, 0x5A, sizeof(d));
+  CHECK(h3k_get_device_info(1, &d) == H3K_ERR_HIP);
+  CHECK(h3k_get_device_info(-1, &d) == H3K_ERR_HIP);
+  CHECK(d.compute_units == 0x5A5A5A5A);   // untouched on error
+  CHECK(h3k_get_device_info(0, &d) == H3K_OK);
+  CHECK(d.compute_units == 256 && d.peak_clock_khz == 2400000 && d.lds_bytes_per_cu == 160 * 1024);
+  CHECK(d.wavefront_size == 64 && d.hbm_bytes == (uint64_t(288) << 30));
+  CHECK(std::strcmp(d.arch, "gfx950:sramecc+:xnack-") == 0);
+}
+
 }  // namespace
 
 int main(int argc, char** argv) {
@@ -244,6 +257,7 @@ int main(int argc, char** argv) {
   }
   kernel_entry_points();
   profiler();
+  device_info();
   if (g_fail) {
     std::printf("host sanitize FAILED: %d checks\n", g_fail);
     return 1;

@@ -11,6 +11,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
+#include <cstring>
 
 #include "kernels.hpp"
 
@@ -176,6 +177,22 @@ hipError_t hipEventRecord(hipEvent_t, hipStream_t) { return hipSuccess; }
 hipError_t hipEventSynchronize(hipEvent_t) { return hipSuccess; }
 hipError_t hipEventElapsedTime(float* ms, hipEvent_t, hipEvent_t) {
   *ms = 1.0f;
+  return hipSuccess;
+}
+// one device with MI355X-like properties
+hipError_t hipGetDeviceCount(int* count) {
+  *count = 1;
+  return hipSuccess;
+}
+hipError_t hipGetDeviceProperties(hipDeviceProp_t* prop, int device) {
+  if (device != 0) return hipErrorInvalidDevice;
+  std::memset(prop, 0, sizeof(*prop));
+  prop->multiProcessorCount = 256;
+  prop->clockRate = 2400000;
+  prop->maxSharedMemoryPerMultiProcessor = 160 * 1024;
+  prop->warpSize = 64;
+  prop->totalGlobalMem = size_t(288) << 30;
+  std::snprintf(prop->gcnArchName, sizeof(prop->gcnArchName), "gfx950:sramecc+:xnack-");
   return hipSuccess;
 }
 }

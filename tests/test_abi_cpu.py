@@ -36,6 +36,16 @@ def test_struct_sizes_match_header_layout():
     assert ctypes.sizeof(B.DitBlockWeights) == 14 * 8
     assert ctypes.sizeof(B.DitStats) == 40
     assert ctypes.sizeof(B.DitPlanInfo) == 9 * 8 * 2 + 9 * 4 * 2 + 8 * 5 + 8
+    assert ctypes.sizeof(B.DeviceInfo) == 4 * 4 + 8 + 64
+
+
+def test_device_info_rejects_null_and_missing_devices():
+    lib = h3k.lib()
+    assert lib.h3k_get_device_info(0, None) == B.H3K_ERR_NULL
+    d = B.DeviceInfo()
+    assert lib.h3k_get_device_info(-1, ctypes.byref(d)) == B.H3K_ERR_HIP
+    assert lib.h3k_get_device_info(1 << 20, ctypes.byref(d)) == B.H3K_ERR_HIP
+    assert d.compute_units == 0 and d.arch == b""   # untouched on error
 
 
 def cfg_c2(**kw):

@@ -41,6 +41,21 @@ def _ht(a, dtype):
     return si._finish(np.ascontiguousarray(a, dtype=np.float32), dtype)
 
 
+# ------------------------------------------------------------------ device query
+
+def test_device_info_matches_runtime(B):
+    import torch
+    d = B.h3k_get_device_info(0)
+    p = torch.cuda.get_device_properties(0)
+    flush(f"device info {d}")
+    assert d["compute_units"] == p.multi_processor_count
+    assert d["arch"].split(":")[0] == p.gcnArchName.split(":")[0]
+    assert d["wavefront_size"] == 64
+    assert d["hbm_bytes"] == p.total_memory
+    assert 1_000_000 <= d["peak_clock_khz"] <= 4_000_000
+    assert d["lds_bytes_per_cu"] >= 160 * 1024   # the GEMM's operand ring uses all of it
+
+
 # ------------------------------------------------------------------ AdaLN GEMV
 
 @pytest.mark.parametrize("rows,cols,dtype", [(6 * 5120, 5120, "bf16"), (6 * 256, 256, "f32"), (72, 24, "bf16"), (30, 40, "bf16"), (42, 16, "f32"),

@@ -58,6 +58,11 @@ class DitPlanInfo(ctypes.Structure):
                 ("alias_activations", c_int32), ("_reserved", c_int32)]
 
 
+class DeviceInfo(ctypes.Structure):
+    _fields_ = [("compute_units", c_int32), ("peak_clock_khz", c_int32), ("lds_bytes_per_cu", c_int32),
+                ("wavefront_size", c_int32), ("hbm_bytes", c_uint64), ("arch", ctypes.c_char * 64)]
+
+
 class H3KError(RuntimeError):
     def __init__(self, status: int, message: str):
         super().__init__(f"h3k {STATUS_NAMES.get(status, status)}: {message}")
@@ -108,6 +113,7 @@ _SIGNATURES = [
     ("h3k_profiler_reset", c_int32, [c_void_p]),
     ("h3k_profiler_read", c_int32, [c_void_p, c_int32, ctypes.POINTER(ctypes.c_double),
                                     ctypes.POINTER(c_int32)]),
+    ("h3k_get_device_info", c_int32, [c_int32, ctypes.POINTER(DeviceInfo)]),
 ]
 EXPORTED = tuple(n for n, _, _ in _SIGNATURES)
 
@@ -278,6 +284,14 @@ def h3k_attention(dtype: int, n: int, n_heads: int, head_dim: int, q, ldq: int, 
                   ldo: int, q_prescaled: bool = False, stream=None) -> None:
     check(lib().h3k_attention(dtype, n, n_heads, head_dim, _ptr(q), ldq, _ptr(k), ldk, _ptr(vt), ldvt, _ptr(o),
                               ldo, 1 if q_prescaled else 0, _stream(stream)))
+
+
+def h3k_get_device_info(device: int = 0) -> dict:
+    d = DeviceInfo()
+    check(lib().h3k_get_device_info(device, ctypes.byref(d)))
+    return {"compute_units": d.compute_units, "peak_clock_khz": d.peak_clock_khz,
+            "lds_bytes_per_cu": d.lds_bytes_per_cu, "wavefront_size": d.wavefront_size,
+            "hbm_bytes": d.hbm_bytes, "arch": d.arch.decode(errors="replace")}
 
 
 class Profiler:

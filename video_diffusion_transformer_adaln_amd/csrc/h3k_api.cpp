@@ -876,4 +876,25 @@ h3k_status h3k_profiler_read(h3k_profiler* p, int32_t kind, double* total_ms, in
   return H3K_OK;
 }
 
+h3k_status h3k_get_device_info(int32_t device, h3k_device_info* out) {
+  if (!out) return fail(H3K_ERR_NULL, "out is NULL");
+  int count = 0;
+  const hipError_t ec = hipGetDeviceCount(&count);
+  if (ec != hipSuccess) return fail(H3K_ERR_HIP, "no usable HIP device: %s", hipGetErrorString(ec));
+  if (device < 0 || device >= count) return fail(H3K_ERR_HIP, "device %d: the runtime sees %d devices", device, count);
+  hipDeviceProp_t pr;
+  const hipError_t ep = hipGetDeviceProperties(&pr, device);
+  if (ep != hipSuccess) return fail(H3K_ERR_HIP, "hipGetDeviceProperties(%d) failed: %s", device, hipGetErrorString(ep));
+  h3k_device_info d;
+  std::memset(&d, 0, sizeof(d));
+  d.compute_units = pr.multiProcessorCount;
+  d.peak_clock_khz = pr.clockRate;
+  d.lds_bytes_per_cu = (int32_t)pr.maxSharedMemoryPerMultiProcessor;
+  d.wavefront_size = pr.warpSize;
+  d.hbm_bytes = (uint64_t)pr.totalGlobalMem;
+  std::snprintf(d.arch, sizeof(d.arch), "%s", pr.gcnArchName);
+  *out = d;
+  return H3K_OK;
+}
+
 }  // extern "C"
