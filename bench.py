@@ -561,12 +561,20 @@ def extra_blocks(b0, x, c):
     x1 = si.torch_device_normal((N, D), 1.0, si.BASE_SEED, 599_000, "cuda", torch.bfloat16)
     c1 = si.torch_device_normal((C,), 1.0, si.BASE_SEED, 599_001, "cuda", torch.bfloat16)
     cfg1 = B.make_config(N, D, H, d, F, C, B.H3K_BF16, B.H3K_BF16, True)
-    ms1, _ = _time_block(cfg1, t1, x1, c1)
-    fl1 = sum(block_flops(N, D, F, C).values())
+    ms1, k1 = _time_block(cfg1, t1, x1, c1)
+    flk = block_flops(N, D, F, C)
+    fl1 = sum(flk.values())
+    kern1 = {}
+    for name, v in k1.items():
+        if v["launches"]:
+            avg = v["total_ms"] / v["launches"]
+            kern1[name] = {"avg_ms": round(avg, 4)}
+            if name in flk and name != "adaln":
+                kern1[name]["tflops"] = round(flk[name] / (avg * 1e-3) / 1e12, 1)
     res["block_6144_tokens"] = {
         "workload": "one bf16 block at 6144 tokens (6x32x32 latent of 512x512x22 frames), D=3072, "
                     "24x128 heads, F=12288",
-        "ms_per_block": round(ms1, 3), "tflops": round(fl1 / (ms1 * 1e-3) / 1e12, 1)}
+        "ms_per_block": round(ms1, 3), "tflops": round(fl1 / (ms1 * 1e-3) / 1e12, 1), "kernels": kern1}
     log(f"6144-token block: {ms1:.2f} ms")
     return res
 

@@ -176,6 +176,9 @@ typedef struct h3k_dit_stats {
   uint64_t unaliased_bytes;     /* out: workspace the same call needs without aliasing */
   int32_t  dispatches;          /* out: kernels enqueued by the call                */
   int32_t  alias_activations;   /* out: aliasing actually used (after the env switch) */
+  int32_t  split_gemms;         /* out: GEMMs whose tail tiles were split along k
+                                   (each enqueued one more kernel, counted in dispatches) */
+  int32_t  _reserved;
   h3k_profiler* profiler;       /* in: NULL, or a profiler that records every launch */
 } h3k_dit_stats;
 
@@ -183,7 +186,13 @@ typedef struct h3k_dit_stats {
  * Index with H3K_T_*.  Offsets are byte offsets into the workspace.
  * The QKV region holds Q and K as one row-major [N, 2D] matrix, followed at
  * qkv_vt_offset by V transposed, [D, vt_pitch] (vt_pitch = N rounded up to 8),
- * so that the attention kernel reads V along the key axis. */
+ * so that the attention kernel reads V along the key axis.  After the tensors
+ * (part_offset) lies the scratch of the bf16 out-projection and MLP GEMMs:
+ * when a GEMM's last wave of 256x256 output tiles would leave at least half
+ * of the GPU's compute units idle, each of those tiles is split along k into
+ * up to 8 workgroups whose fp32 partial tiles a second kernel sums in a fixed
+ * order (sized for 256 CUs; H3K_DISABLE_TAIL_SPLIT=1 turns the split off).
+ * With token reduction the merged stream follows it. */
 #define H3K_T_MOD  0   /* fp32 [6D]   */
 #define H3K_T_H    1   /* [N, D]      */
 #define H3K_T_QKV  2   /* [N, 2D] + [D, vt_pitch] */
@@ -206,6 +215,8 @@ typedef struct h3k_dit_plan_info {
   uint64_t unaliased_bytes;
   int32_t  alias_activations;
   int32_t  _reserved;
+  uint64_t part_offset;              /* scratch of the k-split GEMM tails: byte offset ... */
+  uint64_t part_bytes;               /* ... and size (0 when no projection can split)     */
 } h3k_dit_plan_info;
 
 /* Message for the last non-OK status returned on this thread (never NULL). */

@@ -88,3 +88,31 @@ def upload_block(shape, hw, mlp_group=0):
             d[name] = dev(ht)
             ow[name] = ht.values
     return d, ow
+
+
+def tail_split_ways(tiles, kt, cus, cap_tiles):
+    """The block's k-split rule for a bf16 GEMM of `tiles` 256x256 tiles and `kt`
+    k-tiles of 64 on `cus` compute units, restated for the tests: the last
+    tiles % cus tiles split S ways when they would leave at least half the
+    CUs idle, S <= 8, >= 4 k-tiles per split, tail * S <= min(cus, cap), and
+    only if each split sheds at least 2048 of k, (1 - 1/S) 64 kt >= 2048."""
+    if tiles < 1 or cus < 1:
+        return 0
+    tail = tiles % cus
+    if tail == 0 or 2 * tail > cus:
+        return 0
+    s = min(8, kt // 4, min(cap_tiles, cus) // tail)
+    return s if s >= 2 and (s - 1) * kt >= 32 * s else 0
+
+
+def expected_split_gemms(n_tokens, hidden, mlp, part_bytes, cus):
+    """How many of a bf16 block's out / up / down GEMMs split their tail."""
+    tm = (n_tokens + 255) // 256
+    cap = part_bytes // (256 * 256 * 4)
+    return sum(tail_split_ways(tm * ((n + 255) // 256), k // 64, cus, cap) > 0
+               for n, k in ((hidden, hidden), (mlp, hidden), (hidden, mlp)))
+
+
+def device_cus():
+    from video_diffusion_transformer_adaln_amd import binding as B
+    return B.h3k_get_device_info(0)["compute_units"]

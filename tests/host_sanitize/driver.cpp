@@ -89,7 +89,9 @@ void run_config(const char* name, h3k_dit_config c, int n_blocks) {
   Pool pool;
   h3k_dit_plan_info info;
   CHECK(h3k_dit_plan(&c, &info) == H3K_OK);
-  for (int t = 0; t < H3K_T_COUNT; ++t) CHECK(info.offset[t] % 256 == 0 && info.offset[t] + info.bytes[t] <= info.workspace_bytes);
+  for (int t = 0; t < H3K_T_COUNT; ++t)
+    CHECK(info.offset[t] % 256 == 0 && info.offset[t] + info.bytes[t] <= info.part_offset &&
+          info.part_offset + info.part_bytes <= info.workspace_bytes);
   for (int s = 0; s <= 8; ++s)
     for (int a = 0; a < H3K_T_COUNT; ++a)
       for (int b = a + 1; b < H3K_T_COUNT; ++b) {
@@ -112,11 +114,15 @@ void run_config(const char* name, h3k_dit_config c, int n_blocks) {
   const int64_t before = h3k_stub_launches();
   if (c.token_reduction_last <= c.token_reduction_first) {
     CHECK(h3k_dit_block_forward(&c, &blocks[0], x, cond, out, ws, ws_bytes, nullptr, &st) == H3K_OK);
-    CHECK(st.dispatches == (c.int8_fc2_rows ? 9 : 8));
+    CHECK(st.dispatches == (c.int8_fc2_rows ? 9 : 8) + st.split_gemms);
+    CHECK(st.split_gemms >= 0 && st.split_gemms <= 3);
     CHECK(h3k_stub_launches() - before == st.dispatches);
     CHECK(st.workspace_bytes == ws_bytes);
   }
+  const int64_t before_stack = h3k_stub_launches();
   CHECK(h3k_dit_stack_forward(&c, blocks.data(), n_blocks, x, cond, out, ws, ws_bytes, nullptr, &st) == H3K_OK);
+  CHECK(h3k_stub_launches() - before_stack == st.dispatches);
+  CHECK(info.part_offset + info.part_bytes <= ws_bytes);
   // rejected before any launch: short workspace, out inside the workspace, misaligned x
   const int64_t mark = h3k_stub_launches();
   CHECK(h3k_dit_stack_forward(&c, blocks.data(), n_blocks, x, cond, out, ws, ws_bytes - 1, nullptr, nullptr) ==

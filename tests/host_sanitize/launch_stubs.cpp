@@ -77,8 +77,23 @@ hipError_t launch_ln_modulate(DType dt, int n, int D, float, const void* x, int6
   return hipSuccess;
 }
 
-hipError_t launch_linear(const LinearArgs& a, hipStream_t) {
+hipError_t launch_linear(const LinearArgs& a, hipStream_t, int* kernels) {
   ++g_launches;
+  if (kernels) *kernels = 1;
+  // the tail split as the bf16 launcher takes it on 256 compute units: the
+  // partial tiles it writes must lie inside the scratch it was given
+  if (a.part && a.act == kBF16 && a.weight == kBF16 && a.epi != kEpiBiasRope && a.split_col >= a.n) {
+    const int64_t tiles = ((a.m + 255) / 256) * ((a.n + 255) / 256);
+    const int S = tail_split_ways(tiles, a.k / 64, 256, a.part_bytes / kPartTileBytes);
+    if (S) {
+      const int64_t used = (tiles % 256) * S * kPartTileBytes;
+      need(used <= a.part_bytes, "k-split partial tiles inside their scratch");
+      touch_write(a.part, 1, used, used, 1);
+      touch_read(a.part, 1, used, used, 1);
+      ++g_launches;
+      if (kernels) *kernels = 2;
+    }
+  }
   const int64_t ex = es(a.act), ew = es(a.weight), ey = a.act == kINT8 ? 2 : es(a.act);
   if (a.act != kF32) {
     need(a.k % (a.act == kINT8 ? 128 : 64) == 0, "k-tile multiple");

@@ -34,8 +34,8 @@ def test_library_exports_every_declared_symbol():
 def test_struct_sizes_match_header_layout():
     assert ctypes.sizeof(B.DitConfig) == 72
     assert ctypes.sizeof(B.DitBlockWeights) == 14 * 8
-    assert ctypes.sizeof(B.DitStats) == 40
-    assert ctypes.sizeof(B.DitPlanInfo) == 9 * 8 * 2 + 9 * 4 * 2 + 8 * 5 + 8
+    assert ctypes.sizeof(B.DitStats) == 48
+    assert ctypes.sizeof(B.DitPlanInfo) == 9 * 8 * 2 + 9 * 4 * 2 + 8 * 5 + 8 + 16
     assert ctypes.sizeof(B.DeviceInfo) == 4 * 4 + 8 + 64
 
 
@@ -116,9 +116,37 @@ def test_plan_c2_sizes_and_layout():
 def test_token_reduction_adds_the_merged_stream_to_the_workspace():
     plain = h3k.h3k_dit_workspace_size(cfg_c2())
     red = h3k.h3k_dit_workspace_size(cfg_c2(token_reduction=(12, 38)))
-    assert red - plain == ((22680 // 2) * 5120 * 2 + 255) // 256 * 256
+    merged = ((22680 // 2) * 5120 * 2 + 255) // 256 * 256
     info = h3k.h3k_dit_plan(cfg_c2(token_reduction=(12, 38)))
-    assert max(info.offset[t] + info.bytes[t] for t in range(9)) <= info.workspace_bytes - (red - plain)
+    # 22680 tokens: no GEMM tail is split (no scratch); the reduced blocks' 11340 tokens leave
+    # 126 MLP-up tiles in the last wave, split two ways: 126 * 2 partial tiles of 256 KiB
+    assert h3k.h3k_dit_plan(cfg_c2()).part_bytes == 0
+    assert info.part_bytes == 126 * 2 * 256 * 256 * 4
+    assert red - plain == merged + info.part_bytes
+    tensors_end = max(info.offset[t] + info.bytes[t] for t in range(9))
+    assert tensors_end <= info.part_offset
+    assert info.part_offset + info.part_bytes == info.workspace_bytes - merged
+
+
+def test_tail_split_scratch_sizes():
+    """The k-split scratch the plan reserves: the largest of the out / up / down GEMMs' last-wave
+    tiles times their split ways, on 256 compute units (one 256x256 tile per CU and wave)."""
+    # 6144 x 3072 (F = 12288): out and down have 24 x 12 = 288 tiles, 32 in the last wave, split
+    # 8 ways (256 partial tiles); up has 24 x 48 = 1152, 128 in the last wave, whose 2-way split
+    # would shed only 1536 of its k = 3072 per workgroup: not split
+    c1 = B.make_config(6144, 3072, 24, 128, 12288, 3072, B.H3K_BF16)
+    assert h3k.h3k_dit_plan(c1).part_bytes == 256 * 256 * 256 * 4
+    # the same up GEMM with k = 4096 sheds 2048: 128 tiles split 2 ways, out and down 32 x 8
+    wide = B.make_config(6144, 4096, 32, 128, 12288, 64, B.H3K_BF16)   # out/down: 24 x 16 = 384, tail 128
+    assert h3k.h3k_dit_plan(wide).part_bytes == 128 * 2 * 256 * 256 * 4
+    # fp32 and int8-weight configs never split
+    assert h3k.h3k_dit_plan(B.make_config(512, 256, 4, 64, 1024, 256, B.H3K_F32)).part_bytes == 0
+    assert h3k.h3k_dit_plan(cfg_c2(weight_dtype=B.H3K_INT8)).part_bytes == 0
+    # a one-tile GEMM with 64 k-tiles splits 8 ways; with 4 k-tiles it does not split
+    small = B.make_config(200, 256, 2, 128, 4096, 64, B.H3K_BF16)   # down: 1 tile, k = 4096
+    assert h3k.h3k_dit_plan(small).part_bytes == 1 * 8 * 256 * 256 * 4
+    tiny = B.make_config(200, 256, 2, 128, 256, 64, B.H3K_BF16)     # every k = 256: 4 k-tiles
+    assert h3k.h3k_dit_plan(tiny).part_bytes == 0
 
 
 def test_env_switch_disables_aliasing(monkeypatch):

@@ -17,7 +17,8 @@ import pytest
 
 import oracle
 import seeded_inputs as si
-from gpu_util import config_for, dev, flush, has_gpu, sample_rows, to_np, upload_block
+from gpu_util import (config_for, dev, device_cus, expected_split_gemms, flush, has_gpu, sample_rows, to_np,
+                      upload_block)
 from helpers import record, rel_l2
 
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not has_gpu(), reason="needs a GPU")]
@@ -62,7 +63,7 @@ def test_block_c0_fp32_full(R):
     out = _run_block(R, shape, dw, dev(hx), dev(hc), stats=st)
     ref = oracle.block_forward(hx.values, hc.values, ow, shape.n_heads)
     got = to_np(out)
-    assert st.dispatches == 8
+    assert st.dispatches == 8 and st.split_gemms == 0
     assert record("block c0 fp32 (512x256)", rel_l2(got, ref), 1e-4) < 1e-4
 
 
@@ -79,16 +80,49 @@ def test_block_ragged_bf16_full(R, n):
 
 
 def test_block_c1_full(R):
-    shape = si.C1
+    """The 512x512x22-frame block, every element, with the k-split of the GEMM
+    tails (on 256 CUs the out-projection and MLP-down leave 32 tiles in their
+    last wave and split them 8 ways) and without it (H3K_DISABLE_TAIL_SPLIT=1):
+    both against the oracle, and close to each other (only the fp32 summation
+    order of the tail tiles differs)."""
+    _split_on_off(R, si.C1, "block c1 (6144x3072)", 2)
+
+
+def test_block_ragged_tail_split(R):
+    """The k-split with ragged tiles in the split tail: 6000 tokens (the last
+    m-tile holds 112 rows) and D = 2944 (the last n-tile 128 columns); out and
+    down leave 32 of 288 tiles in the last wave and split them 8 ways."""
+    shape = si.custom_shape("ragged_split", 990, 6000, 23, 128, 11776, "bf16")
+    _split_on_off(R, shape, "block ragged 6000x2944", 2)
+
+
+def _split_on_off(R, shape, label, want_256):
+    import os
+    from video_diffusion_transformer_adaln_amd import binding as B
     flush(f"block {shape.name}")
     hx, hc, hw = _block_case(shape)
     dw, ow = upload_block(shape, hw)
-    got = to_np(_run_block(R, shape, dw, dev(hx), dev(hc)))
     ref = oracle.block_forward(hx.values, hc.values, ow, shape.n_heads)
-    err = rel_l2(got, ref)
-    flush(f"  rel_l2 = {err:.3e}")
-    record("block c1 (6144x3072)", err, TOL)
-    assert err < TOL
+    cfg = config_for(shape)
+    part = B.h3k_dit_plan(cfg).part_bytes
+    outs = {}
+    for split in (True, False):
+        st = B.DitStats()
+        if not split:
+            os.environ["H3K_DISABLE_TAIL_SPLIT"] = "1"
+        try:
+            outs[split] = to_np(_run_block(R, shape, dw, dev(hx), dev(hc), stats=st))
+        finally:
+            os.environ.pop("H3K_DISABLE_TAIL_SPLIT", None)
+        want = expected_split_gemms(shape.n_tokens, shape.hidden, shape.mlp_hidden, part, device_cus()) if split else 0
+        assert st.split_gemms == want and st.dispatches == 8 + want
+        err = rel_l2(outs[split], ref)
+        flush(f"  split={split}: {st.split_gemms} GEMMs split, rel_l2 = {err:.3e}")
+        record(f"{label}{'' if split else ', tail split off'}", err, TOL)
+        assert err < TOL
+    if device_cus() == 256:
+        assert expected_split_gemms(shape.n_tokens, shape.hidden, shape.mlp_hidden, part, 256) == want_256
+    assert rel_l2(outs[True], outs[False]) < 2e-3
 
 
 @pytest.fixture(scope="module")
@@ -257,7 +291,10 @@ def test_stack50_reduced_width_vs_oracle(R):
     st = B.DitStats()
     stack.forward(xd, cd, out, stats=st)
     torch.cuda.synchronize()
-    assert st.dispatches == 8 * 50
+    part = B.h3k_dit_plan(config_for(shape)).part_bytes
+    assert st.split_gemms == 50 * expected_split_gemms(shape.n_tokens, shape.hidden, shape.mlp_hidden, part,
+                                                       device_cus())
+    assert st.dispatches == 8 * 50 + st.split_gemms
     ref = oracle.stack_forward(hx.values, hc.values, [u[1] for u in up], shape.n_heads)
     err = rel_l2(to_np(out), ref)
     flush(f"  rel_l2 after 50 blocks = {err:.3e}")
@@ -294,7 +331,14 @@ def test_stack_token_reduction(R, n_blocks, rng_):
         st = B.DitStats()
         stack.forward(xd, cd, out, stats=st)
         torch.cuda.synchronize()
-        assert st.dispatches == 8 * n_blocks + 2
+        part = B.h3k_dit_plan(cfg).part_bytes
+        n_red = rng_[1] - rng_[0]
+        want = ((n_blocks - n_red) * expected_split_gemms(shape.n_tokens, shape.hidden, shape.mlp_hidden, part,
+                                                          device_cus())
+                + n_red * expected_split_gemms(shape.n_tokens // 2, shape.hidden, shape.mlp_hidden, part,
+                                               device_cus()))
+        assert st.split_gemms == want
+        assert st.dispatches == 8 * n_blocks + 2 + st.split_gemms
         outs.append(out)
     assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
     got = to_np(outs[0])
@@ -325,7 +369,11 @@ def test_stack50_reduced_width_token_reduction(R):
     st = B.DitStats()
     stack.forward(xd, cd, out, stats=st)
     torch.cuda.synchronize()
-    assert st.dispatches == 8 * 50 + 2
+    part = B.h3k_dit_plan(cfg).part_bytes
+    want = (24 * expected_split_gemms(shape.n_tokens, shape.hidden, shape.mlp_hidden, part, device_cus())
+            + 26 * expected_split_gemms(shape.n_tokens // 2, shape.hidden, shape.mlp_hidden, part, device_cus()))
+    assert st.split_gemms == want
+    assert st.dispatches == 8 * 50 + 2 + st.split_gemms
     ref = oracle.stack_forward(hx.values, hc.values, [u[1] for u in up], shape.n_heads, token_reduction=(12, 38))
     err = rel_l2(to_np(out), ref)
     flush(f"  rel_l2 after 50 blocks = {err:.3e}")

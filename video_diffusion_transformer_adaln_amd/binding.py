@@ -48,14 +48,16 @@ class DitBlockWeights(ctypes.Structure):
 
 class DitStats(ctypes.Structure):
     _fields_ = [("workspace_bytes", c_uint64), ("peak_live_bytes", c_uint64), ("unaliased_bytes", c_uint64),
-                ("dispatches", c_int32), ("alias_activations", c_int32), ("profiler", c_void_p)]
+                ("dispatches", c_int32), ("alias_activations", c_int32), ("split_gemms", c_int32),
+                ("_reserved", c_int32), ("profiler", c_void_p)]
 
 
 class DitPlanInfo(ctypes.Structure):
     _fields_ = [("offset", c_uint64 * 9), ("bytes", c_uint64 * 9), ("first_step", c_int32 * 9),
                 ("last_step", c_int32 * 9), ("qkv_vt_offset", c_uint64), ("vt_pitch", c_int64),
                 ("workspace_bytes", c_uint64), ("peak_live_bytes", c_uint64), ("unaliased_bytes", c_uint64),
-                ("alias_activations", c_int32), ("_reserved", c_int32)]
+                ("alias_activations", c_int32), ("_reserved", c_int32), ("part_offset", c_uint64),
+                ("part_bytes", c_uint64)]
 
 
 class DeviceInfo(ctypes.Structure):

@@ -57,6 +57,11 @@ struct GemmParams {
   float col_scale;
   int m, n, k;
   int tiles_m, tiles_n;
+  // Tail split (bf16 x bf16, row-major output): tiles full_tiles .. of the
+  // tile order below are each split along k into tail_split workgroups that
+  // store fp32 partial tiles to part; gemm_tail_kernel finishes them.
+  int full_tiles, tail_split;
+  float* part;
 };
 
 constexpr int BM = 256, BN = 256;
@@ -354,6 +359,17 @@ constexpr int kSlots = 5;          // 160 KiB
 // on one XCD then cover 2 m-tiles x 16 n-tiles); measured best of 1..32
 constexpr int kRingGroupM = 2;
 
+// Tile `lin` of that order: groups of kRingGroupM m-tiles, m fastest.
+__device__ __forceinline__ void tile_origin(const GemmParams& p, int lin, int& tok0, int& feat0) {
+  const int per_group = kRingGroupM * p.tiles_n;
+  const int group = lin / per_group;
+  const int first_m = group * kRingGroupM;
+  const int gm = min(p.tiles_m - first_m, kRingGroupM);
+  const int in_group = lin - group * per_group;
+  tok0 = (first_m + in_group % gm) * BM;
+  feat0 = (in_group / gm) * BN;
+}
+
 template <int EPI, bool I8, bool W8 = false, bool GRP = false>
 __global__ __launch_bounds__(512) void gemm_ring_kernel(GemmParams p) {
   static_assert(!(I8 && W8), "int8 activations take the int8 MFMA path");
@@ -364,20 +380,26 @@ __global__ __launch_bounds__(512) void gemm_ring_kernel(GemmParams p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  const int nblk = p.tiles_m * p.tiles_n;
-  const int lin = xcd_remap(blockIdx.x, nblk);
-  const int per_group = kRingGroupM * p.tiles_n;
-  const int group = lin / per_group;
-  const int first_m = group * kRingGroupM;
-  const int gm = min(p.tiles_m - first_m, kRingGroupM);
-  const int in_group = lin - group * per_group;
-  const int tile_m = first_m + in_group % gm;
-  const int tile_n = in_group / gm;
-  const int tok0 = tile_m * BM, feat0 = tile_n * BN;
-  const bool trans = (int64_t)feat0 >= p.split_col;
   // a k-tile is 128 bytes of every operand row: 64 bf16 or 128 int8 values
   constexpr int ES = I8 ? 1 : 2;
-  const int KT = p.k / (128 / ES);
+  const int nblk = p.tiles_m * p.tiles_n;
+  // Whole tiles come first, in the XCD-aware order; with a tail split, block
+  // full_tiles + s * tail + j takes k-tiles [s KT / S, (s + 1) KT / S) of tail
+  // tile j (S = tail_split ways) and stores its partial tile part_idx.
+  int lin, kt0 = 0, KT = p.k / (128 / ES), part_idx = -1;
+  if (I8 || W8 || (int)blockIdx.x < p.full_tiles) {
+    lin = xcd_remap(blockIdx.x, I8 || W8 ? nblk : p.full_tiles);
+  } else {
+    const int tail = nblk - p.full_tiles, q = (int)blockIdx.x - p.full_tiles;
+    const int j = q % tail, sp = q / tail;
+    lin = p.full_tiles + j;
+    kt0 = sp * KT / p.tail_split;
+    KT = (sp + 1) * KT / p.tail_split - kt0;
+    part_idx = j * p.tail_split + sp;
+  }
+  int tok0, feat0;
+  tile_origin(p, lin, tok0, feat0);
+  const bool trans = (int64_t)feat0 >= p.split_col;
 
   // Ring of 5 operand slots; position q holds operand q&1 (0: activations,
   // 1: weights) of k-tile q>>1, in slot q%5.  Loads: instruction j (0..3)
@@ -386,8 +408,8 @@ __global__ __launch_bounds__(512) void gemm_ring_kernel(GemmParams p) {
   const __amdgpu_buffer_rsrc_t rsw = make_rsrc(p.w, (uint32_t)((uint64_t)p.n * p.ldw * (W8 ? 1 : ES)));
   const int lrow = wave * 8 + (lane >> 3);
   const uint32_t c16 = (uint32_t)(((lane & 7) ^ sw(lrow)) * 16);
-  const uint32_t xo0 = (uint32_t)(tok0 + lrow) * (uint32_t)p.ldx * ES + c16;
-  const uint32_t wo0 = (uint32_t)(feat0 + lrow) * (uint32_t)p.ldw * ES + c16;
+  const uint32_t xo0 = (uint32_t)(tok0 + lrow) * (uint32_t)p.ldx * ES + c16 + (uint32_t)kt0 * 128u;
+  const uint32_t wo0 = (uint32_t)(feat0 + lrow) * (uint32_t)p.ldw * ES + c16 + (uint32_t)kt0 * 128u;
   const uint32_t xstep = 64u * (uint32_t)p.ldx * ES, wstep = 64u * (uint32_t)p.ldw * ES;
   // half h (0/1) of position q: instructions 2h, 2h+1; past the end the last
   // k-tile is re-loaded into the (unread) slot so the load counts stay uniform
@@ -581,6 +603,18 @@ __global__ __launch_bounds__(512) void gemm_ring_kernel(GemmParams p) {
   }
   }
   wait_vmcnt<0>();
+  if constexpr (!I8 && !W8) {
+    if (part_idx >= 0) {   // same for the whole workgroup
+      // raw fp32 accumulators: wave w, quad (i, j) and lane l at float4 index
+      // part_idx * 16384 + w * 2048 + (8 i + j) * 64 + l (1 KiB per store)
+      f32x4* dst = reinterpret_cast<f32x4*>(p.part) + ((int64_t)part_idx << 14) + wave * 2048 + lane;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) dst[(8 * i + j) * 64] = acc16[i][j];
+      return;
+    }
+  }
   // a tile wholly on one side of split_col (features >= n are never stored)
   // stages its epilogue in the ring:
   // every wave's loads (including the clamped re-loads past the last k-tile)
@@ -631,6 +665,47 @@ __global__ __launch_bounds__(512) void gemm_ring_kernel(GemmParams p) {
     };
     finish(acc16);
   }
+}
+
+// ---------------------------------------------------------------------------
+// Second kernel of a tail split: each thread sums the S partial values of one
+// accumulator quad (4 consecutive features of one token) in split order, then
+// applies the ring kernel's epilogue (scale_bias4, epilogue4, one rounding).
+// Row-major output only (the launcher splits no tile with a transposed part).
+template <int EPI>
+__global__ __launch_bounds__(256) void gemm_tail_kernel(GemmParams p) {
+  const int tail = p.tiles_m * p.tiles_n - p.full_tiles, S = p.tail_split;
+  const int idx = blockIdx.x * 256 + threadIdx.x;   // quad index over the tail tiles
+  const int j = idx >> 14, e4 = idx & 16383;
+  if (j >= tail) return;
+  int tok0, feat0;
+  tile_origin(p, p.full_tiles + j, tok0, feat0);
+  // the layout the ring kernel stored: wave w, quad (i, jb), lane l
+  const int w = e4 >> 11, i = (e4 >> 9) & 3, jb = (e4 >> 6) & 7, l = e4 & 63;
+  const int f = feat0 + (w & 3) * 64 + 16 * i + 4 * (l >> 4);
+  const int t = tok0 + (w >> 2) * 128 + 16 * jb + (l & 15);
+  const f32x4* src = reinterpret_cast<const f32x4*>(p.part) + ((int64_t)j * S << 14) + e4;
+  f32x4 a = __builtin_nontemporal_load(src);
+  for (int sp = 1; sp < S; ++sp) a += __builtin_nontemporal_load(src + ((int64_t)sp << 14));
+  if (t >= p.m || f >= p.n) return;
+  float v[4] = {a[0], a[1], a[2], a[3]};
+  scale_bias4<false>(p, v, f);
+  epilogue4<EPI>(p, v, t, f);
+  *reinterpret_cast<u32x2*>(p.y + (int64_t)t * p.ldy + f) = pack4(v);
+}
+
+// Compute units of the current device (one query per device and thread).
+static int device_cus() {
+  constexpr int kMaxDev = 64;
+  thread_local int cached[kMaxDev] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 0;
+  if (!cached[dev]) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cached[dev] = v;
+  }
+  return cached[dev];
 }
 
 // ---------------------------------------------------------------------------
@@ -700,7 +775,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParamsF p) {
 
 // ---------------------------------------------------------------------------
 template <int EPI, bool W8>
-static void launch_bf16(const LinearArgs& a, hipStream_t stream) {
+static void launch_bf16(const LinearArgs& a, hipStream_t stream, int* kernels) {
   GemmParams p;
   p.x = a.x; p.ldx = a.ldx;
   p.x_scale = a.x_scale;
@@ -719,16 +794,38 @@ static void launch_bf16(const LinearArgs& a, hipStream_t stream) {
   p.tiles_n = (p.n + BN - 1) / BN;
   p.group_shift = a.group > 0 ? __builtin_ctz((unsigned)a.group) : 0;
   p.rope = RopeGeom{a.rope_hd, a.rope_h, a.rope_w, a.rope_spatial};
-  if (a.act == kINT8)
-    gemm_ring_kernel<EPI, true><<<dim3(p.tiles_m * p.tiles_n), dim3(512), 0, stream>>>(p);
-  else if constexpr (W8) {
-    if (a.group > 0)
-      gemm_ring_kernel<EPI, false, true, true><<<dim3(p.tiles_m * p.tiles_n), dim3(512), 0, stream>>>(p);
-    else
-      gemm_ring_kernel<EPI, false, true><<<dim3(p.tiles_m * p.tiles_n), dim3(512), 0, stream>>>(p);
+  const int nblk = p.tiles_m * p.tiles_n;
+  p.full_tiles = nblk;
+  p.tail_split = 0;
+  p.part = nullptr;
+  *kernels = 1;
+  if (a.act == kINT8) {
+    gemm_ring_kernel<EPI, true><<<dim3(nblk), dim3(512), 0, stream>>>(p);
+    return;
   }
-  else
-    gemm_ring_kernel<EPI, false><<<dim3(p.tiles_m * p.tiles_n), dim3(512), 0, stream>>>(p);
+  if constexpr (W8) {
+    if (a.group > 0)
+      gemm_ring_kernel<EPI, false, true, true><<<dim3(nblk), dim3(512), 0, stream>>>(p);
+    else
+      gemm_ring_kernel<EPI, false, true><<<dim3(nblk), dim3(512), 0, stream>>>(p);
+  } else {
+    int S = 0;
+    if constexpr (EPI != kEpiBiasRope) {   // row-major outputs only: no transposed or rotated part
+      const int cus = (a.part && a.split_col >= a.n) ? device_cus() : 0;
+      if (cus > 0) S = tail_split_ways(nblk, p.k / 64, cus, a.part_bytes / kPartTileBytes);
+      if (S) {
+        p.full_tiles = nblk - nblk % cus;
+        p.tail_split = S;
+        p.part = a.part;
+      }
+    }
+    const int grid = p.full_tiles + (nblk - p.full_tiles) * S;
+    gemm_ring_kernel<EPI, false><<<dim3(grid), dim3(512), 0, stream>>>(p);
+    if (S) {
+      gemm_tail_kernel<EPI><<<dim3((nblk - p.full_tiles) * 64), dim3(256), 0, stream>>>(p);
+      *kernels = 2;
+    }
+  }
 }
 
 template <int EPI>
@@ -747,8 +844,12 @@ static void launch_f32(const LinearArgs& a, hipStream_t stream) {
   gemm_f32_kernel<EPI><<<grid, dim3(256), 0, stream>>>(p);
 }
 
-hipError_t launch_linear(const LinearArgs& a, hipStream_t stream) {
+hipError_t launch_linear(const LinearArgs& a, hipStream_t stream, int* kernels) {
+  int dummy = 0;
+  if (!kernels) kernels = &dummy;
+  *kernels = 0;
   if (a.m == 0 || a.n == 0) return hipSuccess;
+  *kernels = 1;
   if (a.act == kF32) {
     switch (a.epi) {
       case kEpiBias: launch_f32<kEpiBias>(a, stream); break;
@@ -758,17 +859,17 @@ hipError_t launch_linear(const LinearArgs& a, hipStream_t stream) {
     }
   } else if (a.weight == kINT8) {
     switch (a.epi) {
-      case kEpiBias: launch_bf16<kEpiBias, true>(a, stream); break;
-      case kEpiGelu: launch_bf16<kEpiGelu, true>(a, stream); break;
-      case kEpiGatedResidual: launch_bf16<kEpiGatedResidual, true>(a, stream); break;
-      default: launch_bf16<kEpiBiasRope, true>(a, stream); break;
+      case kEpiBias: launch_bf16<kEpiBias, true>(a, stream, kernels); break;
+      case kEpiGelu: launch_bf16<kEpiGelu, true>(a, stream, kernels); break;
+      case kEpiGatedResidual: launch_bf16<kEpiGatedResidual, true>(a, stream, kernels); break;
+      default: launch_bf16<kEpiBiasRope, true>(a, stream, kernels); break;
     }
   } else {
     switch (a.epi) {
-      case kEpiBias: launch_bf16<kEpiBias, false>(a, stream); break;
-      case kEpiGelu: launch_bf16<kEpiGelu, false>(a, stream); break;
-      case kEpiGatedResidual: launch_bf16<kEpiGatedResidual, false>(a, stream); break;
-      default: launch_bf16<kEpiBiasRope, false>(a, stream); break;
+      case kEpiBias: launch_bf16<kEpiBias, false>(a, stream, kernels); break;
+      case kEpiGelu: launch_bf16<kEpiGelu, false>(a, stream, kernels); break;
+      case kEpiGatedResidual: launch_bf16<kEpiGatedResidual, false>(a, stream, kernels); break;
+      default: launch_bf16<kEpiBiasRope, false>(a, stream, kernels); break;
     }
   }
   return hipGetLastError();

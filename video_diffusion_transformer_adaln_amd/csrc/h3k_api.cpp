@@ -169,6 +169,33 @@ uint64_t reduction_bytes(const h3k_dit_config* c) {
   return align_up((uint64_t)(c->n_tokens / 2) * c->hidden * esize(c->act_dtype), kAlign);
 }
 
+// Scratch for the fp32 partial tiles of k-split tail tiles: the bf16 x bf16
+// out-projection, MLP up and MLP down GEMMs of one block (the launcher's
+// rule, tail_split_ways, at the 256 compute units of MI355X; on another CU
+// count the launcher caps its split ways by this size).  With token
+// reduction the reduced blocks use the same region, so it covers both token
+// counts.  Placed after the block's tensors (before the merged stream).
+constexpr int64_t kPlanCus = 256;
+uint64_t split_bytes_for(int64_t N, int64_t D, int64_t F) {
+  const int64_t tm = (N + 255) / 256;
+  const int64_t nk[3][2] = {{D, D}, {F, D}, {D, F}};   // (n, k) of out, up, down
+  int64_t need = 0;
+  for (const auto& g : nk) {
+    const int64_t tiles = tm * ((g[0] + 255) / 256);
+    const int S = tail_split_ways(tiles, g[1] / 64, kPlanCus, kPlanCus);
+    if (S) need = std::max(need, (tiles % kPlanCus) * S * kPartTileBytes);
+  }
+  return (uint64_t)need;
+}
+uint64_t split_bytes(const h3k_dit_config* c) {
+  if (c->act_dtype != H3K_BF16 || c->weight_dtype != H3K_BF16) return 0;
+  uint64_t b = split_bytes_for(c->n_tokens, c->hidden, c->mlp_hidden);
+  if (c->token_reduction_last > c->token_reduction_first)
+    b = std::max(b, split_bytes_for(c->n_tokens / 2, c->hidden, c->mlp_hidden));
+  return b;
+}
+constexpr int kSplitSteps[3] = {4, 6, 8};   // kernel steps of the out, up and down GEMMs
+
 void make_plan(const h3k_dit_config* c, bool alias, h3k_dit_plan_info* P) {
   std::memset(P, 0, sizeof(*P));
   const uint64_t N = c->n_tokens, D = c->hidden, F = c->mlp_hidden, eb = esize(c->act_dtype);
@@ -208,12 +235,15 @@ void make_plan(const h3k_dit_config* c, bool alias, h3k_dit_plan_info* P) {
       off[t] = cand;
     }
   }
+  const uint64_t sp = split_bytes(c);
   uint64_t ws = 0, peak = 0;
   for (int t = 0; t < H3K_T_COUNT; ++t) ws = std::max(ws, off[t] + align_up(bytes[t], kAlign));
   for (int s = 0; s <= 8; ++s) {
     uint64_t live = 0;
     for (int t = 0; t < H3K_T_COUNT; ++t)
       if (first[t] <= s && s <= last[t]) live += align_up(bytes[t], kAlign);
+    for (int k : kSplitSteps)
+      if (s == k) live += sp;
     peak = std::max(peak, live);
   }
   for (int t = 0; t < H3K_T_COUNT; ++t) {
@@ -225,9 +255,11 @@ void make_plan(const h3k_dit_config* c, bool alias, h3k_dit_plan_info* P) {
   P->qkv_vt_offset = off[H3K_T_QKV] + qk_bytes;
   P->vt_pitch = (int64_t)vt_pitch;
   const uint64_t red = reduction_bytes(c);
-  P->workspace_bytes = ws + red;
+  P->part_offset = ws;
+  P->part_bytes = sp;
+  P->workspace_bytes = ws + sp + red;
   P->peak_live_bytes = peak + red;
-  P->unaliased_bytes = unaliased + red;
+  P->unaliased_bytes = unaliased + sp + red;
   P->alias_activations = alias ? 1 : 0;
 }
 
@@ -341,8 +373,20 @@ h3k_status validate_forward(const h3k_dit_config* c, const h3k_dit_block_weights
 // Enqueue the eight kernels of one block (nine with int8_fc2_rows).  x may
 // equal out (stack in place: x is last read by the out-projection, out is
 // first written by MLP down).
+// `part`/`part_bytes`: the k-split scratch (see split_bytes); null / 0: no
+// split.  `kernels` counts the kernels enqueued, `splits` the GEMMs split.
 h3k_status run_block(const h3k_dit_config* c, const h3k_dit_plan_info* P, const h3k_dit_block_weights* w,
-                     const void* x, const void* cond, void* out, char* ws, hipStream_t s, Recorder& rec) {
+                     const void* x, const void* cond, void* out, char* ws, float* part, uint64_t part_bytes,
+                     hipStream_t s, Recorder& rec, int& kernels, int& splits) {
+  // one GEMM: its kernels (one, or two when its tail tiles are split) counted
+  auto gemm = [&](LinearArgs& L, const char* what, bool may_split) -> h3k_status {
+    if (may_split) { L.part = part; L.part_bytes = (int64_t)part_bytes; }
+    int nk = 0;
+    H3K_TRY(launched(launch_linear(L, s, &nk), what));
+    kernels += nk;
+    splits += nk > 1;
+    return H3K_OK;
+  };
   const DType act = (DType)c->act_dtype;
   const DType wt = (DType)c->weight_dtype;
   const int N = c->n_tokens, D = c->hidden, F = c->mlp_hidden;
@@ -362,6 +406,7 @@ h3k_status run_block(const h3k_dit_config* c, const h3k_dit_plan_info* P, const 
   rec.done(H3K_K_ADALN);
   H3K_TRY(launched(launch_ln_modulate(act, N, D, c->ln_eps, x, D, shift_a, scale_a, h, D, s), "LayerNorm 1"));
   rec.done(H3K_K_LN_MOD);
+  kernels += 2;
 
   LinearArgs L{};
   L.act = act; L.weight = wt;
@@ -380,7 +425,7 @@ h3k_status run_block(const h3k_dit_config* c, const h3k_dit_plan_info* P, const 
     L.scale_cols = D;
     L.col_scale = 1.4426950408889634f / std::sqrt((float)c->head_dim);
   }
-  H3K_TRY(launched(launch_linear(L, s), "QKV projection"));
+  H3K_TRY(gemm(L, "QKV projection", false));
   rec.done(H3K_K_QKV);
 
   AttentionArgs A{};
@@ -389,6 +434,7 @@ h3k_status run_block(const h3k_dit_config* c, const h3k_dit_plan_info* P, const 
   A.o = o; A.ldo = D; A.q_prescaled = q_pre;
   H3K_TRY(launched(launch_attention(A, s), "attention"));
   rec.done(H3K_K_ATTENTION);
+  ++kernels;
 
   L = LinearArgs{};
   L.act = act; L.weight = wt;
@@ -396,11 +442,12 @@ h3k_status run_block(const h3k_dit_config* c, const h3k_dit_plan_info* P, const 
   L.x = o; L.ldx = D; L.w = w->w_out; L.ldw = D; L.w_scale = w->s_out; L.bias = w->b_out;
   L.epi = kEpiGatedResidual; L.residual = x; L.ldr = D; L.gate = gate_a;
   L.y = x1; L.ldy = D; L.split_col = D;
-  H3K_TRY(launched(launch_linear(L, s), "out projection"));
+  H3K_TRY(gemm(L, "out projection", true));
   rec.done(H3K_K_OUT);
 
   H3K_TRY(launched(launch_ln_modulate(act, N, D, c->ln_eps, x1, D, shift_m, scale_m, h2, D, s), "LayerNorm 2"));
   rec.done(H3K_K_LN_MOD);
+  ++kernels;
 
   L = LinearArgs{};
   L.act = act; L.weight = wt;
@@ -408,7 +455,7 @@ h3k_status run_block(const h3k_dit_config* c, const h3k_dit_plan_info* P, const 
   L.x = h2; L.ldx = D; L.w = w->w_up; L.ldw = D; L.w_scale = w->s_up; L.bias = w->b_up;
   L.group = c->int8_mlp_group;
   L.epi = kEpiGelu; L.y = u; L.ldy = F; L.split_col = F;
-  H3K_TRY(launched(launch_linear(L, s), "MLP up"));
+  H3K_TRY(gemm(L, "MLP up", true));
   rec.done(H3K_K_UP);
 
   L = LinearArgs{};
@@ -421,11 +468,12 @@ h3k_status run_block(const h3k_dit_config* c, const h3k_dit_plan_info* P, const 
     float* us = reinterpret_cast<float*>(ws + P->offset[H3K_T_US]);
     H3K_TRY(launched(launch_quantize_int8(act, u, N, F, uq, us, s), "row quantiser of u"));
     rec.done(H3K_K_ACT_QUANT);
+    ++kernels;
     L.act = kINT8; L.x = uq; L.x_scale = us;
   }
   L.epi = kEpiGatedResidual; L.residual = x1; L.ldr = D; L.gate = gate_m;
   L.y = out; L.ldy = D; L.split_col = D;
-  H3K_TRY(launched(launch_linear(L, s), "MLP down"));
+  H3K_TRY(gemm(L, "MLP down", true));
   rec.done(H3K_K_DOWN);
   return H3K_OK;
 }
@@ -456,27 +504,35 @@ h3k_status forward(const h3k_dit_config* cfg, const h3k_dit_block_weights* block
   }
   const DType act = (DType)cfg->act_dtype;
   const int64_t N = cfg->n_tokens, D = cfg->hidden;
+  // the k-split scratch of the full plan serves the reduced blocks too
+  float* part = reinterpret_cast<float*>(ws + plan.part_offset);
+  const char* nosplit = std::getenv("H3K_DISABLE_TAIL_SPLIT");
+  const uint64_t part_bytes = (nosplit && std::strcmp(nosplit, "1") == 0) ? 0 : plan.part_bytes;
+  int kernels = 0, splits = 0;
   for (int l = 0; l < n_blocks; ++l) {
     const void* src = l == 0 ? x : out;
     if (reduce && l == tf) {
       H3K_TRY(launched(launch_token_merge(act, N, D, src, D, xm, D, stream), "token merge"));
       rec.done(H3K_K_TOKEN_MERGE);
+      ++kernels;
     }
     if (reduce && l >= tf && l < tl)
-      H3K_TRY(run_block(&half, &plan_half, &blocks[l], xm, c, xm, ws, stream, rec));
+      H3K_TRY(run_block(&half, &plan_half, &blocks[l], xm, c, xm, ws, part, part_bytes, stream, rec, kernels, splits));
     else
-      H3K_TRY(run_block(cfg, &plan, &blocks[l], src, c, out, ws, stream, rec));
+      H3K_TRY(run_block(cfg, &plan, &blocks[l], src, c, out, ws, part, part_bytes, stream, rec, kernels, splits));
     if (reduce && l == tl - 1) {                // entry state: x if the range starts at block 0, else out
       H3K_TRY(launched(launch_token_unmerge(act, N, D, tf == 0 ? x : out, D, xm, D, out, D, stream),
                        "token unmerge"));
       rec.done(H3K_K_TOKEN_UNMERGE);
+      ++kernels;
     }
   }
   if (stats) {
     stats->workspace_bytes = plan.workspace_bytes;
     stats->peak_live_bytes = plan.peak_live_bytes;
     stats->unaliased_bytes = plan.unaliased_bytes;
-    stats->dispatches = (cfg->int8_fc2_rows ? 9 : 8) * n_blocks + (reduce ? 2 : 0);
+    stats->dispatches = kernels;
+    stats->split_gemms = splits;
     stats->alias_activations = plan.alias_activations;
   }
   return H3K_OK;

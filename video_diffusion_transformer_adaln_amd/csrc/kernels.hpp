@@ -38,8 +38,35 @@ struct LinearArgs {
   float rope_spatial;            // 1, or 0.5 to halve the spatial coordinates
   int64_t scale_cols;            // bf16 row-major output: columns < scale_cols are multiplied by
   float col_scale;               // col_scale after the bias (and rotation), before the rounding
+  float* part;                   // bf16 x bf16, row-major output: scratch for k-split tail tiles
+  int64_t part_bytes;            // (fp32 partial tiles); null / 0: no split
 };
-hipError_t launch_linear(const LinearArgs& a, hipStream_t stream);
+// Enqueues the GEMM (and, when its tail tiles are split along k, the kernel
+// that sums their partial tiles and applies the epilogue); *kernels (if not
+// null) receives the number of kernels enqueued.
+hipError_t launch_linear(const LinearArgs& a, hipStream_t stream, int* kernels = nullptr);
+
+// Tail split of the 256x256-tile bf16 GEMM (one workgroup per compute unit):
+// with `tiles` tiles on `cus` CUs, the last tiles % cus tiles form a partial
+// last wave.  When that wave would leave at least half the CUs idle, each of
+// its tiles is split along k into S workgroups (S <= 8, at least 4 k-tiles
+// of 64 each, tail * S <= min(cus, cap_tiles)), whose fp32 partial tiles a
+// second kernel sums in a fixed order.  The split must shed at least 2048 of
+// k per tail workgroup, (1 - 1/S) k >= 2048: measured on MI355X, writing and
+// re-reading up to 64 MiB of partial tiles and the second launch cost about
+// 30 us, what a 256x256 tile's MFMAs take for about 1000 of k.  Returns S, or
+// 0 for no split.
+constexpr int64_t kPartTileBytes = 256 * 256 * 4;
+inline int tail_split_ways(int64_t tiles, int64_t kt, int64_t cus, int64_t cap_tiles) {
+  if (tiles < 1 || cus < 1) return 0;
+  const int64_t tail = tiles % cus;
+  if (tail == 0 || 2 * tail > cus) return 0;
+  int64_t s = kt / 4 < 8 ? kt / 4 : 8;
+  const int64_t room = (cap_tiles < cus ? cap_tiles : cus) / tail;
+  if (room < s) s = room;
+  if (s < 2 || (s - 1) * kt < 32 * s) return 0;   // (1 - 1/S) * 64 kt >= 2048
+  return (int)s;
+}
 
 struct AttentionArgs {
   DType dt;
