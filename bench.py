@@ -109,11 +109,15 @@ def kernel_role(name):
         epi, i8 = args[0], args[1] == "true"
         w8 = len(args) > 2 and args[2] == "true"
         grp = len(args) > 3 and args[3] == "true"
+        staged = args[4] if len(args) > 4 else "0"      # int8 weights widened into the staging buffer
         kind = "int8xint8" if i8 else ("w8a16_group" if grp else ("w8a16" if w8 else "bf16"))
+        if staged in ("1", "2"):
+            kind = "w8a16_staged" if staged == "1" else "w8a16_group_staged"
         return {"0": "qkv", "1": "mlp_up", "2": "gated", "3": "qkv_rope"}.get(epi, "gemm") + ":" + kind
     for key, role in (("ln_modulate_kernel", "ln_mod"), ("adaln_gemv_kernel", "adaln"),
                       ("quantize_int8_rows_kernel", "quantize_rows"), ("quantize_int8_kernel", "quantize_rows"),
-                      ("quantize_int8_groups_kernel", "quantize_groups"), ("copyBuffer", "copy")):
+                      ("quantize_int8_groups_kernel", "quantize_groups"), ("dequant_int8_kernel", "dequant"),
+                      ("gemm_tail_kernel", "gemm_tail"), ("copyBuffer", "copy")):
         if key in n:
             return role
     return None

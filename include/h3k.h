@@ -192,7 +192,12 @@ typedef struct h3k_dit_stats {
  * of the GPU's compute units idle, each of those tiles is split along k into
  * up to 8 workgroups whose fp32 partial tiles a second kernel sums in a fixed
  * order (sized for 256 CUs; H3K_DISABLE_TAIL_SPLIT=1 turns the split off).
- * With token reduction the merged stream follows it. */
+ * With INT8 weights the staging buffer follows (wstage_offset): each int8
+ * projection weight is widened to bf16 there (times its group scales, if
+ * any) right before its GEMM, which then runs as a bf16 GEMM with the
+ * per-channel scale in its epilogue; the resident weights stay int8
+ * (H3K_DISABLE_WEIGHT_STAGING=1 widens inside the GEMM instead, same bits).
+ * With token reduction the merged stream comes last. */
 #define H3K_T_MOD  0   /* fp32 [6D]   */
 #define H3K_T_H    1   /* [N, D]      */
 #define H3K_T_QKV  2   /* [N, 2D] + [D, vt_pitch] */
@@ -217,6 +222,8 @@ typedef struct h3k_dit_plan_info {
   int32_t  _reserved;
   uint64_t part_offset;              /* scratch of the k-split GEMM tails: byte offset ... */
   uint64_t part_bytes;               /* ... and size (0 when no projection can split)     */
+  uint64_t wstage_offset;            /* int8 weights: bf16 staging buffer, byte offset ...  */
+  uint64_t wstage_bytes;             /* ... and size (0 unless INT8 weights)               */
 } h3k_dit_plan_info;
 
 /* Message for the last non-OK status returned on this thread (never NULL). */

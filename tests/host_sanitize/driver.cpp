@@ -114,7 +114,10 @@ void run_config(const char* name, h3k_dit_config c, int n_blocks) {
   const int64_t before = h3k_stub_launches();
   if (c.token_reduction_last <= c.token_reduction_first) {
     CHECK(h3k_dit_block_forward(&c, &blocks[0], x, cond, out, ws, ws_bytes, nullptr, &st) == H3K_OK);
-    CHECK(st.dispatches == (c.int8_fc2_rows ? 9 : 8) + st.split_gemms);
+    // int8 weights: each projection with bf16 activations widens its weights first
+    const int staged = c.weight_dtype == H3K_INT8 ? (c.int8_fc2_rows ? 3 : 4) : 0;
+    CHECK((staged == 0) == (info.wstage_bytes == 0));
+    CHECK(st.dispatches == (c.int8_fc2_rows ? 9 : 8) + st.split_gemms + staged);
     CHECK(st.split_gemms >= 0 && st.split_gemms <= 3);
     CHECK(h3k_stub_launches() - before == st.dispatches);
     CHECK(st.workspace_bytes == ws_bytes);

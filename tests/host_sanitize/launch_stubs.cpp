@@ -80,9 +80,18 @@ hipError_t launch_ln_modulate(DType dt, int n, int D, float, const void* x, int6
 hipError_t launch_linear(const LinearArgs& a, hipStream_t, int* kernels) {
   ++g_launches;
   if (kernels) *kernels = 1;
+  // int8 weights widened into the staging buffer first (one more kernel),
+  // then a bf16 GEMM
+  const bool staged = a.weight == kINT8 && a.act == kBF16 && a.wstage && a.wstage_bytes >= a.n * a.k * 2;
+  if (staged) {
+    touch_write(a.wstage, a.n, a.k, a.k, 2);
+    touch_read(a.wstage, a.n, a.k, a.k, 2);
+    ++g_launches;
+    if (kernels) *kernels = 2;
+  }
   // the tail split as the bf16 launcher takes it on 256 compute units: the
   // partial tiles it writes must lie inside the scratch it was given
-  if (a.part && a.act == kBF16 && a.weight == kBF16 && a.epi != kEpiBiasRope && a.split_col >= a.n) {
+  if (a.part && a.act == kBF16 && (a.weight == kBF16 || staged) && a.epi != kEpiBiasRope && a.split_col >= a.n) {
     const int64_t tiles = ((a.m + 255) / 256) * ((a.n + 255) / 256);
     const int S = tail_split_ways(tiles, a.k / 64, 256, a.part_bytes / kPartTileBytes);
     if (S) {
@@ -91,7 +100,7 @@ hipError_t launch_linear(const LinearArgs& a, hipStream_t, int* kernels) {
       touch_write(a.part, 1, used, used, 1);
       touch_read(a.part, 1, used, used, 1);
       ++g_launches;
-      if (kernels) *kernels = 2;
+      if (kernels) ++*kernels;
     }
   }
   const int64_t ex = es(a.act), ew = es(a.weight), ey = a.act == kINT8 ? 2 : es(a.act);

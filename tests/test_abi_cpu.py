@@ -35,7 +35,7 @@ def test_struct_sizes_match_header_layout():
     assert ctypes.sizeof(B.DitConfig) == 72
     assert ctypes.sizeof(B.DitBlockWeights) == 14 * 8
     assert ctypes.sizeof(B.DitStats) == 48
-    assert ctypes.sizeof(B.DitPlanInfo) == 9 * 8 * 2 + 9 * 4 * 2 + 8 * 5 + 8 + 16
+    assert ctypes.sizeof(B.DitPlanInfo) == 9 * 8 * 2 + 9 * 4 * 2 + 8 * 5 + 8 + 32
     assert ctypes.sizeof(B.DeviceInfo) == 4 * 4 + 8 + 64
 
 
@@ -126,6 +126,20 @@ def test_token_reduction_adds_the_merged_stream_to_the_workspace():
     tensors_end = max(info.offset[t] + info.bytes[t] for t in range(9))
     assert tensors_end <= info.part_offset
     assert info.part_offset + info.part_bytes == info.workspace_bytes - merged
+
+
+def test_int8_weight_staging_buffer():
+    """INT8 weights with BF16 activations: a staging buffer of the largest bf16 projection
+    weight (QKV, 3D x D) after the k-split scratch; nothing for bf16 or fp32 weights."""
+    D, F = 5120, 13824
+    info = h3k.h3k_dit_plan(cfg_c2(weight_dtype=B.H3K_INT8))
+    assert info.wstage_bytes == 3 * D * D * 2
+    assert info.wstage_offset == info.part_offset + info.part_bytes
+    assert info.wstage_offset + info.wstage_bytes == info.workspace_bytes
+    wide = h3k.h3k_dit_plan(B.make_config(512, 1024, 8, 128, 8192, 1024, B.H3K_BF16, B.H3K_INT8))
+    assert wide.wstage_bytes == 1024 * 8192 * 2                 # D x F > 3D x D
+    assert h3k.h3k_dit_plan(cfg_c2()).wstage_bytes == 0
+    assert h3k.h3k_dit_plan(B.make_config(512, 256, 4, 64, 1024, 256, B.H3K_F32)).wstage_bytes == 0
 
 
 def test_tail_split_scratch_sizes():

@@ -170,13 +170,37 @@ def test_block_c4_int8_sampled_rows(R):
         q, s = ow[name]
         assert np.array_equal(dw[name].cpu().numpy(), q)
         assert np.array_equal(dw["s_" + name[2:]].cpu().numpy(), s)
-    got = to_np(_run_block(R, shape, dw, dev(hx), dev(hc)))
+    from video_diffusion_transformer_adaln_amd import binding as B
+    st = B.DitStats()
+    got_t = _run_block(R, shape, dw, dev(hx), dev(hc), stats=st)
+    assert st.dispatches == 8 + 4 and st.split_gemms == 0   # four weight-widening passes; no tail split
+    got = to_np(got_t)
     rows = sample_rows(shape.n_tokens)
     ref = oracle.block_forward(hx.values, hc.values, ow, shape.n_heads, rows=rows)
     err = rel_l2(got[rows], ref)
     flush(f"  rel_l2 = {err:.3e}")
     record("block c4 int8 weights (22680x5120) sampled rows", err, TOL)
     assert err < TOL
+    # widening inside the GEMM instead of into the staging buffer: the same bits
+    _assert_staging_identical(R, shape, dw, dev(hx), dev(hc), got_t)
+
+
+def _assert_staging_identical(R, shape, dw, xd, cd, staged, **kw):
+    """The int8 projections with their weights widened in the GEMM's ring
+    (H3K_DISABLE_WEIGHT_STAGING=1) give the bytes of the staged path: the same
+    bf16 operands (bf16(q), or bf16(q s) with group scales) in the same
+    order, and the channel scale applied before the bias in both."""
+    import os
+    import torch
+    from video_diffusion_transformer_adaln_amd import binding as B
+    os.environ["H3K_DISABLE_WEIGHT_STAGING"] = "1"
+    try:
+        st = B.DitStats()
+        ring = _run_block(R, shape, dw, xd, cd, stats=st, **kw)
+    finally:
+        os.environ.pop("H3K_DISABLE_WEIGHT_STAGING", None)
+    assert st.split_gemms == 0
+    assert torch.equal(ring.view(torch.int16), staged.view(torch.int16))
 
 
 @pytest.mark.parametrize("case", ["c4", "small"])
@@ -193,7 +217,8 @@ def test_block_int8_fc2_rows(R, case):
     xd, cd = dev(hx), dev(hc)
     st = B.DitStats()
     got_t = _run_block(R, shape, dw, xd, cd, stats=st, int8_fc2_rows=True)
-    assert st.dispatches == 9
+    assert st.dispatches == 9 + 3 and st.split_gemms == 0   # QKV, out and up widen their weights first
+    _assert_staging_identical(R, shape, dw, xd, cd, got_t, int8_fc2_rows=True)
     got = to_np(got_t)
     rows = sample_rows(shape.n_tokens) if case == "c4" else np.arange(shape.n_tokens)
     ref = oracle.block_forward(hx.values, hc.values, ow, shape.n_heads, rows=rows, int8_fc2_rows=True)
@@ -222,7 +247,8 @@ def test_block_int8_mlp_groups(R, case, group):
     xd, cd = dev(hx), dev(hc)
     st = B.DitStats()
     got_t = _run_block(R, shape, dw, xd, cd, stats=st, int8_mlp_group=group)
-    assert st.dispatches == 8
+    assert st.dispatches == 8 + 4 and st.split_gemms == 0
+    _assert_staging_identical(R, shape, dw, xd, cd, got_t, int8_mlp_group=group)
     got = to_np(got_t)
     rows = sample_rows(shape.n_tokens) if case == "c4" else np.arange(shape.n_tokens)
     ref = oracle.block_forward(hx.values, hc.values, ow, shape.n_heads, rows=rows)

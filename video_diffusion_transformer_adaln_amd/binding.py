@@ -57,7 +57,7 @@ class DitPlanInfo(ctypes.Structure):
                 ("last_step", c_int32 * 9), ("qkv_vt_offset", c_uint64), ("vt_pitch", c_int64),
                 ("workspace_bytes", c_uint64), ("peak_live_bytes", c_uint64), ("unaliased_bytes", c_uint64),
                 ("alias_activations", c_int32), ("_reserved", c_int32), ("part_offset", c_uint64),
-                ("part_bytes", c_uint64)]
+                ("part_bytes", c_uint64), ("wstage_offset", c_uint64), ("wstage_bytes", c_uint64)]
 
 
 class DeviceInfo(ctypes.Structure):

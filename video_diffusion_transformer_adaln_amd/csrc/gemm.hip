@@ -370,7 +370,11 @@ __device__ __forceinline__ void tile_origin(const GemmParams& p, int lin, int& t
   feat0 = (in_group / gm) * BN;
 }
 
-template <int EPI, bool I8, bool W8 = false, bool GRP = false>
+// SC: bf16 weights that are int8 weights widened beforehand (dequant_int8_kernel):
+// 1 with per-channel scales (w_scale applied in the epilogue, as for W8), 2
+// with group scales (already in the widened values).  The same code as SC = 0
+// otherwise; the value only tells the two apart (and in a kernel trace).
+template <int EPI, bool I8, bool W8 = false, bool GRP = false, int SC = 0>
 __global__ __launch_bounds__(512) void gemm_ring_kernel(GemmParams p) {
   static_assert(!(I8 && W8), "int8 activations take the int8 MFMA path");
   // bf16 MFMA 16x16x32, int8 MFMA 16x16x64: both take a 16-byte chunk of a
@@ -656,12 +660,13 @@ __global__ __launch_bounds__(512) void gemm_ring_kernel(GemmParams p) {
     else if (staged) store_tile_staged<EPI, true, 4>(p, accf, a_row0, b_row0, tok0, feat0, false, lane, stage);
     else store_tile<EPI, true>(p, accf, a_row0, b_row0, tok0, feat0, false, lane);
   } else {
+    constexpr bool kScale = (W8 && !GRP) || SC == 1;   // per-channel weight scale in the epilogue
     auto finish = [&](const auto& ac) {
       if (staged && EPI == kEpiGatedResidual && !trans)
-        store_tile_staged_residual<W8 && !GRP, 2>(p, ac, a_row0, b_row0, tok0, feat0, lane, stage);
+        store_tile_staged_residual<kScale, 2>(p, ac, a_row0, b_row0, tok0, feat0, lane, stage);
       else if (staged)
-        store_tile_staged<EPI, W8 && !GRP, 4>(p, ac, a_row0, b_row0, tok0, feat0, trans, lane, stage, rope_tab);
-      else store_tile<EPI, W8 && !GRP>(p, ac, a_row0, b_row0, tok0, feat0, trans, lane);
+        store_tile_staged<EPI, kScale, 4>(p, ac, a_row0, b_row0, tok0, feat0, trans, lane, stage, rope_tab);
+      else store_tile<EPI, kScale>(p, ac, a_row0, b_row0, tok0, feat0, trans, lane);
     };
     finish(acc16);
   }
@@ -672,7 +677,7 @@ __global__ __launch_bounds__(512) void gemm_ring_kernel(GemmParams p) {
 // accumulator quad (4 consecutive features of one token) in split order, then
 // applies the ring kernel's epilogue (scale_bias4, epilogue4, one rounding).
 // Row-major output only (the launcher splits no tile with a transposed part).
-template <int EPI>
+template <int EPI, int SC>
 __global__ __launch_bounds__(256) void gemm_tail_kernel(GemmParams p) {
   const int tail = p.tiles_m * p.tiles_n - p.full_tiles, S = p.tail_split;
   const int idx = blockIdx.x * 256 + threadIdx.x;   // quad index over the tail tiles
@@ -689,9 +694,37 @@ __global__ __launch_bounds__(256) void gemm_tail_kernel(GemmParams p) {
   for (int sp = 1; sp < S; ++sp) a += __builtin_nontemporal_load(src + ((int64_t)sp << 14));
   if (t >= p.m || f >= p.n) return;
   float v[4] = {a[0], a[1], a[2], a[3]};
-  scale_bias4<false>(p, v, f);
+  scale_bias4<SC == 1>(p, v, f);
   epilogue4<EPI>(p, v, t, f);
   *reinterpret_cast<u32x2*>(p.y + (int64_t)t * p.ldy + f) = pack4(v);
+}
+
+// int8 weights [rows, cols] -> bf16 [rows, cols] (dense), 16 values per
+// thread: with group scales (group_shift > 0) bf16(q * s[row, col / group]),
+// the value the W8A16 ring kernel widens to with group scales; else bf16(q),
+// exact, the per-row scale being applied in the GEMM epilogue.  cols is a
+// multiple of 16 (of 128 for the GEMM).
+__global__ __launch_bounds__(256) void dequant_int8_kernel(const int8_t* __restrict__ q, int64_t ldq,
+                                                           const float* __restrict__ s, int64_t rows, int64_t cols,
+                                                           int group_shift, bf16* __restrict__ out) {
+  const int64_t i16 = (int64_t)blockIdx.x * 256 + threadIdx.x;   // 16-value chunk
+  const int64_t per_row = cols >> 4;
+  if (i16 >= rows * per_row) return;
+  const int64_t r = i16 / per_row, c0 = (i16 - r * per_row) << 4;
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(q + r * ldq + c0));
+  const u32x2 lo = {v[0], v[1]}, hi = {v[2], v[3]};
+  u32x4 o0, o1;
+  if (group_shift > 0) {
+    const float sc = s[r * (cols >> group_shift) + (c0 >> group_shift)];   // 16 values lie in one group
+    o0 = i8x8_to_bf16<true>(lo, sc);
+    o1 = i8x8_to_bf16<true>(hi, sc);
+  } else {
+    o0 = i8x8_to_bf16<false>(lo, 1.0f);
+    o1 = i8x8_to_bf16<false>(hi, 1.0f);
+  }
+  u32x4* dst = reinterpret_cast<u32x4*>(out + r * cols + c0);
+  __builtin_nontemporal_store(o0, dst);
+  __builtin_nontemporal_store(o1, dst + 1);
 }
 
 // Compute units of the current device (one query per device and thread).
@@ -774,7 +807,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParamsF p) {
 }
 
 // ---------------------------------------------------------------------------
-template <int EPI, bool W8>
+template <int EPI, bool W8, int SC = 0>
 static void launch_bf16(const LinearArgs& a, hipStream_t stream, int* kernels) {
   GemmParams p;
   p.x = a.x; p.ldx = a.ldx;
@@ -820,12 +853,41 @@ static void launch_bf16(const LinearArgs& a, hipStream_t stream, int* kernels) {
       }
     }
     const int grid = p.full_tiles + (nblk - p.full_tiles) * S;
-    gemm_ring_kernel<EPI, false><<<dim3(grid), dim3(512), 0, stream>>>(p);
+    gemm_ring_kernel<EPI, false, false, false, SC><<<dim3(grid), dim3(512), 0, stream>>>(p);
     if (S) {
-      gemm_tail_kernel<EPI><<<dim3((nblk - p.full_tiles) * 64), dim3(256), 0, stream>>>(p);
+      gemm_tail_kernel<EPI, SC><<<dim3((nblk - p.full_tiles) * 64), dim3(256), 0, stream>>>(p);
       *kernels = 2;
     }
   }
+}
+
+// int8 weights with a staging buffer (bf16 activations): the weights are
+// widened to bf16 there (with group scales, times the scale), then the bf16
+// ring kernel runs on them with the per-channel scale (if any) in its
+// epilogue.  The same MFMA operands in the same order as the W8A16 ring
+// kernel, so the same bits, at the bf16 kernel's speed plus one pass over the
+// weights.
+template <int EPI>
+static void launch_w8_staged(const LinearArgs& a, hipStream_t stream, int* kernels) {
+  const int64_t chunks = a.n * (a.k / 16);
+  const int gs = a.group > 0 ? __builtin_ctz((unsigned)a.group) : 0;
+  dequant_int8_kernel<<<dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, stream>>>(
+      (const int8_t*)a.w, a.ldw, a.w_scale, a.n, a.k, gs, (bf16*)a.wstage);
+  LinearArgs b = a;
+  b.weight = kBF16;
+  b.w = a.wstage;
+  b.ldw = a.k;
+  b.group = 0;
+  b.wstage = nullptr;
+  b.wstage_bytes = 0;
+  int nk = 0;
+  if (a.group > 0) {
+    b.w_scale = nullptr;
+    launch_bf16<EPI, false, 2>(b, stream, &nk);
+  } else {
+    launch_bf16<EPI, false, 1>(b, stream, &nk);
+  }
+  *kernels = 1 + nk;
 }
 
 template <int EPI>
@@ -856,6 +918,13 @@ hipError_t launch_linear(const LinearArgs& a, hipStream_t stream, int* kernels) 
       case kEpiGelu: launch_f32<kEpiGelu>(a, stream); break;
       case kEpiGatedResidual: launch_f32<kEpiGatedResidual>(a, stream); break;
       default: return hipErrorInvalidValue;   // no rotary epilogue on the fp32 path
+    }
+  } else if (a.weight == kINT8 && a.act == kBF16 && a.wstage && a.wstage_bytes >= a.n * a.k * 2) {
+    switch (a.epi) {
+      case kEpiBias: launch_w8_staged<kEpiBias>(a, stream, kernels); break;
+      case kEpiGelu: launch_w8_staged<kEpiGelu>(a, stream, kernels); break;
+      case kEpiGatedResidual: launch_w8_staged<kEpiGatedResidual>(a, stream, kernels); break;
+      default: launch_w8_staged<kEpiBiasRope>(a, stream, kernels); break;
     }
   } else if (a.weight == kINT8) {
     switch (a.epi) {

@@ -196,6 +196,18 @@ uint64_t split_bytes(const h3k_dit_config* c) {
 }
 constexpr int kSplitSteps[3] = {4, 6, 8};   // kernel steps of the out, up and down GEMMs
 
+// Staging buffer of the int8-weight projections (bf16 activations): each
+// int8 weight matrix is widened to bf16 there right before its GEMM, which
+// then runs as a bf16 GEMM with the channel scale in its epilogue.  Sized for
+// the largest of the block's projection weights (the int8 x int8 FC2 reads
+// its int8 weights directly).  Placed after the k-split scratch.
+uint64_t stage_bytes(const h3k_dit_config* c) {
+  if (c->weight_dtype != H3K_INT8 || c->act_dtype != H3K_BF16) return 0;
+  const uint64_t D = c->hidden, F = c->mlp_hidden;
+  return align_up(std::max(3 * D * D, D * F) * 2, kAlign);
+}
+constexpr int kGemmSteps[4] = {2, 4, 6, 8};  // QKV, out, up, down
+
 void make_plan(const h3k_dit_config* c, bool alias, h3k_dit_plan_info* P) {
   std::memset(P, 0, sizeof(*P));
   const uint64_t N = c->n_tokens, D = c->hidden, F = c->mlp_hidden, eb = esize(c->act_dtype);
@@ -235,7 +247,7 @@ void make_plan(const h3k_dit_config* c, bool alias, h3k_dit_plan_info* P) {
       off[t] = cand;
     }
   }
-  const uint64_t sp = split_bytes(c);
+  const uint64_t sp = split_bytes(c), st = stage_bytes(c);
   uint64_t ws = 0, peak = 0;
   for (int t = 0; t < H3K_T_COUNT; ++t) ws = std::max(ws, off[t] + align_up(bytes[t], kAlign));
   for (int s = 0; s <= 8; ++s) {
@@ -244,6 +256,8 @@ void make_plan(const h3k_dit_config* c, bool alias, h3k_dit_plan_info* P) {
       if (first[t] <= s && s <= last[t]) live += align_up(bytes[t], kAlign);
     for (int k : kSplitSteps)
       if (s == k) live += sp;
+    for (int k : kGemmSteps)
+      if (s == k) live += st;
     peak = std::max(peak, live);
   }
   for (int t = 0; t < H3K_T_COUNT; ++t) {
@@ -257,9 +271,11 @@ void make_plan(const h3k_dit_config* c, bool alias, h3k_dit_plan_info* P) {
   const uint64_t red = reduction_bytes(c);
   P->part_offset = ws;
   P->part_bytes = sp;
-  P->workspace_bytes = ws + sp + red;
+  P->wstage_offset = ws + sp;
+  P->wstage_bytes = st;
+  P->workspace_bytes = ws + sp + st + red;
   P->peak_live_bytes = peak + red;
-  P->unaliased_bytes = unaliased + sp + red;
+  P->unaliased_bytes = unaliased + sp + st + red;
   P->alias_activations = alias ? 1 : 0;
 }
 
@@ -377,14 +393,16 @@ h3k_status validate_forward(const h3k_dit_config* c, const h3k_dit_block_weights
 // split.  `kernels` counts the kernels enqueued, `splits` the GEMMs split.
 h3k_status run_block(const h3k_dit_config* c, const h3k_dit_plan_info* P, const h3k_dit_block_weights* w,
                      const void* x, const void* cond, void* out, char* ws, float* part, uint64_t part_bytes,
-                     hipStream_t s, Recorder& rec, int& kernels, int& splits) {
-  // one GEMM: its kernels (one, or two when its tail tiles are split) counted
+                     void* wstage, uint64_t wstage_bytes, hipStream_t s, Recorder& rec, int& kernels, int& splits) {
+  // one GEMM: its kernels (one, or two when its tail tiles are split; one more
+  // when int8 weights are widened into the staging buffer first) counted
   auto gemm = [&](LinearArgs& L, const char* what, bool may_split) -> h3k_status {
     if (may_split) { L.part = part; L.part_bytes = (int64_t)part_bytes; }
+    if (L.weight == kINT8 && L.act == kBF16) { L.wstage = wstage; L.wstage_bytes = (int64_t)wstage_bytes; }
     int nk = 0;
     H3K_TRY(launched(launch_linear(L, s, &nk), what));
     kernels += nk;
-    splits += nk > 1;
+    splits += nk - 1 - (L.wstage != nullptr && L.wstage_bytes >= L.n * L.k * 2);
     return H3K_OK;
   };
   const DType act = (DType)c->act_dtype;
@@ -508,6 +526,9 @@ h3k_status forward(const h3k_dit_config* cfg, const h3k_dit_block_weights* block
   float* part = reinterpret_cast<float*>(ws + plan.part_offset);
   const char* nosplit = std::getenv("H3K_DISABLE_TAIL_SPLIT");
   const uint64_t part_bytes = (nosplit && std::strcmp(nosplit, "1") == 0) ? 0 : plan.part_bytes;
+  void* wstage = ws + plan.wstage_offset;
+  const char* nostage = std::getenv("H3K_DISABLE_WEIGHT_STAGING");
+  const uint64_t wstage_bytes = (nostage && std::strcmp(nostage, "1") == 0) ? 0 : plan.wstage_bytes;
   int kernels = 0, splits = 0;
   for (int l = 0; l < n_blocks; ++l) {
     const void* src = l == 0 ? x : out;
@@ -517,9 +538,11 @@ h3k_status forward(const h3k_dit_config* cfg, const h3k_dit_block_weights* block
       ++kernels;
     }
     if (reduce && l >= tf && l < tl)
-      H3K_TRY(run_block(&half, &plan_half, &blocks[l], xm, c, xm, ws, part, part_bytes, stream, rec, kernels, splits));
+      H3K_TRY(run_block(&half, &plan_half, &blocks[l], xm, c, xm, ws, part, part_bytes, wstage, wstage_bytes, stream,
+                        rec, kernels, splits));
     else
-      H3K_TRY(run_block(cfg, &plan, &blocks[l], src, c, out, ws, part, part_bytes, stream, rec, kernels, splits));
+      H3K_TRY(run_block(cfg, &plan, &blocks[l], src, c, out, ws, part, part_bytes, wstage, wstage_bytes, stream, rec,
+                        kernels, splits));
     if (reduce && l == tl - 1) {                // entry state: x if the range starts at block 0, else out
       H3K_TRY(launched(launch_token_unmerge(act, N, D, tf == 0 ? x : out, D, xm, D, out, D, stream),
                        "token unmerge"));

@@ -40,6 +40,8 @@ struct LinearArgs {
   float col_scale;               // col_scale after the bias (and rotation), before the rounding
   float* part;                   // bf16 x bf16, row-major output: scratch for k-split tail tiles
   int64_t part_bytes;            // (fp32 partial tiles); null / 0: no split
+  void* wstage;                  // int8 weights, bf16 activations: n * k bf16 to widen the weights
+  int64_t wstage_bytes;          // into before a bf16 GEMM; null / too small: widened in the GEMM
 };
 // Enqueues the GEMM (and, when its tail tiles are split along k, the kernel
 // that sums their partial tiles and applies the epilogue); *kernels (if not
