@@ -176,8 +176,9 @@ typedef struct h3k_dit_stats {
   uint64_t unaliased_bytes;     /* out: workspace the same call needs without aliasing */
   int32_t  dispatches;          /* out: kernels enqueued by the call                */
   int32_t  alias_activations;   /* out: aliasing actually used (after the env switch) */
-  int32_t  split_gemms;         /* out: GEMMs whose tail tiles were split along k
-                                   (each enqueued one more kernel, counted in dispatches) */
+  int32_t  tail_splits;         /* out: kernels whose partial last wave was split (GEMM
+                                   tiles along k, attention workgroups along the keys);
+                                   each enqueued one more kernel, counted in dispatches */
   int32_t  _reserved;
   h3k_profiler* profiler;       /* in: NULL, or a profiler that records every launch */
 } h3k_dit_stats;
@@ -187,11 +188,13 @@ typedef struct h3k_dit_stats {
  * The QKV region holds Q and K as one row-major [N, 2D] matrix, followed at
  * qkv_vt_offset by V transposed, [D, vt_pitch] (vt_pitch = N rounded up to 8),
  * so that the attention kernel reads V along the key axis.  After the tensors
- * (part_offset) lies the scratch of the bf16 out-projection and MLP GEMMs:
- * when a GEMM's last wave of 256x256 output tiles would leave at least half
+ * (part_offset) lies the scratch of split tails: when a bf16 out-projection
+ * or MLP GEMM's last wave of 256x256 output tiles would leave at least half
  * of the GPU's compute units idle, each of those tiles is split along k into
  * up to 8 workgroups whose fp32 partial tiles a second kernel sums in a fixed
- * order (sized for 256 CUs; H3K_DISABLE_TAIL_SPLIT=1 turns the split off).
+ * order; likewise the attention's last round of workgroups (head_dim 128) is
+ * split along the keys and combined by a second kernel (sized for 256 CUs;
+ * H3K_DISABLE_TAIL_SPLIT=1 turns both off).
  * With INT8 weights the staging buffer follows (wstage_offset): each int8
  * projection weight is widened to bf16 there (times its group scales, if
  * any) right before its GEMM, which then runs as a bf16 GEMM with the
@@ -220,8 +223,8 @@ typedef struct h3k_dit_plan_info {
   uint64_t unaliased_bytes;
   int32_t  alias_activations;
   int32_t  _reserved;
-  uint64_t part_offset;              /* scratch of the k-split GEMM tails: byte offset ... */
-  uint64_t part_bytes;               /* ... and size (0 when no projection can split)     */
+  uint64_t part_offset;              /* scratch of split tails: byte offset ...            */
+  uint64_t part_bytes;               /* ... and size (0 when no kernel can split)          */
   uint64_t wstage_offset;            /* int8 weights: bf16 staging buffer, byte offset ...  */
   uint64_t wstage_bytes;             /* ... and size (0 unless INT8 weights)               */
 } h3k_dit_plan_info;

@@ -105,12 +105,39 @@ def tail_split_ways(tiles, kt, cus, cap_tiles):
     return s if s >= 2 and (s - 1) * kt >= 32 * s else 0
 
 
-def expected_split_gemms(n_tokens, hidden, mlp, part_bytes, cus):
-    """How many of a bf16 block's out / up / down GEMMs split their tail."""
+def attn_split_ways(blocks, tiles, slots, cap_units):
+    """The block's key-split rule for the bf16 attention (head_dim 128), restated
+    for the tests: `blocks` workgroups, `slots` resident at once, `tiles` key
+    tiles of 32; the last round splits S ways when it would leave at least half
+    the slots idle, S <= 8, >= 8 tiles per range, tail * S <= min(slots, cap),
+    and only if each range sheds at least 2048 keys, (1 - 1/S) 32 tiles >= 2048."""
+    if blocks < 1 or slots < 1:
+        return 0
+    tail = blocks % slots
+    if tail == 0 or 2 * tail > slots:
+        return 0
+    s = min(8, tiles // 8, min(cap_units, slots) // tail)
+    return s if s >= 2 and (s - 1) * tiles >= 64 * s else 0
+
+
+def expected_tail_splits(n_tokens, hidden, mlp, part_bytes, cus, n_heads=None, head_dim=128):
+    """How many of a bf16 block's kernels split their last wave: the out / up /
+    down GEMMs and (head_dim 128) the attention."""
     tm = (n_tokens + 255) // 256
     cap = part_bytes // (256 * 256 * 4)
-    return sum(tail_split_ways(tm * ((n + 255) // 256), k // 64, cus, cap) > 0
-               for n, k in ((hidden, hidden), (mlp, hidden), (hidden, mlp)))
+    n = sum(tail_split_ways(tm * ((nn + 255) // 256), k // 64, cus, cap) > 0
+            for nn, k in ((hidden, hidden), (mlp, hidden), (hidden, mlp)))
+    if head_dim == 128:
+        # 8-wave workgroups when their last round can split, else the 4-wave
+        # shape (short sequences, few workgroups) with its own split, if any
+        heads = hidden // head_dim if n_heads is None else n_heads
+        tiles = (n_tokens + 31) // 32
+        unit = lambda nw: nw * 32 * 130 * 4
+        s8 = attn_split_ways((n_tokens + 255) // 256 * heads, tiles, cus, part_bytes // unit(8))
+        four = (n_tokens + 255) // 256 * heads < 1024 and n_tokens <= 8192
+        s4 = attn_split_ways((n_tokens + 127) // 128 * heads, tiles, 2 * cus, part_bytes // unit(4)) if four else 0
+        n += (s8 > 0 or s4 > 0) and part_bytes > 0
+    return n
 
 
 def device_cus():

@@ -117,8 +117,8 @@ void run_config(const char* name, h3k_dit_config c, int n_blocks) {
     // int8 weights: each projection with bf16 activations widens its weights first
     const int staged = c.weight_dtype == H3K_INT8 ? (c.int8_fc2_rows ? 3 : 4) : 0;
     CHECK((staged == 0) == (info.wstage_bytes == 0));
-    CHECK(st.dispatches == (c.int8_fc2_rows ? 9 : 8) + st.split_gemms + staged);
-    CHECK(st.split_gemms >= 0 && st.split_gemms <= 3);
+    CHECK(st.dispatches == (c.int8_fc2_rows ? 9 : 8) + st.tail_splits + staged);
+    CHECK(st.tail_splits >= 0 && st.tail_splits <= 4);
     CHECK(h3k_stub_launches() - before == st.dispatches);
     CHECK(st.workspace_bytes == ws_bytes);
   }

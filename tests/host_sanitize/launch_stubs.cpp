@@ -126,14 +126,31 @@ hipError_t launch_linear(const LinearArgs& a, hipStream_t, int* kernels) {
   return hipSuccess;
 }
 
-hipError_t launch_attention(const AttentionArgs& a, hipStream_t) {
+hipError_t launch_attention(const AttentionArgs& a, hipStream_t, int* kernels) {
   ++g_launches;
+  if (kernels) *kernels = 1;
   const int64_t e = es(a.dt), D = (int64_t)a.n_heads * a.head_dim;
   need(a.ldvt >= (a.n + 7) / 8 * 8, "V^T pitch covers the 8-padded keys");
   touch_read(a.q, a.n, D, a.ldq, e);
   touch_read(a.k, a.n, D, a.ldk, e);
   touch_read(a.vt, D, a.n, a.ldvt, e);
   touch_write(a.o, a.n, D, a.ldo, e);
+  // the key split as the bf16 launcher takes it on 256 compute units: the
+  // partial results it writes must lie inside the scratch it was given
+  if (a.part && a.dt == kBF16 && a.head_dim == 128 && a.n > 0) {
+    int S = 0;
+    const int nw = attn_shape128(a.n, a.n_heads, 256, a.part_bytes, &S);
+    const int64_t slots = 256 * (nw == 4 ? 2 : 1);
+    const int64_t blocks = (a.n + nw * 32 - 1) / (nw * 32) * a.n_heads;
+    if (S) {
+      const int64_t used = (blocks % slots) * S * attn_unit_bytes(nw);
+      need(used <= a.part_bytes, "key-split partial results inside their scratch");
+      touch_write(a.part, 1, used, used, 1);
+      touch_read(a.part, 1, used, used, 1);
+      ++g_launches;
+      if (kernels) *kernels = 2;
+    }
+  }
   return hipSuccess;
 }
 

@@ -17,7 +17,7 @@ import pytest
 
 import oracle
 import seeded_inputs as si
-from gpu_util import (config_for, dev, device_cus, expected_split_gemms, flush, has_gpu, sample_rows, to_np,
+from gpu_util import (config_for, dev, device_cus, expected_tail_splits, flush, has_gpu, sample_rows, to_np,
                       upload_block)
 from helpers import record, rel_l2
 
@@ -47,6 +47,12 @@ def _run_block(R, shape, dw, xd, cd, alias=True, poison=True, stats=None, int8_f
     return out
 
 
+def _want(shape, n_tokens, part_bytes, cus=None):
+    """Kernels of a bf16 block of `shape` at n_tokens that split their last wave."""
+    return expected_tail_splits(n_tokens, shape.hidden, shape.mlp_hidden, part_bytes,
+                                device_cus() if cus is None else cus, shape.n_heads, shape.head_dim)
+
+
 def _block_case(shape, bias_std=0.0):
     hx, hc = si.gen_activation(shape)
     hw = si.gen_block_weights(shape, 0, bias_std=bias_std)
@@ -63,7 +69,7 @@ def test_block_c0_fp32_full(R):
     out = _run_block(R, shape, dw, dev(hx), dev(hc), stats=st)
     ref = oracle.block_forward(hx.values, hc.values, ow, shape.n_heads)
     got = to_np(out)
-    assert st.dispatches == 8 and st.split_gemms == 0
+    assert st.dispatches == 8 and st.tail_splits == 0
     assert record("block c0 fp32 (512x256)", rel_l2(got, ref), 1e-4) < 1e-4
 
 
@@ -80,20 +86,24 @@ def test_block_ragged_bf16_full(R, n):
 
 
 def test_block_c1_full(R):
-    """The 512x512x22-frame block, every element, with the k-split of the GEMM
-    tails (on 256 CUs the out-projection and MLP-down leave 32 tiles in their
-    last wave and split them 8 ways) and without it (H3K_DISABLE_TAIL_SPLIT=1):
-    both against the oracle, and close to each other (only the fp32 summation
-    order of the tail tiles differs)."""
-    _split_on_off(R, si.C1, "block c1 (6144x3072)", 2)
+    """The 512x512x22-frame block, every element, with the split tails (on 256
+    CUs the out-projection and MLP-down leave 32 tiles in their last wave and
+    split them 8 ways along k; the attention then takes 576 eight-wave
+    workgroups, 64 in the last round of 256, and splits those 4 ways along the
+    keys) and
+    without them (H3K_DISABLE_TAIL_SPLIT=1): both against the oracle, the split
+    no further from it, and the two within the rounding of P (see below)."""
+    _split_on_off(R, si.C1, "block c1 (6144x3072)", 3)
 
 
 def test_block_ragged_tail_split(R):
-    """The k-split with ragged tiles in the split tail: 6000 tokens (the last
-    m-tile holds 112 rows) and D = 2944 (the last n-tile 128 columns); out and
-    down leave 32 of 288 tiles in the last wave and split them 8 ways."""
+    """The split tails with ragged edges: 6000 tokens (the last m-tile holds 112
+    rows, the last 128-query workgroup 112 queries, the last key tile 16 keys)
+    and D = 2944 (the last n-tile 128 columns); out and down leave 32 of 288
+    tiles in the last wave and split them 8 ways, the attention 40 of its 552
+    eight-wave workgroups 6 ways along the keys."""
     shape = si.custom_shape("ragged_split", 990, 6000, 23, 128, 11776, "bf16")
-    _split_on_off(R, shape, "block ragged 6000x2944", 2)
+    _split_on_off(R, shape, "block ragged 6000x2944", 3)
 
 
 def _split_on_off(R, shape, label, want_256):
@@ -114,15 +124,23 @@ def _split_on_off(R, shape, label, want_256):
             outs[split] = to_np(_run_block(R, shape, dw, dev(hx), dev(hc), stats=st))
         finally:
             os.environ.pop("H3K_DISABLE_TAIL_SPLIT", None)
-        want = expected_split_gemms(shape.n_tokens, shape.hidden, shape.mlp_hidden, part, device_cus()) if split else 0
-        assert st.split_gemms == want and st.dispatches == 8 + want
+        want = _want(shape, shape.n_tokens, part) if split else 0
+        assert st.tail_splits == want and st.dispatches == 8 + want
         err = rel_l2(outs[split], ref)
-        flush(f"  split={split}: {st.split_gemms} GEMMs split, rel_l2 = {err:.3e}")
+        flush(f"  split={split}: {st.tail_splits} kernels split, rel_l2 = {err:.3e}")
         record(f"{label}{'' if split else ', tail split off'}", err, TOL)
         assert err < TOL
     if device_cus() == 256:
-        assert expected_split_gemms(shape.n_tokens, shape.hidden, shape.mlp_hidden, part, 256) == want_256
-    assert rel_l2(outs[True], outs[False]) < 2e-3
+        assert _want(shape, shape.n_tokens, part, 256) == want_256
+    # The split moves the result no further from the oracle.  The two runs are
+    # not bit-equal: the GEMM tails sum in another fp32 order, and each key
+    # range of a split attention workgroup rounds its probabilities to bf16
+    # against its own running reference, so the outputs carry independent bf16
+    # roundings of P (about 3e-3 apart after a full block at 6144 tokens,
+    # each 4.4e-3 from the oracle).
+    errs = {k: rel_l2(v, ref) for k, v in outs.items()}
+    assert errs[True] <= 1.05 * errs[False]
+    assert rel_l2(outs[True], outs[False]) < 5e-3
 
 
 @pytest.fixture(scope="module")
@@ -173,7 +191,7 @@ def test_block_c4_int8_sampled_rows(R):
     from video_diffusion_transformer_adaln_amd import binding as B
     st = B.DitStats()
     got_t = _run_block(R, shape, dw, dev(hx), dev(hc), stats=st)
-    assert st.dispatches == 8 + 4 and st.split_gemms == 0   # four weight-widening passes; no tail split
+    assert st.dispatches == 8 + 4 and st.tail_splits == 0   # four weight-widening passes; no tail split
     got = to_np(got_t)
     rows = sample_rows(shape.n_tokens)
     ref = oracle.block_forward(hx.values, hc.values, ow, shape.n_heads, rows=rows)
@@ -199,7 +217,7 @@ def _assert_staging_identical(R, shape, dw, xd, cd, staged, **kw):
         ring = _run_block(R, shape, dw, xd, cd, stats=st, **kw)
     finally:
         os.environ.pop("H3K_DISABLE_WEIGHT_STAGING", None)
-    assert st.split_gemms == 0
+    assert st.tail_splits == 0
     assert torch.equal(ring.view(torch.int16), staged.view(torch.int16))
 
 
@@ -217,7 +235,7 @@ def test_block_int8_fc2_rows(R, case):
     xd, cd = dev(hx), dev(hc)
     st = B.DitStats()
     got_t = _run_block(R, shape, dw, xd, cd, stats=st, int8_fc2_rows=True)
-    assert st.dispatches == 9 + 3 and st.split_gemms == 0   # QKV, out and up widen their weights first
+    assert st.dispatches == 9 + 3 and st.tail_splits == 0   # QKV, out and up widen their weights first
     _assert_staging_identical(R, shape, dw, xd, cd, got_t, int8_fc2_rows=True)
     got = to_np(got_t)
     rows = sample_rows(shape.n_tokens) if case == "c4" else np.arange(shape.n_tokens)
@@ -247,7 +265,7 @@ def test_block_int8_mlp_groups(R, case, group):
     xd, cd = dev(hx), dev(hc)
     st = B.DitStats()
     got_t = _run_block(R, shape, dw, xd, cd, stats=st, int8_mlp_group=group)
-    assert st.dispatches == 8 + 4 and st.split_gemms == 0
+    assert st.dispatches == 8 + 4 and st.tail_splits == 0
     _assert_staging_identical(R, shape, dw, xd, cd, got_t, int8_mlp_group=group)
     got = to_np(got_t)
     rows = sample_rows(shape.n_tokens) if case == "c4" else np.arange(shape.n_tokens)
@@ -318,9 +336,8 @@ def test_stack50_reduced_width_vs_oracle(R):
     stack.forward(xd, cd, out, stats=st)
     torch.cuda.synchronize()
     part = B.h3k_dit_plan(config_for(shape)).part_bytes
-    assert st.split_gemms == 50 * expected_split_gemms(shape.n_tokens, shape.hidden, shape.mlp_hidden, part,
-                                                       device_cus())
-    assert st.dispatches == 8 * 50 + st.split_gemms
+    assert st.tail_splits == 50 * _want(shape, shape.n_tokens, part)
+    assert st.dispatches == 8 * 50 + st.tail_splits
     ref = oracle.stack_forward(hx.values, hc.values, [u[1] for u in up], shape.n_heads)
     err = rel_l2(to_np(out), ref)
     flush(f"  rel_l2 after 50 blocks = {err:.3e}")
@@ -359,12 +376,10 @@ def test_stack_token_reduction(R, n_blocks, rng_):
         torch.cuda.synchronize()
         part = B.h3k_dit_plan(cfg).part_bytes
         n_red = rng_[1] - rng_[0]
-        want = ((n_blocks - n_red) * expected_split_gemms(shape.n_tokens, shape.hidden, shape.mlp_hidden, part,
-                                                          device_cus())
-                + n_red * expected_split_gemms(shape.n_tokens // 2, shape.hidden, shape.mlp_hidden, part,
-                                               device_cus()))
-        assert st.split_gemms == want
-        assert st.dispatches == 8 * n_blocks + 2 + st.split_gemms
+        want = ((n_blocks - n_red) * _want(shape, shape.n_tokens, part)
+                + n_red * _want(shape, shape.n_tokens // 2, part))
+        assert st.tail_splits == want
+        assert st.dispatches == 8 * n_blocks + 2 + st.tail_splits
         outs.append(out)
     assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
     got = to_np(outs[0])
@@ -396,10 +411,10 @@ def test_stack50_reduced_width_token_reduction(R):
     stack.forward(xd, cd, out, stats=st)
     torch.cuda.synchronize()
     part = B.h3k_dit_plan(cfg).part_bytes
-    want = (24 * expected_split_gemms(shape.n_tokens, shape.hidden, shape.mlp_hidden, part, device_cus())
-            + 26 * expected_split_gemms(shape.n_tokens // 2, shape.hidden, shape.mlp_hidden, part, device_cus()))
-    assert st.split_gemms == want
-    assert st.dispatches == 8 * 50 + 2 + st.split_gemms
+    want = (24 * _want(shape, shape.n_tokens, part)
+            + 26 * _want(shape, shape.n_tokens // 2, part))
+    assert st.tail_splits == want
+    assert st.dispatches == 8 * 50 + 2 + st.tail_splits
     ref = oracle.stack_forward(hx.values, hc.values, [u[1] for u in up], shape.n_heads, token_reduction=(12, 38))
     err = rel_l2(to_np(out), ref)
     flush(f"  rel_l2 after 50 blocks = {err:.3e}")

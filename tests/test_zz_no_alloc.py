@@ -43,7 +43,7 @@ def test_noalloc_matches_workspace_entry_point():
         ref = torch.full_like(x, float("nan"))
         B.h3k_dit_block_forward(cfg, w, x, c, ref, ws)
         torch.cuda.synchronize()
-        assert st.dispatches == 8 + st.split_gemms and st.workspace_bytes == need
+        assert st.dispatches == 8 + st.tail_splits and st.workspace_bytes == need
         assert torch.isfinite(got.float()).all()
         bits = torch.int32 if got.dtype == torch.float32 else torch.int16
         assert torch.equal(got.view(bits), ref.view(bits))

@@ -48,7 +48,7 @@ class DitBlockWeights(ctypes.Structure):
 
 class DitStats(ctypes.Structure):
     _fields_ = [("workspace_bytes", c_uint64), ("peak_live_bytes", c_uint64), ("unaliased_bytes", c_uint64),
-                ("dispatches", c_int32), ("alias_activations", c_int32), ("split_gemms", c_int32),
+                ("dispatches", c_int32), ("alias_activations", c_int32), ("tail_splits", c_int32),
                 ("_reserved", c_int32), ("profiler", c_void_p)]
 
 

@@ -70,6 +70,11 @@ struct AttnParams {
   bf16* o; int64_t ldo;
   int n, n_heads, q_tiles;
   float scale_log2;   // log2(e) / sqrt(d)
+  // Key split: workgroups full_blocks .. of the order below are each split
+  // into kv_split key ranges whose unnormalised results go to part
+  // (attention_combine_kernel finishes them).
+  int full_blocks, kv_split;
+  float* part;
 };
 
 // a tile is redone when a query's probability sum over the tile's 32 keys exceeds this
@@ -118,11 +123,30 @@ void attention_bf16_kernel(AttnParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, x16 = lane & 15;
   const int nblk = p.q_tiles * p.n_heads;
-  const int lin = xcd_remap(blockIdx.x, nblk);
+  // Whole workgroups first, in the XCD-aware order; with a key split, block
+  // full_blocks + s * tail + j takes key tiles [s TA / S, (s + 1) TA / S) of
+  // tail workgroup j (TA tiles in all, S = kv_split) and stores partial unit
+  // j S + s.  The workgroup then sees the keys of its range as a sequence of
+  // NK keys (K and V^T addressed from the range's first key).
+  const int TA = (p.n + KT - 1) / KT;
+  int lin, unit = -1, key_first = 0, key_end = p.n;
+  if ((int)blockIdx.x < p.full_blocks) {
+    lin = xcd_remap(blockIdx.x, p.full_blocks);
+  } else {
+    const int tail = nblk - p.full_blocks, qb_ = (int)blockIdx.x - p.full_blocks;
+    const int j = qb_ % tail, sp = qb_ / tail;
+    lin = p.full_blocks + j;
+    key_first = sp * TA / p.kv_split * KT;
+    key_end = min(p.n, (sp + 1) * TA / p.kv_split * KT);
+    unit = j * p.kv_split + sp;
+  }
   const int head = lin / p.q_tiles;
   const int qtile = lin - head * p.q_tiles;
-  const int N = p.n;
-  const int T = (N + KT - 1) / KT;
+  const int N = p.n;                           // queries
+  const int NK = key_end - key_first;          // keys of this workgroup
+  const int T = (NK + KT - 1) / KT;
+  const bf16* const kp = p.k + (int64_t)key_first * p.ldk;
+  const bf16* const vtp = p.vt + key_first;
   constexpr int QW = 16 * QB;                  // queries per wave
   const int q0 = qtile * (NW * QW) + wave * QW;
   const float sc = p.scale_log2;
@@ -150,7 +174,7 @@ void attention_bf16_kernel(AttnParams p) {
   // the load counts stay uniform.
   constexpr int CPR = KROW / 16;               // chunks per K row
   constexpr int RPI = 64 / CPR;                // rows per load instruction
-  const __amdgpu_buffer_rsrc_t rk = rsrc(p.k, (uint32_t)((uint64_t)N * p.ldk * 2));
+  const __amdgpu_buffer_rsrc_t rk = rsrc(kp, (uint32_t)((uint64_t)NK * p.ldk * 2));
   uint32_t kdma_off[LPW];
 #pragma unroll
   for (int j = 0; j < LPW; ++j) {
@@ -170,20 +194,20 @@ void attention_bf16_kernel(AttnParams p) {
   // per lane; piece j: plane lane/32, row (wave + NW j)*16 + (lane%32)/2,
   // half lane&1 (keys 16 plane + 8 half .. +8)
   const int st_pl = lane >> 5, st_h = lane & 1;
-  const __amdgpu_buffer_rsrc_t rvt = rsrc(p.vt, (uint32_t)((uint64_t)p.n_heads * HD * p.ldvt * 2));
+  const __amdgpu_buffer_rsrc_t rvt = rsrc(vtp, (uint32_t)(((uint64_t)p.n_heads * HD * p.ldvt - key_first) * 2));
   auto st_row = [&](int j) { return (wave + NW * j) * 16 + ((lane & 31) >> 1); };
-  auto vload_masked = [&](int t, u32x4 (&v)[LPW]) {   // zero for keys >= N
+  auto vload_masked = [&](int t, u32x4 (&v)[LPW]) {   // zero for keys >= NK
     const int key0 = t * KT + st_pl * 16 + st_h * 8;
 #pragma unroll
     for (int j = 0; j < LPW; ++j) {
       v[j] = u32x4{0, 0, 0, 0};
-      if (key0 < N) {
+      if (key0 < NK) {
         const uint32_t off = ((uint32_t)(head * HD + st_row(j)) * (uint32_t)p.ldvt + st_pl * 16 + st_h * 8) * 2u;
         v[j] = bload16(rvt, off, (uint32_t)t * (KT * 2));
         uint16_t* e = reinterpret_cast<uint16_t*>(&v[j]);
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-          if (key0 + i >= N) e[i] = 0;
+          if (key0 + i >= NK) e[i] = 0;
       }
     }
   };
@@ -285,13 +309,13 @@ void attention_bf16_kernel(AttnParams p) {
       for (int qb = 0; qb < QB; ++qb) O[db][qb] = mfma16(a, pb(pp[qb]), O[db][qb]);
     }
   };
-  // keys >= N of tile t
+  // keys >= NK of tile t
   auto mask_tail = [&](f32x4 (&s)[2][QB], int t) __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        if (t * KT + 8 * g + 4 * kb + j >= N) {
+        if (t * KT + 8 * g + 4 * kb + j >= NK) {
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) s[kb][qb][j] = -INFINITY;
         }
@@ -500,7 +524,7 @@ void attention_bf16_kernel(AttnParams p) {
   using Full = std::integral_constant<bool, false>;
   using Tail = std::integral_constant<bool, true>;
   int t0 = 1;
-  for (; (t0 + 5) * KT <= N; t0 += 4) {        // V^T tiles up to t0+4 are full
+  for (; (t0 + 5) * KT <= NK; t0 += 4) {       // V^T tiles up to t0+4 are full
     pass(t0, C1{}, Full{});
     pass(t0 + 2, C3{}, Full{});
   }
@@ -515,6 +539,24 @@ void attention_bf16_kernel(AttnParams p) {
     else pv(vl, P[0]);
   }
   wait_vmcnt<0>();                             // no load left in flight at exit
+
+  if (unit >= 0) {   // same for the whole workgroup
+    // a key range's partial result: O unnormalised (relative to 2^m), then
+    // the reference m and the row sum l, for the workgroup's NW QW queries
+    constexpr int QWG = NW * QW;
+    float* const po = p.part + (int64_t)unit * (QWG * (HD + 2));
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int ql = wave * QW + 16 * qb + x16;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4*>(po + ql * HD + 16 * db + 4 * g) = O[db][qb];
+      if (g == 0) {
+        po[QWG * HD + ql] = m_ref[qb];
+        po[QWG * HD + QWG + ql] = l_run[qb];
+      }
+    }
+    return;
+  }
 
   // ---- normalise and store (every lane holds its query's full row sum)
 #pragma unroll
@@ -603,8 +645,58 @@ __global__ __launch_bounds__(64) void attention_f32_kernel(AttnParamsF p) {
 }
 
 // ---------------------------------------------------------------------------
+// Second kernel of a key split: each thread merges the S partial results of 4
+// dims of one query, the usual way: with M the largest reference, O = sum_s
+// 2^(m_s - M) O_s and l = sum_s 2^(m_s - M) l_s, out = O / l (as in the main
+// kernel, times the reciprocal), one bf16 rounding.
+template <int HD, int QWG>
+__global__ __launch_bounds__(256) void attention_combine_kernel(AttnParams p) {
+  constexpr int C4 = HD / 4, UF = QWG * (HD + 2);
+  const int tail = p.q_tiles * p.n_heads - p.full_blocks, S = p.kv_split;
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  const int j = idx / (QWG * C4);
+  if (j >= tail) return;
+  const int r = idx - j * (QWG * C4), ql = r / C4, c = r - ql * C4;
+  const int lin = p.full_blocks + j, head = lin / p.q_tiles, qtile = lin - head * p.q_tiles;
+  const int q = qtile * QWG + ql;
+  if (q >= p.n) return;
+  const float* const base = p.part + (int64_t)j * S * UF;
+  float M = -INFINITY;
+  for (int sp = 0; sp < S; ++sp) M = fmaxf(M, base[sp * UF + QWG * HD + ql]);
+  float l = 0.f;
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+  for (int sp = 0; sp < S; ++sp) {
+    const float* u = base + sp * UF;
+    const float w = __builtin_amdgcn_exp2f(u[QWG * HD + ql] - M);
+    l += w * u[QWG * HD + QWG + ql];
+    o += w * *reinterpret_cast<const f32x4*>(u + ql * HD + 4 * c);
+  }
+  const float inv = 1.0f / l;
+  u32x2 out;
+  bf16* oe = reinterpret_cast<bf16*>(&out);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) oe[e] = static_cast<bf16>(o[e] * inv);
+  *reinterpret_cast<u32x2*>(p.o + (int64_t)q * p.ldo + head * HD + 4 * c) = out;
+}
+
+// Compute units of the current device (one query per device and thread).
+static int attn_device_cus() {
+  constexpr int kMaxDev = 64;
+  thread_local int cached[kMaxDev] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 0;
+  if (!cached[dev]) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cached[dev] = v;
+  }
+  return cached[dev];
+}
+
+// ---------------------------------------------------------------------------
+// S: key split of the last round (0: none; head_dim 128 only)
 template <int HD, int NW, int QB, bool QPRE>
-static void launch_bf16_attn_nw(const AttentionArgs& a, hipStream_t stream) {
+static void launch_bf16_attn_nw(const AttentionArgs& a, hipStream_t stream, int* kernels, int S, int cus) {
   AttnParams p;
   p.q = (const bf16*)a.q; p.ldq = a.ldq;
   p.k = (const bf16*)a.k; p.ldk = a.ldk;
@@ -613,23 +705,46 @@ static void launch_bf16_attn_nw(const AttentionArgs& a, hipStream_t stream) {
   p.n = a.n; p.n_heads = a.n_heads;
   p.q_tiles = (a.n + NW * 16 * QB - 1) / (NW * 16 * QB);
   p.scale_log2 = 1.4426950408889634f / sqrtf((float)HD);
-  attention_bf16_kernel<HD, NW, QB, QPRE><<<dim3(p.q_tiles * p.n_heads), dim3(NW * 64), 0, stream>>>(p);
+  const int nblk = p.q_tiles * p.n_heads;
+  p.full_blocks = nblk;
+  p.kv_split = 0;
+  p.part = nullptr;
+  if (S) {
+    // one 8-wave workgroup or two 4-wave ones per CU (256 VGPRs per wave, 64 KiB of LDS each)
+    const int64_t slots = (int64_t)cus * (NW == 4 ? 2 : 1);
+    p.full_blocks = nblk - (int)(nblk % slots);
+    p.kv_split = S;
+    p.part = a.part;
+  }
+  const int grid = p.full_blocks + (nblk - p.full_blocks) * S;
+  attention_bf16_kernel<HD, NW, QB, QPRE><<<dim3(grid), dim3(NW * 64), 0, stream>>>(p);
+  *kernels = 1;
+  if (S) {
+    constexpr int QWG = NW * 16 * QB;
+    const int64_t threads = (int64_t)(nblk - p.full_blocks) * QWG * (HD / 4);
+    attention_combine_kernel<HD, QWG><<<dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream>>>(p);
+    *kernels = 2;
+  }
 }
 // head_dim 128: 8-wave workgroups (256 queries), or 4-wave ones (128 queries,
 // two per CU) for short sequences with few workgroups, where the last round
-// of workgroups is then spread over twice as many CUs.  Measured on MI355X
-// (same bits): 6144 tokens x 24 heads 452 -> 417 us, 2000 x 40 108 -> 91 us;
-// but 22680 tokens x 5 heads (as few workgroups, a long key loop) 1055 ->
-// 1177 us, so the long sequences keep 8 waves.
+// of workgroups is then spread over twice as many CUs, unless the caller's
+// scratch lets 8-wave workgroups split their last round (attn_shape128).
+// Measured on MI355X (same bits): 6144 tokens x 24 heads 452 -> 417 us, 2000
+// x 40 108 -> 91 us; but 22680 tokens x 5 heads (as few workgroups, a long
+// key loop) 1055 -> 1177 us, so the long sequences keep 8 waves.
 template <int HD, bool QPRE>
-static void launch_bf16_attn(const AttentionArgs& a, hipStream_t stream) {
+static void launch_bf16_attn(const AttentionArgs& a, hipStream_t stream, int* kernels) {
   if constexpr (HD == 128) {
-    const int64_t wg8 = (int64_t)((a.n + 16 * kAttnWaves128 * kAttnQBlocks128 - 1) /
-                                  (16 * kAttnWaves128 * kAttnQBlocks128)) * a.n_heads;
-    if (wg8 < 4 * 256 && a.n <= 8192) launch_bf16_attn_nw<128, 4, kAttnQBlocks128, QPRE>(a, stream);
-    else launch_bf16_attn_nw<128, kAttnWaves128, kAttnQBlocks128, QPRE>(a, stream);
+    static_assert(kAttnWaves128 == 8 && kAttnQBlocks128 == 2, "attn_shape128 assumes 8 waves of two blocks");
+    const int cus = a.part ? attn_device_cus() : 0;
+    int S = 0;
+    if (attn_shape128(a.n, a.n_heads, cus, a.part ? a.part_bytes : 0, &S) == 4)
+      launch_bf16_attn_nw<128, 4, kAttnQBlocks128, QPRE>(a, stream, kernels, S, cus);
+    else
+      launch_bf16_attn_nw<128, kAttnWaves128, kAttnQBlocks128, QPRE>(a, stream, kernels, S, cus);
   } else {
-    launch_bf16_attn_nw<HD, 4, 2, QPRE>(a, stream);
+    launch_bf16_attn_nw<HD, 4, 2, QPRE>(a, stream, kernels, 0, 0);
   }
 }
 
@@ -645,18 +760,22 @@ static void launch_f32_attn(const AttentionArgs& a, hipStream_t stream) {
   attention_f32_kernel<HD><<<dim3((a.n + 63) / 64, a.n_heads), dim3(64), 0, stream>>>(p);
 }
 
-hipError_t launch_attention(const AttentionArgs& a, hipStream_t stream) {
+hipError_t launch_attention(const AttentionArgs& a, hipStream_t stream, int* kernels) {
+  int dummy = 0;
+  if (!kernels) kernels = &dummy;
+  *kernels = 0;
   if (a.n == 0) return hipSuccess;
+  *kernels = 1;
   if (a.dt == kF32) {
     if (a.head_dim == 64) launch_f32_attn<64>(a, stream);
     else launch_f32_attn<128>(a, stream);
   } else {
     if (a.q_prescaled) {
-      if (a.head_dim == 64) launch_bf16_attn<64, true>(a, stream);
-      else launch_bf16_attn<128, true>(a, stream);
+      if (a.head_dim == 64) launch_bf16_attn<64, true>(a, stream, kernels);
+      else launch_bf16_attn<128, true>(a, stream, kernels);
     } else {
-      if (a.head_dim == 64) launch_bf16_attn<64, false>(a, stream);
-      else launch_bf16_attn<128, false>(a, stream);
+      if (a.head_dim == 64) launch_bf16_attn<64, false>(a, stream, kernels);
+      else launch_bf16_attn<128, false>(a, stream, kernels);
     }
   }
   return hipGetLastError();

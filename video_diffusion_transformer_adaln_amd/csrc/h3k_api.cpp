@@ -169,32 +169,45 @@ uint64_t reduction_bytes(const h3k_dit_config* c) {
   return align_up((uint64_t)(c->n_tokens / 2) * c->hidden * esize(c->act_dtype), kAlign);
 }
 
-// Scratch for the fp32 partial tiles of k-split tail tiles: the bf16 x bf16
-// out-projection, MLP up and MLP down GEMMs of one block (the launcher's
-// rule, tail_split_ways, at the 256 compute units of MI355X; on another CU
-// count the launcher caps its split ways by this size).  With token
-// reduction the reduced blocks use the same region, so it covers both token
-// counts.  Placed after the block's tensors (before the merged stream).
+// Scratch for the partial results of split tails, by the launchers' rules at
+// the 256 compute units of MI355X (on another CU count the launchers cap
+// their split ways by this size): the fp32 partial tiles of k-split tail
+// tiles of the bf16 out-projection, MLP up and MLP down GEMMs
+// (tail_split_ways), and the partial results of the key-split last round of
+// the bf16 attention (attn_split_ways).  The steps never overlap, so one
+// region serves all.  With token reduction the reduced blocks use the same
+// region, so it covers both token counts.  Placed after the block's tensors
+// (before the merged stream).
 constexpr int64_t kPlanCus = 256;
-uint64_t split_bytes_for(int64_t N, int64_t D, int64_t F) {
-  const int64_t tm = (N + 255) / 256;
-  const int64_t nk[3][2] = {{D, D}, {F, D}, {D, F}};   // (n, k) of out, up, down
+uint64_t split_bytes_for(const h3k_dit_config* c, int64_t N) {
+  const int64_t D = c->hidden, F = c->mlp_hidden, H = c->n_heads;
   int64_t need = 0;
-  for (const auto& g : nk) {
-    const int64_t tiles = tm * ((g[0] + 255) / 256);
-    const int S = tail_split_ways(tiles, g[1] / 64, kPlanCus, kPlanCus);
-    if (S) need = std::max(need, (tiles % kPlanCus) * S * kPartTileBytes);
+  if (c->weight_dtype == H3K_BF16 || c->weight_dtype == H3K_INT8) {   // bf16 or staged int8 weights
+    const int64_t tm = (N + 255) / 256;
+    const int64_t nk[3][2] = {{D, D}, {F, D}, {D, F}};   // (n, k) of out, up, down
+    for (int i = 0; i < 3; ++i) {
+      if (i == 2 && c->int8_fc2_rows) continue;            // int8 x int8: not split
+      const int64_t tiles = tm * ((nk[i][0] + 255) / 256);
+      const int S = tail_split_ways(tiles, nk[i][1] / 64, kPlanCus, kPlanCus);
+      if (S) need = std::max(need, (tiles % kPlanCus) * S * kPartTileBytes);
+    }
+  }
+  if (c->head_dim == 128) {
+    int S = 0;
+    const int nw = attn_shape128(N, H, kPlanCus, INT64_MAX / 4, &S);
+    const int64_t slots = kPlanCus * (nw == 4 ? 2 : 1);
+    const int64_t blocks = (N + nw * 32 - 1) / (nw * 32) * H;
+    if (S) need = std::max(need, (blocks % slots) * S * attn_unit_bytes(nw));
   }
   return (uint64_t)need;
 }
 uint64_t split_bytes(const h3k_dit_config* c) {
-  if (c->act_dtype != H3K_BF16 || c->weight_dtype != H3K_BF16) return 0;
-  uint64_t b = split_bytes_for(c->n_tokens, c->hidden, c->mlp_hidden);
-  if (c->token_reduction_last > c->token_reduction_first)
-    b = std::max(b, split_bytes_for(c->n_tokens / 2, c->hidden, c->mlp_hidden));
-  return b;
+  if (c->act_dtype != H3K_BF16) return 0;
+  uint64_t b = split_bytes_for(c, c->n_tokens);
+  if (c->token_reduction_last > c->token_reduction_first) b = std::max(b, split_bytes_for(c, c->n_tokens / 2));
+  return align_up(b, kAlign);
 }
-constexpr int kSplitSteps[3] = {4, 6, 8};   // kernel steps of the out, up and down GEMMs
+constexpr int kSplitSteps[4] = {3, 4, 6, 8};   // attention, out, up and down
 
 // Staging buffer of the int8-weight projections (bf16 activations): each
 // int8 weight matrix is widened to bf16 there right before its GEMM, which
@@ -389,8 +402,9 @@ h3k_status validate_forward(const h3k_dit_config* c, const h3k_dit_block_weights
 // Enqueue the eight kernels of one block (nine with int8_fc2_rows).  x may
 // equal out (stack in place: x is last read by the out-projection, out is
 // first written by MLP down).
-// `part`/`part_bytes`: the k-split scratch (see split_bytes); null / 0: no
-// split.  `kernels` counts the kernels enqueued, `splits` the GEMMs split.
+// `part`/`part_bytes`: the scratch of split tails (see split_bytes); null / 0:
+// no split.  `kernels` counts the kernels enqueued, `splits` the kernels
+// (GEMMs, attention) whose last wave was split.
 h3k_status run_block(const h3k_dit_config* c, const h3k_dit_plan_info* P, const h3k_dit_block_weights* w,
                      const void* x, const void* cond, void* out, char* ws, float* part, uint64_t part_bytes,
                      void* wstage, uint64_t wstage_bytes, hipStream_t s, Recorder& rec, int& kernels, int& splits) {
@@ -450,9 +464,15 @@ h3k_status run_block(const h3k_dit_config* c, const h3k_dit_plan_info* P, const 
   A.dt = act; A.n = N; A.n_heads = c->n_heads; A.head_dim = c->head_dim;
   A.q = qkv; A.ldq = 2 * D; A.k = qkv + D * eb; A.ldk = 2 * D; A.vt = vt; A.ldvt = P->vt_pitch;
   A.o = o; A.ldo = D; A.q_prescaled = q_pre;
-  H3K_TRY(launched(launch_attention(A, s), "attention"));
+  A.part = part;
+  A.part_bytes = (int64_t)part_bytes;
+  {
+    int nk = 0;
+    H3K_TRY(launched(launch_attention(A, s, &nk), "attention"));
+    kernels += nk;
+    splits += nk - 1;
+  }
   rec.done(H3K_K_ATTENTION);
-  ++kernels;
 
   L = LinearArgs{};
   L.act = act; L.weight = wt;
@@ -555,7 +575,7 @@ h3k_status forward(const h3k_dit_config* cfg, const h3k_dit_block_weights* block
     stats->peak_live_bytes = plan.peak_live_bytes;
     stats->unaliased_bytes = plan.unaliased_bytes;
     stats->dispatches = kernels;
-    stats->split_gemms = splits;
+    stats->tail_splits = splits;
     stats->alias_activations = plan.alias_activations;
   }
   return H3K_OK;

@@ -78,8 +78,60 @@ struct AttentionArgs {
   const void* vt; int64_t ldvt;
   void* o; int64_t ldo;
   bool q_prescaled;       // bf16: q already multiplied by log2(e) / sqrt(head_dim)
+  float* part;            // bf16, head_dim 128: scratch for key-split tail blocks
+  int64_t part_bytes;     // (unnormalised partial results); null / 0: no split
 };
-hipError_t launch_attention(const AttentionArgs& a, hipStream_t stream);
+// *kernels (if not null): kernels enqueued (two when the tail blocks are split along the keys)
+hipError_t launch_attention(const AttentionArgs& a, hipStream_t stream, int* kernels = nullptr);
+
+// Workgroup shape of the bf16 attention for head_dim 128: 4 waves (128
+// queries, two workgroups per CU) for sequences of at most 8192 tokens with
+// fewer than 1024 workgroups of 8 waves, else 8 waves (256 queries, one per CU).
+inline int attn_waves128(int64_t n, int64_t heads) {
+  const int64_t wg8 = (n + 255) / 256 * heads;
+  return (wg8 < 4 * 256 && n <= 8192) ? 4 : 8;
+}
+// Bytes of one key-split partial result: the workgroup's queries' unnormalised
+// O (fp32, head_dim 128) plus their running reference and row sum.
+inline int64_t attn_unit_bytes(int nw) { return (int64_t)nw * 32 * (128 + 2) * 4; }
+// Key split of the attention's last round (bf16, head_dim 128): `blocks`
+// workgroups, `slots` resident at once, T key tiles of 32.  When the last
+// round would leave at least half the slots idle, each of its workgroups is
+// split into S key ranges (S <= 8, at least 8 tiles each, tail * S <=
+// min(slots, cap_units)) whose partial results a second kernel combines; the
+// split must shed at least 2048 keys per workgroup, (1 - 1/S) 32 T >= 2048.
+// Returns S, or 0 for no split.
+inline int attn_split_ways(int64_t blocks, int64_t T, int64_t slots, int64_t cap_units) {
+  if (blocks < 1 || slots < 1) return 0;
+  const int64_t tail = blocks % slots;
+  if (tail == 0 || 2 * tail > slots) return 0;
+  int64_t s = T / 8 < 8 ? T / 8 : 8;
+  const int64_t room = (cap_units < slots ? cap_units : slots) / tail;
+  if (room < s) s = room;
+  if (s < 2 || (s - 1) * T < 64 * s) return 0;
+  return (int)s;
+}
+// Workgroup shape (returned: 4 or 8 waves) and key split (*split, 0 for none)
+// of the bf16 attention for head_dim 128 on `cus` compute units with
+// `cap_bytes` of scratch for partial results (0: no split).  Where 8-wave
+// workgroups can split their last round, they are taken even for short
+// sequences: measured on MI355X at 6144 tokens x 24 heads, 8 waves with the
+// split 400 us, 4 waves with it 415 us, 4 waves without 430 us.
+inline int attn_shape128(int64_t n, int64_t heads, int64_t cus, int64_t cap_bytes, int* split) {
+  const int64_t T = (n + 31) / 32;
+  int nw = attn_waves128(n, heads), s = 0;
+  if (cus > 0 && cap_bytes > 0) {
+    const int s8 = attn_split_ways((n + 255) / 256 * heads, T, cus, cap_bytes / attn_unit_bytes(8));
+    if (s8) {
+      nw = 8;
+      s = s8;
+    } else if (nw == 4) {
+      s = attn_split_ways((n + 127) / 128 * heads, T, 2 * cus, cap_bytes / attn_unit_bytes(4));
+    }
+  }
+  *split = s;
+  return nw;
+}
 
 // token reduction: xm[m] = (x[2m] + x[2m+1]) / 2 for m < n/2 (D a multiple of 8)
 hipError_t launch_token_merge(DType dt, int64_t n, int64_t D, const void* x, int64_t ldx, void* xm, int64_t ldm,
