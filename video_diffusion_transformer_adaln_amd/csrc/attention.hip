@@ -56,6 +56,11 @@
 //     carries no fence: each wave waits for its own loads first.  Keys
 //     beyond N contribute exactly zero (their K rows load as zero, their
 //     scores are set to -inf and their V^T entries to zero).
+//   * key split of the last round (with a caller scratch, head_dim 128): when
+//     the last round of workgroups would leave at least half the slots idle,
+//     each of its workgroups becomes S workgroups over S key ranges, each
+//     storing its unnormalised O, m and l; attention_combine_kernel merges
+//     them (attn_shape128 / attn_split_ways give the shape and S).
 // fp32 path: one thread per query, K/V tiles in LDS, for the small fp32
 // workload.
 #include "common.hpp"

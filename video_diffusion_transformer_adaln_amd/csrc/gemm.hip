@@ -25,6 +25,14 @@
 //    v_mfma_i32_16x16x64_i8 takes a 16-byte chunk per lane like the bf16
 //    MFMA (int32 accumulators, exact).  Measured on MI355X, 5 % faster than
 //    the 32x32x32 form with the same results.
+//  * int8 weights with a staging buffer (inside the block): the weight is
+//    widened to bf16 by dequant_int8_kernel first, then the bf16 ring kernel
+//    runs with the channel scale in its epilogue (template value SC): the same
+//    bits as the W8A16 ring kernel, at the bf16 kernel's speed.
+//  * tail split (with a caller scratch, bf16 operands, row-major output): when
+//    the last wave of tiles would leave at least half the CUs idle, its tiles
+//    are split along k; gemm_tail_kernel sums the fp32 partial tiles in a
+//    fixed order and applies the epilogue (tail_split_ways gives S).
 //  * fp32 path: a plain LDS-tiled SIMT kernel for the small fp32 workload.
 //
 // Epilogues (fused, fp32 math, one rounding at the store): bias; bias + GELU
