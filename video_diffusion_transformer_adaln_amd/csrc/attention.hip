@@ -684,19 +684,6 @@ __global__ __launch_bounds__(256) void attention_combine_kernel(AttnParams p) {
   *reinterpret_cast<u32x2*>(p.o + (int64_t)q * p.ldo + head * HD + 4 * c) = out;
 }
 
-// Compute units of the current device (one query per device and thread).
-static int attn_device_cus() {
-  constexpr int kMaxDev = 64;
-  thread_local int cached[kMaxDev] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 0;
-  if (!cached[dev]) {
-    int v = 0;
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    cached[dev] = v;
-  }
-  return cached[dev];
-}
 
 // ---------------------------------------------------------------------------
 // S: key split of the last round (0: none; head_dim 128 only)
@@ -742,7 +729,7 @@ template <int HD, bool QPRE>
 static void launch_bf16_attn(const AttentionArgs& a, hipStream_t stream, int* kernels) {
   if constexpr (HD == 128) {
     static_assert(kAttnWaves128 == 8 && kAttnQBlocks128 == 2, "attn_shape128 assumes 8 waves of two blocks");
-    const int cus = a.part ? attn_device_cus() : 0;
+    const int cus = a.part ? device_compute_units() : 0;
     int S = 0;
     if (attn_shape128(a.n, a.n_heads, cus, a.part ? a.part_bytes : 0, &S) == 4)
       launch_bf16_attn_nw<128, 4, kAttnQBlocks128, QPRE>(a, stream, kernels, S, cus);

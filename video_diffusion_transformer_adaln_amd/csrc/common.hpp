@@ -187,4 +187,19 @@ __device__ __forceinline__ float gelu_tanh(float z) {
   return z * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
+// Compute units of the current device (host; one runtime query per device and
+// thread), 0 if the runtime cannot tell.
+inline int device_compute_units() {
+  constexpr int kMaxDev = 64;
+  thread_local int cached[kMaxDev] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 0;
+  if (!cached[dev]) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cached[dev] = v;
+  }
+  return cached[dev];
+}
+
 }  // namespace h3k

@@ -735,19 +735,6 @@ __global__ __launch_bounds__(256) void dequant_int8_kernel(const int8_t* __restr
   __builtin_nontemporal_store(o1, dst + 1);
 }
 
-// Compute units of the current device (one query per device and thread).
-static int device_cus() {
-  constexpr int kMaxDev = 64;
-  thread_local int cached[kMaxDev] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 0;
-  if (!cached[dev]) {
-    int v = 0;
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    cached[dev] = v;
-  }
-  return cached[dev];
-}
 
 // ---------------------------------------------------------------------------
 // fp32 SIMT GEMM: 64x64 tile, k-steps of 16, 4x4 outputs per thread.
@@ -852,7 +839,7 @@ static void launch_bf16(const LinearArgs& a, hipStream_t stream, int* kernels) {
   } else {
     int S = 0;
     if constexpr (EPI != kEpiBiasRope) {   // row-major outputs only: no transposed or rotated part
-      const int cus = (a.part && a.split_col >= a.n) ? device_cus() : 0;
+      const int cus = (a.part && a.split_col >= a.n) ? device_compute_units() : 0;
       if (cus > 0) S = tail_split_ways(nblk, p.k / 64, cus, a.part_bytes / kPartTileBytes);
       if (S) {
         p.full_tiles = nblk - nblk % cus;
