@@ -280,18 +280,24 @@ def test_block_int8_mlp_groups(R, case, group):
 
 
 @pytest.mark.parametrize("case,grid,half", [("c2", (14, 30, 54), False), ("ragged", (3, 3, 37), False),
-                                             ("ragged", (3, 3, 37), True), ("d64", (2, 8, 16), True)])
+                                             ("ragged", (3, 3, 37), True), ("d64", (2, 8, 16), True),
+                                             ("ragged_int8", (3, 3, 37), True)])
 def test_block_rope(R, case, grid, half):
     """3D RoPE of q and k fused into the QKV projection's epilogue, against the
     oracle's block with the same grid; byte-identical with aliasing on and
     off.  c2: the 864x480x56-frame latent (14 frames, 30 rows, 54 columns).
     The QKV weights are scaled up so that the output depends on the
-    positions: the block without RoPE must be far from the reference."""
+    positions: the block without RoPE must be far from the reference.
+    ragged_int8: int8 projection weights, the QKV weights widened into the
+    staging buffer before the rotary epilogue (the same bytes as widening in
+    the GEMM)."""
     import torch
     if case == "c2":
         shape = si.C2
     elif case == "ragged":
         shape = si.custom_shape("rope", 974, 333, 2, 128, 640, "bf16")
+    elif case == "ragged_int8":
+        shape = si.custom_shape("rope8", 977, 333, 2, 128, 640, "bf16", int8_weights=True)
     else:
         shape = si.custom_shape("rope64", 975, 256, 4, 64, 512, "bf16")
     flush(f"block {shape.name} rope grid={grid} half={half}")
@@ -299,7 +305,8 @@ def test_block_rope(R, case, grid, half):
     # QKV weights scaled so that q and k have std ~1.4 (logits of std ~2) at every width, as the
     # N(0, 0.02^2) weights give at D = 5120: attention, and the block, then depend on the positions
     boost = max(1.0, 70.0 / np.sqrt(shape.hidden))
-    hw["w_qkv"] = si._finish(np.ascontiguousarray(hw["w_qkv"].values * boost, dtype=np.float32), shape.dtype)
+    hw["w_qkv"] = si._finish(np.ascontiguousarray(hw["w_qkv"].values * boost, dtype=np.float32),
+                             "f32" if shape.int8_weights else shape.dtype)   # int8: fp32 before quantising
     dw, ow = upload_block(shape, hw)
     xd, cd = dev(hx), dev(hc)
     rope = (grid[0], grid[1], grid[2], half)
@@ -311,6 +318,8 @@ def test_block_rope(R, case, grid, half):
     flush(f"  rel_l2 = {err:.3e}")
     record(f"block RoPE {case} grid={grid} half={half}", err, TOL)
     assert err < TOL
+    if case == "ragged_int8":
+        _assert_staging_identical(R, shape, dw, xd, cd, got_t, rope=rope)
     plain = oracle.block_forward(hx.values, hc.values, ow, shape.n_heads, rows=rows)
     flush(f"  rel_l2 to the block without RoPE = {rel_l2(got[rows], plain):.3e}")
     assert rel_l2(got[rows], plain) > 5 * err          # the positions are in the output
