@@ -51,6 +51,12 @@ def device_block():
             "int8_peak_from_cus_and_clock_tops": round(2 * per_s * BF16_FLOP_PER_CLK_CU / 1e12, 1)}
 
 
+def bw(nbytes, ms):
+    """GB/s of `nbytes` moved in `ms`, and its fraction of the 8 TB/s HBM peak."""
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return round(gbs, 1), round(gbs / PEAK_HBM_GBS, 4)
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -337,9 +343,9 @@ def main():
             e["tflops"] = round(fl[name] / (avg_ms * 1e-3) / 1e12, 1)
             e["mfma_frac"] = round(e["tflops"] / PEAK_BF16_TFLOPS, 4) if name != "adaln" else None
         if name == "ln_mod":
-            e["gbs"] = round(ln_bytes(N, D) / (avg_ms * 1e-3) / 1e9, 1)
+            e["gbs"], e["hbm_frac"] = bw(ln_bytes(N, D), avg_ms)
         if name == "adaln":
-            e["gbs"] = round((6 * D * C * 2 + C * 2 + 6 * D * 4) / (avg_ms * 1e-3) / 1e9, 1)
+            e["gbs"], e["hbm_frac"] = bw(6 * D * C * 2 + C * 2 + 6 * D * 4, avg_ms)
         per_kernel[name] = e
     dom = max((k for k in per_kernel if k in fl and k != "adaln"), key=lambda k: kern[k]["total_ms"])
     dom_avg = per_kernel[dom]["avg_ms"]
@@ -504,11 +510,12 @@ def extra_blocks(b0, x, c):
         k8[name] = {"avg_ms": round(avg, 4), "tflops": round(fl[name] / (avg * 1e-3) / 1e12, 1)}
     res["int8_block"] = {
         "workload": "one block at 22680 tokens with int8 QKV/out/up/down weights (per-row scales), "
-                    "bf16 activations, W8A16 GEMMs on the bf16 MFMA",
+                    "bf16 activations; each int8 weight widened to bf16 into a staging buffer, then the bf16 "
+                    "GEMM with the row scale in its epilogue (W8A16 on the bf16 MFMA)",
         "ms_per_block": round(ms8, 3), "tflops": round(sum(fl.values()) / (ms8 * 1e-3) / 1e12, 1),
         "gemm_kernels": k8,
         "projection_weight_bytes": {"int8": int(n_el + rows * 4), "bf16": int(2 * n_el)},
-        "quantiser": {"ms_for_4_matrices": round(q_ms, 3), "gbs": round(q_bytes / (q_ms * 1e-3) / 1e9, 1)},
+        "quantiser": dict(zip(("ms_for_4_matrices", "gbs", "hbm_frac"), (round(q_ms, 3), *bw(q_bytes, q_ms)))),
     }
     log(f"int8-weight block: {ms8:.2f} ms; quantiser {q_ms:.3f} ms")
     # ---- the same block with the row-quantised FC2 (int8 x int8 MLP-down)
@@ -524,7 +531,7 @@ def extra_blocks(b0, x, c):
         "fc2": {"avg_ms": round(fc2, 4), "tops": round(fc2_tops, 1), "peak_tops": PEAK_INT8_TOPS,
                 "frac": round(fc2_tops / PEAK_INT8_TOPS, 4)},
         "u_row_quantiser": {"avg_ms": round(aq, 4),
-                            "gbs": round((N * F * 3 + N * 4) / (aq * 1e-3) / 1e9, 1)},
+                            "gbs": bw(N * F * 3 + N * 4, aq)[0], "hbm_frac": bw(N * F * 3 + N * 4, aq)[1]},
     }
     log(f"int8-FC2 block: {msq:.2f} ms (FC2 {fc2:.3f} ms, u quantiser {aq:.3f} ms)")
     # ---- the same block with the group-wise int8 MLP (w_up, w_down in groups of 128 input channels)
@@ -548,11 +555,13 @@ def extra_blocks(b0, x, c):
         kgr[name] = {"avg_ms": round(avg, 4), "tflops": round(fl[name] / (avg * 1e-3) / 1e12, 1)}
     res["int8_group_block"] = {
         "workload": f"the int8-weight block with group-wise int8 MLP weights (one scale per {G} input "
-                    "channels, dequantised to bf16 on the way to the bf16 MFMA)",
+                    "channels, widened to bf16 times their group scales into a staging buffer before the "
+                    "bf16 MFMA)",
         "ms_per_block": round(msg, 3), "tflops": round(sum(fl.values()) / (msg * 1e-3) / 1e12, 1),
         "mlp_kernels": kgr,
         "group_quantiser": {"ms_for_2_matrices": round(qg_ms, 3),
-                            "gbs": round((g_el * 3 + g_el // G * 4) / (qg_ms * 1e-3) / 1e9, 1)},
+                            "gbs": bw(g_el * 3 + g_el // G * 4, qg_ms)[0],
+                            "hbm_frac": bw(g_el * 3 + g_el // G * 4, qg_ms)[1]},
     }
     log(f"int8 group-MLP block: {msg:.2f} ms; group quantiser {qg_ms:.3f} ms")
     del t8, tg
@@ -661,7 +670,7 @@ def sp_share(b0, P=8, reps=5):
         if flops is not None:
             e["tflops"] = round(flops / (ms * 1e-3) / 1e12, 1)
         else:
-            e["gbs"] = round(ln_bytes(M, D) / (ms * 1e-3) / 1e9, 1)
+            e["gbs"], e["hbm_frac"] = bw(ln_bytes(M, D), ms)
         res[name] = e
     for t in (y, u, oa):
         if not torch.isfinite(t.float()).all():
