@@ -401,6 +401,46 @@ def test_stack_token_reduction(R, n_blocks, rng_):
     assert rel_l2(got, plain) > 3 * err                   # the reduction is visible in the output
 
 
+def test_stack_token_reduction_split_attention(R):
+    """Token reduction where the attention splits its last round along the keys
+    in the full blocks (8192 tokens: 64 eight-wave workgroups on 256 CUs) and
+    in the reduced ones (4096 tokens: 32 workgroups), both using the one
+    scratch region of the full plan: against the oracle's stack with the same
+    range, and byte-identical with aliasing on and off."""
+    import torch
+    from video_diffusion_transformer_adaln_amd import binding as B
+    shape = si.custom_shape("tokred_split", 978, 8192, 2, 128, 1024, "bf16", n_blocks=4)
+    rng_ = (1, 3)
+    flush(f"stack of 4 at 8192 tokens with token reduction {rng_}")
+    hx, hc = si.gen_activation(shape)
+    blocks_h = [si.gen_block_weights(shape, l, bias_std=0.05) for l in range(4)]
+    up = [upload_block(shape, hw) for hw in blocks_h]
+    xd, cd = dev(hx), dev(hc)
+    outs = []
+    for alias in (True, False):
+        cfg = config_for(shape, alias)
+        cfg.token_reduction_first, cfg.token_reduction_last = rng_
+        stack = R.DitStack(cfg, [u[0] for u in up])
+        stack.workspace.fill_(0xFF)
+        out = torch.full_like(xd, float("nan"))
+        st = B.DitStats()
+        stack.forward(xd, cd, out, stats=st)
+        torch.cuda.synchronize()
+        part = B.h3k_dit_plan(cfg).part_bytes
+        want = 2 * _want(shape, shape.n_tokens, part) + 2 * _want(shape, shape.n_tokens // 2, part)
+        assert st.tail_splits == want and st.dispatches == 8 * 4 + 2 + want
+        if device_cus() == 256:
+            assert want == 4                                   # the attention of every block
+        outs.append(out)
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+    got = to_np(outs[0])
+    ref = oracle.stack_forward(hx.values, hc.values, [u[1] for u in up], shape.n_heads, token_reduction=rng_)
+    err = rel_l2(got, ref)
+    flush(f"  rel_l2 = {err:.3e}")
+    record("stack 4 at 8192 tokens, token reduction (1, 3), split attention", err, TOL)
+    assert err < TOL
+
+
 def test_stack50_reduced_width_token_reduction(R):
     """50 reduced-width blocks with the middle half (blocks 12..37) on merged tokens."""
     import torch
