@@ -123,7 +123,8 @@ def kernel_role(name):
     for key, role in (("ln_modulate_kernel", "ln_mod"), ("adaln_gemv_kernel", "adaln"),
                       ("quantize_int8_rows_kernel", "quantize_rows"), ("quantize_int8_kernel", "quantize_rows"),
                       ("quantize_int8_groups_kernel", "quantize_groups"), ("dequant_int8_kernel", "dequant"),
-                      ("gemm_tail_kernel", "gemm_tail"), ("copyBuffer", "copy")):
+                      ("gemm_tail_kernel", "gemm_tail"), ("attention_combine_kernel", "attention_combine"),
+                      ("copyBuffer", "copy")):
         if key in n:
             return role
     return None
