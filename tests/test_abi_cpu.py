@@ -142,6 +142,59 @@ def test_int8_weight_staging_buffer():
     assert h3k.h3k_dit_plan(B.make_config(512, 256, 4, 64, 1024, 256, B.H3K_F32)).wstage_bytes == 0
 
 
+def _rule_part_bytes(N, D, H, d, F, int8_fc2=False, reduction=False):
+    """The split-tail scratch from the rules restated in tests/gpu_util.py at
+    256 CUs: the largest need of the out / up / down GEMMs and the attention,
+    over N tokens and (with token reduction) N/2."""
+    import gpu_util as G
+
+    def need(n):
+        tm = (n + 255) // 256
+        best = 0
+        for i, (nn, k) in enumerate(((D, D), (F, D), (D, F))):
+            if i == 2 and int8_fc2:
+                continue
+            tiles = tm * ((nn + 255) // 256)
+            S = G.tail_split_ways(tiles, k // 64, 256, 256)
+            if S:
+                best = max(best, (tiles % 256) * S * 256 * 256 * 4)
+        if d == 128:
+            tiles = (n + 31) // 32
+            unit = lambda nw: nw * 32 * 130 * 4
+            b8 = (n + 255) // 256 * H
+            s8 = G.attn_split_ways(b8, tiles, 256, 1 << 40)
+            four = (n + 255) // 256 * H < 1024 and n <= 8192
+            if s8:
+                best = max(best, (b8 % 256) * s8 * unit(8))
+            elif four:
+                b4 = (n + 127) // 128 * H
+                s4 = G.attn_split_ways(b4, tiles, 512, 1 << 40)
+                if s4:
+                    best = max(best, (b4 % 512) * s4 * unit(4))
+        return best
+
+    b = need(N)
+    if reduction:
+        b = max(b, need(N // 2))
+    return (b + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("N", [1, 300, 2000, 4096, 6000, 6144, 8192, 11340, 12000, 22680])
+@pytest.mark.parametrize("H,F", [(2, 1024), (8, 4096), (24, 12288), (40, 13824)])
+def test_split_scratch_matches_the_launch_rules(N, H, F):
+    """The plan's split-tail scratch is what the GEMM and attention launchers
+    would use on 256 CUs, for bf16 and int8 weights, with and without token
+    reduction (tests/gpu_util.py restates both rules)."""
+    d = 128
+    D = H * d
+    for w8, fc2 in ((False, False), (True, False), (True, True)):
+        for red in ((False,) if N % 2 else (False, True)):
+            cfg = B.make_config(N, D, H, d, F, D, B.H3K_BF16, B.H3K_INT8 if w8 else B.H3K_BF16,
+                                int8_fc2_rows=fc2, token_reduction=(0, 1) if red else None)
+            want = _rule_part_bytes(N, D, H, d, F, int8_fc2=fc2, reduction=red)
+            assert h3k.h3k_dit_plan(cfg).part_bytes == want, (N, H, F, w8, fc2, red)
+
+
 def test_tail_split_scratch_sizes():
     """The k-split scratch the plan reserves: the largest of the out / up / down GEMMs' last-wave
     tiles times their split ways, on 256 compute units (one 256x256 tile per CU and wave)."""
