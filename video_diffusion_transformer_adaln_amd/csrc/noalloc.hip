@@ -1,8 +1,9 @@
 // The block forward for callers that cannot allocate device memory (code
 // under HIP graph capture, tight serving loops, harnesses that forbid
 // hipMalloc): instead of a caller workspace, the block's intermediates (mod,
-// h, q|k|V^T, o, x1, h2, u) live in a static device array of this library,
-// `scratch`, of H3K_NOALLOC_SCRATCH_BYTES.  Each GPU the library runs on holds
+// h, q|k|V^T, o, x1, h2, u, and the scratch of split tails and of widened
+// int8 weights where the config has them) live in a static device array of
+// this library, `scratch`, of H3K_NOALLOC_SCRATCH_BYTES.  Each GPU the library runs on holds
 // its own copy of the array until the process ends.
 //
 // In host code `scratch` is only a host-side stand-in for the array: its
