@@ -106,6 +106,18 @@ def test_block_ragged_tail_split(R):
     _split_on_off(R, shape, "block ragged 6000x2944", 3)
 
 
+@pytest.mark.parametrize("int8", [False, True])
+def test_block_wide_tail_split_all_gemms(R, int8):
+    """6144 tokens at D = 4096 (32 x 128 heads), F = 12288: the out-projection
+    and MLP-down (384 tiles) and the MLP-up with its GELU epilogue (1152 tiles)
+    each leave 128 tiles in their last wave on 256 CUs and split them 2 ways
+    along k.  With int8 weights the same happens to the bf16 GEMMs on the
+    staged (widened) weights, the channel scale in the split epilogue."""
+    shape = si.custom_shape("wide_split" + ("_int8" if int8 else ""), 992 + int8, 6144, 32, 128, 12288, "bf16",
+                            int8_weights=int8)
+    _split_on_off(R, shape, f"block 6144x4096{' int8 weights' if int8 else ''}", 3)
+
+
 def _split_on_off(R, shape, label, want_256):
     import os
     from video_diffusion_transformer_adaln_amd import binding as B
@@ -125,7 +137,8 @@ def _split_on_off(R, shape, label, want_256):
         finally:
             os.environ.pop("H3K_DISABLE_TAIL_SPLIT", None)
         want = _want(shape, shape.n_tokens, part) if split else 0
-        assert st.tail_splits == want and st.dispatches == 8 + want
+        staged = 4 if shape.int8_weights else 0                # int8: the four weight-widening passes
+        assert st.tail_splits == want and st.dispatches == 8 + staged + want
         err = rel_l2(outs[split], ref)
         flush(f"  split={split}: {st.tail_splits} kernels split, rel_l2 = {err:.3e}")
         record(f"{label}{'' if split else ', tail split off'}", err, TOL)
