@@ -120,8 +120,8 @@ GEMM_CASES = [
     (257, 328, 192, 2, "bf16", False, None, True),    # 3 k-tiles, ragged n
     (129, 264, 320, 1, "bf16", False, None, True),    # 5 k-tiles: the operand ring wraps
     (700, 520, 704, 0, "bf16", False, 264, True),     # 11 k-tiles, straddling transposed split
-    (4200, 4096, 128, 2, "bf16", False, None, True),  # 272 tiles: some workgroups take two
-    (4200, 4352, 192, 0, "bf16", False, 2824, True),  # 289 tiles, straddling split, two tiles per workgroup
+    (4200, 4096, 128, 2, "bf16", False, None, True),  # 272 tiles: a second, partial round of workgroups
+    (4200, 4352, 192, 0, "bf16", False, 2824, True),  # 289 tiles, straddling split, a second round
     (300, 320, 128, 0, "bf16", True, None, True),
     (300, 576, 192, 2, "bf16", True, None, True),
     (97, 1024, 256, 0, "bf16", True, 512, True),
