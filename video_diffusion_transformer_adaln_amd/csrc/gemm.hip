@@ -133,18 +133,109 @@ __device__ __forceinline__ void quad(const f32x4 (&acc)[4][8], int jb, int q, in
 // Epilogue math, fp32, one bf16 rounding at the store.
 // Row-major output, first step: features f..f+3 of token t, channel scale and
 // bias, then the column scale (the attention scale folded into q; f..f+3 lie
-// on one side of scale_cols, a multiple of 8).
+// on one side of scale_cols, a multiple of 8).  Channel scale and bias are
+// one explicit fma (a v * s + b the compiler would be free to fuse or not,
+// which would let kernels with the same arithmetic round differently).
+__device__ __forceinline__ float scale_add(float v, float s, float b, bool has_bias) {
+  return has_bias ? __builtin_fmaf(v, s, b) : v * s;
+}
 template <bool W8>
 __device__ __forceinline__ void scale_bias4(const GemmParams& p, float (&v)[4], int f) {
   const float cs = (int64_t)f < p.scale_cols ? p.col_scale : 1.0f;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    if constexpr (W8) v[e] *= p.w_scale[f + e];
-    if (p.bias) v[e] += static_cast<float>(p.bias[f + e]);
+    const float b = p.bias ? static_cast<float>(p.bias[f + e]) : 0.0f;
+    if constexpr (W8) v[e] = scale_add(v[e], p.w_scale[f + e], b, p.bias != nullptr);
+    else if (p.bias) v[e] += b;
     v[e] *= cs;
   }
 }
-// Second step: the activation, rotation or gated residual.
+// The ring kernel's epilogue takes a lane's bias and channel-scale values from
+// registers, read together once per tile (EpiConsts): read per quad, each
+// read and its wait in turn, they cost about as much as the tile's stores
+// (measured on MI355X: 8-12 % of a projection GEMM with k = 5120).
+// Row-major output: feature feat0 + a_row0 + 16 I + 4 (lane/16) + e at
+// [4 I + e]; transposed output: feature feat0 + b_row0 + 32 jb + 16 h +
+// lane%16 at [2 jb + h].  s is filled only where the channel scale applies.
+struct EpiConsts {
+  float b[16];
+  float s[16];
+};
+template <bool SCALE>
+__device__ __forceinline__ void load_epi_consts(const GemmParams& p, int feat0, int a_row0, int b_row0, bool trans,
+                                                int lane, EpiConsts& c) {
+  // buffer reads: a null bias (or no scales) reads as zero, and so do
+  // features >= n, which are never stored
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.bias, p.bias ? (uint32_t)p.n * 2u : 0u);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.w_scale, SCALE ? (uint32_t)p.n * 4u : 0u);
+  auto lo = [](uint32_t w) { return __builtin_bit_cast(float, w << 16); };
+  auto hi = [](uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); };
+  if (!trans) {
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+      const uint32_t f = (uint32_t)(feat0 + a_row0 + 16 * I + 4 * (lane >> 4));
+      const u32x2 b = __builtin_amdgcn_raw_buffer_load_b64(rb, f * 2u, 0, 0);
+      c.b[4 * I + 0] = lo(b[0]);
+      c.b[4 * I + 1] = hi(b[0]);
+      c.b[4 * I + 2] = lo(b[1]);
+      c.b[4 * I + 3] = hi(b[1]);
+      if constexpr (SCALE) {
+        const u32x4 sc = __builtin_amdgcn_raw_buffer_load_b128(rs, f * 4u, 0, 0);
+        // each element copied out before the cast: this compiler reads a
+        // bit-cast vector element such as sc[e] at element 0's address
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t w = sc[e];
+          c.s[4 * I + e] = __builtin_bit_cast(float, w);
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t f = (uint32_t)(feat0 + b_row0 + 32 * (i >> 1) + 16 * (i & 1) + (lane & 15));
+      c.b[i] = lo(__builtin_amdgcn_raw_buffer_load_b16(rb, f * 2u, 0, 0));
+      if constexpr (SCALE) c.s[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, f * 4u, 0, 0));
+    }
+    // the unused half written too, so that both branches end with the same
+    // stores (which the compiler may then merge without indexing the array)
+#pragma unroll
+    for (int i = 8; i < 16; ++i) {
+      c.b[i] = 0.0f;
+      if constexpr (SCALE) c.s[i] = 0.0f;
+    }
+  }
+}
+// scale_bias4 with the values of quad row I from EpiConsts (the same
+// arithmetic); with PRE false they are read from memory instead
+template <bool W8, bool PRE>
+__device__ __forceinline__ void scale_bias4c(const GemmParams& p, float (&v)[4], int f, const EpiConsts& ec, int I) {
+  if constexpr (!PRE) {
+    scale_bias4<W8>(p, v, f);
+  } else {
+    const float cs = (int64_t)f < p.scale_cols ? p.col_scale : 1.0f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if constexpr (W8) v[e] = scale_add(v[e], ec.s[4 * I + e], ec.b[4 * I + e], p.bias != nullptr);
+      else if (p.bias) v[e] += ec.b[4 * I + e];
+      v[e] *= cs;
+    }
+  }
+}
+// bias and channel scale of transposed-output feature f (EpiConsts index i)
+template <bool W8, bool PRE>
+__device__ __forceinline__ void bias_scale1(const GemmParams& p, int f, const EpiConsts& ec, int i, float& bb,
+                                            float& sc) {
+  if constexpr (PRE) {
+    bb = ec.b[i];
+    sc = W8 ? ec.s[i] : 1.0f;
+  } else {
+    bb = p.bias ? static_cast<float>(p.bias[f]) : 0.0f;
+    sc = W8 ? p.w_scale[f] : 1.0f;
+  }
+}
+// Second step: the activation, rotation or gated residual (r + g z as one
+// explicit fma, for the reason given at scale_add).
 template <int EPI>
 __device__ __forceinline__ void epilogue4(const GemmParams& p, float (&v)[4], int t, int f,
                                           const float2* rope_tab = nullptr) {
@@ -167,7 +258,7 @@ __device__ __forceinline__ void epilogue4(const GemmParams& p, float (&v)[4], in
     const u32x2 rr = *reinterpret_cast<const u32x2*>(p.residual + (int64_t)t * p.ldr + f);
     const bf16* re = reinterpret_cast<const bf16*>(&rr);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = static_cast<float>(re[e]) + p.gate[f + e] * v[e];
+    for (int e = 0; e < 4; ++e) v[e] = __builtin_fmaf(p.gate[f + e], v[e], static_cast<float>(re[e]));
   }
 }
 __device__ __forceinline__ u32x2 pack4(const float (&v)[4]) {
@@ -181,10 +272,9 @@ __device__ __forceinline__ u32x2 pack4(const float (&v)[4]) {
 // Fused epilogue of one wave's 64x128 accumulator sub-tile, stored straight
 // from the accumulator layout (8-byte pieces, 32 rows per instruction); used
 // for the tile that straddles split_col.
-template <int EPI, bool W8, typename AccT>
+template <int EPI, bool W8, bool PRE, typename AccT>
 __device__ __forceinline__ void store_tile(const GemmParams& p, const AccT& acc, int a_row0, int b_row0, int tok0,
-                                           int feat0, bool trans, int lane) {
-  const float* wsc = p.w_scale;
+                                           int feat0, bool trans, int lane, const EpiConsts& ec) {
 #pragma unroll
   for (int jb = 0; jb < 4; ++jb)
 #pragma unroll
@@ -196,7 +286,7 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, const AccT& acc,
         const int f = feat0 + a_row0 + ai;
         const int t = tok0 + b_row0 + jb * 32 + br;
         if (t >= p.m || f >= p.n) continue;
-        scale_bias4<W8>(p, v, f);
+        scale_bias4c<W8, PRE>(p, v, f, ec, q >> 1);
         if ((int64_t)f >= p.split_col) {   // straddling tile: transposed part, bias only
 #pragma unroll
           for (int e = 0; e < 4; ++e) p.yt[(int64_t)(f + e - p.split_col) * p.ldyt + t] = static_cast<bf16>(v[e]);
@@ -208,15 +298,13 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, const AccT& acc,
         const int t0 = tok0 + a_row0 + ai;
         const int f = feat0 + b_row0 + jb * 32 + br;
         if (f >= p.n || t0 >= p.m) continue;
-        const float sc = W8 ? wsc[f] : 1.0f;
-        const float bb = p.bias ? static_cast<float>(p.bias[f]) : 0.0f;
+        float sc, bb;
+        bias_scale1<W8, PRE>(p, f, ec, 2 * jb + (q & 1), bb, sc);
         u32x2 out;
         bf16* oe = reinterpret_cast<bf16*>(&out);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          float x = v[e];
-          if constexpr (W8) x *= sc;
-          oe[e] = static_cast<bf16>(x + bb);
+          oe[e] = static_cast<bf16>(W8 ? __builtin_fmaf(v[e], sc, bb) : v[e] + bb);
         }
         bf16* dst = p.yt + (int64_t)(f - p.split_col) * p.ldyt + t0;
         if (t0 + 3 < p.m) {
@@ -238,10 +326,10 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, const AccT& acc,
 // chunk c ^ ((r ^ r/8) % 8); each lane then stores 16 bytes, 8 lanes per
 // row.  Row-major output: B-rows are tokens and the 64 A-values features;
 // transposed output (V^T): B-rows are features and the A-values tokens.
-template <int EPI, bool W8, int JR, typename AccT>
+template <int EPI, bool W8, bool PRE, int JR, typename AccT>
 __device__ __forceinline__ void store_tile_staged(const GemmParams& p, const AccT& acc, int a_row0, int b_row0,
                                                   int tok0, int feat0, bool trans, int lane, char* stage,
-                                                  const float2* rope_tab = nullptr) {
+                                                  const EpiConsts& ec, const float2* rope_tab = nullptr) {
   auto swz = [](int r) { return (r ^ (r >> 3)) & 7; };
 #pragma unroll
   for (int rnd = 0; rnd < 4 / JR; ++rnd) {
@@ -257,19 +345,16 @@ __device__ __forceinline__ void store_tile_staged(const GemmParams& p, const Acc
         if (!trans) {
           const int f = feat0 + a_row0 + ai, t = tok0 + b_row0 + j * 32 + br;
           if (t < p.m && f < p.n) {
-            scale_bias4<W8>(p, v, f);
+            scale_bias4c<W8, PRE>(p, v, f, ec, q >> 1);
             epilogue4<EPI>(p, v, t, f, rope_tab);
           }
         } else {
           const int f = feat0 + b_row0 + j * 32 + br;
           if (f < p.n) {
-            const float sc = W8 ? p.w_scale[f] : 1.0f;
-            const float bb = p.bias ? static_cast<float>(p.bias[f]) : 0.0f;
+            float sc, bb;
+            bias_scale1<W8, PRE>(p, f, ec, 2 * j + (q & 1), bb, sc);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              if constexpr (W8) v[e] *= sc;
-              v[e] += bb;
-            }
+            for (int e = 0; e < 4; ++e) v[e] = W8 ? __builtin_fmaf(v[e], sc, bb) : v[e] + bb;
           }
         }
         *reinterpret_cast<u32x2*>(stage + brow * 128 + (((ai >> 3) ^ swz(brow)) << 4) + ((ai >> 2) & 1) * 8) =
@@ -307,11 +392,26 @@ __device__ __forceinline__ void store_tile_staged(const GemmParams& p, const Acc
 // holds 64 fp32 values, 16-byte chunk c at chunk c ^ (r % 16).  Each lane
 // then finishes 8 consecutive features of one token: y = r + g * z, one
 // rounding.
-template <bool W8, int JR, typename AccT>
+template <bool W8, bool PRE, int JR, typename AccT>
 __device__ __forceinline__ void store_tile_staged_residual(const GemmParams& p, const AccT& acc, int a_row0,
-                                                           int b_row0, int tok0, int feat0, int lane, char* stage) {
+                                                           int b_row0, int tok0, int feat0, int lane, char* stage,
+                                                           const EpiConsts& ec) {
+  // the lane's 8 gate values, and each round's residual pieces, are read
+  // before they are needed, all at once (rows and features clamped into
+  // range; what lies outside is never stored)
+  const int fg = min(feat0 + a_row0 + 8 * (lane & 7), p.n - 8);
+  const f32x4 g0 = *reinterpret_cast<const f32x4*>(p.gate + fg);
+  const f32x4 g1 = *reinterpret_cast<const f32x4*>(p.gate + fg + 4);
 #pragma unroll
   for (int rnd = 0; rnd < 4 / JR; ++rnd) {
+    // one round's residual pieces in registers at a time
+    __builtin_amdgcn_sched_barrier(0);
+    u32x4 rres[4 * JR];
+#pragma unroll
+    for (int s8 = 0; s8 < 4 * JR; ++s8) {
+      const int t = min(tok0 + b_row0 + rnd * JR * 32 + s8 * 8 + (lane >> 3), p.m - 1);
+      rres[s8] = *reinterpret_cast<const u32x4*>(p.residual + (int64_t)t * p.ldr + fg);
+    }
 #pragma unroll
     for (int jj = 0; jj < JR; ++jj)
 #pragma unroll
@@ -322,7 +422,7 @@ __device__ __forceinline__ void store_tile_staged_residual(const GemmParams& p, 
         quad(acc, j, q, lane, v, ai, br);
         const int brow = jj * 32 + br;
         const int f = feat0 + a_row0 + ai, t = tok0 + b_row0 + j * 32 + br;
-        if (t < p.m && f < p.n) scale_bias4<W8>(p, v, f);
+        if (t < p.m && f < p.n) scale_bias4c<W8, PRE>(p, v, f, ec, q >> 1);
         f32x4 z = {v[0], v[1], v[2], v[3]};
         *reinterpret_cast<f32x4*>(stage + brow * 256 + (((ai >> 2) ^ (brow & 15)) << 4)) = z;
       }
@@ -333,14 +433,13 @@ __device__ __forceinline__ void store_tile_staged_residual(const GemmParams& p, 
       const f32x4 z0 = *reinterpret_cast<const f32x4*>(stage + row * 256 + (((2 * c) ^ (row & 15)) << 4));
       const f32x4 z1 = *reinterpret_cast<const f32x4*>(stage + row * 256 + (((2 * c + 1) ^ (row & 15)) << 4));
       if (t < p.m && f < p.n) {
-        const u32x4 rr = *reinterpret_cast<const u32x4*>(p.residual + (int64_t)t * p.ldr + f);
-        const bf16* re = reinterpret_cast<const bf16*>(&rr);
+        const bf16* re = reinterpret_cast<const bf16*>(&rres[s8]);
         u32x4 out;
         bf16* oe = reinterpret_cast<bf16*>(&out);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          oe[e] = static_cast<bf16>(static_cast<float>(re[e]) + p.gate[f + e] * z0[e]);
-          oe[4 + e] = static_cast<bf16>(static_cast<float>(re[4 + e]) + p.gate[f + 4 + e] * z1[e]);
+          oe[e] = static_cast<bf16>(__builtin_fmaf(g0[e], z0[e], static_cast<float>(re[e])));
+          oe[4 + e] = static_cast<bf16>(__builtin_fmaf(g1[e], z1[e], static_cast<float>(re[4 + e])));
         }
         *reinterpret_cast<u32x4*>(p.y + (int64_t)t * p.ldy + f) = out;
       }
@@ -614,6 +713,13 @@ __global__ __launch_bounds__(512) void gemm_ring_kernel(GemmParams p) {
     wg_barrier();
   }
   }
+  // the epilogue's bias and channel scales, read now so that they overlap the
+  // last loads' wait (the in-GEMM widening kernels, whose epilogue has no
+  // registers to spare for them, read them per quad)
+  constexpr bool kScale = W8 ? !GRP : (I8 || SC == 1);
+  constexpr bool kPre = !W8;
+  EpiConsts ec;
+  if constexpr (kPre) load_epi_consts<kScale>(p, feat0, a_row0, b_row0, trans, lane, ec);
   wait_vmcnt<0>();
   if constexpr (!I8 && !W8) {
     if (part_idx >= 0) {   // same for the whole workgroup
@@ -657,24 +763,24 @@ __global__ __launch_bounds__(512) void gemm_ring_kernel(GemmParams p) {
 #pragma unroll
     for (int j8 = 0; j8 < 8; ++j8) {
       const int t = tok0 + b_row0 + j8 * 16 + (lane & 15);
-      const float xs = t < p.m ? p.x_scale[t] : 0.0f;
+      const float xs0 = p.x_scale[min(t, p.m - 1)];   // unconditional: the reads go out together
+      const float xs = t < p.m ? xs0 : 0.0f;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int r = 0; r < 4; ++r) accf[i][j8][r] = static_cast<float>(acc16[i][j8][r]) * xs;
     }
     if (staged && EPI == kEpiGatedResidual)
-      store_tile_staged_residual<true, 2>(p, accf, a_row0, b_row0, tok0, feat0, lane, stage);
-    else if (staged) store_tile_staged<EPI, true, 4>(p, accf, a_row0, b_row0, tok0, feat0, false, lane, stage);
-    else store_tile<EPI, true>(p, accf, a_row0, b_row0, tok0, feat0, false, lane);
+      store_tile_staged_residual<true, true, 2>(p, accf, a_row0, b_row0, tok0, feat0, lane, stage, ec);
+    else if (staged) store_tile_staged<EPI, true, true, 4>(p, accf, a_row0, b_row0, tok0, feat0, false, lane, stage, ec);
+    else store_tile<EPI, true, true>(p, accf, a_row0, b_row0, tok0, feat0, false, lane, ec);
   } else {
-    constexpr bool kScale = (W8 && !GRP) || SC == 1;   // per-channel weight scale in the epilogue
     auto finish = [&](const auto& ac) {
       if (staged && EPI == kEpiGatedResidual && !trans)
-        store_tile_staged_residual<kScale, 2>(p, ac, a_row0, b_row0, tok0, feat0, lane, stage);
+        store_tile_staged_residual<kScale, kPre, 2>(p, ac, a_row0, b_row0, tok0, feat0, lane, stage, ec);
       else if (staged)
-        store_tile_staged<EPI, kScale, 4>(p, ac, a_row0, b_row0, tok0, feat0, trans, lane, stage, rope_tab);
-      else store_tile<EPI, kScale>(p, ac, a_row0, b_row0, tok0, feat0, trans, lane);
+        store_tile_staged<EPI, kScale, kPre, 4>(p, ac, a_row0, b_row0, tok0, feat0, trans, lane, stage, ec, rope_tab);
+      else store_tile<EPI, kScale, kPre>(p, ac, a_row0, b_row0, tok0, feat0, trans, lane, ec);
     };
     finish(acc16);
   }
