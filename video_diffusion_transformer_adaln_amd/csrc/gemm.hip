@@ -155,11 +155,14 @@ __device__ __forceinline__ void scale_bias4(const GemmParams& p, float (&v)[4], 
 // read and its wait in turn, they cost about as much as the tile's stores
 // (measured on MI355X: 8-12 % of a projection GEMM with k = 5120).
 // Row-major output: feature feat0 + a_row0 + 16 I + 4 (lane/16) + e at
-// [4 I + e]; transposed output: feature feat0 + b_row0 + 32 jb + 16 h +
-// lane%16 at [2 jb + h].  s is filled only where the channel scale applies.
+// [4 I + e], and cs[I] its column scale; transposed output: feature feat0 +
+// b_row0 + 32 jb + 16 h + lane%16 at [2 jb + h].  s is filled only where the
+// channel scale applies.  Without a bias, b holds -0: x + (-0) = x and
+// fma(x, s, -0) = x s for every x, so the bias is added unconditionally.
 struct EpiConsts {
   float b[16];
   float s[16];
+  float cs[4];
 };
 template <bool SCALE>
 __device__ __forceinline__ void load_epi_consts(const GemmParams& p, int feat0, int a_row0, int b_row0, bool trans,
@@ -168,43 +171,62 @@ __device__ __forceinline__ void load_epi_consts(const GemmParams& p, int feat0, 
   // features >= n, which are never stored
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.bias, p.bias ? (uint32_t)p.n * 2u : 0u);
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.w_scale, SCALE ? (uint32_t)p.n * 4u : 0u);
-  auto lo = [](uint32_t w) { return __builtin_bit_cast(float, w << 16); };
-  auto hi = [](uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); };
+  const uint32_t sign = p.bias ? 0u : 0x80000000u;
+  auto lo = [sign](uint32_t w) { return __builtin_bit_cast(float, (w << 16) | sign); };
+  auto hi = [sign](uint32_t w) { return __builtin_bit_cast(float, (w & 0xffff0000u) | sign); };
+  // Both branches read into locals first and then write every member in the
+  // same order, so that the compiler can merge the two sets of writes
+  // element by element (a mismatched order makes it index the struct, which
+  // then lives in scratch memory).
+  float b[16], sc[16], cs[4];
   if (!trans) {
+    u32x2 bw[4];
+    u32x4 sw[4];
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
       const uint32_t f = (uint32_t)(feat0 + a_row0 + 16 * I + 4 * (lane >> 4));
-      const u32x2 b = __builtin_amdgcn_raw_buffer_load_b64(rb, f * 2u, 0, 0);
-      c.b[4 * I + 0] = lo(b[0]);
-      c.b[4 * I + 1] = hi(b[0]);
-      c.b[4 * I + 2] = lo(b[1]);
-      c.b[4 * I + 3] = hi(b[1]);
-      if constexpr (SCALE) {
-        const u32x4 sc = __builtin_amdgcn_raw_buffer_load_b128(rs, f * 4u, 0, 0);
-        // each element copied out before the cast: this compiler reads a
-        // bit-cast vector element such as sc[e] at element 0's address
+      bw[I] = __builtin_amdgcn_raw_buffer_load_b64(rb, f * 2u, 0, 0);
+      if constexpr (SCALE) sw[I] = __builtin_amdgcn_raw_buffer_load_b128(rs, f * 4u, 0, 0);
+      cs[I] = (int64_t)f < p.scale_cols ? p.col_scale : 1.0f;
+    }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t w = sc[e];
-          c.s[4 * I + e] = __builtin_bit_cast(float, w);
-        }
+    for (int I = 0; I < 4; ++I) {
+      const uint32_t w0 = bw[I][0], w1 = bw[I][1];
+      b[4 * I + 0] = lo(w0);
+      b[4 * I + 1] = hi(w0);
+      b[4 * I + 2] = lo(w1);
+      b[4 * I + 3] = hi(w1);
+      // each element copied out before the cast: this compiler reads a
+      // bit-cast vector element such as v[e] at element 0's address
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t w = SCALE ? (uint32_t)sw[I][e] : 0u;
+        sc[4 * I + e] = __builtin_bit_cast(float, w);
       }
     }
   } else {
+    uint32_t bw[8], sw[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const uint32_t f = (uint32_t)(feat0 + b_row0 + 32 * (i >> 1) + 16 * (i & 1) + (lane & 15));
-      c.b[i] = lo(__builtin_amdgcn_raw_buffer_load_b16(rb, f * 2u, 0, 0));
-      if constexpr (SCALE) c.s[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, f * 4u, 0, 0));
+      bw[i] = __builtin_amdgcn_raw_buffer_load_b16(rb, f * 2u, 0, 0);
+      sw[i] = SCALE ? __builtin_amdgcn_raw_buffer_load_b32(rs, f * 4u, 0, 0) : 0u;
     }
-    // the unused half written too, so that both branches end with the same
-    // stores (which the compiler may then merge without indexing the array)
 #pragma unroll
-    for (int i = 8; i < 16; ++i) {
-      c.b[i] = 0.0f;
-      if constexpr (SCALE) c.s[i] = 0.0f;
+    for (int i = 0; i < 16; ++i) {
+      b[i] = i < 8 ? lo(bw[i & 7]) : 0.0f;
+      sc[i] = i < 8 ? __builtin_bit_cast(float, sw[i & 7]) : 0.0f;
     }
+#pragma unroll
+    for (int I = 0; I < 4; ++I) cs[I] = 1.0f;
   }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    c.b[i] = b[i];
+    c.s[i] = sc[i];
+  }
+#pragma unroll
+  for (int I = 0; I < 4; ++I) c.cs[I] = cs[I];
 }
 // scale_bias4 with the values of quad row I from EpiConsts (the same
 // arithmetic); with PRE false they are read from memory instead
@@ -213,13 +235,9 @@ __device__ __forceinline__ void scale_bias4c(const GemmParams& p, float (&v)[4],
   if constexpr (!PRE) {
     scale_bias4<W8>(p, v, f);
   } else {
-    const float cs = (int64_t)f < p.scale_cols ? p.col_scale : 1.0f;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if constexpr (W8) v[e] = scale_add(v[e], ec.s[4 * I + e], ec.b[4 * I + e], p.bias != nullptr);
-      else if (p.bias) v[e] += ec.b[4 * I + e];
-      v[e] *= cs;
-    }
+    for (int e = 0; e < 4; ++e)
+      v[e] = (W8 ? __builtin_fmaf(v[e], ec.s[4 * I + e], ec.b[4 * I + e]) : v[e] + ec.b[4 * I + e]) * ec.cs[I];
   }
 }
 // bias and channel scale of transposed-output feature f (EpiConsts index i)
@@ -230,7 +248,7 @@ __device__ __forceinline__ void bias_scale1(const GemmParams& p, int f, const Ep
     bb = ec.b[i];
     sc = W8 ? ec.s[i] : 1.0f;
   } else {
-    bb = p.bias ? static_cast<float>(p.bias[f]) : 0.0f;
+    bb = p.bias ? static_cast<float>(p.bias[f]) : -0.0f;   // as in EpiConsts
     sc = W8 ? p.w_scale[f] : 1.0f;
   }
 }
@@ -331,59 +349,71 @@ __device__ __forceinline__ void store_tile_staged(const GemmParams& p, const Acc
                                                   int tok0, int feat0, bool trans, int lane, char* stage,
                                                   const EpiConsts& ec, const float2* rope_tab = nullptr) {
   auto swz = [](int r) { return (r ^ (r >> 3)) & 7; };
+  // The orientation is the same for the whole tile, so each gets its own
+  // unrolled copy of the loops, with no per-quad branch on it.  With the
+  // constants in registers, the bias and GELU epilogues read no memory and
+  // run on every quad (rows >= m and features >= n are computed from the
+  // zero-filled operands and never stored); the rotary and residual ones,
+  // and the memory-read constants, keep the bounds test.
+  constexpr bool kAll = PRE && (EPI == kEpiBias || EPI == kEpiGelu);
+  auto run = [&](auto tr) {
+    constexpr bool TR = decltype(tr)::value;
 #pragma unroll
-  for (int rnd = 0; rnd < 4 / JR; ++rnd) {
+    for (int rnd = 0; rnd < 4 / JR; ++rnd) {
 #pragma unroll
-    for (int jj = 0; jj < JR; ++jj)
+      for (int jj = 0; jj < JR; ++jj)
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int j = rnd * JR + jj;
-        float v[4];
-        int ai, br;
-        quad(acc, j, q, lane, v, ai, br);
-        const int brow = jj * 32 + br;
-        if (!trans) {
-          const int f = feat0 + a_row0 + ai, t = tok0 + b_row0 + j * 32 + br;
-          if (t < p.m && f < p.n) {
-            scale_bias4c<W8, PRE>(p, v, f, ec, q >> 1);
-            epilogue4<EPI>(p, v, t, f, rope_tab);
-          }
-        } else {
-          const int f = feat0 + b_row0 + j * 32 + br;
-          if (f < p.n) {
-            float sc, bb;
-            bias_scale1<W8, PRE>(p, f, ec, 2 * j + (q & 1), bb, sc);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = W8 ? __builtin_fmaf(v[e], sc, bb) : v[e] + bb;
-          }
-        }
-        *reinterpret_cast<u32x2*>(stage + brow * 128 + (((ai >> 3) ^ swz(brow)) << 4) + ((ai >> 2) & 1) * 8) =
-            pack4(v);
-      }
-#pragma unroll
-    for (int s8 = 0; s8 < 4 * JR; ++s8) {
-      const int row = s8 * 8 + (lane >> 3), c = lane & 7;
-      const int brow = rnd * JR * 32 + row;
-      const u32x4 val = *reinterpret_cast<const u32x4*>(stage + row * 128 + ((c ^ swz(row)) << 4));
-      if (!trans) {
-        const int t = tok0 + b_row0 + brow, f = feat0 + a_row0 + 8 * c;
-        if (t < p.m && f < p.n) *reinterpret_cast<u32x4*>(p.y + (int64_t)t * p.ldy + f) = val;
-      } else {
-        const int f = feat0 + b_row0 + brow, t0 = tok0 + a_row0 + 8 * c;
-        if (f < p.n && t0 < p.m) {
-          bf16* dst = p.yt + (int64_t)(f - p.split_col) * p.ldyt + t0;
-          if (t0 + 7 < p.m) {
-            *reinterpret_cast<u32x4*>(dst) = val;
+        for (int q = 0; q < 8; ++q) {
+          const int j = rnd * JR + jj;
+          float v[4];
+          int ai, br;
+          quad(acc, j, q, lane, v, ai, br);
+          const int brow = jj * 32 + br;
+          if constexpr (!TR) {
+            const int f = feat0 + a_row0 + ai, t = tok0 + b_row0 + j * 32 + br;
+            if (kAll || (t < p.m && f < p.n)) {
+              scale_bias4c<W8, PRE>(p, v, f, ec, q >> 1);
+              epilogue4<EPI>(p, v, t, f, rope_tab);
+            }
           } else {
-            const bf16* ve = reinterpret_cast<const bf16*>(&val);
+            const int f = feat0 + b_row0 + j * 32 + br;
+            if (PRE || f < p.n) {
+              float sc, bb;
+              bias_scale1<W8, PRE>(p, f, ec, 2 * j + (q & 1), bb, sc);
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-              if (t0 + e < p.m) dst[e] = ve[e];
+              for (int e = 0; e < 4; ++e) v[e] = W8 ? __builtin_fmaf(v[e], sc, bb) : v[e] + bb;
+            }
+          }
+          *reinterpret_cast<u32x2*>(stage + brow * 128 + (((ai >> 3) ^ swz(brow)) << 4) + ((ai >> 2) & 1) * 8) =
+              pack4(v);
+        }
+#pragma unroll
+      for (int s8 = 0; s8 < 4 * JR; ++s8) {
+        const int row = s8 * 8 + (lane >> 3), c = lane & 7;
+        const int brow = rnd * JR * 32 + row;
+        const u32x4 val = *reinterpret_cast<const u32x4*>(stage + row * 128 + ((c ^ swz(row)) << 4));
+        if constexpr (!TR) {
+          const int t = tok0 + b_row0 + brow, f = feat0 + a_row0 + 8 * c;
+          if (t < p.m && f < p.n) *reinterpret_cast<u32x4*>(p.y + (int64_t)t * p.ldy + f) = val;
+        } else {
+          const int f = feat0 + b_row0 + brow, t0 = tok0 + a_row0 + 8 * c;
+          if (f < p.n && t0 < p.m) {
+            bf16* dst = p.yt + (int64_t)(f - p.split_col) * p.ldyt + t0;
+            if (t0 + 7 < p.m) {
+              *reinterpret_cast<u32x4*>(dst) = val;
+            } else {
+              const bf16* ve = reinterpret_cast<const bf16*>(&val);
+#pragma unroll
+              for (int e = 0; e < 8; ++e)
+                if (t0 + e < p.m) dst[e] = ve[e];
+            }
           }
         }
       }
     }
-  }
+  };
+  if (trans) run(std::true_type{});
+  else run(std::false_type{});
 }
 
 // Gated residual, row-major: the residual is read in the same coalesced
@@ -422,7 +452,7 @@ __device__ __forceinline__ void store_tile_staged_residual(const GemmParams& p, 
         quad(acc, j, q, lane, v, ai, br);
         const int brow = jj * 32 + br;
         const int f = feat0 + a_row0 + ai, t = tok0 + b_row0 + j * 32 + br;
-        if (t < p.m && f < p.n) scale_bias4c<W8, PRE>(p, v, f, ec, q >> 1);
+        if (PRE || (t < p.m && f < p.n)) scale_bias4c<W8, PRE>(p, v, f, ec, q >> 1);
         f32x4 z = {v[0], v[1], v[2], v[3]};
         *reinterpret_cast<f32x4*>(stage + brow * 256 + (((ai >> 2) ^ (brow & 15)) << 4)) = z;
       }
