@@ -198,6 +198,75 @@ def test_linear(B, m, n, k, epi, dtype, int8, split, full):
         assert np.isnan(to_np(yt)[:, m:]).all()                # padding columns untouched
 
 
+NO_BIAS_CASES = [
+    # m, n, k, epilogue, weights, split
+    (300, 320, 128, 0, "bf16", None),
+    (513, 768, 256, 0, "bf16", 512),     # transposed part, straddling tile
+    (300, 1536, 256, 0, "bf16", 1024),   # transposed part on a tile boundary
+    (257, 328, 192, 2, "bf16", None),
+    (300, 576, 192, 2, "int8", None),
+    (97, 1024, 256, 0, "int8", 512),
+    (129, 264, 256, 1, "int8x8", None),
+    (257, 328, 384, 2, "int8x8", None),
+]
+
+
+@pytest.mark.parametrize("m,n,k,epi,weights,split", NO_BIAS_CASES)
+def test_linear_without_bias(B, m, n, k, epi, weights, split):
+    """A null bias (the epilogue adds -0, which leaves every value as it is)
+    on the bf16, int8-weight and int8 x int8 paths, row-major and transposed
+    parts, against the oracle's linear without a bias."""
+    import torch
+    from video_diffusion_transformer_adaln_amd import runtime as R
+    flush(f"linear without bias m={m} n={n} k={k} epi={epi} {weights} split={split}")
+    cid = 870 + epi
+    x32 = _f32((m, k), 1.0, cid)
+    w32 = _f32((n, k), 0.02, cid, "w_up")
+    split = n if split is None else split
+    res = gate = resd = gated = None
+    if epi == 2:
+        res = _ht(_f32((m, split), 1.0, cid, "x", 1), "bf16")
+        gate = _f32((split,), 0.5, cid, "b_down")
+        resd, gated = dev(res), torch.from_numpy(gate).cuda()
+    y = torch.full((m, split), float("nan"), dtype=torch.bfloat16, device="cuda")
+    ldyt = ((m + 7) // 8) * 8
+    yt = torch.full((n - split, ldyt), float("nan"), dtype=torch.bfloat16, device="cuda") if split < n else None
+    if weights == "int8x8":
+        xq, xs = R.quantize_int8(torch.from_numpy(x32).cuda())
+        wq, ws = R.quantize_int8(torch.from_numpy(w32).cuda())
+        B.h3k_linear_int8(m, n, k, xq, k, xs, wq, k, ws, None, epi, resd, split, gated, y, split)
+        torch.cuda.synchronize()
+        qx, sx = oracle.quantize_int8(x32)
+        qw, sw = oracle.quantize_int8(w32)
+        z = oracle.linear_w8a8(qx, sx, qw, sw, None)
+    else:
+        x = _ht(x32, "bf16")
+        if weights == "int8":
+            wd, sd = R.quantize_int8(torch.from_numpy(w32).cuda())
+            qw, sw = oracle.quantize_int8(w32)
+            w_ref, wcode = oracle.dequantize_int8(qw, sw), B.H3K_INT8
+        else:
+            wt = _ht(w32, "bf16")
+            wd, sd, w_ref, wcode = dev(wt), None, wt.values, B.H3K_BF16
+        B.h3k_linear(B.H3K_BF16, wcode, m, n, k, dev(x), k, wd, k, sd, None, epi, resd, split, gated, y, split,
+                     yt, ldyt if yt is not None else 0, split)
+        torch.cuda.synchronize()
+        z = oracle.linear(x.values, w_ref, None)
+    if epi == 1:
+        ref = oracle.gelu_tanh(z)
+    elif epi == 2:
+        ref = res.values + gate * z[:, :split]
+    else:
+        ref = z
+    got = to_np(y)
+    assert np.isfinite(got).all()
+    assert rel_l2(got, ref[:, :split]) < BF16_TOL / 2
+    if split < n:
+        got_t = to_np(yt)[:, :m].T
+        assert rel_l2(got_t, z[:, split:]) < BF16_TOL / 2
+        assert np.isnan(to_np(yt)[:, m:]).all()
+
+
 # ------------------------------------------------------------------ int8 x int8 linear
 
 LINEAR_INT8_CASES = [
