@@ -156,8 +156,8 @@ __device__ __forceinline__ void scale_bias4(const GemmParams& p, float (&v)[4], 
 // (measured on MI355X: 8-12 % of a projection GEMM with k = 5120).
 // Row-major output: feature feat0 + a_row0 + 16 I + 4 (lane/16) + e at
 // [4 I + e], and cs[I] its column scale; transposed output: feature feat0 +
-// b_row0 + 32 jb + 16 h + lane%16 at [2 jb + h].  s is filled only where the
-// channel scale applies.  Without a bias, b holds -0: x + (-0) = x and
+// b_row0 + 32 jb + 16 h + lane%16 at [2 jb + h].  s holds the channel scales
+// where they apply (zero otherwise).  Without a bias, b holds -0: x + (-0) = x and
 // fma(x, s, -0) = x s for every x, so the bias is added unconditionally.
 struct EpiConsts {
   float b[16];
