@@ -277,7 +277,6 @@ void attention_bf16_kernel(AttnParams p) {
   }
   f32x4 S[2][2][QB];                           // [tile parity][kb][qb]
   u32x4 P[2][QB];                              // [tile parity][qb]: eight bf16 probabilities, in pairs
-  const bf16x2 ones2 = {static_cast<bf16>(1.0f), static_cast<bf16>(1.0f)};
   auto sel = [&](const f32x4 (&s)[2][QB], int r) __attribute__((always_inline)) -> float { return s[(r >> 2) & 1][r >> 3][r & 3]; };
   // exponent of element r: s - m in log2 units
   auto xval = [&](const f32x4 (&s)[2][QB], int r) __attribute__((always_inline)) -> float {
@@ -465,7 +464,6 @@ void attention_bf16_kernel(AttnParams p) {
   // barrier.  TAIL passes mask the last tile and its V^T, and skip tiles >= T.
   using C0 = std::integral_constant<int, 0>;
   using C1 = std::integral_constant<int, 1>;
-  using C2 = std::integral_constant<int, 2>;
   using C3 = std::integral_constant<int, 3>;
   auto pass = [&](int t0, auto sl_c, auto tail_c) {
     constexpr int SL = decltype(sl_c)::value;  // 1 or 3
