@@ -469,7 +469,8 @@ def test_attention(B, n, heads, hd, dtype, full, pre):
     flush(f"attention n={n} heads={heads} d={hd} {dtype} prescaled={pre}")
     D = heads * hd
     # q and k entries ~ N(0, 3^2), so q.k / sqrt(d) has std 3^2 = 9: softmax rows as peaked as the
-    # block's (its logits have std about 10), so the running reference moves through the key tiles
+    # block's (its logits have std about 10); test_attention_moving_reference moves the reference
+    # after the first tile
     q32 = _f32((n, D), 1.0, 820, "x") * 3.0
     q = _ht(q32, dtype)
     q_in, q_ref = (q, q.values) if not pre else _prescaled_q(q32, hd)
@@ -503,7 +504,10 @@ def test_attention(B, n, heads, hd, dtype, full, pre):
 def test_attention_moving_reference(B, n, hd, kind, pre):
     """The kernel's softmax reference moves only when a tile's probabilities
     would exceed a bound; these inputs make it move after the first tile.
-    ramp: key rows scaled by 1 + 6 j / n, so later keys score ever higher;
+    ramp: key rows scaled by 1 + 60 j / n, so later keys score ever higher
+    (the logits' std grows from about 0.5 to about 30 in log2 units: for
+    nearly every query a later tile's probabilities pass the kernel's bound
+    of 2^48 against the first tile's reference, once, checked on the CPU);
     huge: queries scaled by 300 (logits of std ~100 in log2 units), where
     exponentials taken without moving the reference would overflow."""
     import torch
@@ -513,7 +517,7 @@ def test_attention_moving_reference(B, n, hd, kind, pre):
     q = _f32((n, D), 1.0, 821, "x") * 0.6
     k = _f32((n, D), 1.0, 821, "c") * 0.6
     if kind == "ramp":
-        k = k * (1.0 + 6.0 * np.arange(n, dtype=np.float32)[:, None] / n)
+        k = k * (1.0 + 60.0 * np.arange(n, dtype=np.float32)[:, None] / n)
     else:
         q = q * 300.0
     q_in, q_ref = (_ht(q, "bf16"), None) if not pre else _prescaled_q(q, hd)
